@@ -1,0 +1,346 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+None of these checks retypes the oracle's formula: each compares it with a
+value printed on a page, a closed form, an invariant the pages state, or an
+independent library routine (torch's scaled_dot_product_attention in fp64).
+The pins are written as functions of the oracle module so that
+test_oracle_mutations.py can run them against oracles with planted mistakes.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.attn_oracle as orc_mod
+from golden import load
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+RNG = np.random.default_rng(20260724)
+
+
+def _heads(x):
+    """[n, d] -> [1, 1, n, d]"""
+    return np.asarray(x, dtype=np.float64)[None, None]
+
+
+# ---------------------------------------------------------------- page values
+def pin_p4_two_token_example(orc):
+    """baxdailygit page, "셀프 어텐션 수치 계산 시뮬레이션" steps 2-5."""
+    g = load("p4_two_token_example.txt")
+    Q, K, V = g["Q"], g["K"], g["V"]
+    O, W = orc.attention(_heads(Q), _heads(K), _heads(V), return_weights=True)
+    W, O = W[0, 0], O[0, 0]
+    # step 4: the weights, printed to 2 decimals
+    assert np.array_equal(np.round(W, 2), g["A"]), W
+    # steps 2-3 fix the scaled logits; log-weight differences recover them
+    # (softmax is shift invariant): s_i1 - s_i0 = log(w_i1 / w_i0)
+    diff = np.log(W[:, 1] / W[:, 0])
+    page = g["scaled"][:, 1] - g["scaled"][:, 0]
+    assert np.allclose(diff, page, atol=1e-3), (diff, page)
+    # step 5 was computed from A rounded to 2 dp: |dZ| <= 0.005 * sum_j |V_j|
+    bound = 0.005 * np.abs(V).sum(axis=0) + 5e-4
+    assert np.all(np.abs(O - g["Z"]) <= bound), (O, g["Z"])
+    # and the page's own step 5 is the rounded weights times V
+    assert np.allclose(np.round(W, 2) @ V, g["Z"], atol=5e-4)
+
+
+def pin_p5_unmasked_and_causal(orc):
+    """sj-techlog page, "직접 검증": unmasked and causal 3-token run, 6 dp."""
+    g = load("p5_verification_run.txt")
+    q, k, v = g["q"], g["k"], g["v"]
+    tol = 1e-6  # printed with round(x, 6)
+    assert abs(math.sqrt(2) - g["scale_sqrt_dk"]) < tol
+    O, W = orc.attention(_heads(q), _heads(k), _heads(v), return_weights=True)
+    assert np.allclose(W[0, 0, 0], g["unmasked_w0"], atol=tol)
+    assert np.allclose(O[0, 0, 0], g["unmasked_out0"], atol=tol)
+    Oc, Wc = orc.attention(_heads(q), _heads(k), _heads(v), mask_kind=orc.MASK_CAUSAL,
+                           return_weights=True)
+    for i in range(3):
+        assert np.allclose(Wc[0, 0, i], g[f"causal_w{i}"], atol=tol), (i, Wc[0, 0, i])
+        assert np.allclose(Oc[0, 0, i], g[f"causal_out{i}"], atol=tol), (i, Oc[0, 0, i])
+
+
+def pin_p5_mask_before_softmax(orc):
+    """sj-techlog page: masking *after* softmax is the page's wrong variant
+    (weights sum to 0.401112, output [4.011121, 0]); the oracle must reproduce
+    that number from its unmasked weights and must not produce it as its
+    causal answer."""
+    g = load("p5_verification_run.txt")
+    q, k, v = g["q"], g["k"], g["v"]
+    _, W = orc.attention(_heads(q), _heads(k), _heads(v), return_weights=True)
+    wrong = np.array([W[0, 0, 0, 0], 0.0, 0.0])
+    assert abs(wrong.sum() - g["wrong_post_softmax_sum"]) < 1e-6
+    assert np.allclose(wrong @ v, g["wrong_post_softmax_out0"], atol=1e-6)
+    Oc = orc.attention(_heads(q), _heads(k), _heads(v), mask_kind=orc.MASK_CAUSAL)
+    assert not np.allclose(Oc[0, 0, 0], g["wrong_post_softmax_out0"], atol=1e-2)
+    assert np.array_equal(Oc[0, 0, 0], v[0])
+
+
+def pin_pe_values(orc):
+    """sj-techlog page "직접 검증" (6 dp) and baxdailygit page PE simulation (2 dp)."""
+    g = load("p5_verification_run.txt")
+    assert np.allclose(orc.sinusoidal_pe(0, 4), g["PE_pos0_d4"], atol=1e-6)
+    assert np.allclose(orc.sinusoidal_pe(1, 4), g["PE_pos1_d4"], atol=1e-6)
+    p = load("p4_positional_encoding.txt")
+    d = int(p["d_model"])
+    for pos in range(3):
+        pe = orc.sinusoidal_pe(pos, d)
+        assert np.allclose(pe, p[f"PE{pos}"], atol=5e-3 + 1e-12), (pos, pe)
+        # embedding + PE; the page added the rounded PE, so allow its rounding
+        assert np.allclose(p[f"emb{pos}"] + pe, p[f"in{pos}"], atol=5e-3 + 1e-9)
+
+
+def pin_pe_rotation(orc):
+    """kimjiil page §3.5 fold-out: PE_{pos+k} = M(k) PE_pos with 2x2 blocks
+    [[cos wk, sin wk], [-sin wk, cos wk]] on each (sin, cos) pair, w_i =
+    10000^(-2i/d_model), independent of pos."""
+    d = 512
+    w = 10000.0 ** (-np.arange(0, d, 2) / d)
+    for k in (1, 3, 17, 250):
+        c, s = np.cos(w * k), np.sin(w * k)
+        for pos in (0, 5, 63, 1000):
+            a = orc.sinusoidal_pe(pos, d)
+            b = orc.sinusoidal_pe(pos + k, d)
+            sin_p, cos_p = a[0::2], a[1::2]
+            assert np.allclose(b[0::2], c * sin_p + s * cos_p, atol=1e-9)
+            assert np.allclose(b[1::2], -s * sin_p + c * cos_p, atol=1e-9)
+
+
+def pin_default_scale_variance(orc):
+    """kimjiil page §3.2.1 fold-out: with q, k iid N(0,1), Var(q.k) = d_k and
+    the 1/sqrt(d_k) scale brings the logits to variance 1.  The oracle's
+    default scale is read back through its weights: for two keys,
+    log(w1/w0) = s1 - s0 has variance 2 * Var(s) = 2."""
+    rng = np.random.default_rng(7)
+    n, d = 20000, 64
+    Q = rng.standard_normal((1, 1, n, d))
+    K = rng.standard_normal((1, n, 2, d))  # a fresh key pair per query row
+    ratios = np.empty(n)
+    for i in range(0, n, 2000):
+        _, W = orc.attention(Q[:, :, i:i + 2000].transpose(0, 2, 1, 3),
+                             K[:, i:i + 2000], np.zeros((1, 2000, 2, d)),
+                             return_weights=True)
+        ratios[i:i + 2000] = np.log(W[:, :, 0, 1] / W[:, :, 0, 0])[0]
+    var = ratios.var()
+    # sampling sd of the variance estimate: 2 * sqrt(2/n) ~ 0.02
+    assert abs(var - 2.0) < 0.1, var
+
+
+def pin_rows_sum_to_one(orc):
+    """baxdailygit page step 4 / sj-techlog Eq.(1) table: each softmax row
+    sums to 1, under every mask; a ones column of V gives an output of 1."""
+    B, H, n, d = 3, 2, 9, 8
+    Q, K, V = (RNG.standard_normal((B, H, n, d)) for _ in range(3))
+    V[..., 0] = 1.0
+    kv = np.array([9, 4, 1])
+    for mask in (0, 1, 2, 3):
+        O, W = orc.attention(Q, K, V, mask_kind=mask, kv_lens=kv, return_weights=True)
+        assert np.allclose(W.sum(-1), 1.0, atol=1e-12)
+        assert np.allclose(O[..., 0], 1.0, atol=1e-12)
+
+
+def pin_masked_weight_exactly_zero(orc):
+    """kimjiil page §3.2.3: illegal connections get -inf logits, so their
+    weight after softmax is exactly 0; sj-techlog page: no weight on pads."""
+    B, H, n, d = 2, 2, 7, 8
+    Q, K, V = (RNG.standard_normal((B, H, n, d)) for _ in range(3))
+    kv = np.array([5, 2])
+    _, W = orc.attention(Q, K, V, mask_kind=3, kv_lens=kv, return_weights=True)
+    for b in range(B):
+        for i in range(n):
+            for j in range(n):
+                if j > i or j >= kv[b]:
+                    assert np.all(W[b, :, i, j] == 0.0)
+                else:
+                    assert np.all(W[b, :, i, j] > 0.0)
+
+
+def pin_causal_prefix_invariance(orc):
+    """kimjiil page §3.1 (position i depends only on outputs before it) and
+    sj-techlog page failure section 2: rows <= i do not change, bit for bit,
+    when any Q/K/V row after i is perturbed -- even to NaN."""
+    n, d = 12, 8
+    Q, K, V = (RNG.standard_normal((1, 2, n, d)) for _ in range(3))
+    O = orc.attention(Q, K, V, mask_kind=orc.MASK_CAUSAL)
+    for i in (0, 4, 10):
+        Q2, K2, V2 = Q.copy(), K.copy(), V.copy()
+        Q2[:, :, i + 1:] = 1e3 * RNG.standard_normal(Q2[:, :, i + 1:].shape)
+        K2[:, :, i + 1:] = np.nan
+        V2[:, :, i + 1:] = np.inf
+        O2 = orc.attention(Q2, K2, V2, mask_kind=orc.MASK_CAUSAL)
+        assert np.array_equal(O[:, :, :i + 1], O2[:, :, :i + 1])
+
+
+def pin_padding_invariance(orc):
+    """sj-techlog page: no attention to pad; K/V rows at or beyond kv_len
+    (even NaN) cannot change the output; padded query rows are 0."""
+    B, H, n, d = 3, 2, 10, 8
+    Q, K, V = (RNG.standard_normal((B, H, n, d)) for _ in range(3))
+    kv = np.array([10, 3, 7])
+    ql = np.array([10, 3, 5])
+    O = orc.attention(Q, K, V, mask_kind=1, kv_lens=kv, q_lens=ql)
+    K2, V2 = K.copy(), V.copy()
+    for b in range(B):
+        K2[b, :, kv[b]:] = np.nan
+        V2[b, :, kv[b]:] = np.nan
+    O2 = orc.attention(Q, K2, V2, mask_kind=1, kv_lens=kv, q_lens=ql)
+    assert np.array_equal(O, O2)
+    for b in range(B):
+        assert np.all(O[b, :, ql[b]:] == 0.0)
+        assert np.all(np.abs(O[b, :, :ql[b]]).sum(-1) > 0)
+
+
+def pin_permutation(orc):
+    """baxdailygit page ("I love cats" / "cats love I") and sj-techlog page
+    failure section 1: without positions attention is order-blind.  Jointly
+    permuting Q, K, V rows permutes O's rows; permuting K, V rows together
+    leaves O unchanged."""
+    n, d = 11, 8
+    Q, K, V = (RNG.standard_normal((1, 1, n, d)) for _ in range(3))
+    O = orc.attention(Q, K, V)
+    p = RNG.permutation(n)
+    O2 = orc.attention(Q[:, :, p], K[:, :, p], V[:, :, p])
+    assert np.allclose(O2, O[:, :, p], atol=1e-12)
+    O3 = orc.attention(Q, K[:, :, p], V[:, :, p])
+    assert np.allclose(O3, O, atol=1e-12)
+
+
+def pin_one_hot_key(orc):
+    """A single allowed key takes weight 1 (sj-techlog page: causal position 0
+    sees only its own V, [10, 0]); with a dominant logit the output tends to
+    that key's value row."""
+    n, d = 6, 8
+    Q, K, V = (RNG.standard_normal((2, 2, n, d)) for _ in range(3))
+    O = orc.attention(Q, K, V, mask_kind=1, kv_lens=np.array([1, 1]))
+    assert np.array_equal(O, np.broadcast_to(V[:, :, :1], O.shape))
+    Oc = orc.attention(Q, K, V, mask_kind=2)
+    assert np.array_equal(Oc[:, :, 0], V[:, :, 0])
+    # approximate one-hot: K rows alpha * e_j, q = e_j
+    Kd = np.zeros((1, 1, n, n))
+    Kd[0, 0] = 60.0 * np.eye(n)
+    Qd = np.eye(n)[None, None]
+    Vd = RNG.standard_normal((1, 1, n, 4))
+    Od = orc.attention(Qd, Kd, Vd, scale=1.0)
+    assert np.allclose(Od[0, 0], Vd[0, 0], atol=1e-20 + 1e-12)
+
+
+def pin_uniform_scores(orc):
+    """Q = 0 makes every allowed logit equal, so O is the plain mean of the
+    allowed value rows (softmax of a constant row)."""
+    B, H, n, d = 2, 2, 8, 4
+    K, V = (RNG.standard_normal((B, H, n, d)) for _ in range(2))
+    Q = np.zeros((B, H, n, d))
+    kv = np.array([8, 5])
+    O = orc.attention(Q, K, V, mask_kind=3, kv_lens=kv)
+    for b in range(B):
+        for i in range(n):
+            lim = min(i + 1, kv[b])
+            assert np.allclose(O[b, :, i], V[b, :, :lim].mean(axis=1), atol=1e-12)
+
+
+def pin_large_logits_stable(orc):
+    """The max-shifted softmax (the verification script on the sj-techlog
+    page subtracts the max finite score) stays finite for logits far beyond
+    exp's range, and reaches the one-hot limit."""
+    n, d = 5, 4
+    Q, K, V = (RNG.standard_normal((1, 1, n, d)) for _ in range(3))
+    O = orc.attention(Q, K, V, scale=1e4)
+    assert np.all(np.isfinite(O))
+    S = (Q[0, 0] @ K[0, 0].T)
+    assert np.allclose(O[0, 0], V[0, 0][S.argmax(axis=1)], atol=1e-12)
+
+
+def pin_library_crosscheck(orc):
+    """Brute force on tiny inputs against an independent library routine:
+    torch's scaled_dot_product_attention in float64 on the CPU with a boolean
+    mask, over every mask kind and random lengths."""
+    rng = np.random.default_rng(11)
+    for trial in range(40):
+        B, H = rng.integers(1, 4), rng.integers(1, 3)
+        mask = int(rng.integers(0, 4))
+        n_q = int(rng.integers(1, 9))
+        n_k = n_q if mask & 2 else int(rng.integers(1, 9))
+        d = int(rng.choice([1, 2, 4, 8]))
+        Q = rng.standard_normal((B, H, n_q, d))
+        K = rng.standard_normal((B, H, n_k, d))
+        V = rng.standard_normal((B, H, n_k, int(rng.choice([1, 3, 8]))))
+        kv = rng.integers(1, n_k + 1, size=B)
+        ql = rng.integers(1, n_q + 1, size=B)
+        scale = float(rng.choice([0.125, 1.0 / math.sqrt(d), 2.0]))
+        O = orc.attention(Q, K, V, mask_kind=mask, kv_lens=kv, q_lens=ql, scale=scale)
+        allowed = np.ones((B, 1, n_q, n_k), dtype=bool)
+        if mask & 1:
+            allowed &= (np.arange(n_k)[None, :] < kv[:, None])[:, None, None, :]
+        if mask & 2:
+            allowed &= np.tril(np.ones((n_q, n_k), dtype=bool))[None, None]
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(Q), torch.from_numpy(K), torch.from_numpy(V),
+            attn_mask=torch.from_numpy(allowed), scale=scale).numpy()
+        for b in range(B):
+            assert np.allclose(O[b, :, :ql[b]], ref[b, :, :ql[b]], atol=1e-12), trial
+            assert np.all(O[b, :, ql[b]:] == 0.0)
+
+
+def pin_decode_equals_recompute(orc):
+    """kimjiil page §3.7 / sj-techlog page KV cache: the cached step computes
+    the same thing as recomputing the causal self-attention of the whole
+    prefix; the new token's own K/V is part of the cache."""
+    n, d, B, H = 10, 8, 3, 2
+    Q, K, V = (RNG.standard_normal((B, H, n, d)) for _ in range(3))
+    full = orc.attention(Q, K, V, mask_kind=orc.MASK_CAUSAL)
+    lens = np.array([1, 6, 10])
+    q = np.stack([Q[b, :, lens[b] - 1] for b in range(B)])[:, :, None]
+    Kc = K.copy()
+    Vc = V.copy()
+    for b in range(B):  # rows past the valid length hold garbage
+        Kc[b, :, lens[b]:] = 1e6
+        Vc[b, :, lens[b]:] = np.nan
+    out = orc.decode(q, Kc, Vc, lens)
+    for b in range(B):
+        assert np.allclose(out[b, :, 0], full[b, :, lens[b] - 1], atol=1e-13)
+
+
+def pin_kv_cache_size(orc):
+    """sj-techlog page KV cache arithmetic: 2 x 6 x 128 x 512 scalars,
+    3.0 MiB in fp32 and 1.5 MiB in fp16."""
+    g = load("p5_verification_run.txt")
+    n = orc.kv_cache_scalars(6, 128, 512)
+    assert n == int(g["kv_cache_scalars"])
+    assert round(n * 4 / 2 ** 20, 3) == g["kv_cache_mib_fp32"]
+    assert round(n * 2 / 2 ** 20, 3) == g["kv_cache_mib_fp16"]
+
+
+PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=[p.__name__[4:] for p in PINS])
+def test_pin(pin):
+    pin(orc_mod)
+
+
+def test_monte_carlo_dot_product_variance():
+    """kimjiil page §3.2.1 fold-out and sj-techlog page "왜 √d_k로 나누는가":
+    E[q.k] = 0 and Var(q.k) = d_k for iid N(0,1) entries; after 1/sqrt(d_k)
+    the variance is 1.  10^6 samples: the sd of the variance estimate is
+    about 0.14 %, so +-1 % is a > 6 sigma band."""
+    rng = np.random.default_rng(123)
+    d = 64
+    s = np.empty(10 ** 6)
+    for i in range(0, 10 ** 6, 10 ** 5):
+        q = rng.standard_normal((10 ** 5, d))
+        k = rng.standard_normal((10 ** 5, d))
+        s[i:i + 10 ** 5] = (q * k).sum(1)
+    assert abs(s.mean()) < 0.05
+    assert abs(s.var() / d - 1) < 0.01
+    assert abs((s / math.sqrt(d)).var() - 1) < 0.01
+
+
+def test_flop_model_long_causal():
+    """Only allowed pairs are counted: n(n+1)/2 per head under the causal
+    mask; 4 d flops per pair (kimjiil page §4 Table 1: O(n^2 d))."""
+    import workloads
+    pairs = workloads.allowed_pairs(2, 8192, 8192, 1)
+    assert pairs == 8192 * 8193 // 2
+    assert orc_mod.attention_flops(pairs * 16, 64) == 137_455_730_688

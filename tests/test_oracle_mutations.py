@@ -1,0 +1,165 @@
+"""Planted mistakes in the oracle (on the CPU) must each fail at least one pin.
+
+Each mutant replaces one step of the oracle with a plausible slip -- an
+off-by-one mask, a transposed operand, a wrong scale, masking after the
+softmax, a dropped term or sign -- and the full pin suite of test_oracle.py
+is run against it.  A mutant that passes every pin would mean the pins do not
+constrain that step.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle.attn_oracle as orc
+from test_oracle import PINS
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+_row = orc.attention_row
+_allowed = orc.allowed_keys
+_attention = orc.attention
+_decode = orc.decode
+_pe = orc.sinusoidal_pe
+
+
+def m_causal_strict(i, n_k, kv_len, causal):
+    j = np.arange(n_k)
+    ok = j < kv_len
+    if causal:
+        ok &= j < i  # off by one: excludes the diagonal
+    return ok
+
+
+def m_padding_inclusive(i, n_k, kv_len, causal):
+    j = np.arange(n_k)
+    ok = j <= kv_len  # off by one: admits the first pad
+    if causal:
+        ok &= j <= i
+    return ok
+
+
+def m_causal_transposed(i, n_k, kv_len, causal):
+    j = np.arange(n_k)
+    ok = j < kv_len
+    if causal:
+        ok &= j >= i  # upper instead of lower triangle
+    return ok
+
+
+def m_no_max_shift(q, K, V, allowed, scale, return_weights=False):
+    q, K, V = (np.asarray(a, dtype=np.float64) for a in (q, K, V))
+    idx = np.flatnonzero(allowed)
+    w_full = np.zeros(K.shape[0])
+    if idx.size == 0:
+        out = np.zeros(V.shape[1])
+        return (out, w_full) if return_weights else out
+    e = np.exp(scale * (K[idx] @ q))  # no pivot: overflows for large logits
+    w = e / e.sum()
+    out = w @ V[idx]
+    w_full[idx] = w
+    return (out, w_full) if return_weights else out
+
+
+def _row_variant(kind):
+    def row(q, K, V, allowed, scale, return_weights=False):
+        q, K, V = (np.asarray(a, dtype=np.float64) for a in (q, K, V))
+        n_k = K.shape[0]
+        w_full = np.zeros(n_k)
+        if kind == "mask_after_softmax":
+            s = scale * (K @ q)
+            e = np.exp(s - s.max())
+            w = e / e.sum()
+            w = np.where(allowed, w, 0.0)  # zeroed after softmax, not renormalised
+            out = w @ np.where(allowed[:, None], V, 0.0)
+            return (out, w) if return_weights else out
+        idx = np.flatnonzero(allowed)
+        if idx.size == 0:
+            out = np.zeros(V.shape[1])
+            return (out, w_full) if return_weights else out
+        s = scale * (K[idx] @ q)
+        if kind == "no_normalise":
+            w = np.exp(s - s.max())
+        elif kind == "sign":
+            e = np.exp(s.max() - s)
+            w = e / e.sum()
+        elif kind == "value_of_query":
+            e = np.exp(s - s.max())
+            w = e / e.sum()
+            out = w @ K[idx]  # sums the keys instead of the values
+            w_full[idx] = w
+            return (out, w_full) if return_weights else out
+        else:
+            raise AssertionError(kind)
+        out = w @ V[idx]
+        w_full[idx] = w
+        return (out, w_full) if return_weights else out
+    return row
+
+
+def m_swap_qk(Q, K, V, *a, **kw):
+    # transposed operand: scores K Q^T instead of Q K^T (square cases only)
+    if np.shape(Q) == np.shape(K):
+        Q, K = K, Q
+    return _attention(Q, K, V, *a, **kw)
+
+
+def m_scale_one_over_dk(Q, K, V, mask_kind=0, q_lens=None, kv_lens=None, scale=None, **kw):
+    if scale is None:
+        scale = 1.0 / np.shape(Q)[-1]  # 1/d_k instead of 1/sqrt(d_k)
+    return _attention(Q, K, V, mask_kind, q_lens, kv_lens, scale, **kw)
+
+
+def m_ignore_q_lens(Q, K, V, mask_kind=0, q_lens=None, kv_lens=None, scale=None, **kw):
+    return _attention(Q, K, V, mask_kind, None, kv_lens, scale, **kw)
+
+
+def m_decode_without_new_token(q, Kc, Vc, kv_lens, scale=None, pairs=None):
+    return _decode(q, Kc, Vc, np.maximum(np.asarray(kv_lens) - 1, 1), scale, pairs)
+
+
+def m_pe_swapped(pos, d_model):
+    out = np.zeros(d_model)
+    for dim in range(d_model):
+        angle = pos / (10000.0 ** ((2 * (dim // 2)) / d_model))
+        out[dim] = math.cos(angle) if dim % 2 == 0 else math.sin(angle)
+    return out
+
+
+def m_pe_exponent(pos, d_model):
+    out = np.zeros(d_model)
+    for dim in range(d_model):
+        angle = pos / (10000.0 ** ((dim // 2) / d_model))  # i instead of 2i
+        out[dim] = math.sin(angle) if dim % 2 == 0 else math.cos(angle)
+    return out
+
+
+MUTANTS = {
+    "causal_excludes_diagonal": ("allowed_keys", m_causal_strict),
+    "padding_admits_first_pad": ("allowed_keys", m_padding_inclusive),
+    "causal_upper_triangle": ("allowed_keys", m_causal_transposed),
+    "no_max_shift": ("attention_row", m_no_max_shift),
+    "mask_after_softmax": ("attention_row", _row_variant("mask_after_softmax")),
+    "no_normalisation": ("attention_row", _row_variant("no_normalise")),
+    "sign_flip_in_exp": ("attention_row", _row_variant("sign")),
+    "sums_keys_not_values": ("attention_row", _row_variant("value_of_query")),
+    "scores_K_Qt": ("attention", m_swap_qk),
+    "scale_1_over_dk": ("attention", m_scale_one_over_dk),
+    "q_lens_ignored": ("attention", m_ignore_q_lens),
+    "decode_drops_new_token": ("decode", m_decode_without_new_token),
+    "pe_sin_cos_swapped": ("sinusoidal_pe", m_pe_swapped),
+    "pe_exponent_i": ("sinusoidal_pe", m_pe_exponent),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    monkeypatch.setattr(orc, attr, fn)
+    caught = []
+    for pin in PINS:
+        try:
+            pin(orc)
+        except Exception:  # AssertionError or a crash both count as caught
+            caught.append(pin.__name__)
+    assert caught, f"mutant {name} passed every pin"
