@@ -1,0 +1,331 @@
+#!/usr/bin/env python3
+"""Bench of the attention hot path on one MI355X.
+
+One step is one pass of the whole hot path over one batch of each workload
+the metric names ("attention TFLOP/s (bf16 fwd) at n=128 & 8192; KV-cache
+decode HBM GB/s"):
+  encoder_base  bf16 encoder self-attention, key padding, B32 h8 n128
+  decoder_big   bf16 causal self-attention n128 + cross-attention 128->160
+                with source padding, B32 h16
+  long_causal   bf16 causal self-attention B1 h16 n8192
+  kv_decode     bf16 KV-cache decode, B64 h16, cache 4096, L in [1, 4096]
+Inputs are the seeded synthetic tensors of workloads.py, resident in HBM
+before timing starts.  Each leg is bracketed by HIP events on the stream
+the library launches on (torch's current stream); the step is bracketed by
+device synchronisation.  The last step's outputs are sanity-checked against
+sampled rows of the fp64 oracle at the end (outside the timed region).
+
+value = bf16 forward TFLOP/s over the forward legs (algorithmic flops:
+4 d per allowed (query, key) pair, masked pairs not counted); per-leg
+TFLOP/s and GB/s, the decode GB/s and the roofline fractions are reported
+beside it.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E
+D = 64
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+KERNEL_SOURCES = ["attn_fwd_bf16.hip", "attn_decode.hip", "common.h"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "head_attention_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+# ------------------------------------------------------------------ legs
+class Leg:
+    def __init__(self, name, calls=None, decode=None):
+        self.name = name
+        self.calls = calls or []   # forward calls (dicts of CPU tensors)
+        self.decode = decode       # decode call (dict of CPU tensors)
+        self.flops = 0
+        self.bytes = 0
+
+    def count(self):
+        """Algorithmic flops and bytes (valid Q/K/V rows read, all O rows
+        written, lengths read)."""
+        for c in self.calls:
+            B, H, n_q, _ = c["Q"].shape
+            n_k = c["K"].shape[2]
+            el = c["Q"].element_size()
+            pairs = workloads.allowed_pairs(c["mask"], n_q, n_k, B, c["q_lens"], c["kv_lens"])
+            self.flops += 4 * D * pairs * H
+            ql = n_q * B if c["q_lens"] is None else int(c["q_lens"].sum())
+            kl = n_k * B if not (c["mask"] & 1) else int(c["kv_lens"].clamp(0, n_k).sum())
+            row = H * D * el
+            self.bytes += (ql + 2 * kl + B * n_q) * row
+            self.bytes += 4 * B * ((c["q_lens"] is not None) + (c["kv_lens"] is not None))
+        if self.decode is not None:
+            d = self.decode
+            B, H, _, _ = d["q"].shape
+            el = d["q"].element_size()
+            L = int(d["kv_lens"].sum())
+            self.flops += 4 * D * L * H
+            self.bytes += 2 * L * H * D * el + 2 * B * H * D * el + 4 * B
+
+
+def make_legs():
+    legs = []
+    for name in ("encoder_base", "decoder_big", "long_causal"):
+        legs.append(Leg(name, calls=workloads.make(name)["calls"]))
+    legs.append(Leg("kv_decode", decode=workloads.make("kv_decode")))
+    for leg in legs:
+        leg.count()
+    return legs
+
+
+def to_device(legs):
+    import head_attention_amd as ha
+    for leg in legs:
+        leg.dev_calls = []
+        for c in leg.calls:
+            dc = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in c.items()}
+            dc["O"] = torch.empty_like(dc["Q"])
+            leg.dev_calls.append(dc)
+        if leg.decode is not None:
+            d = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in leg.decode.items()}
+            B, H, _, _ = d["q"].shape
+            n_max = d["Kcache"].shape[2]
+            d["O"] = torch.empty_like(d["q"])
+            d["ws"] = torch.empty(ha.decode_workspace_bytes(B, H, n_max, d["q"].dtype),
+                                  dtype=torch.uint8, device="cuda")
+            leg.dev_decode = d
+        else:
+            leg.dev_decode = None
+
+
+def run_leg(leg):
+    import head_attention_amd as ha
+    for c in leg.dev_calls:
+        ha.forward(c["Q"], c["K"], c["V"], mask_kind=c["mask"], q_lens=c["q_lens"],
+                   kv_lens=c["kv_lens"], scale=c["scale"], out=c["O"])
+    d = leg.dev_decode
+    if d is not None:
+        ha.decode(d["q"], d["Kcache"], d["Vcache"], d["kv_lens"], scale=d["scale"], out=d["O"],
+                  workspace=d["ws"])
+
+
+# --------------------------------------------------------- sanity vs oracle
+def sanity_check(legs):
+    """Sampled rows of the last step's outputs against the fp64 oracle."""
+    import oracle.attn_oracle as orc
+
+    def np64(t):
+        return t.detach().to("cpu", torch.float32).double().numpy()
+
+    worst = 0.0
+    rng = np.random.default_rng(0)
+    for leg in legs:
+        for c, dc in zip(leg.calls, leg.dev_calls):
+            B, H, n_q, _ = c["Q"].shape
+            rows = [(int(rng.integers(B)), int(rng.integers(H)), int(rng.integers(n_q)))
+                    for _ in range(24)]
+            ref = orc.attention(np64(c["Q"]), np64(c["K"]), np64(c["V"]), mask_kind=c["mask"],
+                                q_lens=None if c["q_lens"] is None else c["q_lens"].numpy(),
+                                kv_lens=None if c["kv_lens"] is None else c["kv_lens"].numpy(),
+                                scale=c["scale"], rows=rows)
+            out = np64(dc["O"])
+            worst = max(worst, max(float(np.abs(out[r] - ref[r]).max()) for r in rows))
+        if leg.decode is not None:
+            d = leg.decode
+            pairs = [(int(rng.integers(64)), int(rng.integers(16))) for _ in range(16)]
+            out = np64(leg.dev_decode["O"])
+            for (b, h) in pairs:
+                ref = orc.decode(np64(d["q"][b:b + 1, h:h + 1]), np64(d["Kcache"][b:b + 1, h:h + 1]),
+                                 np64(d["Vcache"][b:b + 1, h:h + 1]), d["kv_lens"][b:b + 1].numpy(),
+                                 scale=d["scale"])
+                worst = max(worst, float(np.abs(out[b, h] - ref[0, 0]).max()))
+    return worst
+
+
+# ------------------------------------------------------------ CPU baseline
+def cpu_baseline(target_s: float = 15.0):
+    """The fp64 oracle as it stands, single-threaded BLAS, on a bounded
+    sample of the long_causal workload: evenly spaced query rows of head 0
+    (each row does its full causal prefix).  Throughput in the same
+    algorithmic flop units as the GPU number."""
+    import oracle.attn_oracle as orc
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    c = workloads.make("long_causal")["calls"][0]
+    Q = c["Q"][:, :1].float().double().numpy()
+    K = c["K"][:, :1].float().double().numpy()
+    V = c["V"][:, :1].float().double().numpy()
+    n = Q.shape[2]
+    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    try:
+        if ctx:
+            ctx.__enter__()
+        # size the sample from a short probe so the run lasts about target_s
+        probe = [(0, 0, i) for i in range(n - 1, 0, -(n // 8))]
+        t0 = time.perf_counter()
+        orc.attention(Q, K, V, mask_kind=orc.MASK_CAUSAL, scale=0.125, rows=probe)
+        per_row = (time.perf_counter() - t0) / len(probe) * 0.5  # average row is half length
+        n_rows = int(max(16, min(n, target_s / max(per_row, 1e-6))))
+        stride = max(1, n // n_rows)
+        rows = [(0, 0, i) for i in range(stride // 2, n, stride)]
+        t0 = time.perf_counter()
+        orc.attention(Q, K, V, mask_kind=orc.MASK_CAUSAL, scale=0.125, rows=rows)
+        dt = time.perf_counter() - t0
+    finally:
+        if ctx:
+            ctx.__exit__(None, None, None)
+    flops = sum(4 * D * (i + 1) for (_, _, i) in rows)
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"long_causal head 0, {len(rows)} query rows evenly spaced over n=8192 "
+                  f"(stride {stride}), full causal prefix each; fp64 NumPy, 1 BLAS thread; "
+                  f"{dt:.1f} s",
+    }
+
+
+# ------------------------------------------------------------------ main
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sanity", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print(json.dumps({"error": "this build runs on one GPU only: the attention path has no "
+                                   "multi-GPU mode (see the sharding notes in DESIGN.md); "
+                                   "run with --gpus 1"}))
+        sys.exit(2)
+
+    import head_attention_amd as ha
+    ha.lib()  # fail loudly if the library is missing
+    torch.cuda.set_device(0)
+    legs = make_legs()
+    to_device(legs)
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        for leg in legs:
+            run_leg(leg)
+    torch.cuda.synchronize()
+
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in legs] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        for j, leg in enumerate(legs):
+            ev[s][j][0].record(stream)
+            run_leg(leg)
+            ev[s][j][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    leg_ms = [sum(ev[s][j][0].elapsed_time(ev[s][j][1]) for s in range(args.steps)) / args.steps
+              for j in range(len(legs))]
+    step_ms = sum(leg_ms)
+    fwd = [j for j, leg in enumerate(legs) if leg.dev_decode is None]
+    fwd_flops = sum(legs[j].flops for j in fwd)
+    fwd_ms = sum(leg_ms[j] for j in fwd)
+    value = fwd_flops / (fwd_ms * 1e-3) / 1e12
+
+    per_leg = {}
+    for leg, ms in zip(legs, leg_ms):
+        per_leg[leg.name] = {
+            "us": round(ms * 1e3, 2),
+            "TFLOP/s": round(leg.flops / (ms * 1e-3) / 1e12, 2),
+            "GB/s": round(leg.bytes / (ms * 1e-3) / 1e9, 1),
+            "alg_flops": leg.flops,
+            "alg_bytes": leg.bytes,
+        }
+    lc = legs[[l.name for l in legs].index("long_causal")]
+    kd = legs[[l.name for l in legs].index("kv_decode")]
+    lc_ms = leg_ms[legs.index(lc)]
+    kd_ms = leg_ms[legs.index(kd)]
+    lc_tflops = lc.flops / (lc_ms * 1e-3) / 1e12
+    kd_gbps = kd.bytes / (kd_ms * 1e-3) / 1e9
+
+    traffic = None
+    try:
+        with open(TRAFFIC_FILE) as f:
+            tc = json.load(f)
+        if tc.get("kernel_source_hash") == kernel_source_hash():
+            traffic = tc.get("long_causal_fwd_bytes_per_launch")
+    except (OSError, ValueError):
+        pass
+
+    out = {
+        "metric": "attention TFLOP/s (bf16 fwd) at n=128 & 8192; KV-cache decode HBM GB/s",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "wall_ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1), workloads.py)",
+        "config": {
+            "workload": "attention hot path: encoder self-attn B32 h8 n128 key-padding + "
+                        "decoder causal self n128 & cross 128->160 B32 h16 + causal self "
+                        "B1 h16 n8192 + KV decode B64 h16 cache 4096; d=64",
+            "value_covers": "bf16 forward legs (n=128 and n=8192)",
+            "decode_GBps": round(kd_gbps, 1),
+            "long_causal_TFLOPs": round(lc_tflops, 2),
+            "legs": per_leg,
+        },
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "attn_fwd_bf16_kernel<causal> on long_causal (B1 h16 n8192)",
+            "achieved": round(lc_tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(lc_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+        },
+        "roofline_decode": {
+            "bound": "hbm",
+            "kernel": "decode_partial_kernel + decode_merge_kernel on kv_decode",
+            "achieved": round(kd_gbps, 1),
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": round(kd_gbps / PEAK_HBM_GBPS, 4),
+        },
+    }
+    if not args.no_sanity:
+        out["sanity_max_abs_err_vs_oracle"] = round(sanity_check(legs), 6)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

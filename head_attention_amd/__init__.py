@@ -1,0 +1,23 @@
+"""MI355X-native scaled dot-product attention (gfx950 HIP kernels behind a C ABI).
+
+    from head_attention_amd import forward, decode
+    O = forward(Q, K, V, mask_kind=ATTN_MASK_CAUSAL, scale=0.125)
+
+The C ABI is include/headattn.h; libheadattn.so is built in-tree with
+`python -m head_attention_amd.build`.
+"""
+from ._binding import (  # noqa: F401
+    ATTN_BF16,
+    ATTN_F32,
+    ATTN_MASK_CAUSAL,
+    ATTN_MASK_KEY_PADDING,
+    ATTN_MASK_NONE,
+    LIB_PATH,
+    AttnError,
+    attn_layout,
+    decode,
+    decode_workspace_bytes,
+    forward,
+    lib,
+    status_string,
+)

@@ -1,0 +1,186 @@
+"""ctypes binding of libheadattn.so: argument marshalling only.
+
+Every step of the attention path runs in the library's HIP kernels; this
+module only checks that torch tensors have the layout the C ABI documents
+(contiguous [B, h, n, 64], on the GPU, matching dtypes), allocates outputs and
+workspaces with torch (plumbing), passes raw device pointers plus torch's
+current HIP stream, and turns a non-zero attn_status into an exception.
+There is no fallback: if the library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libheadattn.so")
+
+ATTN_BF16 = 0
+ATTN_F32 = 1
+ATTN_MASK_NONE = 0
+ATTN_MASK_KEY_PADDING = 1
+ATTN_MASK_CAUSAL = 2
+
+STATUS_NAMES = {
+    0: "ATTN_OK", 1: "ATTN_ERR_NULL_POINTER", 2: "ATTN_ERR_BAD_SHAPE", 3: "ATTN_ERR_BAD_DTYPE",
+    4: "ATTN_ERR_BAD_MASK", 5: "ATTN_ERR_BAD_LENGTHS", 6: "ATTN_ERR_BAD_SCALE",
+    7: "ATTN_ERR_WORKSPACE", 8: "ATTN_ERR_HIP",
+}
+
+
+class attn_layout(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("h", ctypes.c_int32), ("n_q", ctypes.c_int32),
+                ("n_k", ctypes.c_int32), ("d", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = f"{where}: {status_string(status)}"
+        if status == 8:
+            msg += f" ({lib().attn_last_hip_error().decode()})"
+        super().__init__(msg)
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libheadattn.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m head_attention_amd.build` "
+                "(there is no fallback implementation)")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32p = ctypes.c_void_p, ctypes.c_void_p
+        L.attn_forward.argtypes = [vp, vp, vp, attn_layout, ctypes.c_int32, i32p, i32p,
+                                   ctypes.c_float, vp, vp]
+        L.attn_forward.restype = ctypes.c_int
+        L.attn_decode.argtypes = [vp, vp, vp, attn_layout, i32p, ctypes.c_float, vp, vp,
+                                  ctypes.c_size_t, vp]
+        L.attn_decode.restype = ctypes.c_int
+        L.attn_decode_workspace_bytes.argtypes = [attn_layout]
+        L.attn_decode_workspace_bytes.restype = ctypes.c_size_t
+        L.attn_status_string.argtypes = [ctypes.c_int]
+        L.attn_status_string.restype = ctypes.c_char_p
+        L.attn_last_hip_error.argtypes = []
+        L.attn_last_hip_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().attn_status_string(int(status)).decode()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    if t.dtype == torch.float32:
+        return ATTN_F32
+    raise TypeError(f"attention tensors must be bfloat16 or float32, got {t.dtype}")
+
+
+def _check_tensor(name: str, t: torch.Tensor, dtype) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU, got {t.device}")
+    if t.dim() != 4:
+        raise ValueError(f"{name} must be [B, h, n, d], got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def _lens_ptr(name: str, t, B: int):
+    if t is None:
+        return None
+    if t.device.type != "cuda" or t.dtype != torch.int32 or t.dim() != 1 or t.numel() != B \
+            or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous int32 GPU tensor of shape [{B}]")
+    return t.data_ptr()
+
+
+def _stream_handle(stream) -> int | None:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream or None
+
+
+def forward(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, mask_kind: int = ATTN_MASK_NONE,
+            q_lens: torch.Tensor | None = None, kv_lens: torch.Tensor | None = None,
+            scale: float | None = None, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """attn_forward: O = softmax(Q K^T * scale + M) V per (b, h), on the GPU.
+
+    Q [B, h, n_q, 64]; K, V [B, h, n_k, 64]; all bf16 or all fp32, contiguous.
+    q_lens / kv_lens: int32 GPU tensors [B] or None (see include/headattn.h).
+    scale defaults to 1/sqrt(d).  Runs on torch's current stream (or `stream`).
+    """
+    dt = Q.dtype
+    for n, t in (("Q", Q), ("K", K), ("V", V)):
+        _check_tensor(n, t, dt)
+    B, H, n_q, d = Q.shape
+    n_k = K.shape[2]
+    if tuple(K.shape) != (B, H, n_k, d) or tuple(V.shape) != (B, H, n_k, d):
+        raise ValueError(f"K {tuple(K.shape)} / V {tuple(V.shape)} do not match Q {tuple(Q.shape)}")
+    if out is None:
+        out = torch.empty_like(Q)
+    else:
+        _check_tensor("out", out, dt)
+        if out.shape != Q.shape:
+            raise ValueError("out must have Q's shape")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    layout = attn_layout(B, H, n_q, n_k, d, _dtype_code(Q))
+    st = lib().attn_forward(Q.data_ptr(), K.data_ptr(), V.data_ptr(), layout, int(mask_kind),
+                            _lens_ptr("q_lens", q_lens, B), _lens_ptr("kv_lens", kv_lens, B),
+                            float(scale), out.data_ptr(), _stream_handle(stream))
+    if st != 0:
+        raise AttnError(st, "attn_forward")
+    return out
+
+
+def decode_workspace_bytes(B: int, h: int, n_max: int, dtype=torch.bfloat16, d: int = 64) -> int:
+    code = ATTN_BF16 if dtype == torch.bfloat16 else ATTN_F32
+    return int(lib().attn_decode_workspace_bytes(attn_layout(B, h, 1, n_max, d, code)))
+
+
+def decode(q: torch.Tensor, Kcache: torch.Tensor, Vcache: torch.Tensor, kv_lens: torch.Tensor,
+           scale: float | None = None, out: torch.Tensor | None = None,
+           workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """attn_decode: one KV-cache decode step on the GPU.
+
+    q [B, h, 1, 64]; Kcache, Vcache [B, h, n_max, 64]; kv_lens int32 GPU [B]
+    counts valid cache rows including the new token.  `workspace` (a GPU
+    tensor of at least decode_workspace_bytes(...) bytes) is allocated with
+    torch when not given.
+    """
+    dt = q.dtype
+    for n, t in (("q", q), ("Kcache", Kcache), ("Vcache", Vcache)):
+        _check_tensor(n, t, dt)
+    B, H, one, d = q.shape
+    n_max = Kcache.shape[2]
+    if one != 1 or tuple(Kcache.shape) != (B, H, n_max, d) or Vcache.shape != Kcache.shape:
+        raise ValueError("q must be [B, h, 1, d] and the caches [B, h, n_max, d]")
+    layout = attn_layout(B, H, 1, n_max, d, _dtype_code(q))
+    need = int(lib().attn_decode_workspace_bytes(layout))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_tensor("out", out, dt)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = lib().attn_decode(q.data_ptr(), Kcache.data_ptr(), Vcache.data_ptr(), layout,
+                           _lens_ptr("kv_lens", kv_lens, B), float(scale), out.data_ptr(),
+                           workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                           _stream_handle(stream))
+    if st != 0:
+        raise AttnError(st, "attn_decode")
+    return out

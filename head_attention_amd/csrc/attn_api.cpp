@@ -1,0 +1,186 @@
+// Host entry points of libheadattn.so (the C ABI declared in
+// include/headattn.h): argument validation, kernel selection and launch.
+//
+// Everything here is plain host code.  Validation happens before the first
+// HIP call, so a bad argument is reported without touching a device; a valid
+// call only enqueues work on the caller's stream.
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "common.h"
+#include "headattn.h"
+
+namespace {
+
+using namespace headattn;
+
+thread_local hipError_t g_last_hip = hipSuccess;
+
+bool length_check_enabled() {
+  static std::once_flag once;
+  static bool enabled = false;
+  std::call_once(once, [] {
+    const char* v = std::getenv("ATTN_CHECK");
+    enabled = v != nullptr && std::strcmp(v, "1") == 0;
+  });
+  return enabled;
+}
+
+constexpr int64_t kMaxGrid = 2147483647LL;
+
+// Shape checks common to both entry points.  Sizes must be non-negative and
+// d must be 64; every element count must fit comfortably in int64 and the
+// per-(b, h) row count in int32 (kernels index rows with int).
+attn_status check_layout(const attn_layout& L) {
+  if (L.dtype != ATTN_BF16 && L.dtype != ATTN_F32) return ATTN_ERR_BAD_DTYPE;
+  if (L.B < 0 || L.h < 0 || L.n_q < 0 || L.n_k < 0) return ATTN_ERR_BAD_SHAPE;
+  if (L.d != kHeadDim) return ATTN_ERR_BAD_SHAPE;
+  const long double elems_q = (long double)L.B * L.h * L.n_q * L.d;
+  const long double elems_k = (long double)L.B * L.h * L.n_k * L.d;
+  if (elems_q > 4.0e18L || elems_k > 4.0e18L) return ATTN_ERR_BAD_SHAPE;
+  return ATTN_OK;
+}
+
+hipError_t read_lengths(const int32_t* dev, int n, hipStream_t s, std::vector<int32_t>& out) {
+  out.resize(n);
+  hipError_t e = hipMemcpyAsync(out.data(), dev, sizeof(int32_t) * n, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  return e;
+}
+
+attn_status check_lengths(const int32_t* dev, int B, int n, hipStream_t s) {
+  if (!dev) return ATTN_OK;
+  std::vector<int32_t> h;
+  const hipError_t e = read_lengths(dev, B, s, h);
+  if (e != hipSuccess) {
+    g_last_hip = e;
+    return ATTN_ERR_HIP;
+  }
+  for (int32_t v : h)
+    if (v < 0 || v > n) return ATTN_ERR_BAD_LENGTHS;
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_status_string(attn_status status) {
+  switch (status) {
+    case ATTN_OK: return "ATTN_OK: success";
+    case ATTN_ERR_NULL_POINTER: return "ATTN_ERR_NULL_POINTER: a required pointer is NULL";
+    case ATTN_ERR_BAD_SHAPE: return "ATTN_ERR_BAD_SHAPE: negative size, d != 64, or size overflow";
+    case ATTN_ERR_BAD_DTYPE: return "ATTN_ERR_BAD_DTYPE: dtype must be ATTN_BF16 or ATTN_F32";
+    case ATTN_ERR_BAD_MASK:
+      return "ATTN_ERR_BAD_MASK: unknown mask bits, causal with n_q != n_k, or kv_lens "
+             "given/missing against ATTN_MASK_KEY_PADDING";
+    case ATTN_ERR_BAD_LENGTHS: return "ATTN_ERR_BAD_LENGTHS: a length is outside [0, n]";
+    case ATTN_ERR_BAD_SCALE: return "ATTN_ERR_BAD_SCALE: scale must be finite";
+    case ATTN_ERR_WORKSPACE: return "ATTN_ERR_WORKSPACE: decode workspace missing or too small";
+    case ATTN_ERR_HIP: return "ATTN_ERR_HIP: a HIP runtime call failed";
+  }
+  return "unknown attn_status";
+}
+
+const char* attn_last_hip_error(void) { return hipGetErrorName(g_last_hip); }
+
+attn_status attn_forward(const void* Q, const void* K, const void* V, attn_layout layout,
+                         int32_t mask_kind, const int32_t* q_lens, const int32_t* kv_lens,
+                         float scale, void* O, void* stream) {
+  attn_status st = check_layout(layout);
+  if (st != ATTN_OK) return st;
+  if (mask_kind & ~(ATTN_MASK_KEY_PADDING | ATTN_MASK_CAUSAL)) return ATTN_ERR_BAD_MASK;
+  const bool kpad = (mask_kind & ATTN_MASK_KEY_PADDING) != 0;
+  const bool causal = (mask_kind & ATTN_MASK_CAUSAL) != 0;
+  if (causal && layout.n_q != layout.n_k) return ATTN_ERR_BAD_MASK;
+  if (!kpad && kv_lens != nullptr) return ATTN_ERR_BAD_MASK;
+  if (!std::isfinite(scale)) return ATTN_ERR_BAD_SCALE;
+  const bool empty_out = layout.B == 0 || layout.h == 0 || layout.n_q == 0;
+  if (empty_out) return ATTN_OK;  // nothing to write
+  if (!Q || !O) return ATTN_ERR_NULL_POINTER;
+  if (layout.n_k > 0 && (!K || !V)) return ATTN_ERR_NULL_POINTER;
+  if (kpad && !kv_lens) return ATTN_ERR_NULL_POINTER;
+  if (Q == O || K == O || V == O) return ATTN_ERR_BAD_SHAPE;  // inputs must not alias O
+
+  const int bm = layout.dtype == ATTN_BF16 ? 128 : 64;  // query rows per workgroup
+  const int64_t blocks = (int64_t)((layout.n_q + bm - 1) / bm) * layout.h * layout.B;
+  if (blocks > kMaxGrid) return ATTN_ERR_BAD_SHAPE;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (length_check_enabled()) {
+    if ((st = check_lengths(q_lens, layout.B, layout.n_q, s)) != ATTN_OK) return st;
+    if ((st = check_lengths(kv_lens, layout.B, layout.n_k, s)) != ATTN_OK) return st;
+  }
+
+  FwdArgs a;
+  a.Q = Q;
+  a.K = K;
+  a.V = V;
+  a.O = O;
+  a.q_lens = q_lens;
+  a.kv_lens = kv_lens;
+  a.B = layout.B;
+  a.H = layout.h;
+  a.n_q = layout.n_q;
+  a.n_k = layout.n_k;
+  a.scale = scale;
+  a.causal = causal;
+  const hipError_t e = layout.dtype == ATTN_BF16 ? launch_fwd_bf16(a, s) : launch_fwd_f32(a, s);
+  if (e != hipSuccess) {
+    g_last_hip = e;
+    return ATTN_ERR_HIP;
+  }
+  return ATTN_OK;
+}
+
+size_t attn_decode_workspace_bytes(attn_layout L) {
+  if (check_layout(L) != ATTN_OK || L.n_q != 1) return 0;
+  return (size_t)L.B * L.h * decode_splits(L.n_k) * kPartialStride * sizeof(float);
+}
+
+attn_status attn_decode(const void* q, const void* Kcache, const void* Vcache, attn_layout L,
+                        const int32_t* kv_lens, float scale, void* O, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  attn_status st = check_layout(L);
+  if (st != ATTN_OK) return st;
+  if (L.n_q != 1) return ATTN_ERR_BAD_SHAPE;
+  if (!std::isfinite(scale)) return ATTN_ERR_BAD_SCALE;
+  if (L.B == 0 || L.h == 0) return ATTN_OK;
+  if (!q || !O || !kv_lens) return ATTN_ERR_NULL_POINTER;
+  if (L.n_k > 0 && (!Kcache || !Vcache)) return ATTN_ERR_NULL_POINTER;
+  if (q == O || Kcache == O || Vcache == O) return ATTN_ERR_BAD_SHAPE;
+  const size_t need = attn_decode_workspace_bytes(L);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return ATTN_ERR_WORKSPACE;
+  const int64_t splits = decode_splits(L.n_k);
+  if ((int64_t)L.B * L.h * splits > kMaxGrid || (int64_t)L.B * L.h > kMaxGrid)
+    return ATTN_ERR_BAD_SHAPE;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (length_check_enabled()) {
+    if ((st = check_lengths(kv_lens, L.B, L.n_k, s)) != ATTN_OK) return st;
+  }
+
+  DecodeArgs a;
+  a.q = q;
+  a.Kc = Kcache;
+  a.Vc = Vcache;
+  a.O = O;
+  a.kv_lens = kv_lens;
+  a.work = static_cast<float*>(workspace);
+  a.B = L.B;
+  a.H = L.h;
+  a.n_max = L.n_k;
+  a.n_split = (int)splits;
+  a.scale = scale;
+  const hipError_t e = L.dtype == ATTN_BF16 ? launch_decode_bf16(a, s) : launch_decode_f32(a, s);
+  if (e != hipSuccess) {
+    g_last_hip = e;
+    return ATTN_ERR_HIP;
+  }
+  return ATTN_OK;
+}
+
+}  // extern "C"

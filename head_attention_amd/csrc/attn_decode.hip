@@ -1,0 +1,230 @@
+// KV-cache decode step of attn_decode: one new query per (b, h) against the
+// kv_len valid rows of its cache ("[논문 리뷰]Attention Is All You Need",
+// §3.7: cached K/V mean only the new token's Q is computed per step;
+// "Attention Is All You Need 해부", KV cache section: K,V = the cached
+// 0..t-1 plus the new token's own K,V, appended by the caller).
+//
+// The work is a scan of the cache: every valid K and V row is read once from
+// HBM, and there are only 4 d flops per key, so the kernels are built to keep
+// HBM busy rather than the ALUs.  The cache axis is split into fixed chunks
+// of kDecodeChunk keys, one workgroup per (b, h, chunk), so lengths from 1 to
+// n_max spread evenly over the chip; chunks past kv_len exit at once.
+//
+// Pass 1 (partial): each wave takes 64 keys.  Lanes are grouped by 16-byte
+// slices of a row: LPR lanes cover one 128 B (bf16) / 256 B (fp32) row, so a
+// wave's 16-byte loads cover whole rows, and every lane issues all of its K
+// and V loads before it uses any.  q.k is a slice dot product plus a
+// cross-lane sum; the wave then forms its own softmax partial
+//   m = max_j s_j,  l = sum_j exp2(s_j - m),  acc = sum_j exp2(s_j - m) v_j
+// (s_j in the log2 domain), the workgroup merges its 4 wave partials in LDS,
+// and writes one record (m, l, acc[64]) per chunk.
+// Pass 2 (merge): per (b, h), M = max_s m_s and
+//   O = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s.
+// Both passes are the same exact identity the online softmax uses: partial
+// sums under different pivots combine after rescaling to a common pivot.
+#include "common.h"
+
+namespace headattn {
+namespace {
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+template <typename T>
+struct Elem;
+template <>
+struct Elem<float> {
+  static constexpr int kPerLoad = 4;  // elements per 16-byte load
+  __device__ static void unpack(const uint4& v, float* out) {
+    out[0] = __uint_as_float(v.x); out[1] = __uint_as_float(v.y);
+    out[2] = __uint_as_float(v.z); out[3] = __uint_as_float(v.w);
+  }
+  __device__ static void store(float* dst, const float* v) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dst[i] = v[i];
+  }
+};
+template <>
+struct Elem<__bf16> {
+  static constexpr int kPerLoad = 8;
+  __device__ static void unpack(const uint4& v, float* out) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {  // bf16 -> fp32 is exact: the high 16 bits
+      out[2 * i] = __uint_as_float(w[i] << 16);
+      out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+};
+
+constexpr int kWaveKeys = 64;  // keys per wave per chunk
+
+template <typename T>
+__global__ __launch_bounds__(64 * kDecodeWaves) void decode_partial_kernel(DecodeArgs a) {
+  constexpr int EPL = Elem<T>::kPerLoad;       // elements per lane slice
+  constexpr int LPR = kHeadDim / EPL;          // lanes per cache row
+  constexpr int KPP = 64 / LPR;                // keys per pass of a wave
+  constexpr int NP = kWaveKeys / KPP;          // passes per wave
+
+  const int split = blockIdx.x % a.n_split;
+  const int bh = blockIdx.x / a.n_split;
+  const int b = bh / a.H;
+  const int kv_len = clamp_len(a.kv_lens[b], a.n_max);
+  const int chunk0 = split * kDecodeChunk;
+  if (chunk0 >= kv_len) return;  // workgroup-uniform: past the valid rows
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int sl = lane % LPR;  // slice: d = EPL*sl .. EPL*sl + EPL-1
+  const int kk = lane / LPR;  // key within a pass
+  const int w0 = chunk0 + wave * kWaveKeys;
+
+  const T* q = static_cast<const T*>(a.q) + (size_t)bh * kHeadDim;
+  const T* Kc = static_cast<const T*>(a.Kc) + (size_t)bh * a.n_max * kHeadDim;
+  const T* Vc = static_cast<const T*>(a.Vc) + (size_t)bh * a.n_max * kHeadDim;
+
+  // Issue every K and V load of this wave up front (2 x NP x 16 B per lane).
+  uint4 kraw[NP], vraw[NP];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int key = w0 + p * KPP + kk;
+    if (key < kv_len) {
+      kraw[p] = *reinterpret_cast<const uint4*>(Kc + (size_t)key * kHeadDim + EPL * sl);
+      vraw[p] = *reinterpret_cast<const uint4*>(Vc + (size_t)key * kHeadDim + EPL * sl);
+    } else {  // never read: padded rows may hold anything, even NaN
+      kraw[p] = make_uint4(0, 0, 0, 0);
+      vraw[p] = make_uint4(0, 0, 0, 0);
+    }
+  }
+  float qv[EPL];
+  Elem<T>::unpack(*reinterpret_cast<const uint4*>(q + EPL * sl), qv);
+
+  // c > 0; see the forward kernel for why the floor changes no result.
+  const float c = fmaxf(fabsf(a.scale) * kLog2e, 0x1p-100f);
+  const float sgn = a.scale < 0.f ? -1.f : 1.f;
+
+  // Scores in the log2 domain, one per key of each pass (all LPR lanes of a
+  // row end up holding the row's score).
+  float s[NP];
+  float mloc = -INFINITY;
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    float kv[EPL];
+    Elem<T>::unpack(kraw[p], kv);
+    float part = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) part = fmaf(qv[e], kv[e], part);
+#pragma unroll
+    for (int off = 1; off < LPR; off <<= 1) part += __shfl_xor(part, off);
+    const int key = w0 + p * KPP + kk;
+    s[p] = key < kv_len ? sgn * part * c : -INFINITY;
+    mloc = fmaxf(mloc, s[p]);
+  }
+#pragma unroll
+  for (int off = LPR; off < 64; off <<= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, off));
+  const float m = mloc;  // wave max (-inf if the wave has no valid key)
+
+  float acc[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+  float lsum = 0.f;
+  if (m != -INFINITY) {
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const float w = __builtin_amdgcn_exp2f(s[p] - m);  // 0 for invalid keys
+      float vv[EPL];
+      Elem<T>::unpack(vraw[p], vv);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[e] = fmaf(w, vv[e], acc[e]);
+      lsum += w;
+    }
+  }
+  // Sum over the keys of the wave: the lanes with the same slice sit LPR
+  // apart, and each of them saw every key of its own passes once.
+#pragma unroll
+  for (int off = LPR; off < 64; off <<= 1) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] += __shfl_xor(acc[e], off);
+    lsum += __shfl_xor(lsum, off);
+  }
+
+  // ---- merge the 4 wave partials of this chunk in LDS
+  __shared__ float sm[kDecodeWaves], sl_[kDecodeWaves];
+  __shared__ float sacc[kDecodeWaves][kHeadDim];
+  if (lane < LPR) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) sacc[wave][EPL * sl + e] = acc[e];
+  }
+  if (lane == 0) {
+    sm[wave] = m;
+    sl_[wave] = lsum;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    float M = sm[0];
+#pragma unroll
+    for (int w = 1; w < kDecodeWaves; ++w) M = fmaxf(M, sm[w]);
+    // M is finite: the chunk holds at least one valid key (chunk0 < kv_len).
+    float L = 0.f, A = 0.f;
+#pragma unroll
+    for (int w = 0; w < kDecodeWaves; ++w) {
+      const float f = sm[w] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sm[w] - M);
+      L = fmaf(f, sl_[w], L);
+      A = fmaf(f, sacc[w][lane], A);
+    }
+    float* rec = a.work + ((size_t)bh * a.n_split + split) * kPartialStride;
+    rec[2 + lane] = A;
+    if (lane == 0) {
+      rec[0] = M;
+      rec[1] = L;
+    }
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void store_out(T* dst, float v);
+template <>
+__device__ __forceinline__ void store_out<float>(float* dst, float v) { *dst = v; }
+template <>
+__device__ __forceinline__ void store_out<__bf16>(__bf16* dst, float v) { *dst = (__bf16)v; }
+
+template <typename T>
+__global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
+  const int bh = blockIdx.x;
+  const int b = bh / a.H;
+  const int d = threadIdx.x;
+  const int kv_len = clamp_len(a.kv_lens[b], a.n_max);
+  const int ns = (kv_len + kDecodeChunk - 1) / kDecodeChunk;
+  const float* rec = a.work + (size_t)bh * a.n_split * kPartialStride;
+  float M = -INFINITY;
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, rec[s * kPartialStride]);
+  float L = 0.f, A = 0.f;
+  for (int s = 0; s < ns; ++s) {
+    const float f = __builtin_amdgcn_exp2f(rec[s * kPartialStride] - M);
+    L = fmaf(f, rec[s * kPartialStride + 1], L);
+    A = fmaf(f, rec[s * kPartialStride + 2 + d], A);
+  }
+  // kv_len = 0: no partials, the row is 0.
+  const float out = L > 0.f ? A / L : 0.f;
+  store_out<T>(static_cast<T*>(a.O) + (size_t)bh * kHeadDim + d, out);
+}
+
+template <typename T>
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
+  DecodeArgs args = a;
+  void* kargs[] = {&args};
+  const long long blocks = (long long)a.B * a.H * a.n_split;
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&decode_partial_kernel<T>),
+                                 dim3((unsigned)blocks), dim3(64 * kDecodeWaves), kargs, 0, s);
+  if (e != hipSuccess) return e;
+  return hipLaunchKernel(reinterpret_cast<const void*>(&decode_merge_kernel<T>),
+                         dim3((unsigned)(a.B * a.H)), dim3(64), kargs, 0, s);
+}
+
+}  // namespace
+
+hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t s) { return launch_decode<float>(a, s); }
+hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s) { return launch_decode<__bf16>(a, s); }
+
+}  // namespace headattn

@@ -1,0 +1,67 @@
+// Internal definitions shared by the HIP kernels and the host entry points of
+// libheadattn.so.  Not part of the public ABI (that is include/headattn.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace headattn {
+
+constexpr int kHeadDim = 64;  // d_k = d_v = d_model / h = 64 for every call
+
+// log2(e): the kernels evaluate exp(x) as exp2(x * log2(e)) with the
+// hardware's v_exp_f32 (a base-2 exponential), folding log2(e) into the
+// softmax scale once per call.
+constexpr float kLog2e = 1.4426950408889634f;
+
+// One forward call, as validated by the host entry point.
+struct FwdArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  void* O;
+  const int32_t* q_lens;   // device int32[B] or nullptr (all rows valid)
+  const int32_t* kv_lens;  // device int32[B] or nullptr (no key padding)
+  int B, H, n_q, n_k;
+  float scale;             // multiplies Q K^T; finite
+  bool causal;
+};
+
+// One decode call.
+struct DecodeArgs {
+  const void* q;
+  const void* Kc;
+  const void* Vc;
+  void* O;
+  const int32_t* kv_lens;  // device int32[B], required
+  float* work;             // [B*H][n_split][kPartialStride] fp32 partials
+  int B, H, n_max;
+  int n_split;             // splits per (b, h) = ceil(n_max / kDecodeChunk)
+  float scale;
+};
+
+// Decode: keys per split (one workgroup of 4 waves x 64 keys).
+constexpr int kDecodeWaves = 4;
+constexpr int kDecodeChunk = 64 * kDecodeWaves;
+// Partial record per split: m (max logit, log2 domain), l (sum of weights),
+// acc[64] (unnormalised weighted sum of V).
+constexpr int kPartialStride = 2 + kHeadDim;
+
+// At least one split, so the merge pass always runs and writes O (a cache of
+// capacity 0 gives zero rows).
+inline int decode_splits(int n_max) {
+  const int s = (n_max + kDecodeChunk - 1) / kDecodeChunk;
+  return s > 0 ? s : 1;
+}
+
+// Launchers; each returns the hipError_t of its launch(es).
+hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);
+hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s);
+hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s);
+
+// Clamp a device-provided length into [0, n] so that a bad length can never
+// index outside the caller's buffers.
+__device__ __forceinline__ int clamp_len(int v, int n) { return v < 0 ? 0 : (v > n ? n : v); }
+
+}  // namespace headattn

@@ -1,0 +1,166 @@
+/*
+ * headattn.h -- C ABI of the MI355X (gfx950) scaled dot-product attention
+ * library libheadattn.so.
+ *
+ * The library computes, per batch entry b and head h,
+ *     O = softmax(Q K^T * scale + M) V
+ * ("[논문 리뷰]Attention Is All You Need", §3.2.1, the Attention(Q,K,V)
+ * equation; the masked form with an additive M of 0 / -inf is the one on
+ * "Attention Is All You Need를 지금 다시 읽는 법", computation section), for
+ * the three uses the pages list (kimjiil page §3.2.3 table: encoder
+ * self-attention, masked decoder self-attention, encoder-decoder attention)
+ * and for one KV-cache decode step (kimjiil page §3.7; "Attention Is All You
+ * Need 해부", section "KV cache는 추론의 같은 계산을 반복하지 않게 한다").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Layout.  Every tensor is contiguous row-major [B, h, n, d]: Q and O use
+ *   n = n_q, K and V use n = n_k.  d must be 64 (d_k = d_v = d_model / h =
+ *   64, kimjiil page §3.2.2).  Element type is bf16 or fp32 (attn_dtype), the
+ *   same for inputs and output.  Accumulation is always fp32.
+ * Pointers.  Tensor and length pointers are DEVICE pointers (HIP device
+ *   memory, or memory the device can read) owned by the caller; the library
+ *   keeps no reference after the call returns.  Inputs must not alias O.
+ * Streams.  `stream` is a hipStream_t passed as void* (NULL = the default
+ *   stream).  All work is enqueued on it; calls return without synchronising,
+ *   and a fault inside a kernel surfaces at the caller's next synchronisation.
+ * Errors.  Arguments are validated on the host before any HIP call; on error
+ *   nothing is enqueued and a non-zero attn_status is returned.  The library
+ *   never aborts, prints or synchronises (except in the opt-in length check
+ *   below).  ATTN_ERR_HIP means a HIP launch reported an error.
+ * Lengths.  q_lens / kv_lens are device int32[B].  They are NOT read on the
+ *   host: 0 <= len <= n is a precondition.  Kernels clamp every length into
+ *   [0, n], so an out-of-range length never causes an out-of-bounds access.
+ *   With the environment variable ATTN_CHECK=1 the entry points copy the
+ *   lengths to the host (a synchronising copy on `stream`) and return
+ *   ATTN_ERR_BAD_LENGTHS when one is out of range.
+ * Allocation.  Entry points allocate no memory; decode's scratch is a
+ *   caller-provided workspace.
+ * Empty calls.  B = 0, h = 0 or n_q = 0 is a valid call that does nothing.
+ *   n_k = 0 (no keys) writes every row of O as 0; K and V may then be NULL.
+ */
+#ifndef HEADATTN_H
+#define HEADATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of Q, K, V and O. */
+typedef enum {
+  ATTN_BF16 = 0, /* bfloat16 storage, bf16 MFMA products, fp32 accumulation */
+  ATTN_F32 = 1   /* float32 storage and arithmetic (the fp32 check path)     */
+} attn_dtype;
+
+/* Shape of one call.  For attn_decode, n_q must be 1 and n_k is the cache
+ * capacity n_max (rows per (b, h) slice of Kcache / Vcache). */
+typedef struct {
+  int32_t B;     /* batch entries, >= 0                 */
+  int32_t h;     /* heads, >= 0                         */
+  int32_t n_q;   /* query rows per (b, h), >= 0         */
+  int32_t n_k;   /* key/value rows per (b, h), >= 0     */
+  int32_t d;     /* head dimension, must be 64          */
+  int32_t dtype; /* attn_dtype                          */
+} attn_layout;
+
+/* Mask kinds, bit flags; 3 = causal with key padding.
+ * Key padding (kimjiil page §3.2.3; sj-techlog page failure section 2, "pad
+ * token에 attention이 가지 않는가"): key j of batch entry b is excluded when
+ * j >= kv_lens[b].
+ * Causal (kimjiil page §3.2.3 and §3.1; sj-techlog page, section "mask는
+ * softmax 전에 더해야 한다", 4x4 table): key j is excluded for query i when
+ * j > i (top-left aligned; requires n_q == n_k).
+ * An excluded key gets logit -inf before the softmax: its weight is exactly 0
+ * and its K/V contents (even NaN) never reach O. */
+enum {
+  ATTN_MASK_NONE = 0,
+  ATTN_MASK_KEY_PADDING = 1,
+  ATTN_MASK_CAUSAL = 2
+};
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_NULL_POINTER = 1, /* a required pointer is NULL                    */
+  ATTN_ERR_BAD_SHAPE = 2,    /* negative size, d != 64, size overflow, n_q != 1
+                                for decode, or an input pointer equal to O    */
+  ATTN_ERR_BAD_DTYPE = 3,    /* dtype not an attn_dtype                       */
+  ATTN_ERR_BAD_MASK = 4,     /* unknown bits; causal with n_q != n_k; kv_lens
+                                given without ATTN_MASK_KEY_PADDING           */
+  ATTN_ERR_BAD_LENGTHS = 5,  /* (ATTN_CHECK=1 only) a length outside [0, n]   */
+  ATTN_ERR_BAD_SCALE = 6,    /* scale is not finite                           */
+  ATTN_ERR_WORKSPACE = 7,    /* decode workspace NULL or smaller than needed  */
+  ATTN_ERR_HIP = 8           /* a HIP runtime call failed                     */
+} attn_status;
+
+/*
+ * attn_forward -- O = softmax(Q K^T * scale + M) V for every (b, h).
+ *
+ *   Q       [B, h, n_q, 64]  device, read
+ *   K, V    [B, h, n_k, 64]  device, read
+ *   layout  shapes and element type (bf16 or fp32)
+ *   mask_kind  ATTN_MASK_* flags (see above)
+ *   q_lens  device int32[B] or NULL.  Query rows i >= q_lens[b] of O are
+ *           written as 0 (padded query positions); NULL = all n_q rows valid.
+ *   kv_lens device int32[B]; required iff mask_kind has
+ *           ATTN_MASK_KEY_PADDING, must be NULL otherwise.
+ *   scale   multiplies Q K^T; finite.  The pages' choice is 1/sqrt(d_k) =
+ *           0.125 (kimjiil page §3.2.1 variance argument); the caller passes it.
+ *   O       [B, h, n_q, 64]  device, written in full (every row).
+ *   stream  hipStream_t or NULL.
+ * A row with no allowed key (kv_len = 0) is written as 0, never NaN.
+ * Numerics: bf16 inputs are multiplied on MFMA with fp32 accumulation; the
+ * softmax weights are rounded to bf16 once before the product with V; the
+ * running max, running sum and output accumulator stay fp32; O is rounded
+ * to bf16 (nearest even).  The fp32 path computes in fp32 throughout.
+ */
+attn_status attn_forward(const void* Q, const void* K, const void* V,
+                         attn_layout layout, int32_t mask_kind,
+                         const int32_t* q_lens, const int32_t* kv_lens,
+                         float scale, void* O, void* stream);
+
+/*
+ * attn_decode -- one KV-cache decode step: for each (b, h) the single new
+ * query attends to the kv_lens[b] valid rows of the cache, which already
+ * include the new token's own K/V (the caller appends first; sj-techlog
+ * page, KV cache section: "K,V = cached 0..t-1 + the new token").
+ *
+ *   q              [B, h, 1, 64]      device, read
+ *   Kcache, Vcache [B, h, n_max, 64]  device, read; rows >= kv_lens[b] are
+ *                  never used (may hold anything, including NaN)
+ *   cache_layout   B, h, n_q = 1, n_k = n_max, d = 64, dtype
+ *   kv_lens        device int32[B], required; kv_lens[b] = 0 gives a 0 row
+ *   scale          finite
+ *   O              [B, h, 1, 64]      device, written
+ *   workspace      device buffer of at least
+ *                  attn_decode_workspace_bytes(cache_layout) bytes, owned by
+ *                  the caller; its contents on entry do not matter and are
+ *                  overwritten (split partials).  Two calls that share a
+ *                  workspace must be ordered (same stream).
+ *   stream         hipStream_t or NULL.
+ * Two kernels run on `stream`: split partials over fixed-size key chunks,
+ * then a merge of the partials into O.
+ */
+attn_status attn_decode(const void* q, const void* Kcache, const void* Vcache,
+                        attn_layout cache_layout, const int32_t* kv_lens,
+                        float scale, void* O, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/* Bytes of fp32 split partials attn_decode needs for this cache layout; 0 if
+ * the layout is invalid.  Pure host arithmetic. */
+size_t attn_decode_workspace_bytes(attn_layout cache_layout);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* attn_status_string(attn_status status);
+
+/* Name of the HIP error behind the last ATTN_ERR_HIP returned on the calling
+ * thread ("hipSuccess" if none).  Static string, never NULL. */
+const char* attn_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HEADATTN_H */

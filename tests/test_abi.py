@@ -1,0 +1,142 @@
+"""C-ABI tests that need no GPU: the library loads, exports every function
+include/headattn.h declares, and rejects bad arguments with the documented
+status codes before any HIP call (so nothing here launches a kernel)."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+import head_attention_amd as ha
+from head_attention_amd import attn_layout
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+OK, NULLP, SHAPE, DTYPE, MASK, LENS, SCALE, WORK, HIP = range(9)
+BF16, F32 = 0, 1
+FAKE = 0x1000  # never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    names = []
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h, encoding="utf-8").read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names += re.findall(r"^[A-Za-z_][\w \*]*?\b(attn_\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("attn_forward", "attn_decode", "attn_decode_workspace_bytes",
+              "attn_status_string", "attn_last_hip_error"):
+        assert n in names, names
+
+
+def test_library_exports_every_declared_symbol():
+    L = ha.lib()
+    for n in declared_functions():
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    for code in range(9):
+        s = ha.status_string(code)
+        assert s.startswith(ha._binding.STATUS_NAMES[code]), s
+    assert "unknown" in ha.status_string(99)
+    assert ha.lib().attn_last_hip_error() == b"hipSuccess"
+
+
+def fwd(layout, mask=0, q=FAKE, k=FAKE, v=FAKE, o=FAKE + 64, ql=None, kl=None, scale=0.125):
+    return ha.lib().attn_forward(q, k, v, layout, mask, ql, kl, scale, o, None)
+
+
+def lay(B=2, h=3, nq=16, nk=16, d=64, dt=BF16):
+    return attn_layout(B, h, nq, nk, d, dt)
+
+
+@pytest.mark.parametrize("layout,code", [
+    (lay(d=32), SHAPE), (lay(d=128), SHAPE), (lay(B=-1), SHAPE), (lay(nq=-5), SHAPE),
+    (lay(dt=2), DTYPE), (lay(dt=-1), DTYPE),
+    (lay(B=2 ** 30, h=2 ** 30, nq=2 ** 20), SHAPE),
+])
+def test_forward_bad_layout(layout, code):
+    assert fwd(layout) == code
+
+
+def test_forward_validation_order_and_codes():
+    L = lay()
+    assert fwd(L, mask=4) == MASK
+    assert fwd(L, mask=-1) == MASK
+    assert fwd(lay(nq=8, nk=16), mask=2) == MASK       # causal needs n_q == n_k
+    assert fwd(L, mask=0, kl=FAKE) == MASK              # kv_lens without key padding
+    assert fwd(L, mask=1, kl=None) == NULLP             # key padding without kv_lens
+    assert fwd(L, scale=float("inf")) == SCALE
+    assert fwd(L, scale=float("nan")) == SCALE
+    assert fwd(L, q=None) == NULLP
+    assert fwd(L, o=None) == NULLP
+    assert fwd(L, k=None) == NULLP
+    assert fwd(L, v=None) == NULLP
+    assert fwd(L, o=FAKE) == SHAPE                      # output aliases Q
+    assert fwd(lay(dt=F32), mask=3, kl=None) == NULLP
+
+
+def test_forward_empty_calls_are_noops():
+    # nothing to write: OK without touching any pointer or the device
+    assert fwd(lay(B=0), q=None, k=None, v=None, o=None) == OK
+    assert fwd(lay(h=0), q=None, k=None, v=None, o=None) == OK
+    assert fwd(lay(nq=0, nk=5), q=None, k=None, v=None, o=None) == OK
+
+
+def dec(layout, q=FAKE, k=FAKE, v=FAKE, kl=FAKE + 32, o=FAKE + 64, ws=FAKE + 128, wsb=None,
+        scale=0.125):
+    if wsb is None:
+        wsb = ha.lib().attn_decode_workspace_bytes(layout)
+    return ha.lib().attn_decode(q, k, v, layout, kl, scale, o, ws, wsb, None)
+
+
+def test_decode_workspace_bytes():
+    L = ha.lib()
+    # (B*h) records per split, splits of 256 keys, record = (m, l, acc[64]) fp32
+    assert L.attn_decode_workspace_bytes(attn_layout(64, 16, 1, 4096, 64, BF16)) == 64 * 16 * 16 * 66 * 4
+    assert L.attn_decode_workspace_bytes(attn_layout(1, 1, 1, 257, 64, F32)) == 2 * 66 * 4
+    assert L.attn_decode_workspace_bytes(attn_layout(1, 1, 1, 0, 64, F32)) == 66 * 4
+    assert L.attn_decode_workspace_bytes(attn_layout(1, 1, 2, 64, 64, F32)) == 0   # n_q != 1
+    assert L.attn_decode_workspace_bytes(attn_layout(1, 1, 1, 64, 32, F32)) == 0   # d != 64
+    assert ha.decode_workspace_bytes(64, 16, 4096) == 64 * 16 * 16 * 66 * 4
+
+
+def test_decode_validation():
+    L = attn_layout(4, 2, 1, 300, 64, BF16)
+    assert dec(attn_layout(4, 2, 2, 300, 64, BF16)) == SHAPE
+    assert dec(attn_layout(4, 2, 1, 300, 16, BF16)) == SHAPE
+    assert dec(attn_layout(4, 2, 1, 300, 64, 7)) == DTYPE
+    assert dec(L, scale=float("-inf")) == SCALE
+    assert dec(L, q=None) == NULLP
+    assert dec(L, kl=None) == NULLP
+    assert dec(L, k=None) == NULLP
+    assert dec(L, o=None) == NULLP
+    assert dec(L, ws=None) == WORK
+    assert dec(L, wsb=ha.lib().attn_decode_workspace_bytes(L) - 1) == WORK
+    assert dec(L, o=FAKE) == SHAPE
+    assert dec(attn_layout(0, 2, 1, 300, 64, BF16), q=None, o=None, kl=None) == OK
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    from head_attention_amd import _binding
+    monkeypatch.setattr(_binding, "_lib", None)
+    monkeypatch.setattr(_binding, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="no fallback"):
+        _binding.lib()
+
+
+def test_header_is_plain_c():
+    # The header compiles as C99 with no HIP or torch headers in sight.
+    import subprocess
+    src = "#include \"headattn.h\"\nint main(void){attn_layout l={1,1,1,1,64,ATTN_BF16};" \
+          "(void)l;return ATTN_OK;}\n"
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"),
+                        "-x", "c", "-", "-o", os.devnull], input=src.encode(),
+                       capture_output=True)
+    assert r.returncode == 0, r.stderr.decode()
