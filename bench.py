@@ -206,6 +206,94 @@ def cpu_baseline(target_s: float = 15.0):
     }
 
 
+# ------------------------------------------------------- rocprof summaries
+def _short_kernel(name: str) -> str:
+    """attn_fwd_bf16_kernel<causal, ...> -> attn_fwd_bf16_kernel<true|false>; other
+    kernels of the library by their plain name."""
+    import re
+    m = re.search(r"attn_fwd_bf16_kernel<(true|false)", name) or \
+        re.search(r"attn_fwd_bf16_kernelILb(\d)", name)
+    if m:
+        causal = m.group(1) in ("true", "1")
+        return f"attn_fwd_bf16_kernel<{'true' if causal else 'false'}>"
+    for key in ("attn_fwd_f32_kernel", "decode_partial_kernel", "decode_merge_kernel",
+                "copyBuffer", "elementwise"):
+        if key in name:
+            return key
+    return name[:60]
+
+
+# Grid sizes (threads) of each leg's launches, to tell apart launches of the
+# same kernel in a trace of the default bench command.
+LEG_GRIDS = {("attn_fwd_bf16_kernel<false>", 65536): "encoder_base",
+             ("attn_fwd_bf16_kernel<true>", 131072): "decoder_big (causal self)",
+             ("attn_fwd_bf16_kernel<false>", 131072): "decoder_big (cross)",
+             ("attn_fwd_bf16_kernel<true>", 262144): "long_causal",
+             ("decode_partial_kernel", 4194304): "kv_decode",
+             ("decode_merge_kernel", 65536): "kv_decode"}
+
+
+def summarize_trace(path: str) -> str:
+    """Per (kernel, grid) launch statistics from a rocprofv3 kernel-trace CSV."""
+    import csv
+    import collections
+    g = collections.defaultdict(list)
+    for r in csv.DictReader(open(path)):
+        grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+        g[(_short_kernel(r["Kernel_Name"]), grid)].append(
+            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    lines = ["| kernel | grid (threads) | leg | launches | avg us | min us | max us |",
+             "|---|---|---|---|---|---|---|"]
+    for (k, grid), v in sorted(g.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"| {k} | {grid} | {LEG_GRIDS.get((k, grid), '')} | {len(v)} | "
+                     f"{sum(v) / len(v):.2f} | {min(v):.2f} | {max(v):.2f} |")
+    return "\n".join(lines)
+
+
+def summarize_counters(fetch_csv: str, write_csv: str, copy_mib: int, out_json: str | None):
+    """HBM traffic per launch from FETCH_SIZE / WRITE_SIZE runs (KiB per
+    dispatch), each scaled by what the same counter reads for the plain copy
+    of copy_mib MiB that bench.py --copy-probe-mib runs."""
+    import csv
+    import collections
+
+    def load(path, counter):
+        g = collections.defaultdict(list)
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] == counter:
+                g[(_short_kernel(r["Kernel_Name"]), int(r["Grid_Size"]))].append(float(r["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in g.items()}
+
+    fetch, write = load(fetch_csv, "FETCH_SIZE"), load(write_csv, "WRITE_SIZE")
+    known_kib = copy_mib * 1024.0
+    copy_key = max((k for k in fetch if k[0] == "copyBuffer"), key=lambda k: k[1])
+    f_fetch = known_kib / fetch[copy_key]
+    f_write = known_kib / write[copy_key]
+    lines = [f"copy probe ({copy_mib} MiB each way, {copy_key[0]} grid {copy_key[1]}): "
+             f"FETCH_SIZE {fetch[copy_key]:.1f} KiB -> scale {f_fetch:.4f}; "
+             f"WRITE_SIZE {write[copy_key]:.1f} KiB -> scale {f_write:.4f}", "",
+             "| kernel | grid | leg | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM read MB | HBM write MB |",
+             "|---|---|---|---|---|---|---|"]
+    res = {}
+    for k in sorted(fetch):
+        if k[0] in ("copyBuffer", "elementwise"):
+            continue
+        rd = fetch[k] * f_fetch * 1024 / 1e6
+        wr = write.get(k, 0.0) * f_write * 1024 / 1e6
+        lines.append(f"| {k[0]} | {k[1]} | {LEG_GRIDS.get(k, '')} | {fetch[k]:.1f} | "
+                     f"{write.get(k, 0.0):.1f} | {rd:.2f} | {wr:.2f} |")
+        res[f"{k[0]}@{k[1]}"] = {"read_bytes": rd * 1e6, "write_bytes": wr * 1e6}
+    if out_json:
+        lc = res.get("attn_fwd_bf16_kernel<true>@262144")
+        with open(out_json, "w") as f:
+            json.dump({"kernel_source_hash": kernel_source_hash(),
+                       "fetch_scale": f_fetch, "write_scale": f_write,
+                       "long_causal_fwd_bytes_per_launch":
+                           None if lc is None else round(lc["read_bytes"] + lc["write_bytes"]),
+                       "per_kernel": res}, f, indent=1)
+    return "\n".join(lines)
+
+
 # ------------------------------------------------------------------ main
 def main():
     ap = argparse.ArgumentParser()
@@ -214,7 +302,24 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sanity", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after timing, run one plain device copy of this many MiB "
+                         "(the known-size reference for HBM counter calibration)")
+    ap.add_argument("--summarize-trace", metavar="KERNEL_TRACE_CSV",
+                    help="print per-kernel launch statistics of a rocprofv3 trace and exit")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="print HBM traffic per launch from rocprofv3 --pmc runs (with "
+                         "--copy-probe-mib naming the probe size) and exit")
+    ap.add_argument("--traffic-json", help="with --summarize-counters: write the figures here")
     args = ap.parse_args()
+
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace))
+        return
+    if args.summarize_counters:
+        print(summarize_counters(*args.summarize_counters, args.copy_probe_mib or 1024,
+                                 args.traffic_json))
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(json.dumps({"error": "this build runs on one GPU only: the attention path has no "
@@ -320,6 +425,13 @@ def main():
             "frac": round(kd_gbps / PEAK_HBM_GBPS, 4),
         },
     }
+    if args.copy_probe_mib:
+        src = torch.ones(args.copy_probe_mib * 2 ** 18, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_probe_bytes_each_way"] = args.copy_probe_mib * 2 ** 20
     if not args.no_sanity:
         out["sanity_max_abs_err_vs_oracle"] = round(sanity_check(legs), 6)
     if not args.no_cpu_baseline:

@@ -6,68 +6,83 @@
 // in registers, so no n x n score matrix ever leaves the register file.
 //
 // Workgroup: 4 waves (256 lanes) own 128 consecutive query rows of one (b, h);
-// each wave owns 32 rows.  The key axis is walked in tiles of 64 keys; K and
-// V tiles are staged in LDS (double buffered, one barrier per tile) from
-// coalesced 16-byte global loads.
+// each wave owns 32 rows.  The key axis is walked in tiles of 64 keys.  K and
+// V^T tiles are staged in LDS from 16-byte buffer loads whose range check
+// returns zeros for rows at or beyond the valid length, so padded K/V memory
+// (even NaN) is never read.
 //
 // Contractions (v_mfma_f32_32x32x16_bf16, fp32 accumulate):
-//   S^T[key, query] = K[key, :] . Q[query, :]   A = K tile (LDS), B = Q (regs)
+//   S^T[key, query] = K[key, :] . Qc[query, :]   A = K tile (LDS), B = Qc (regs)
 //   O^T[d, query]  += V^T[d, key] . P^T[key, query]
-//                                               A = V^T (LDS), B = P (regs)
-// With S^T, each lane holds one query row (lane % 32) and 16 of its keys per
-// 32x32 block, so the row max and row sum are in-lane reductions plus one
-// exchange between the two half-waves that hold the same row.  P then feeds
-// the second product straight from registers: the contraction order over
-// keys is free, so V^T is written to LDS with its keys in exactly the order
-// in which each lane's accumulator registers hold P.
+//                                                A = V^T tile (LDS), B = P (regs)
+// With S^T each lane holds one query row (lane % 32) and 16 of its keys per
+// 32x32 block, so row reductions are in-lane plus one exchange between the
+// two half-waves; P feeds the second product from registers, since the
+// contraction order over keys is free and V^T is written to LDS with its keys
+// in the order in which each lane's accumulator registers hold P.
 //
-// Softmax is the online form: a running pivot m and running sum l per row in
-// fp32 registers.  This is exact up to rounding because softmax does not
-// depend on the pivot; the pivot is moved only when a tile's max exceeds it by
-// more than 2^8 in weight (then the accumulator and l are rescaled by
-// exp(m_old - m_new)), so every weight used is at most 2^8 and fits bf16
-// and fp32 comfortably.  Weights are rounded to bf16 once for the product
-// with V; l sums the unrounded fp32 weights; O = acc / l is rounded to bf16.
+// Q enters the product exactly (the sign of scale is folded in as a sign
+// flip); a weight is exp2(score * c - pivot * c) with c = |scale| * log2(e):
+// one FMA and one v_exp_f32 per score.  (Prescaling Q by c in bf16 would save
+// the FMA but shifts every logit by about 2^-9/sqrt(3) of the logits' spread,
+// which exceeds the error budget on peaky rows.)
+//
+// Softmax is the online form with a lazy pivot m per row (the subtracted
+// constant of a stable softmax; softmax does not depend on it, so any choice
+// is exact up to rounding).  m stays 0 -- no subtraction at all -- unless a
+// tile's weights would sum past 2^64 or a row's first tile underflows; then
+// that row's m moves to its tile max and O and the running sum l are rescaled
+// by exp2(m_old - m_new).  Weights are rounded to bf16 once; l sums those
+// same bf16 weights (v_dot2 with ones), so numerator and denominator use
+// identical weights; O = acc / l is rounded to bf16.
+//
+// Pipeline per wave: while the weights of tile t are formed and multiplied
+// with V (VALU + MFMA), the scores of tile t+1 are computed (MFMA) in the same
+// straight-line block, so the matrix cores have independent work during the
+// softmax.  Tiles that need a mask or a pivot take a general step with
+// branches.  K runs one tile ahead of V in LDS; each is double buffered, and
+// one barrier per tile separates reuse.
 #include "common.h"
 
 namespace headattn {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
 constexpr int kBM = 32 * kWaves;  // query rows per workgroup
 constexpr int kBN = 64;           // keys per tile
 constexpr int kThreads = 64 * kWaves;
+constexpr uint32_t kRowBytes = kHeadDim * 2;  // one bf16 row of K or V
+constexpr uint32_t kBufferWord3 = 0x00020000u;  // raw buffer, 32-bit elements (gfx9 family)
+constexpr float kPivotHigh = 0x1p64f;  // a tile sum above this moves the pivot up
+constexpr float kPivotLow = 0x1p-64f;  // a first-tile row sum below this moves it down
 
-// One LDS stage: K tile [64 keys][64 d] and V^T tile [64 d][64 key slots],
-// bf16, each row 128 B = 8 chunks of 16 B.  Chunks are XOR-swizzled per row
-// so that 8 lanes reading the same logical chunk of 8 consecutive rows hit 8
+// One LDS tile: 64 rows x 128 B as 8 chunks of 16 B.  K tiles are stored
+// [key][chunk], V^T tiles [d][chunk of 8 keys].  Chunks are XOR-swizzled per
+// row so 8 lanes reading the same logical chunk of 8 consecutive rows hit 8
 // different chunk positions.
-struct Stage {
-  uint4 k[kBN * 8];
-  uint4 vt[kHeadDim * 8];
+struct Tile {
+  uint4 c[64 * 8];
 };
 
 __device__ __forceinline__ int k_swz(int key) { return key & 7; }
 __device__ __forceinline__ int vt_swz(int d) { return (d ^ (d >> 3)) & 7; }
 
-// Position of key group g (keys 4g..4g+3 of a 64-key tile) inside a V^T row.
-// A lane of half-wave hh feeds the P.V product of 16-key step (blk, j) with
-// the 8 keys {16j + 4hh + t, 16j + 8 + 4hh + t : t = 0..3} (+ 32 blk), which is
-// how its S^T accumulator registers 8j..8j+7 are laid out.  Those 8 keys form
-// one 16-byte chunk: chunk 4 blk + 2 j + hh, first half keys 16j+4hh.., second
-// half keys 16j+8+4hh..
+// Position of key group g (keys 4g..4g+3 of a tile) inside a V^T row.  A lane
+// of half-wave hh feeds the P.V product of 16-key step (blk, j) with the keys
+// {16j + 4hh + t, 16j + 8 + 4hh + t : t = 0..3} (+ 32 blk) -- how its S^T
+// accumulator registers 8j..8j+7 are laid out -- so those 8 keys form chunk
+// 4 blk + 2 j + hh of the row: first half keys 16j+4hh.., second 16j+8+4hh..
 __device__ __forceinline__ int vt_chunk_of_group(int g) { return 2 * (g >> 2) + (g & 1); }
 __device__ __forceinline__ int vt_half_of_group(int g) { return (g >> 1) & 1; }
 
+// Lanes l and l ^ 32 hold the same query row: combine the two half-waves.
 __device__ __forceinline__ float half_swap_max(float x) {
-  // Combine the two half-waves (lanes l and l ^ 32 hold the same query row).
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
@@ -76,14 +91,43 @@ __device__ __forceinline__ float half_swap_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+__device__ __forceinline__ bool half_swap_or(bool x) {
+  auto r = __builtin_amdgcn_permlane32_swap((uint32_t)x, (uint32_t)x, false, false);
+  return (r[0] | r[1]) != 0;
+}
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   f32x2 v = {lo, hi};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
+__device__ __forceinline__ uint4 as_uint4(u32x4 v) { return make_uint4(v[0], v[1], v[2], v[3]); }
+
+// Weight of a raw score s under pivot term mc = m * c.
+__device__ __forceinline__ float ex2(float s, float c, float mc) {
+  return __builtin_amdgcn_exp2f(fmaf(s, c, -mc));
+}
+
+// Weights of one tile: P = exp2(S - pivot), packed to bf16 pairs in the order
+// the P.V product consumes them, and the sum of the packed (rounded) weights.
+__device__ __forceinline__ float exp_pack_sum(const f32x16& s0, const f32x16& s1, float c, float mc,
+                                              uint32_t (&pk)[16]) {
+  const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
+  float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    pk[i] = pack_bf16x2(ex2(s0[2 * i], c, mc), ex2(s0[2 * i + 1], c, mc));
+    pk[8 + i] = pack_bf16x2(ex2(s1[2 * i], c, mc), ex2(s1[2 * i + 1], c, mc));
+    acc0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[i]), ones, acc0, false);
+    acc1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[8 + i]), ones, acc1, false);
+  }
+  return acc0 + acc1;
+}
+
 template <bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
-  __shared__ Stage lds[2];
+  __shared__ Tile kbuf[2];
+  __shared__ Tile vbuf[2];
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -116,8 +160,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
   const __bf16* V = static_cast<const __bf16*>(a.V) + (size_t)bh * a.n_k * kHeadDim;
   __bf16* O = static_cast<__bf16*>(a.O) + (size_t)bh * a.n_q * kHeadDim;
 
-  const int q_len = a.q_lens ? clamp_len(a.q_lens[b], a.n_q) : a.n_q;
-  const int kv_lim = a.kv_lens ? clamp_len(a.kv_lens[b], a.n_k) : a.n_k;
+  // Lengths are per batch entry, hence uniform over the workgroup; saying so
+  // keeps them (and the buffer descriptors built from them) in SGPRs.
+  const int q_len = __builtin_amdgcn_readfirstlane(a.q_lens ? clamp_len(a.q_lens[b], a.n_q) : a.n_q);
+  const int kv_lim = __builtin_amdgcn_readfirstlane(a.kv_lens ? clamp_len(a.kv_lens[b], a.n_k) : a.n_k);
   const int q0 = qt * kBM;
   const int qw0 = q0 + 32 * wave;  // first query row of this wave
   const int qi = qw0 + ln;         // query row of this lane
@@ -129,56 +175,72 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
   int wave_end = end;  // keys this wave needs (wave-uniform)
   if (CAUSAL) wave_end = min(wave_end, qw0 + 32);
   if (qw0 >= q_len) wave_end = 0;
+  const int wave_tiles = (wave_end + kBN - 1) / kBN;  // this wave works on tiles [0, wave_tiles)
+
+  // Range-checked views of this (b, h)'s K and V: rows >= kv_lim read as 0.
+  const uint32_t n_bytes = (uint32_t)kv_lim * kRowBytes;
+  const __amdgpu_buffer_rsrc_t rk =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(K), (short)0, (int)n_bytes, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rv =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(V), (short)0, (int)n_bytes, kBufferWord3);
 
   // ---- Q fragment: B operand of S^T = K Q^T (k = d).  Lane (ln, hh) holds
-  // Q[qi][16 s + 8 hh + 0..7] for d-step s.  A negative scale is folded into
-  // Q exactly (sign flip), so the kernel only ever sees c = |scale| log2 e.
-  bf16x8 qf[4];
-  {
-    const uint32_t sign = a.scale < 0.f ? 0x80008000u : 0u;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (qi < a.n_q) v = *reinterpret_cast<const uint4*>(Q + (size_t)qi * kHeadDim + 16 * s + 8 * hh);
-      v.x ^= sign; v.y ^= sign; v.z ^= sign; v.w ^= sign;
-      qf[s] = __builtin_bit_cast(bf16x8, v);
-    }
-  }
-  // c > 0 always: for |scale| log2 e below 2^-100 every weight is exp2 of
-  // something below 2^-80 in magnitude, i.e. exactly 1.0f either way, so the
-  // floor changes nothing while keeping -inf * c = -inf for masked logits.
+  // Q[qi][16 s + 8 hh + 0..7] for d-step s, with the sign of scale folded in
+  // (an exact sign flip), so the kernel only sees c = |scale| * log2(e).  c is
+  // floored at 2^-100: for smaller |scale| every weight is exp2 of a number
+  // below 2^-80 in magnitude, i.e. exactly 1.0f either way.
   const float c = fmaxf(fabsf(a.scale) * kLog2e, 0x1p-100f);
-  const float thr = 8.0f / c;  // pivot moves when a tile max exceeds it by this
-
-  // ---- global -> register -> LDS staging.  Waves 2-3 carry the K tile
-  // (4 x 16 B per lane, stored as is); waves 0-1 carry the V tile (4 rows x
-  // 16 B per lane, transposed to 8 x 8 B on the way into LDS).  Rows at or
-  // beyond kv_lim are zero-filled and never read: padded or out-of-range K/V
-  // (even NaN) cannot reach the products.
-  uint4 pre[4];
-  const bool k_loader = tid >= 2 * 64;
-  const int lu = k_loader ? tid - 128 : tid;
-  const int lc = lu & 7;   // 16-byte chunk = d 8 lc .. 8 lc + 7
-  const int lg = lu >> 3;  // K: row base (rows lg + 16 k); V: key group (keys 4 lg + t)
-
-  auto gload = [&](int k0) {
+  const uint32_t sign = a.scale < 0.f ? 0x80008000u : 0u;
+  bf16x8 qf[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int key = k_loader ? k0 + lg + 16 * t : k0 + 4 * lg + t;
-      const __bf16* src = k_loader ? K : V;
-      pre[t] = key < kv_lim ? *reinterpret_cast<const uint4*>(src + (size_t)key * kHeadDim + 8 * lc)
-                            : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto lstore = [&](Stage& st) {
+  for (int s = 0; s < 4; ++s) {
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (qi < a.n_q) v = *reinterpret_cast<const uint4*>(Q + (size_t)qi * kHeadDim + 16 * s + 8 * hh);
+    v.x ^= sign;
+    v.y ^= sign;
+    v.z ^= sign;
+    v.w ^= sign;
+    qf[s] = __builtin_bit_cast(bf16x8, v);
+  }
+
+  // ---- global -> register -> LDS staging.  Waves 2-3 carry K tiles (4 x
+  // 16 B per lane, stored as is); waves 0-1 carry V tiles (4 rows x 16 B per
+  // lane, transposed to 8 x 8 B on the way into LDS).
+  uint4 pre[4];
+  const bool k_loader = wave >= 2;  // wave-uniform (scalar) role
+  const int lu = tid & 127;
+  const int lc = lu & 7;   // 16-byte chunk = d 8 lc .. 8 lc + 7
+  const int lg = lu >> 3;  // K: row base (rows lg + 16 t); V: key group (keys 4 lg + t)
+
+  auto gload = [&](int tk, int tv, bool checked = true) {  // K tile tk, V tile tv
     if (k_loader) {
+      if (!checked || tk < n_tiles) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const uint32_t row = (uint32_t)(tk * kBN + lg + 16 * t);
+          pre[t] = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(rk, row * kRowBytes + 16 * lc, 0, 0));
+        }
+      }
+    } else if (!checked || tv < n_tiles) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const int r = lg + 16 * t;
-        st.k[r * 8 + (lc ^ k_swz(r))] = pre[t];
+        const uint32_t row = (uint32_t)(tv * kBN + 4 * lg + t);
+        pre[t] = as_uint4(__builtin_amdgcn_raw_buffer_load_b128(rv, row * kRowBytes + 16 * lc, 0, 0));
       }
-    } else {
-      uint2* vt2 = reinterpret_cast<uint2*>(st.vt);
+    }
+  };
+  auto lstore = [&](int tk, int tv, bool checked = true) {
+    if (k_loader) {
+      if (!checked || tk < n_tiles) {
+        Tile& st = kbuf[tk & 1];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int r = lg + 16 * t;
+          st.c[r * 8 + (lc ^ k_swz(r))] = pre[t];
+        }
+      }
+    } else if (!checked || tv < n_tiles) {
+      uint2* vt2 = reinterpret_cast<uint2*>(vbuf[tv & 1].c);
       const int ch = vt_chunk_of_group(lg);
       const int half = vt_half_of_group(lg);
 #pragma unroll
@@ -190,109 +252,198 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
           const uint32_t word = (&pre[t].x)[e >> 1];
           w[t] = (e & 1) ? (word >> 16) : (word & 0xffffu);
         }
-        const uint2 val = make_uint2(w[0] | (w[1] << 16), w[2] | (w[3] << 16));
-        vt2[d * 16 + (ch ^ vt_swz(d)) * 2 + half] = val;
+        vt2[d * 16 + (ch ^ vt_swz(d)) * 2 + half] = make_uint2(w[0] | (w[1] << 16), w[2] | (w[3] << 16));
       }
     }
   };
 
-  f32x16 o0 = {}, o1 = {};  // O^T blocks: d 0..31 and d 32..63, column = query ln
-  float m_use = -INFINITY;  // pivot (raw score units), same in both half-waves
-  float l = 0.f;            // this half-wave's partial row sum
-
-  if (n_tiles > 0) {
-    gload(0);
-    lstore(lds[0]);
-  }
-  __syncthreads();
-
-  for (int t = 0; t < n_tiles; ++t) {
-    const int k0 = t * kBN;
-    if (t + 1 < n_tiles) gload(k0 + kBN);
-    const Stage& st = lds[t & 1];
-
-    if (k0 < wave_end) {
-      // ---- S^T = K Q^T: two 32-key blocks x four 16-wide d steps
-      f32x16 s0 = {}, s1 = {};
+  // Operand fragments of one tile, read from LDS well ahead of the MFMAs that
+  // consume them.  K: [s] = rows ln, [4 + s] = rows 32 + ln, d-step s.
+  // V^T: [2 blk + j] = rows (d) ln, [4 + 2 blk + j] = rows 32 + ln, key step (blk, j).
+  auto read_k = [&](int t, bf16x8 (&ka)[8]) {
+    const Tile& st = kbuf[t & 1];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int ch = 2 * s + hh;
-        const bf16x8 ka = __builtin_bit_cast(bf16x8, st.k[ln * 8 + (ch ^ k_swz(ln))]);
-        const bf16x8 kb = __builtin_bit_cast(bf16x8, st.k[(32 + ln) * 8 + (ch ^ k_swz(32 + ln))]);
-        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[s], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb, qf[s], s1, 0, 0, 0);
-      }
+    for (int s = 0; s < 4; ++s) {
+      const int ch = 2 * s + hh;
+      ka[s] = __builtin_bit_cast(bf16x8, st.c[ln * 8 + (ch ^ k_swz(ln))]);
+      ka[4 + s] = __builtin_bit_cast(bf16x8, st.c[(32 + ln) * 8 + (ch ^ k_swz(32 + ln))]);
+    }
+  };
+  auto read_v = [&](int t, bf16x8 (&va)[8]) {
+    const Tile& vt = vbuf[t & 1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ch = 2 * i + hh;  // = 4 blk + 2 j + hh for i = 2 blk + j
+      va[i] = __builtin_bit_cast(bf16x8, vt.c[ln * 8 + (ch ^ vt_swz(ln))]);
+      va[4 + i] = __builtin_bit_cast(bf16x8, vt.c[(32 + ln) * 8 + (ch ^ vt_swz(32 + ln))]);
+    }
+  };
 
-      // ---- mask in registers (only tiles that cross a boundary).  Register
-      // r of block blk holds key k0 + 32 blk + 8 (r / 4) + 4 hh + r % 4.
-      const bool need_mask = (k0 + kBN > kv_lim) || (CAUSAL && k0 + kBN - 1 > qw0);
-      if (need_mask) {
+  // S^T of a tile: two 32-key blocks x four 16-wide d steps.
+  auto qk = [&](const bf16x8 (&ka)[8], f32x16& s0, f32x16& s1) {
+    s0 = f32x16{};
+    s1 = f32x16{};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s], qf[s], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[4 + s], qf[s], s1, 0, 0, 0);
+    }
+  };
+
+  f32x16 o0 = {}, o1 = {};  // O^T blocks: d 0..31 and d 32..63, column = query ln
+  float mc = 0.f;           // pivot term of the exponent, m * c
+  float l = 0.f;            // this half-wave's partial row sum of bf16 weights
+
+  // O^T += V^T P^T: per 32-key block, two 16-key steps.
+  auto pv = [&](const bf16x8 (&va)[8], const uint32_t (&pk)[16]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bf16x8 pb = __builtin_bit_cast(bf16x8, make_uint4(pk[4 * i], pk[4 * i + 1], pk[4 * i + 2], pk[4 * i + 3]));
+      o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i], pb, o0, 0, 0, 0);
+      o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[4 + i], pb, o1, 0, 0, 0);
+    }
+  };
+
+  // Move the pivot of the rows flagged `move` (by either half-wave) to their
+  // tile max (in exponent units); other rows keep theirs.  Rescales O and l
+  // and recomputes this tile's weights under the pivots now in force.
+  auto move_pivot = [&](bool move, const f32x16& s0, const f32x16& s1, uint32_t (&pk)[16]) -> float {
+    move = half_swap_or(move);  // both half-waves of a row must agree
+    float tmax = fmaxf(s0[0], s1[0]);
+#pragma unroll
+    for (int r = 1; r < 16; ++r) tmax = fmaxf(tmax, fmaxf(s0[r], s1[r]));
+    tmax = half_swap_max(tmax);
+    const float tm = tmax * c;  // tile max in exponent units
+    const float m_new = (move && tm > -INFINITY) ? tm : mc;
+    // Exactly 1 where unmoved.  A downward move only happens on the first
+    // tile (underflow check), where O and l are still 0: keep alpha = 1 there
+    // rather than scaling zeros by a possibly infinite factor.
+    const float alpha = m_new > mc ? __builtin_amdgcn_exp2f(mc - m_new) : 1.f;
+    l *= alpha;
+    o0 *= alpha;
+    o1 *= alpha;
+    mc = m_new;
+    return exp_pack_sum(s0, s1, c, mc, pk);
+  };
+
+  // General step for tile t: scores of tile t+1 into (sn0, sn1), mask and
+  // pivot checks, weights and P.V of tile t from (sc0, sc1), and the staging
+  // of K(t+2), V(t+1).  Used for the first tile and for tiles that cross the
+  // causal diagonal or the key-length boundary.
+  auto general_step = [&](int t, f32x16& sc0, f32x16& sc1, f32x16& sn0, f32x16& sn1) {
+    gload(t + 2, t + 1);
+    if (t + 1 < wave_tiles) {
+      bf16x8 ka[8];
+      read_k(t + 1, ka);
+      qk(ka, sn0, sn1);
+    }
+    if (t < wave_tiles) {
+      const int k0 = t * kBN;
+      // Register r of block blk holds key k0 + 32 blk + 8 (r / 4) + 4 hh + r % 4;
+      // the lane's allowed keys are those below `lim`, so each register is
+      // one compare of a constant offset against lim - k0 - 4 hh.
+      if ((k0 + kBN > kv_lim) || (CAUSAL && k0 + kBN - 1 > qw0)) {
+        const int lim = (CAUSAL ? min(kv_lim, qi + 1) : kv_lim) - k0 - 4 * hh;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = k0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-          const bool ok0 = key < kv_lim && (!CAUSAL || key <= qi);
-          const bool ok1 = key + 32 < kv_lim && (!CAUSAL || key + 32 <= qi);
-          s0[r] = ok0 ? s0[r] : -INFINITY;
-          s1[r] = ok1 ? s1[r] : -INFINITY;
+          const int off = 8 * (r >> 2) + (r & 3);
+          sc0[r] = off < lim ? sc0[r] : -INFINITY;
+          sc1[r] = off + 32 < lim ? sc1[r] : -INFINITY;
         }
       }
-
-      // ---- online softmax
-      float tmax = fmaxf(s0[0], s1[0]);
-#pragma unroll
-      for (int r = 1; r < 16; ++r) tmax = fmaxf(tmax, fmaxf(s0[r], s1[r]));
-      tmax = half_swap_max(tmax);
-      const bool move = tmax > m_use + thr;  // also true on the first allowed tile
-      if (__builtin_amdgcn_ballot_w64(move) != 0) {
-        // Lanes that do not need a move keep their pivot (alpha = 1 exactly),
-        // so a row's arithmetic never depends on the other rows of its wave.
-        const float m_new = move ? fmaxf(m_use, tmax) : m_use;
-        const float alpha = (m_use == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m_use - m_new) * c);
-        l *= alpha;
-        o0 *= alpha;
-        o1 *= alpha;
-        m_use = m_new;
-      }
-      const float mc = (m_use == -INFINITY) ? 0.f : m_use * c;
-      float psum = 0.f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s0[r] = __builtin_amdgcn_exp2f(fmaf(s0[r], c, -mc));
-        s1[r] = __builtin_amdgcn_exp2f(fmaf(s1[r], c, -mc));
-        psum += s0[r] + s1[r];
-      }
-      l += psum;
-
-      // ---- O^T += V^T P^T: per 32-key block, two 16-key steps
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
-        const f32x16& p = blk ? s1 : s0;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          uint4 pw;
-          pw.x = pack_bf16x2(p[8 * j + 0], p[8 * j + 1]);
-          pw.y = pack_bf16x2(p[8 * j + 2], p[8 * j + 3]);
-          pw.z = pack_bf16x2(p[8 * j + 4], p[8 * j + 5]);
-          pw.w = pack_bf16x2(p[8 * j + 6], p[8 * j + 7]);
-          const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
-          const int ch = 4 * blk + 2 * j + hh;
-          const bf16x8 va = __builtin_bit_cast(bf16x8, st.vt[ln * 8 + (ch ^ vt_swz(ln))]);
-          const bf16x8 vb = __builtin_bit_cast(bf16x8, st.vt[(32 + ln) * 8 + (ch ^ vt_swz(32 + ln))]);
-          o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, o0, 0, 0, 0);
-          o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb, pb, o1, 0, 0, 0);
-        }
-      }
+      uint32_t pk[16];
+      float lt = exp_pack_sum(sc0, sc1, c, mc, pk);
+      // Pivot checks: a tile sum past 2^64 (also catches inf), or, on the
+      // first tile, a row sum so small that the row could be lost to
+      // underflow.  NaN (garbage in padded rows) triggers neither.
+      bool move = lt > kPivotHigh;
+      if (t == 0) move = move || half_swap_sum(lt) < kPivotLow;
+      if (__builtin_amdgcn_ballot_w64(move) != 0) lt = move_pivot(move, sc0, sc1, pk);
+      l += lt;
+      bf16x8 va[8];
+      read_v(t, va);
+      pv(va, pk);
     }
-
-    if (t + 1 < n_tiles) lstore(lds[(t + 1) & 1]);
+    lstore(t + 2, t + 1);
     __syncthreads();
+  };
+
+  // Fast step for a tile t >= 1 such that tiles t and t+1 need no mask for
+  // any wave: straight-line code except a rarely taken pivot move, so the
+  // scores of tile t+1 (MFMA) overlap the weights of tile t (VALU).  Staging
+  // is unconditional: rows past the valid keys read as zero and land in a
+  // buffer no later step reads.
+  auto fast_step = [&](int t, f32x16& sc0, f32x16& sc1, f32x16& sn0, f32x16& sn1) {
+    gload(t + 2, t + 1, false);
+    if (wave_tiles > 0) {
+      bf16x8 ka[8], va[8];
+      read_k(t + 1, ka);
+      read_v(t, va);
+      qk(ka, sn0, sn1);
+      uint32_t pk[16];
+      float lt = exp_pack_sum(sc0, sc1, c, mc, pk);
+      const bool move = lt > kPivotHigh;
+      if (__builtin_amdgcn_ballot_w64(move) != 0) lt = move_pivot(move, sc0, sc1, pk);
+      l += lt;
+      pv(va, pk);
+    }
+    lstore(t + 2, t + 1, false);
+    __syncthreads();
+  };
+
+  // Tiles [0, t_free) need no mask for any wave of the workgroup.
+  int t_free = n_tiles;
+  if (CAUSAL) t_free = min(t_free, q0 / kBN);
+  t_free = min(t_free, kv_lim / kBN);
+  const int fast_end = t_free - 1;  // fast steps are t in [1, fast_end)
+
+  f32x16 sa0 = {}, sa1 = {}, sb0 = {}, sb1 = {};
+  int t = 0;
+  if (n_tiles > 0) {
+    gload(0, n_tiles);  // K(0)
+    lstore(0, n_tiles);
+    gload(1, 0);        // K(1), V(0)
+    __syncthreads();
+    if (0 < wave_tiles) {
+      bf16x8 ka[8];
+      read_k(0, ka);
+      qk(ka, sa0, sa1);
+    }
+    lstore(1, 0);
+    __syncthreads();
+    general_step(0, sa0, sa1, sb0, sb1);
+    t = 1;
   }
+  // After step t-1 the scores of tile t sit in (sb0, sb1) for odd t and in
+  // (sa0, sa1) for even t.  Every step ends in exactly one barrier.
+#pragma nounroll
+  for (; t + 1 < fast_end; t += 2) {
+    fast_step(t, sb0, sb1, sa0, sa1);
+    fast_step(t + 1, sa0, sa1, sb0, sb1);
+  }
+  if (t < fast_end) {
+    fast_step(t, sb0, sb1, sa0, sa1);
+    ++t;
+  }
+  if (t & 1) {  // once: put the scores of tile t in (sa0, sa1)
+    const f32x16 x0 = sa0, x1 = sa1;
+    sa0 = sb0;
+    sa1 = sb1;
+    sb0 = x0;
+    sb1 = x1;
+  }
+#pragma nounroll
+  for (; t + 1 < n_tiles; t += 2) {
+    general_step(t, sa0, sa1, sb0, sb1);
+    general_step(t + 1, sb0, sb1, sa0, sa1);
+  }
+  if (t < n_tiles) general_step(t, sa0, sa1, sb0, sb1);
 
   // ---- epilogue: O[qi][d] = acc / l.  Register r of block ob holds
   // d = 32 ob + 8 (r / 4) + 4 hh + r % 4: four consecutive d per group.
-  const float l_row = half_swap_sum(l);
   // Padded query rows and rows with no allowed key are written as exact
   // zeros (a select, so garbage in a padded Q row cannot leak through).
+  const float l_row = half_swap_sum(l);
   const bool live = qi < q_len && l_row > 0.f;
   const float inv = live ? 1.f / l_row : 0.f;
   if (qi < a.n_q) {

@@ -187,3 +187,25 @@ def test_decode_matches_forward_last_row(dtype):
     ref = np.stack([np64(full)[b, :, int(lens[b]) - 1] for b in range(B)])
     tol = 4e-2 if dtype == BF16 else 2e-6
     assert np.abs(got - ref).max() <= tol * max(1.0, np.abs(ref).max())
+
+
+@pytest.mark.parametrize("dtype", [BF16, F32], ids=["bf16", "fp32"])
+@pytest.mark.parametrize("mask,scale", [(0, 0.125), (2, 0.125), (0, 1.0), (1, 0.125)],
+                         ids=["none", "causal", "scale1", "kpad"])
+def test_logit_spikes(dtype, mask, scale):
+    """Planted keys whose logits are far above the rest (exponents beyond 2^64
+    at the pages' scale), late in long rows, and rows whose logits are all far
+    below zero: the softmax must stay stable wherever the spike lands."""
+    B, H, n = 2, 2, 700
+    c = _case(31337, B, H, n, n, mask, dtype, kv_lens=[700, 555] if mask & 1 else None,
+              scale=scale)
+    Q, K = c["Q"].float(), c["K"].float()
+    for b in range(B):
+        for h in range(H):
+            for i, j in ((10, 400), (300, 650), (5, 64), (600, 599)):
+                K[b, h, j] = 9.0 * Q[b, h, i]          # q_i . k_j = 9 |q_i|^2 ~ 576
+            Q[b, h, 640:660] = -6.0 * K[b, h, :20].mean(0)  # uniformly very negative rows
+    c["Q"], c["K"] = Q.to(dtype), K.to(dtype)
+    say(f"[logit spikes {dtype} mask{mask} scale{scale}]")
+    out = _gpu_call(c)
+    check(np64(out), _oracle_call(c), dtype, f"spikes mask{mask} scale{scale}")
