@@ -42,6 +42,8 @@
 // softmax.  Tiles that need a mask or a pivot take a general step with
 // branches.  K runs one tile ahead of V in LDS; each is double buffered, and
 // one barrier per tile separates reuse.
+#include <type_traits>
+
 #include "common.h"
 
 namespace headattn {
@@ -65,7 +67,8 @@ constexpr float kPivotLow = 0x1p-64f;  // a first-tile row sum below this moves 
 // One LDS tile: 64 rows x 128 B as 8 chunks of 16 B.  K tiles are stored
 // [key][chunk], V^T tiles [d][chunk of 8 keys].  Chunks are XOR-swizzled per
 // row so 8 lanes reading the same logical chunk of 8 consecutive rows hit 8
-// different chunk positions.
+// different chunk positions.  (Measured faster than padding the rows to
+// 144 B, although padding needs fewer address registers.)
 struct Tile {
   uint4 c[64 * 8];
 };
@@ -326,118 +329,130 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
     return exp_pack_sum(s0, s1, c, mc, pk);
   };
 
-  // General step for tile t: scores of tile t+1 into (sn0, sn1), mask and
-  // pivot checks, weights and P.V of tile t from (sc0, sc1), and the staging
-  // of K(t+2), V(t+1).  Used for the first tile and for tiles that cross the
-  // causal diagonal or the key-length boundary.
-  auto general_step = [&](int t, f32x16& sc0, f32x16& sc1, f32x16& sn0, f32x16& sn1) {
-    gload(t + 2, t + 1);
-    if (t + 1 < wave_tiles) {
-      bf16x8 ka[8];
-      read_k(t + 1, ka);
-      qk(ka, sn0, sn1);
-    }
-    if (t < wave_tiles) {
-      const int k0 = t * kBN;
-      // Register r of block blk holds key k0 + 32 blk + 8 (r / 4) + 4 hh + r % 4;
-      // the lane's allowed keys are those below `lim`, so each register is
-      // one compare of a constant offset against lim - k0 - 4 hh.
-      if ((k0 + kBN > kv_lim) || (CAUSAL && k0 + kBN - 1 > qw0)) {
-        const int lim = (CAUSAL ? min(kv_lim, qi + 1) : kv_lim) - k0 - 4 * hh;
+  // Weights of tile t from its scores (sc0, sc1): mask (only on tiles that
+  // cross the causal diagonal or the key-length boundary), exp2, bf16 pack
+  // and row sums.  Returns the tile's row-sum contribution.
+  auto weights = [&](int t, f32x16& sc0, f32x16& sc1, uint32_t (&pk)[16]) -> float {
+    const int k0 = t * kBN;
+    // Register r of block blk holds key k0 + 32 blk + 8 (r / 4) + 4 hh + r % 4;
+    // the lane's allowed keys are those below `lim`, so each register is
+    // one compare of a constant offset against lim - k0 - 4 hh.
+    if ((k0 + kBN > kv_lim) || (CAUSAL && k0 + kBN - 1 > qw0)) {
+      const int lim = (CAUSAL ? min(kv_lim, qi + 1) : kv_lim) - k0 - 4 * hh;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int off = 8 * (r >> 2) + (r & 3);
-          sc0[r] = off < lim ? sc0[r] : -INFINITY;
-          sc1[r] = off + 32 < lim ? sc1[r] : -INFINITY;
-        }
+      for (int r = 0; r < 16; ++r) {
+        const int off = 8 * (r >> 2) + (r & 3);
+        sc0[r] = off < lim ? sc0[r] : -INFINITY;
+        sc1[r] = off + 32 < lim ? sc1[r] : -INFINITY;
       }
-      uint32_t pk[16];
-      float lt = exp_pack_sum(sc0, sc1, c, mc, pk);
-      // Pivot checks: a tile sum past 2^64 (also catches inf), or, on the
-      // first tile, a row sum so small that the row could be lost to
-      // underflow.  NaN (garbage in padded rows) triggers neither.
-      bool move = lt > kPivotHigh;
-      if (t == 0) move = move || half_swap_sum(lt) < kPivotLow;
-      if (__builtin_amdgcn_ballot_w64(move) != 0) lt = move_pivot(move, sc0, sc1, pk);
-      l += lt;
-      bf16x8 va[8];
-      read_v(t, va);
-      pv(va, pk);
     }
-    lstore(t + 2, t + 1);
-    __syncthreads();
+    return exp_pack_sum(sc0, sc1, c, mc, pk);
+  };
+  // Pivot checks on a tile's weights: a tile sum past 2^64 (also catches
+  // inf), or, on a row's first tile, a row sum so small that the row could be
+  // lost to underflow.  NaN (garbage in padded rows) triggers neither.
+  auto check = [&](float lt, bool first, f32x16& sc0, f32x16& sc1, uint32_t (&pk)[16]) -> float {
+    bool move = lt > kPivotHigh;
+    if (first) move = move || half_swap_sum(lt) < kPivotLow;
+    if (__builtin_amdgcn_ballot_w64(move) != 0) lt = move_pivot(move, sc0, sc1, pk);
+    return lt;
   };
 
-  // Fast step for a tile t >= 1 such that tiles t and t+1 need no mask for
-  // any wave: straight-line code except a rarely taken pivot move, so the
-  // scores of tile t+1 (MFMA) overlap the weights of tile t (VALU).  Staging
-  // is unconditional: rows past the valid keys read as zero and land in a
-  // buffer no later step reads.
-  auto fast_step = [&](int t, f32x16& sc0, f32x16& sc1, f32x16& sn0, f32x16& sn1) {
-    gload(t + 2, t + 1, false);
-    if (wave_tiles > 0) {
+  // One pipeline step t (0 <= t <= n_tiles).  The matrix cores compute the
+  // scores of tile t+1 (into sn) and O += P(t-1) V(t-1) (from pp, checked in
+  // the previous step) while the vector ALUs form the weights of tile t (from
+  // sc, into pc); then K(t+2) and V(t) are staged and one barrier closes the
+  // step.  GENERAL adds the range, activity and mask checks that the first
+  // and last tiles and the tiles on the causal diagonal or the key-length
+  // boundary need; the fast form is straight-line code apart from a rarely
+  // taken pivot move.
+  auto step = [&](auto general_tag, int t, f32x16& sc0, f32x16& sc1, f32x16& sn0, f32x16& sn1,
+                  uint32_t (&pc)[16], uint32_t (&pp)[16]) {
+    constexpr bool GENERAL = decltype(general_tag)::value;
+    gload(t + 2, t, GENERAL);
+    if (GENERAL) {
+      if (t + 1 < wave_tiles) {
+        bf16x8 ka[8];
+        read_k(t + 1, ka);
+        qk(ka, sn0, sn1);
+      }
+      if (t >= 1 && t - 1 < wave_tiles) {
+        bf16x8 va[8];
+        read_v(t - 1, va);
+        pv(va, pp);
+      }
+      if (t < wave_tiles) l += check(weights(t, sc0, sc1, pc), t == 0, sc0, sc1, pc);
+    } else {
       bf16x8 ka[8], va[8];
       read_k(t + 1, ka);
-      read_v(t, va);
+      read_v(t - 1, va);
       qk(ka, sn0, sn1);
-      uint32_t pk[16];
-      float lt = exp_pack_sum(sc0, sc1, c, mc, pk);
-      const bool move = lt > kPivotHigh;
-      if (__builtin_amdgcn_ballot_w64(move) != 0) lt = move_pivot(move, sc0, sc1, pk);
-      l += lt;
-      pv(va, pk);
+      pv(va, pp);
+      const float lt = weights(t, sc0, sc1, pc);
+      l += check(lt, false, sc0, sc1, pc);
     }
-    lstore(t + 2, t + 1, false);
+    lstore(t + 2, t, GENERAL);
     __syncthreads();
   };
+  using General = std::integral_constant<bool, true>;
+  using Fast = std::integral_constant<bool, false>;
 
-  // Tiles [0, t_free) need no mask for any wave of the workgroup.
+  // Tiles [0, t_free) need no mask for any wave of the workgroup; step t is
+  // fast when 1 <= t and t + 1 < t_free (tiles t-1, t, t+1 all mask-free, so
+  // every active wave works on all three).
   int t_free = n_tiles;
   if (CAUSAL) t_free = min(t_free, q0 / kBN);
   t_free = min(t_free, kv_lim / kBN);
   const int fast_end = t_free - 1;  // fast steps are t in [1, fast_end)
 
   f32x16 sa0 = {}, sa1 = {}, sb0 = {}, sb1 = {};
+  uint32_t pa[16] = {}, pb[16] = {};
   int t = 0;
   if (n_tiles > 0) {
     gload(0, n_tiles);  // K(0)
     lstore(0, n_tiles);
-    gload(1, 0);        // K(1), V(0)
+    gload(1, n_tiles);  // K(1)
     __syncthreads();
     if (0 < wave_tiles) {
       bf16x8 ka[8];
       read_k(0, ka);
       qk(ka, sa0, sa1);
     }
-    lstore(1, 0);
+    lstore(1, n_tiles);
     __syncthreads();
-    general_step(0, sa0, sa1, sb0, sb1);
+    step(General(), 0, sa0, sa1, sb0, sb1, pa, pb);
     t = 1;
   }
-  // After step t-1 the scores of tile t sit in (sb0, sb1) for odd t and in
-  // (sa0, sa1) for even t.  Every step ends in exactly one barrier.
+  // After step t-1: the scores of tile t sit in (sb0, sb1) and the weights of
+  // tile t-1 in pa for odd t; (sa0, sa1) and pb for even t.
 #pragma nounroll
   for (; t + 1 < fast_end; t += 2) {
-    fast_step(t, sb0, sb1, sa0, sa1);
-    fast_step(t + 1, sa0, sa1, sb0, sb1);
+    step(Fast(), t, sb0, sb1, sa0, sa1, pb, pa);
+    step(Fast(), t + 1, sa0, sa1, sb0, sb1, pa, pb);
   }
   if (t < fast_end) {
-    fast_step(t, sb0, sb1, sa0, sa1);
+    step(Fast(), t, sb0, sb1, sa0, sa1, pb, pa);
     ++t;
   }
-  if (t & 1) {  // once: put the scores of tile t in (sa0, sa1)
+  if (t & 1) {  // once: bring tile t's scores to (sa0, sa1) and tile t-1's weights to pb
     const f32x16 x0 = sa0, x1 = sa1;
     sa0 = sb0;
     sa1 = sb1;
     sb0 = x0;
     sb1 = x1;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t x = pa[i];
+      pa[i] = pb[i];
+      pb[i] = x;
+    }
   }
 #pragma nounroll
-  for (; t + 1 < n_tiles; t += 2) {
-    general_step(t, sa0, sa1, sb0, sb1);
-    general_step(t + 1, sb0, sb1, sa0, sa1);
+  for (; t + 1 <= n_tiles; t += 2) {
+    step(General(), t, sa0, sa1, sb0, sb1, pa, pb);
+    step(General(), t + 1, sb0, sb1, sa0, sa1, pb, pa);
   }
-  if (t < n_tiles) general_step(t, sa0, sa1, sb0, sb1);
+  if (n_tiles > 0 && t == n_tiles) step(General(), t, sa0, sa1, sb0, sb1, pa, pb);
 
   // ---- epilogue: O[qi][d] = acc / l.  Register r of block ob holds
   // d = 32 ob + 8 (r / 4) + 4 hh + r % 4: four consecutive d per group.
