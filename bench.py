@@ -161,33 +161,32 @@ def sanity_check(legs):
 
 
 # ------------------------------------------------------------ CPU baseline
-def cpu_baseline(target_s: float = 15.0):
+def cpu_baseline(target_s: float = 25.0):
     """The fp64 oracle as it stands, single-threaded BLAS, on a bounded
-    sample of the long_causal workload: evenly spaced query rows of head 0
-    (each row does its full causal prefix).  Throughput in the same
-    algorithmic flop units as the GPU number."""
+    sample of the long_causal workload: evenly spaced query rows of every
+    head (each row does its full causal prefix), sized from a short probe to
+    take about target_s.  Throughput in the same algorithmic flop units as
+    the GPU number."""
     import oracle.attn_oracle as orc
     try:
         from threadpoolctl import threadpool_limits
     except ImportError:  # pragma: no cover
         threadpool_limits = None
     c = workloads.make("long_causal")["calls"][0]
-    Q = c["Q"][:, :1].float().double().numpy()
-    K = c["K"][:, :1].float().double().numpy()
-    V = c["V"][:, :1].float().double().numpy()
-    n = Q.shape[2]
+    Q, K, V = (c[k].float().double().numpy() for k in ("Q", "K", "V"))
+    H, n = Q.shape[1], Q.shape[2]
     ctx = threadpool_limits(limits=1) if threadpool_limits else None
     try:
         if ctx:
             ctx.__enter__()
-        # size the sample from a short probe so the run lasts about target_s
+        # probe: rows spread over the causal lengths; the mean row is half length
         probe = [(0, 0, i) for i in range(n - 1, 0, -(n // 8))]
         t0 = time.perf_counter()
         orc.attention(Q, K, V, mask_kind=orc.MASK_CAUSAL, scale=0.125, rows=probe)
-        per_row = (time.perf_counter() - t0) / len(probe) * 0.5  # average row is half length
-        n_rows = int(max(16, min(n, target_s / max(per_row, 1e-6))))
-        stride = max(1, n // n_rows)
-        rows = [(0, 0, i) for i in range(stride // 2, n, stride)]
+        per_row = (time.perf_counter() - t0) / sum(i + 1 for (_, _, i) in probe) * (n / 2)
+        per_head = int(max(16, min(n, target_s / max(per_row, 1e-9) / H)))
+        stride = max(1, n // per_head)
+        rows = [(0, h, i) for h in range(H) for i in range((stride // 2 + h) % stride, n, stride)]
         t0 = time.perf_counter()
         orc.attention(Q, K, V, mask_kind=orc.MASK_CAUSAL, scale=0.125, rows=rows)
         dt = time.perf_counter() - t0
@@ -195,13 +194,15 @@ def cpu_baseline(target_s: float = 15.0):
         if ctx:
             ctx.__exit__(None, None, None)
     flops = sum(4 * D * (i + 1) for (_, _, i) in rows)
+    what = ("all query rows" if stride == 1 else
+            f"every {stride}th query row (offset by head)")
     return {
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": f"long_causal head 0, {len(rows)} query rows evenly spaced over n=8192 "
-                  f"(stride {stride}), full causal prefix each; fp64 NumPy, 1 BLAS thread; "
+        "sample": f"long_causal (B1 h16 n=8192 causal): {what} of all {H} heads, "
+                  f"{len(rows)} rows, full causal prefix each; fp64 NumPy, 1 BLAS thread; "
                   f"{dt:.1f} s",
     }
 

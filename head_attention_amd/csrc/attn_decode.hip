@@ -29,6 +29,7 @@ namespace {
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 template <typename T>
 struct Elem;
@@ -59,6 +60,55 @@ struct Elem<__bf16> {
 
 constexpr int kWaveKeys = 64;  // keys per wave per chunk
 
+// One 16-byte non-temporal load.
+template <typename T>
+__device__ __forceinline__ uint4 stream_load(const T* p) {
+  return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)));
+}
+
+// Cross-lane combines on the vector ALUs (DPP and permlane swaps; no LDS
+// traffic).  Each pairs every lane with one partner; repeated, they reduce
+// over aligned groups of 2, 4, 8, 16, 32 and 64 lanes.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+struct Sum {
+  __device__ static float op(float a, float b) { return a + b; }
+};
+struct Max {
+  __device__ static float op(float a, float b) { return fmaxf(a, b); }
+};
+// Combine lane l with lane l ^ step (step = 1, 2), its mirror in its group of
+// 8 (step 4), its partner 8 apart in a row of 16 (step 8), or across rows of
+// 16 (step 16) or halves of the wave (step 32).
+template <class Op, int STEP>
+__device__ __forceinline__ float combine(float v) {
+  if constexpr (STEP == 1) return Op::op(v, dpp_mov<0xB1>(v));   // quad_perm [1,0,3,2]
+  if constexpr (STEP == 2) return Op::op(v, dpp_mov<0x4E>(v));   // quad_perm [2,3,0,1]
+  if constexpr (STEP == 4) return Op::op(v, dpp_mov<0x141>(v));  // row_half_mirror
+  if constexpr (STEP == 8) return Op::op(v, dpp_mov<0x128>(v));  // row_ror:8
+  if constexpr (STEP == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    // take the two halves by value: a bit cast of a vector element lvalue
+    // would read element 0 for both
+    const uint32_t lo = r[0], hi = r[1];
+    return Op::op(__uint_as_float(lo), __uint_as_float(hi));
+  }
+  if constexpr (STEP == 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    const uint32_t lo = r[0], hi = r[1];
+    return Op::op(__uint_as_float(lo), __uint_as_float(hi));
+  }
+  return v;
+}
+// Reduce over lanes [FROM, TO) in the power-of-two ladder of steps.
+template <class Op, int FROM, int TO>
+__device__ __forceinline__ float reduce(float v) {
+  if constexpr (FROM < TO) return reduce<Op, FROM * 2, TO>(combine<Op, FROM>(v));
+  return v;
+}
+
 template <typename T>
 __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partial_kernel(DecodeArgs a) {
   constexpr int EPL = Elem<T>::kPerLoad;       // elements per lane slice
@@ -66,8 +116,15 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partial_kernel(Decod
   constexpr int KPP = 64 / LPR;                // keys per pass of a wave
   constexpr int NP = kWaveKeys / KPP;          // passes per wave
 
-  const int split = blockIdx.x % a.n_split;
-  const int bh = blockIdx.x / a.n_split;
+  // Split-major order: consecutive workgroups, which the dispatcher deals
+  // round-robin to the 8 XCDs, take the same chunk index of different
+  // (b, h).  Chunk s is valid only where kv_len > 256 s, so a (b, h)-major
+  // order would hand XCD x mostly chunks x and x + 8 of every row and load
+  // the XCDs unevenly under ragged lengths; this order gives every XCD the
+  // same mix of heads.
+  const int BH = a.B * a.H;
+  const int split = blockIdx.x / BH;
+  const int bh = blockIdx.x % BH;
   const int b = bh / a.H;
   const int kv_len = clamp_len(a.kv_lens[b], a.n_max);
   const int chunk0 = split * kDecodeChunk;
@@ -85,13 +142,15 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partial_kernel(Decod
   const T* Vc = static_cast<const T*>(a.Vc) + (size_t)bh * a.n_max * kHeadDim;
 
   // Issue every K and V load of this wave up front (2 x NP x 16 B per lane).
+  // The cache is read once per step, so the loads are marked non-temporal:
+  // streamed past the caches instead of evicting lines that are reused.
   uint4 kraw[NP], vraw[NP];
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
     const int key = w0 + p * KPP + kk;
     if (key < kv_len) {
-      kraw[p] = *reinterpret_cast<const uint4*>(Kc + (size_t)key * kHeadDim + EPL * sl);
-      vraw[p] = *reinterpret_cast<const uint4*>(Vc + (size_t)key * kHeadDim + EPL * sl);
+      kraw[p] = stream_load(Kc + (size_t)key * kHeadDim + EPL * sl);
+      vraw[p] = stream_load(Vc + (size_t)key * kHeadDim + EPL * sl);
     } else {  // never read: padded rows may hold anything, even NaN
       kraw[p] = make_uint4(0, 0, 0, 0);
       vraw[p] = make_uint4(0, 0, 0, 0);
@@ -115,14 +174,12 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partial_kernel(Decod
     float part = 0.f;
 #pragma unroll
     for (int e = 0; e < EPL; ++e) part = fmaf(qv[e], kv[e], part);
-#pragma unroll
-    for (int off = 1; off < LPR; off <<= 1) part += __shfl_xor(part, off);
+    part = reduce<Sum, 1, LPR>(part);  // dot product over the row's LPR lanes
     const int key = w0 + p * KPP + kk;
     s[p] = key < kv_len ? sgn * part * c : -INFINITY;
     mloc = fmaxf(mloc, s[p]);
   }
-#pragma unroll
-  for (int off = LPR; off < 64; off <<= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, off));
+  mloc = reduce<Max, LPR, 64>(mloc);
   const float m = mloc;  // wave max (-inf if the wave has no valid key)
 
   float acc[EPL];
@@ -143,11 +200,8 @@ __global__ __launch_bounds__(64 * kDecodeWaves) void decode_partial_kernel(Decod
   // Sum over the keys of the wave: the lanes with the same slice sit LPR
   // apart, and each of them saw every key of its own passes once.
 #pragma unroll
-  for (int off = LPR; off < 64; off <<= 1) {
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] += __shfl_xor(acc[e], off);
-    lsum += __shfl_xor(lsum, off);
-  }
+  for (int e = 0; e < EPL; ++e) acc[e] = reduce<Sum, LPR, 64>(acc[e]);
+  lsum = reduce<Sum, LPR, 64>(lsum);
 
   // ---- merge the 4 wave partials of this chunk in LDS
   __shared__ float sm[kDecodeWaves], sl_[kDecodeWaves];
@@ -197,13 +251,32 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs a) {
   const int kv_len = clamp_len(a.kv_lens[b], a.n_max);
   const int ns = (kv_len + kDecodeChunk - 1) / kDecodeChunk;
   const float* rec = a.work + (size_t)bh * a.n_split * kPartialStride;
+  // M = max of the split maxima: lane s reads m_s, then a wave max.
   float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, rec[s * kPartialStride]);
+  for (int s0 = 0; s0 < ns; s0 += 64) {
+    const int s = s0 + d;
+    M = fmaxf(M, s < ns ? rec[(size_t)s * kPartialStride] : -INFINITY);
+  }
+  M = reduce<Max, 1, 64>(M);
+  // O[d] = sum_s 2^(m_s - M) acc_s[d] / sum_s 2^(m_s - M) l_s, eight splits'
+  // loads in flight at a time.
   float L = 0.f, A = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const float f = __builtin_amdgcn_exp2f(rec[s * kPartialStride] - M);
-    L = fmaf(f, rec[s * kPartialStride + 1], L);
-    A = fmaf(f, rec[s * kPartialStride + 2 + d], A);
+  for (int s0 = 0; s0 < ns; s0 += 8) {
+    float mv[8], lv[8], av[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const bool ok = s0 + i < ns;
+      const float* r = rec + (size_t)(ok ? s0 + i : 0) * kPartialStride;
+      mv[i] = ok ? r[0] : -INFINITY;
+      lv[i] = r[1];
+      av[i] = r[2 + d];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float f = mv[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mv[i] - M);
+      L = fmaf(f, lv[i], L);
+      A = fmaf(f, av[i], A);
+    }
   }
   // kv_len = 0: no partials, the row is 0.
   const float out = L > 0.f ? A / L : 0.f;
