@@ -209,14 +209,14 @@ def cpu_baseline(target_s: float = 25.0):
 
 # ------------------------------------------------------- rocprof summaries
 def _short_kernel(name: str) -> str:
-    """attn_fwd_bf16_kernel<causal, ...> -> attn_fwd_bf16_kernel<true|false>; other
+    """attn_fwd_bf16[_pair]_kernel<causal, ...> -> ..._kernel<true|false>; other
     kernels of the library by their plain name."""
     import re
-    m = re.search(r"attn_fwd_bf16_kernel<(true|false)", name) or \
-        re.search(r"attn_fwd_bf16_kernelILb(\d)", name)
+    m = re.search(r"(attn_fwd_bf16(?:_pair)?_kernel)<(true|false)", name) or \
+        re.search(r"(attn_fwd_bf16(?:_pair)?_kernel)ILb(\d)", name)
     if m:
-        causal = m.group(1) in ("true", "1")
-        return f"attn_fwd_bf16_kernel<{'true' if causal else 'false'}>"
+        causal = m.group(2) in ("true", "1")
+        return f"{m.group(1)}<{'true' if causal else 'false'}>"
     for key in ("attn_fwd_f32_kernel", "decode_partial_kernel", "decode_merge_kernel",
                 "copyBuffer", "elementwise"):
         if key in name:
@@ -229,7 +229,7 @@ def _short_kernel(name: str) -> str:
 LEG_GRIDS = {("attn_fwd_bf16_kernel<false>", 65536): "encoder_base",
              ("attn_fwd_bf16_kernel<true>", 131072): "decoder_big (causal self)",
              ("attn_fwd_bf16_kernel<false>", 131072): "decoder_big (cross)",
-             ("attn_fwd_bf16_kernel<true>", 262144): "long_causal",
+             ("attn_fwd_bf16_pair_kernel<true>", 262144): "long_causal",
              ("decode_partial_kernel", 4194304): "kv_decode",
              ("decode_merge_kernel", 65536): "kv_decode"}
 
@@ -285,7 +285,7 @@ def summarize_counters(fetch_csv: str, write_csv: str, copy_mib: int, out_json: 
                      f"{write.get(k, 0.0):.1f} | {rd:.2f} | {wr:.2f} |")
         res[f"{k[0]}@{k[1]}"] = {"read_bytes": rd * 1e6, "write_bytes": wr * 1e6}
     if out_json:
-        lc = res.get("attn_fwd_bf16_kernel<true>@262144")
+        lc = res.get("attn_fwd_bf16_pair_kernel<true>@262144")
         with open(out_json, "w") as f:
             json.dump({"kernel_source_hash": kernel_source_hash(),
                        "fetch_scale": f_fetch, "write_scale": f_write,
@@ -410,7 +410,7 @@ def main():
         },
         "roofline": {
             "bound": "mfma",
-            "kernel": "attn_fwd_bf16_kernel<causal> on long_causal (B1 h16 n8192)",
+            "kernel": "attn_fwd_bf16_pair_kernel<causal> on long_causal (B1 h16 n8192)",
             "achieved": round(lc_tflops, 2),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",

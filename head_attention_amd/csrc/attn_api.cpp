@@ -128,7 +128,10 @@ attn_status attn_forward(const void* Q, const void* K, const void* V, attn_layou
   a.n_k = layout.n_k;
   a.scale = scale;
   a.causal = causal;
-  const hipError_t e = layout.dtype == ATTN_BF16 ? launch_fwd_bf16(a, s) : launch_fwd_f32(a, s);
+  hipError_t e;
+  if (layout.dtype == ATTN_F32) e = launch_fwd_f32(a, s);
+  else if (layout.n_q >= kPairMinRows) e = launch_fwd_bf16_pair(a, s);
+  else e = launch_fwd_bf16(a, s);
   if (e != hipSuccess) {
     g_last_hip = e;
     return ATTN_ERR_HIP;

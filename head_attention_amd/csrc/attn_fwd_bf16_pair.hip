@@ -1,0 +1,603 @@
+// bf16 forward of attn_forward for long sequences: paired waves on gfx950.
+//
+// Computes O = softmax(Q K^T * scale + M) V per (b, h) ("[논문 리뷰]Attention
+// Is All You Need", §3.2.1 equation; masking by -inf logits before the
+// softmax, §3.2.3) with the same arithmetic as the 4-wave kernel in
+// attn_fwd_bf16.hip: exact bf16 Q (sign of scale folded in), S^T = K Q^T and
+// O^T += V^T P^T on v_mfma_f32_32x32x16_bf16, weights exp2(s c - m c) with a
+// lazy pivot, bf16 weights, fp32 accumulation.  What differs is how the work
+// is laid over the compute unit.
+//
+// Workgroup: 8 waves own 256 query rows of one (b, h).  The hardware puts
+// waves w and w + 4 on the same SIMD; both take the same 64 rows (row group
+// w % 4), and split the key tiles between them: wave w takes the even 64-key
+// tiles, wave w + 4 the odd ones.  Each wave keeps its own online-softmax
+// state (m, l, O) and the pair merges the two at the end -- the same exact
+// rescale-and-add identity as the decode split merge.
+//
+// Per tile a wave does two phases: an MFMA phase (O += P V of its previous
+// tile, then S = K Q^T of this tile: 32 matrix instructions) and a vector
+// phase (mask, row max and pivot check, exp2, bf16 pack of this tile: ~200
+// VALU instructions).  The pair runs one phase apart and a workgroup barrier
+// closes every phase, so while one wave of a SIMD issues matrix instructions
+// the other issues the exponentials: the two kinds of work overlap across the
+// two waves instead of alternating inside one.  (Measured on MI355X: MFMA
+// and fma/exp/cvt work from two waves of one SIMD overlap, while v_dot2
+// waits for the matrix pipe -- so the row sums, v_dot2 of the bf16 weights
+// with ones, run in the MFMA phase of the wave that owns that pipe.)
+//
+// 64 rows per wave means each K or V fragment read from LDS feeds two query
+// blocks, half the LDS traffic per flop of 32-row waves; the per-wave state
+// (Q 32, S 64, P 32, O 64 VGPRs) still fits the 256 registers that two waves
+// per SIMD leave each wave, because a wave's phases run in sequence and no
+// state is double buffered.
+//
+// K and V tiles reach LDS by buffer loads that write LDS directly (no VGPR
+// staging).  Every wave fills 1 KB of each tile; rows at or beyond the valid
+// length read as zero through the descriptor's range check, so padded K/V
+// memory (even NaN) is never read.  Tiles sit in 4-slot rings, K three phases
+// and V one phase ahead of use; a phase ends with a wait for this wave's
+// fills of two phases ago and a barrier.  K rows keep their 16-byte chunks
+// XOR-swizzled by row; V stays row-major (chunks swizzled by row % 4) and is
+// read transposed with ds_read_b64_tr_b16, which hands each lane four
+// consecutive keys of one d -- the A-operand order of O^T += V^T P^T.
+#include <utility>
+
+#include "common.h"
+
+namespace headattn {
+namespace {
+
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>()), ...);
+}
+// f(integral_constant<int, 0>), ..., f(integral_constant<int, N - 1>)
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>());
+}
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
+
+constexpr int kThreads = 512;
+constexpr int kWaveRows = 64;
+constexpr int kBM = 4 * kWaveRows;  // query rows per workgroup
+constexpr int kBN = 64;             // keys per tile
+constexpr uint32_t kRowBytes = kHeadDim * 2;
+constexpr uint32_t kTileBytes = kBN * kRowBytes;
+constexpr uint32_t kBufferWord3 = 0x00020000u;  // raw buffer, 32-bit elements (gfx9 family)
+// Pivot moves, in exponent (log2) units of a tile's largest weight under the
+// pivot in force: up when it would pass 2^64, down (only while a row has
+// summed nothing) when it would fall below 2^-64.
+constexpr float kPivotUp = 64.f;
+constexpr float kPivotDown = -64.f;
+
+// Ring slots, 8 KB each (64 rows x 8 chunks of 16 B).  Distinct objects, so
+// the compiler tracks the asynchronous LDS writes of the fills per slot.
+__shared__ uint4 g_k0[512], g_k1[512], g_k2[512], g_k3[512];
+__shared__ uint4 g_v0[512], g_v1[512], g_v2[512], g_v3[512];
+// Row sums and pivots of the odd-tile waves for the final merge.
+__shared__ float2 g_lm[4][2][64];
+
+template <int S>
+__device__ __forceinline__ uint4* kslot() {
+  return S == 0 ? g_k0 : S == 1 ? g_k1 : S == 2 ? g_k2 : g_k3;
+}
+template <int S>
+__device__ __forceinline__ uint4* vslot() {
+  return S == 0 ? g_v0 : S == 1 ? g_v1 : S == 2 ? g_v2 : g_v3;
+}
+// The 8 slots in order, as the 64 KB merge area.
+template <int S>
+__device__ __forceinline__ uint4* mslot() {
+  return S < 4 ? (S == 0 ? g_k0 : S == 1 ? g_k1 : S == 2 ? g_k2 : g_k3)
+               : (S == 4 ? g_v0 : S == 5 ? g_v1 : S == 6 ? g_v2 : g_v3);
+}
+
+// Lanes l and l ^ 32 hold the same query row: combine the two half-waves.
+__device__ __forceinline__ float half_swap_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const uint32_t a = r[0], b = r[1];
+  return fmaxf(__uint_as_float(a), __uint_as_float(b));
+}
+__device__ __forceinline__ float half_swap_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const uint32_t a = r[0], b = r[1];
+  return __uint_as_float(a) + __uint_as_float(b);
+}
+__device__ __forceinline__ bool half_swap_or(bool x) {
+  const auto r = __builtin_amdgcn_permlane32_swap((uint32_t)x, (uint32_t)x, false, false);
+  const uint32_t a = r[0], b = r[1];
+  return (a | b) != 0;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// Weights 2^x of one query block of a tile from its exponents x (key blocks
+// x0: keys 0..31, x1: keys 32..63), packed to bf16 pairs in the order P.V
+// consumes them.
+__device__ __forceinline__ void exp_pack(const f32x16& x0, const f32x16& x1, uint32_t (&pk)[16]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    pk[i] = pack_bf16x2(__builtin_amdgcn_exp2f(x0[2 * i]), __builtin_amdgcn_exp2f(x0[2 * i + 1]));
+    pk[8 + i] = pack_bf16x2(__builtin_amdgcn_exp2f(x1[2 * i]), __builtin_amdgcn_exp2f(x1[2 * i + 1]));
+  }
+}
+
+// Max of the 32 values of two accumulator blocks as a shallow tree of
+// 3-input maxima.  The inputs are results of fp32 arithmetic (canonical), so
+// each fmaxf pair folds into one v_max3_f32.
+__device__ __forceinline__ float max32(const f32x16& a, const f32x16& b) {
+  float v[32];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    v[i] = a[i];
+    v[16 + i] = b[i];
+  }
+  float m[11];
+#pragma unroll
+  for (int i = 0; i < 10; ++i) m[i] = fmaxf(fmaxf(v[3 * i], v[3 * i + 1]), v[3 * i + 2]);
+  m[10] = fmaxf(v[30], v[31]);
+  const float n0 = fmaxf(fmaxf(m[0], m[1]), m[2]);
+  const float n1 = fmaxf(fmaxf(m[3], m[4]), m[5]);
+  const float n2 = fmaxf(fmaxf(m[6], m[7]), m[8]);
+  const float n3 = fmaxf(m[9], m[10]);
+  return fmaxf(fmaxf(fmaxf(n0, n1), n2), n3);
+}
+
+// Sum of the 32 bf16 weights of one query block held by this lane, in fp32
+// (v_dot2 with ones: each bf16 is exact in fp32, and the adds are fp32 adds).
+__device__ __forceinline__ float bf16_sum(const uint32_t (&pk)[16]) {
+  const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
+  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    a0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[i]), ones, a0, false);
+    a1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[4 + i]), ones, a1, false);
+    a2 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[8 + i]), ones, a2, false);
+    a3 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[12 + i]), ones, a3, false);
+  }
+  return (a0 + a1) + (a2 + a3);
+}
+
+// End the live range of registers whose value no later path reads, at no
+// cost: an empty volatile asm that "writes" them.  A plain assignment would
+// do the same, but the compiler hoists it onto the hot path (64 moves per
+// phase) or folds it into the accumulator initialisation.
+__device__ __forceinline__ void retire(f32x16& a, f32x16& b, f32x16& c, f32x16& d) {
+  asm volatile("" : "=v"(a), "=v"(b), "=v"(c), "=v"(d));
+}
+__device__ __forceinline__ void retire_frag(bf16x8 (&f)[2][4]) {
+  asm volatile("" : "=v"(f[0][0]), "=v"(f[0][1]), "=v"(f[0][2]), "=v"(f[0][3]));
+  asm volatile("" : "=v"(f[1][0]), "=v"(f[1][1]), "=v"(f[1][2]), "=v"(f[1][3]));
+}
+__device__ __forceinline__ void retire_pk(uint32_t (&p)[16]) {
+  asm volatile("" : "=v"(p[0]), "=v"(p[1]), "=v"(p[2]), "=v"(p[3]), "=v"(p[4]), "=v"(p[5]), "=v"(p[6]), "=v"(p[7]));
+  asm volatile("" : "=v"(p[8]), "=v"(p[9]), "=v"(p[10]), "=v"(p[11]), "=v"(p[12]), "=v"(p[13]), "=v"(p[14]), "=v"(p[15]));
+}
+
+__device__ __forceinline__ void barrier_lds() {
+  // Block the compiler from moving memory accesses across, without the
+  // vmcnt(0) a workgroup fence would add for the in-flight LDS fills; the
+  // scheduling barriers keep register-only work (MFMAs on prefetched
+  // fragments) in its phase as well.
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_pair_kernel(FwdArgs a) {
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int ln = lane & 31;
+  const int hh = lane >> 5;
+  const int rg = wave & 3;    // row group (waves rg and rg + 4 share a SIMD)
+  const int par = wave >> 2;  // parity of the tiles this wave takes
+
+  // ---- (b, h, query tile): the 8 XCDs take workgroup ids round robin; when
+  // B*h divides by 8 each XCD gets whole heads.  Longest tiles first under
+  // the causal mask.
+  const int n_qt = (a.n_q + kBM - 1) / kBM;
+  const int HB = a.H * a.B;
+  const int bid = blockIdx.x;
+  int bh, rank;
+  if ((HB & 7) == 0) {
+    const int per = HB >> 3;
+    const int slot = bid >> 3;
+    rank = slot / per;
+    bh = (bid & 7) * per + slot % per;
+  } else {
+    bh = bid % HB;
+    rank = bid / HB;
+  }
+  const int qt = CAUSAL ? (n_qt - 1 - rank) : rank;
+  const int b = bh / a.H;
+
+  const __bf16* Q = static_cast<const __bf16*>(a.Q) + (size_t)bh * a.n_q * kHeadDim;
+  const __bf16* K = static_cast<const __bf16*>(a.K) + (size_t)bh * a.n_k * kHeadDim;
+  const __bf16* V = static_cast<const __bf16*>(a.V) + (size_t)bh * a.n_k * kHeadDim;
+  __bf16* O = static_cast<__bf16*>(a.O) + (size_t)bh * a.n_q * kHeadDim;
+
+  const int q_len = __builtin_amdgcn_readfirstlane(a.q_lens ? clamp_len(a.q_lens[b], a.n_q) : a.n_q);
+  const int kv_lim = __builtin_amdgcn_readfirstlane(a.kv_lens ? clamp_len(a.kv_lens[b], a.n_k) : a.n_k);
+  const int q0 = qt * kBM;
+  const int qw0 = q0 + kWaveRows * rg;  // first query row of this wave
+
+  int end = kv_lim;  // keys the workgroup needs
+  if (CAUSAL) end = min(end, q0 + kBM);
+  if (q0 >= q_len) end = 0;
+  const int n_tiles = (end + kBN - 1) / kBN;
+  int wave_end = end;  // keys this row group needs
+  if (CAUSAL) wave_end = min(wave_end, qw0 + kWaveRows);
+  if (qw0 >= q_len) wave_end = 0;
+  const int wave_tiles = (wave_end + kBN - 1) / kBN;
+
+  const uint32_t n_bytes = (uint32_t)kv_lim * kRowBytes;
+  const __amdgpu_buffer_rsrc_t rk =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(K), (short)0, (int)n_bytes, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rv =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(V), (short)0, (int)n_bytes, kBufferWord3);
+
+  // ---- tile fills: lane l of wave w writes LDS chunk 64 w + l of the slot,
+  // i.e. row 8 w + l / 8, position l % 8, which holds the row's chunk
+  // (l % 8) ^ swizzle(row).
+  const int frow = 8 * wave + (lane >> 3);
+  const int fpos = lane & 7;
+  const uint32_t koff = (uint32_t)frow * kRowBytes + 16u * (uint32_t)(fpos ^ (frow & 7));
+  const uint32_t voff = (uint32_t)frow * kRowBytes + 16u * (uint32_t)(fpos ^ (2 * (frow & 3)));
+  auto fill_k = [&](auto slot_tag, int t) __attribute__((always_inline)) {
+    constexpr int S = decltype(slot_tag)::value;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(kslot<S>() + 64 * wave), 16,
+                                             (uint32_t)t * kTileBytes + koff, 0, 0, 0);
+  };
+  auto fill_v = [&](auto slot_tag, int t) __attribute__((always_inline)) {
+    constexpr int S = decltype(slot_tag)::value;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(vslot<S>() + 64 * wave), 16,
+                                             (uint32_t)t * kTileBytes + voff, 0, 0, 0);
+  };
+
+  // ---- Q fragments: B operand of S^T = K Q^T for query block qb and d-step
+  // s: lane (ln, hh) holds Q[qw0 + 32 qb + ln][16 s + 8 hh + 0..7], sign of
+  // scale folded in; c = |scale| log2(e), floored at 2^-100 (below that
+  // every weight is exactly 1.0f either way).
+  const float c = fmaxf(fabsf(a.scale) * kLog2e, 0x1p-100f);
+  const uint32_t sign = a.scale < 0.f ? 0x80008000u : 0u;
+  bf16x8 qf[2][4];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int qi = qw0 + 32 * qb + ln;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (qi < a.n_q) v = *reinterpret_cast<const uint4*>(Q + (size_t)qi * kHeadDim + 16 * s + 8 * hh);
+      v.x ^= sign;
+      v.y ^= sign;
+      v.z ^= sign;
+      v.w ^= sign;
+      qf[qb][s] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+
+  // ---- per-wave softmax state.  Accumulator register r of a 32x32 block
+  // holds row/column 8 (r / 4) + 4 hh + r % 4 of the block's M side and
+  // column ln of its N side.
+  f32x16 o[2][2];    // O^T[d block][query block]
+  f32x16 sc[2][2];   // S^T[key block][query block] of the current tile
+  uint32_t pk[2][16];  // bf16 weights [query block][8 key block + pair]
+  float mc[2] = {0.f, 0.f};  // pivot term m * c per query block
+  float l[2] = {0.f, 0.f};   // this half-wave's partial row sums
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      o[i][j] = f32x16{};
+      sc[i][j] = f32x16{};
+    }
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) pk[qb][i] = 0u;
+
+  // MFMA operand fragments, read from LDS at the start of the MFMA phase.
+  // K: [key block][d-step]; lane (ln, hh) holds K[32 kb + ln][16 s + 8 hh +
+  // 0..7].
+  auto load_k = [&](auto slot_tag, bf16x8 (&ka)[2][4]) __attribute__((always_inline)) {
+    constexpr int S = decltype(slot_tag)::value;
+    const uint4* kt = kslot<S>();
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int row = 32 * kb + ln;
+        ka[kb][s] = __builtin_bit_cast(bf16x8, kt[row * 8 + ((2 * s + hh) ^ (row & 7))]);
+      }
+  };
+  // V^T: [d block][key step].  Key step j (16 keys) of key block kb = j / 2
+  // takes, in MFMA k order, keys 16 (j % 2) + {0..3, 8..11} + 4 hh of the
+  // block -- the order the S accumulators hold them in, so P feeds the B
+  // operand straight from registers.  Each fragment is two transposed reads
+  // of 4 keys: lane i of 16-lane group g names row (key) kr and 8-byte chunk
+  // h, and the read returns to lane i the 4 keys kr - i/4 .. +3 of d = dbase
+  // + i.
+  auto load_v = [&](auto slot_tag, bf16x8 (&va)[2][4]) __attribute__((always_inline)) {
+    constexpr int S = decltype(slot_tag)::value;
+    const char* vt = reinterpret_cast<const char*>(vslot<S>());
+    const int g = lane >> 4;
+    const int i = lane & 15;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        s16x4 part[2];
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+          const int kr = 16 * j + 8 * x + 4 * (g >> 1) + (i >> 2);
+          const int h = 8 * db + 4 * (g & 1) + (i & 3);
+          const int byte = kr * (int)kRowBytes + 16 * ((h >> 1) ^ (2 * (kr & 3))) + 8 * (h & 1);
+          part[x] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vt + byte));
+        }
+        va[db][j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+  };
+
+  // S^T = K Q^T: 2 key blocks x 2 query blocks x 4 d-steps.
+  auto qk = [&](const bf16x8 (&ka)[2][4]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        f32x16 acc = f32x16{};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kb][s], qf[qb][s], acc, 0, 0, 0);
+        sc[kb][qb] = acc;
+      }
+  };
+  // O^T += V^T P^T.
+  auto pv = [&](const bf16x8 (&va)[2][4]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bf16x8 pb = __builtin_bit_cast(
+            bf16x8, make_uint4(pk[qb][4 * j], pk[qb][4 * j + 1], pk[qb][4 * j + 2], pk[qb][4 * j + 3]));
+#pragma unroll
+        for (int db = 0; db < 2; ++db) o[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db][j], pb, o[db][qb], 0, 0, 0);
+      }
+  };
+
+  // Weights of tile t from sc into pk.  Masks only on the tiles that cross
+  // the causal diagonal or the key-length boundary.  The pivot is checked
+  // first, on the tile's row max: a row's pivot moves to that max when the
+  // max weight would exceed 2^64 (so tile sums stay far below fp32 range),
+  // or, while the row has summed nothing, fall below 2^-64 (so its first
+  // weights cannot underflow); O and l are rescaled by 2^(m_old - m_new).
+  // Both half-waves of a row see the same max, pivot and sum, so they agree.
+  // A fully masked row (max -inf) and NaN (garbage in padded query rows)
+  // never move.
+  auto softmax = [&](int t) __attribute__((always_inline)) {
+    const int k0 = t * kBN;
+    const bool need_mask = (k0 + kBN > kv_lim) || (CAUSAL && k0 + kBN - 1 > qw0);
+    if (need_mask) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const int qi = qw0 + 32 * qb + ln;
+        const int lim = (CAUSAL ? min(kv_lim, qi + 1) : kv_lim) - k0 - 4 * hh;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int off = 8 * (r >> 2) + (r & 3);
+          sc[0][qb][r] = off < lim ? sc[0][qb][r] : -INFINITY;
+          sc[1][qb][r] = off + 32 < lim ? sc[1][qb][r] : -INFINITY;
+        }
+      }
+    }
+    // Exponents x = s c - m c in place (one FMA per score); a masked score
+    // becomes -inf.
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sc[kb][qb][r] = fmaf(sc[kb][qb][r], c, -mc[qb]);
+    float gap[2];  // the row's largest exponent in this tile
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) gap[qb] = half_swap_max(max32(sc[0][qb], sc[1][qb]));
+    bool move[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) move[qb] = gap[qb] > kPivotUp;
+    if (__builtin_amdgcn_ballot_w64(l[0] == 0.f || l[1] == 0.f) != 0) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+        move[qb] = move[qb] || (gap[qb] < kPivotDown && gap[qb] > -INFINITY && half_swap_sum(l[qb]) == 0.f);
+    }
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      if (__builtin_amdgcn_ballot_w64(move[qb]) != 0) {
+        // The pivot moves by gap: exponents shift down by it, O and l scale
+        // by 2^-gap -- except on a downward move, which happens only while
+        // l is 0 (nothing to rescale).
+        const float shift = move[qb] ? gap[qb] : 0.f;
+        const float alpha = shift > 0.f ? __builtin_amdgcn_exp2f(-shift) : 1.f;
+        l[qb] *= alpha;
+        o[0][qb] *= alpha;
+        o[1][qb] *= alpha;
+        mc[qb] += shift;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          sc[0][qb][r] -= shift;
+          sc[1][qb][r] -= shift;
+        }
+      }
+      exp_pack(sc[0][qb], sc[1][qb], pk[qb]);
+    }
+  };
+
+  // Phases.  A phase p begins with this wave's share of the fills of
+  // K(p + 3) and V(p + 1) (tiles past the end read as zeros and are never
+  // used) and ends with a wait for this wave's fills of phase p - 2 and a
+  // barrier, which publishes K(p + 1) and V(p - 1).  Slot of tile t: t % 4;
+  // a slot is refilled only after the phase that last read it has ended.
+  auto fills = [&](auto j_tag, int p) __attribute__((always_inline)) {
+    constexpr int J = decltype(j_tag)::value;
+    fill_k(std::integral_constant<int, (J + 3) & 3>(), p + 3);
+    fill_v(std::integral_constant<int, (J + 1) & 3>(), p + 1);
+  };
+  auto sync = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0x0F70 | 4);  // vmcnt(4): this and the previous phase's fills may fly
+    barrier_lds();
+  };
+  // MFMA phase at phase p (slot J = p % 4): P.V of tile p - 2, then S of
+  // tile p.  Both fragment reads are issued first, so the K reads arrive
+  // while the P.V products run.  Both branches define sc, so the scores
+  // live only until the next vector phase.
+  auto mphase = [&](auto j_tag, int t_pv, int t_qk) __attribute__((always_inline)) {
+    constexpr int J = decltype(j_tag)::value;
+    __builtin_amdgcn_s_setprio(1);
+    const bool do_pv = t_pv >= 0 && t_pv < wave_tiles;
+    const bool do_qk = t_qk < wave_tiles;
+    bf16x8 va[2][4], ka[2][4];
+    if (do_pv) load_v(std::integral_constant<int, (J + 2) & 3>(), va);
+    if (do_qk) load_k(std::integral_constant<int, J>(), ka);
+    if (do_pv) {
+      pv(va);
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) l[qb] += bf16_sum(pk[qb]);
+    }
+    // All of P.V before any of S: the weights and V fragments die before the
+    // scores are born.
+    __builtin_amdgcn_sched_barrier(0);
+    if (do_qk) {
+      qk(ka);
+    } else {
+      retire(sc[0][0], sc[0][1], sc[1][0], sc[1][1]);
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
+  // Vector phase of tile t; both branches define pk.
+  auto vphase = [&](int t) __attribute__((always_inline)) {
+    if (t >= 0 && t < wave_tiles) {
+      softmax(t);
+    } else {
+      retire_pk(pk[0]);
+      retire_pk(pk[1]);
+    }
+  };
+  using J0 = std::integral_constant<int, 0>;
+  using J1 = std::integral_constant<int, 1>;
+  using J2 = std::integral_constant<int, 2>;
+  using J3 = std::integral_constant<int, 3>;
+
+  if (n_tiles > 0) {
+    // Prologue: K(0), K(1) as if filled two and three phases before phase 0,
+    // K(2), V(0) as the fills of phase -1.
+    fill_k(J0(), 0);
+    fill_k(J1(), 1);
+    fill_k(J2(), 2);
+    fill_v(J0(), 0);
+    __builtin_amdgcn_s_waitcnt(0x0F70 | 2);
+    barrier_lds();
+    // Even-tile waves run MFMA phases at even p, odd-tile waves at odd p;
+    // both run the same number of phases (and barriers).
+    const int n_phases = n_tiles + 2;
+    if (par == 0) {
+#pragma nounroll
+      for (int p = 0; p < n_phases; p += 4) {
+        fills(J0(), p);     mphase(J0(), p - 2, p); sync();
+        fills(J1(), p + 1); vphase(p);              sync();
+        fills(J2(), p + 2); mphase(J2(), p, p + 2); sync();
+        fills(J3(), p + 3); vphase(p + 2);          sync();
+      }
+    } else {
+#pragma nounroll
+      for (int p = 0; p < n_phases; p += 4) {
+        fills(J0(), p);     vphase(p - 1);              sync();
+        fills(J1(), p + 1); mphase(J1(), p - 1, p + 1); sync();
+        fills(J2(), p + 2); vphase(p + 1);              sync();
+        fills(J3(), p + 3); mphase(J3(), p + 1, p + 3); sync();
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70 | 0);  // no fill may land in the merge area
+    barrier_lds();
+  }
+
+  // ---- merge the pair: the odd-tile wave hands (O, l, m) to its partner
+  // through LDS.  The 64 KB of ring slots hold O as 16 vec4 groups
+  // ([d block][query block][register / 4]) x 4 row groups x 64 lanes; group
+  // vg sits in slot vg / 2, so every index is a compile-time slot.
+  auto mptr = [&](auto vg_tag) -> float4* __attribute__((always_inline)) {
+    constexpr int VG = decltype(vg_tag)::value;
+    return reinterpret_cast<float4*>(mslot<VG / 2>()) + ((VG & 1) * 4 + rg) * 64 + lane;
+  };
+  if (par == 1) {
+    static_for<16>([&](auto vg_tag) {
+      constexpr int VG = decltype(vg_tag)::value;
+      constexpr int DB = VG / 8, QB = (VG / 4) % 2, R = 4 * (VG % 4);
+      *mptr(vg_tag) = make_float4(o[DB][QB][R], o[DB][QB][R + 1], o[DB][QB][R + 2], o[DB][QB][R + 3]);
+    });
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) g_lm[rg][qb][lane] = make_float2(l[qb], mc[qb]);
+  }
+  __syncthreads();
+  if (par == 1) return;
+
+  // O = (2^(mA - M) O_A + 2^(mB - M) O_B) / (2^(mA - M) l_A + 2^(mB - M) l_B)
+  // with M = max(mA, mB); 2^0 = 1 exactly, and both pivots are finite.
+  float fa[2], fb[2], inv[2];
+  bool live[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const float2 lm = g_lm[rg][qb][lane];
+    const float M = fmaxf(mc[qb], lm.y);
+    fa[qb] = __builtin_amdgcn_exp2f(mc[qb] - M);
+    fb[qb] = __builtin_amdgcn_exp2f(lm.y - M);
+    const float l_row = half_swap_sum(fa[qb] * l[qb] + fb[qb] * lm.x);
+    const int qi = qw0 + 32 * qb + ln;
+    live[qb] = qi < q_len && l_row > 0.f;
+    inv[qb] = live[qb] ? 1.f / l_row : 0.f;
+  }
+  // Register r of block (db, qb) holds d = 32 db + 8 (r / 4) + 4 hh + r % 4
+  // of query row qw0 + 32 qb + ln: four consecutive d per 8-byte store.
+  // Padded rows and rows with no allowed key are written as exact zeros.
+  static_for<16>([&](auto vg_tag) {
+    constexpr int VG = decltype(vg_tag)::value;
+    constexpr int DB = VG / 8, QB = (VG / 4) % 2, G = VG % 4, R = 4 * G;
+    const int qi = qw0 + 32 * QB + ln;
+    const float4 ob = *mptr(vg_tag);
+    const float x0 = (fa[QB] * o[DB][QB][R] + fb[QB] * ob.x) * inv[QB];
+    const float x1 = (fa[QB] * o[DB][QB][R + 1] + fb[QB] * ob.y) * inv[QB];
+    const float x2 = (fa[QB] * o[DB][QB][R + 2] + fb[QB] * ob.z) * inv[QB];
+    const float x3 = (fa[QB] * o[DB][QB][R + 3] + fb[QB] * ob.w) * inv[QB];
+    if (qi < a.n_q) {
+      uint2 w;
+      w.x = live[QB] ? pack_bf16x2(x0, x1) : 0u;
+      w.y = live[QB] ? pack_bf16x2(x2, x3) : 0u;
+      *reinterpret_cast<uint2*>(O + (size_t)qi * kHeadDim + 32 * DB + 8 * G + 4 * hh) = w;
+    }
+  });
+}
+
+}  // namespace
+
+hipError_t launch_fwd_bf16_pair(const FwdArgs& a, hipStream_t s) {
+  const int n_qt = (a.n_q + kBM - 1) / kBM;
+  const long long blocks = (long long)n_qt * a.H * a.B;
+  FwdArgs args = a;
+  void* kargs[] = {&args};
+  const void* fn = a.causal ? reinterpret_cast<const void*>(&attn_fwd_bf16_pair_kernel<true>)
+                            : reinterpret_cast<const void*>(&attn_fwd_bf16_pair_kernel<false>);
+  return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(kThreads), kargs, 0, s);
+}
+
+}  // namespace headattn

@@ -57,6 +57,12 @@ inline int decode_splits(int n_max) {
 // Launchers; each returns the hipError_t of its launch(es).
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s);
+hipError_t launch_fwd_bf16_pair(const FwdArgs& a, hipStream_t s);
+
+// bf16 forward: calls with at least this many query rows run on the paired
+// 8-wave kernel (256 rows per workgroup); shorter ones on the 4-wave kernel
+// (128 rows per workgroup), which leaves fewer rows idle.
+constexpr int kPairMinRows = 512;
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s);
 

@@ -110,6 +110,17 @@ RAGGED = {
     "zero_scale": (2, 2, 40, 90, 1, None, [90, 17], 0.0),
     "big_scale": (1, 2, 70, 70, 0, None, None, 2.0),
     "cross_128x160": (4, 2, 128, 160, 1, None, [16, 160, 99, 128], 0.125),
+    # n_q >= 512: the paired 8-wave bf16 kernel (256 query rows per workgroup)
+    "pair_causal_1000": (1, 2, 1000, 1000, 2, None, None, 0.125),
+    "pair_none_600x700": (2, 2, 600, 700, 0, None, None, 0.125),
+    "pair_kpad_520x777": (3, 2, 520, 777, 1, [520, 300, 0], [777, 65, 1], 0.125),
+    "pair_causal_kpad_768": (2, 2, 768, 768, 3, [768, 700], [768, 129], 0.125),
+    "pair_xcd_causal_512": (8, 1, 512, 512, 2, None, None, 0.125),
+    "pair_one_tile_512x64": (1, 2, 512, 64, 0, None, None, 0.125),
+    "pair_short_k_600x5": (1, 2, 600, 5, 0, None, None, 0.125),
+    "pair_big_scale_600": (1, 2, 600, 600, 0, None, None, 2.0),
+    "pair_negative_scale_540": (1, 2, 540, 540, 2, None, None, -0.3),
+    "pair_zero_scale_530x300": (2, 1, 530, 300, 1, None, [300, 44], 0.0),
 }
 
 
