@@ -86,9 +86,11 @@ def _dtype_code(t: torch.Tensor) -> int:
 
 
 def _check_tensor(name: str, t: torch.Tensor, dtype) -> None:
+    # Cheap attribute reads only: this runs on every call, and at n = 128 a
+    # call's Python time is comparable to the kernel's.
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if t.device.type != "cuda":
+    if not t.is_cuda:
         raise ValueError(f"{name} must be on the GPU, got {t.device}")
     if t.dim() != 4:
         raise ValueError(f"{name} must be [B, h, n, d], got shape {tuple(t.shape)}")
@@ -101,15 +103,24 @@ def _check_tensor(name: str, t: torch.Tensor, dtype) -> None:
 def _lens_ptr(name: str, t, B: int):
     if t is None:
         return None
-    if t.device.type != "cuda" or t.dtype != torch.int32 or t.dim() != 1 or t.numel() != B \
-            or not t.is_contiguous():
+    if not (isinstance(t, torch.Tensor) and t.is_cuda and t.dtype == torch.int32 and t.dim() == 1
+            and t.shape[0] == B and t.is_contiguous()):
         raise ValueError(f"{name} must be a contiguous int32 GPU tensor of shape [{B}]")
     return t.data_ptr()
 
 
-def _stream_handle(stream) -> int | None:
-    s = torch.cuda.current_stream() if stream is None else stream
-    return s.cuda_stream or None
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _stream_handle(stream, t: torch.Tensor) -> int | None:
+    """Raw HIP stream: `stream` if given, else torch's current stream on t's
+    device (read without building a torch Stream object when torch offers
+    that)."""
+    if stream is None:
+        if _raw_stream is not None:
+            return _raw_stream(t.get_device()) or None
+        stream = torch.cuda.current_stream(t.device)
+    return stream.cuda_stream or None
 
 
 def forward(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, mask_kind: int = ATTN_MASK_NONE,
@@ -126,7 +137,7 @@ def forward(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, mask_kind: int = 
         _check_tensor(n, t, dt)
     B, H, n_q, d = Q.shape
     n_k = K.shape[2]
-    if tuple(K.shape) != (B, H, n_k, d) or tuple(V.shape) != (B, H, n_k, d):
+    if K.shape != (B, H, n_k, d) or V.shape != (B, H, n_k, d):
         raise ValueError(f"K {tuple(K.shape)} / V {tuple(V.shape)} do not match Q {tuple(Q.shape)}")
     if out is None:
         out = torch.empty_like(Q)
@@ -139,7 +150,7 @@ def forward(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, mask_kind: int = 
     layout = attn_layout(B, H, n_q, n_k, d, _dtype_code(Q))
     st = lib().attn_forward(Q.data_ptr(), K.data_ptr(), V.data_ptr(), layout, int(mask_kind),
                             _lens_ptr("q_lens", q_lens, B), _lens_ptr("kv_lens", kv_lens, B),
-                            float(scale), out.data_ptr(), _stream_handle(stream))
+                            float(scale), out.data_ptr(), _stream_handle(stream, Q))
     if st != 0:
         raise AttnError(st, "attn_forward")
     return out
@@ -180,7 +191,7 @@ def decode(q: torch.Tensor, Kcache: torch.Tensor, Vcache: torch.Tensor, kv_lens:
     st = lib().attn_decode(q.data_ptr(), Kcache.data_ptr(), Vcache.data_ptr(), layout,
                            _lens_ptr("kv_lens", kv_lens, B), float(scale), out.data_ptr(),
                            workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                           _stream_handle(stream))
+                           _stream_handle(stream, q))
     if st != 0:
         raise AttnError(st, "attn_decode")
     return out

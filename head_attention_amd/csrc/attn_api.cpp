@@ -130,6 +130,7 @@ attn_status attn_forward(const void* Q, const void* K, const void* V, attn_layou
   a.causal = causal;
   hipError_t e;
   if (layout.dtype == ATTN_F32) e = launch_fwd_f32(a, s);
+  else if (layout.n_k <= kShortMaxKeys) e = launch_fwd_bf16_short(a, s);
   else if (layout.n_q >= kPairMinRows) e = launch_fwd_bf16_pair(a, s);
   else e = launch_fwd_bf16(a, s);
   if (e != hipSuccess) {

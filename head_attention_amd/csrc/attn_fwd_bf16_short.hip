@@ -1,0 +1,312 @@
+// bf16 forward of attn_forward for short key ranges (n_k <= 256): one load,
+// then no barriers.
+//
+// Computes O = softmax(Q K^T * scale + M) V per (b, h) ("[논문 리뷰]Attention
+// Is All You Need", §3.2.1 equation; masking by -inf logits before the
+// softmax, §3.2.3) with the arithmetic of the other bf16 kernels: exact bf16
+// Q (sign of scale folded in), S^T = K Q^T and O^T += V^T P^T on
+// v_mfma_f32_32x32x16_bf16 with fp32 accumulation, weights exp2(s c - m c)
+// with a lazy pivot, weights rounded to bf16 once and summed as rounded.
+//
+// The pages' encoder and decoder layers attend over at most a few hundred
+// positions (Transformer-base/big at sentence length), where a kernel is
+// bound by memory latency, not by either pipe: a (b, h) of 128 queries and
+// 128 keys is 2 key tiles.  Streaming tiles through a double-buffered ring
+// puts one global-memory round trip per tile on the critical path.  Here the
+// workgroup (4 waves, 128 query rows, 32 per wave) instead issues every load
+// it needs at once -- its Q rows into registers, all valid K and V rows
+// straight into LDS (buffer loads that write LDS, range-checked so rows at
+// or beyond the valid length read as zero) -- waits once, and then each wave
+// walks its key tiles on its own with no further barrier: one memory round
+// trip per workgroup.  K and V of up to 256 keys take 64 KB of LDS, so two
+// workgroups fit a compute unit.
+//
+// LDS layout, per 64-key tile: K rows keep their 16-byte chunks XOR-swizzled
+// by row; V stays row-major (chunks swizzled by 2 (row % 4)) and is read
+// transposed with ds_read_b64_tr_b16, which hands each lane four consecutive
+// keys of one d -- the A-operand order of O^T += V^T P^T, with the keys in
+// the order the S accumulator registers hold them, so the weights feed the
+// B operand straight from registers.
+#include "common.h"
+
+namespace headattn {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBM = 32 * kWaves;  // query rows per workgroup
+constexpr int kBN = 64;           // keys per tile
+constexpr int kMaxTiles = kShortMaxKeys / kBN;
+constexpr uint32_t kRowBytes = kHeadDim * 2;
+constexpr uint32_t kTileChunks = kBN * 8;  // 16-byte chunks per tile
+constexpr uint32_t kBufferWord3 = 0x00020000u;  // raw buffer, 32-bit elements (gfx9 family)
+constexpr float kPivotHigh = 0x1p64f;  // a tile sum above this moves the pivot up
+constexpr float kPivotLow = 0x1p-64f;  // a first-tile row sum below this moves it down
+
+__shared__ uint4 s_k[kMaxTiles * kTileChunks];
+__shared__ uint4 s_v[kMaxTiles * kTileChunks];
+
+// Lanes l and l ^ 32 hold the same query row: combine the two half-waves.
+__device__ __forceinline__ float half_swap_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_swap_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ bool half_swap_or(bool x) {
+  auto r = __builtin_amdgcn_permlane32_swap((uint32_t)x, (uint32_t)x, false, false);
+  return (r[0] | r[1]) != 0;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// Weights of one tile under pivot term mc = m c: exp2(s c - mc), packed to
+// bf16 pairs in the order P.V consumes them (keys 0..31 from s0, 32..63 from
+// s1), and the sum of the packed (rounded) weights held by this lane.
+__device__ __forceinline__ float exp_pack_sum(const f32x16& s0, const f32x16& s1, float c, float mc,
+                                              uint32_t (&pk)[16]) {
+  const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
+  float acc0 = 0.f, acc1 = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    pk[i] = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(s0[2 * i], c, -mc)),
+                        __builtin_amdgcn_exp2f(fmaf(s0[2 * i + 1], c, -mc)));
+    pk[8 + i] = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(s1[2 * i], c, -mc)),
+                            __builtin_amdgcn_exp2f(fmaf(s1[2 * i + 1], c, -mc)));
+    acc0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[i]), ones, acc0, false);
+    acc1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[8 + i]), ones, acc1, false);
+  }
+  return acc0 + acc1;
+}
+
+template <bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_short_kernel(FwdArgs a) {
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int ln = lane & 31;  // query row within the wave / M,N index of MFMA
+  const int hh = lane >> 5;  // half-wave: selects the 8-wide k block
+
+  // ---- (b, h, query tile).  The 8 XCDs take workgroup ids round robin; when
+  // B*h divides by 8 each XCD gets whole heads.  Longest tiles first under
+  // the causal mask.
+  const int n_qt = (a.n_q + kBM - 1) / kBM;
+  const int HB = a.H * a.B;
+  const int bid = blockIdx.x;
+  int bh, rank;
+  if ((HB & 7) == 0) {
+    const int per = HB >> 3;
+    const int slot = bid >> 3;
+    rank = slot / per;
+    bh = (bid & 7) * per + slot % per;
+  } else {
+    bh = bid % HB;
+    rank = bid / HB;
+  }
+  const int qt = CAUSAL ? (n_qt - 1 - rank) : rank;
+  const int b = bh / a.H;
+
+  const __bf16* Q = static_cast<const __bf16*>(a.Q) + (size_t)bh * a.n_q * kHeadDim;
+  const __bf16* K = static_cast<const __bf16*>(a.K) + (size_t)bh * a.n_k * kHeadDim;
+  const __bf16* V = static_cast<const __bf16*>(a.V) + (size_t)bh * a.n_k * kHeadDim;
+  __bf16* O = static_cast<__bf16*>(a.O) + (size_t)bh * a.n_q * kHeadDim;
+
+  const int q_len = __builtin_amdgcn_readfirstlane(a.q_lens ? clamp_len(a.q_lens[b], a.n_q) : a.n_q);
+  const int kv_lim = __builtin_amdgcn_readfirstlane(a.kv_lens ? clamp_len(a.kv_lens[b], a.n_k) : a.n_k);
+  const int q0 = qt * kBM;
+  const int qw0 = q0 + 32 * wave;  // first query row of this wave
+  const int qi = qw0 + ln;         // query row of this lane
+
+  int end = kv_lim;  // keys the workgroup needs (at most n_k <= 256)
+  if (CAUSAL) end = min(end, q0 + kBM);
+  if (q0 >= q_len) end = 0;
+  const int n_tiles = min((end + kBN - 1) / kBN, kMaxTiles);  // the host sends n_k <= 256 only
+  int wave_end = min(end, kShortMaxKeys);  // keys this wave needs
+  if (CAUSAL) wave_end = min(wave_end, qw0 + 32);
+  if (qw0 >= q_len) wave_end = 0;
+  const int wave_tiles = (wave_end + kBN - 1) / kBN;
+
+  // ---- all loads at once.  Q: B operand of S^T = K Q^T, lane (ln, hh)
+  // holds Q[qi][16 s + 8 hh + 0..7], sign of scale folded in; c = |scale|
+  // log2(e), floored at 2^-100 (below that every weight is exactly 1.0f).
+  const float c = fmaxf(fabsf(a.scale) * kLog2e, 0x1p-100f);
+  const uint32_t sign = a.scale < 0.f ? 0x80008000u : 0u;
+  uint4 qraw[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    qraw[s] = make_uint4(0, 0, 0, 0);
+    if (qi < a.n_q && wave_tiles > 0) qraw[s] = *reinterpret_cast<const uint4*>(Q + (size_t)qi * kHeadDim + 16 * s + 8 * hh);
+  }
+  // K and V tiles: one instruction of the workgroup covers 32 rows of a
+  // tile.  Lane l of wave w writes chunk 64 w + l of that half, i.e. row
+  // 32 half + 8 w + l / 8, position l % 8, which receives the row's chunk
+  // (l % 8) ^ swizzle(row).  The range check of the descriptor returns zeros
+  // for rows at or beyond kv_lim, so padded K/V memory is never read.
+  const uint32_t n_bytes = (uint32_t)kv_lim * kRowBytes;
+  const __amdgpu_buffer_rsrc_t rk =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(K), (short)0, (int)n_bytes, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rv =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(V), (short)0, (int)n_bytes, kBufferWord3);
+  const int fpos = lane & 7;
+  for (int t = 0; t < n_tiles; ++t) {
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int row = 32 * half + 8 * wave + (lane >> 3);
+      const uint32_t base = (uint32_t)(t * kBN + row) * kRowBytes;
+      const uint32_t koff = base + 16u * (uint32_t)(fpos ^ (row & 7));
+      const uint32_t voff = base + 16u * (uint32_t)(fpos ^ (2 * (row & 3)));
+      const uint32_t chunk0 = (uint32_t)t * kTileChunks + 256u * half + 64u * wave;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(s_k + chunk0), 16, koff, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(s_v + chunk0), 16, voff, 0, 0, 0);
+    }
+  }
+  bf16x8 qf[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    uint4 v = qraw[s];
+    v.x ^= sign;
+    v.y ^= sign;
+    v.z ^= sign;
+    v.w ^= sign;
+    qf[s] = __builtin_bit_cast(bf16x8, v);
+  }
+  __syncthreads();  // waits for every load, then publishes the LDS tiles
+
+  f32x16 o0 = {}, o1 = {};  // O^T blocks: d 0..31 and d 32..63, column = query ln
+  float mc = 0.f;           // pivot term of the exponent, m * c
+  float l = 0.f;            // this half-wave's partial row sum of bf16 weights
+
+  const int g = lane >> 4;
+  const int i16 = lane & 15;
+  for (int t = 0; t < wave_tiles; ++t) {
+    // S^T = K Q^T: lane (ln, hh) of key block kb reads K[64 t + 32 kb + ln]
+    // [16 s + 8 hh + 0..7].
+    const uint4* kt = s_k + t * kTileChunks;
+    f32x16 s0 = {}, s1 = {};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int ch = 2 * s + hh;
+      const bf16x8 k0 = __builtin_bit_cast(bf16x8, kt[ln * 8 + (ch ^ (ln & 7))]);
+      const bf16x8 k1 = __builtin_bit_cast(bf16x8, kt[(32 + ln) * 8 + (ch ^ ((32 + ln) & 7))]);
+      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[s], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[s], s1, 0, 0, 0);
+    }
+    // V^T fragments: [d block][key step].  Key step j (16 keys) of key block
+    // j / 2 takes keys 16 (j % 2) + {0..3, 8..11} + 4 hh of the block, the
+    // order in which the S registers hold them.  Lane i of 16-lane group g
+    // names key row kr and 8-byte chunk h; the transposed read returns to
+    // lane i the 4 keys kr - i/4 .. +3 of d = dbase + i.
+    const char* vt = reinterpret_cast<const char*>(s_v + t * kTileChunks);
+    bf16x8 va[2][4];
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        s16x4 part[2];
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+          const int kr = 16 * j + 8 * x + 4 * (g >> 1) + (i16 >> 2);
+          const int h = 8 * db + 4 * (g & 1) + (i16 & 3);
+          const int byte = kr * (int)kRowBytes + 16 * ((h >> 1) ^ (2 * (kr & 3))) + 8 * (h & 1);
+          part[x] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vt + byte));
+        }
+        va[db][j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+
+    // Mask in registers, only on tiles that cross the causal diagonal or the
+    // key-length boundary: register r of block kb holds key 64 t + 32 kb +
+    // 8 (r / 4) + 4 hh + r % 4.
+    const int k0 = t * kBN;
+    if ((k0 + kBN > kv_lim) || (CAUSAL && k0 + kBN - 1 > qw0)) {
+      const int lim = (CAUSAL ? min(kv_lim, qi + 1) : kv_lim) - k0 - 4 * hh;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int off = 8 * (r >> 2) + (r & 3);
+        s0[r] = off < lim ? s0[r] : -INFINITY;
+        s1[r] = off + 32 < lim ? s1[r] : -INFINITY;
+      }
+    }
+    uint32_t pk[16];
+    float lt = exp_pack_sum(s0, s1, c, mc, pk);
+    // Pivot checks on the tile's weights: a sum past 2^64 (also catches inf)
+    // or, on the row's first tile, a row sum small enough to be lost to
+    // underflow.  The row's pivot then moves to its tile max, O and l are
+    // rescaled by 2^(m_old - m_new) (a downward move happens only while O
+    // and l are 0: scale 1), and the tile's weights are recomputed.  NaN
+    // (garbage in padded rows) triggers neither check.
+    bool move = lt > kPivotHigh;
+    if (t == 0) move = move || half_swap_sum(lt) < kPivotLow;
+    if (__builtin_amdgcn_ballot_w64(move) != 0) {
+      move = half_swap_or(move);  // both half-waves of a row must agree
+      float tmax = fmaxf(s0[0], s1[0]);
+#pragma unroll
+      for (int r = 1; r < 16; ++r) tmax = fmaxf(tmax, fmaxf(s0[r], s1[r]));
+      const float tm = half_swap_max(tmax) * c;  // tile max in exponent units
+      const float m_new = (move && tm > -INFINITY) ? tm : mc;
+      const float alpha = m_new > mc ? __builtin_amdgcn_exp2f(mc - m_new) : 1.f;
+      l *= alpha;
+      o0 *= alpha;
+      o1 *= alpha;
+      mc = m_new;
+      lt = exp_pack_sum(s0, s1, c, mc, pk);
+    }
+    l += lt;
+
+    // O^T += V^T P^T.
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bf16x8 pb = __builtin_bit_cast(bf16x8, make_uint4(pk[4 * j], pk[4 * j + 1], pk[4 * j + 2], pk[4 * j + 3]));
+      o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[0][j], pb, o0, 0, 0, 0);
+      o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[1][j], pb, o1, 0, 0, 0);
+    }
+  }
+
+  // ---- epilogue: O[qi][d] = acc / l.  Register r of block ob holds
+  // d = 32 ob + 8 (r / 4) + 4 hh + r % 4: four consecutive d per group.
+  // Padded query rows and rows with no allowed key are written as exact
+  // zeros (a select, so garbage in a padded Q row cannot leak through).
+  const float l_row = half_swap_sum(l);
+  const bool live = qi < q_len && l_row > 0.f;
+  const float inv = live ? 1.f / l_row : 0.f;
+  if (qi < a.n_q) {
+    __bf16* orow = O + (size_t)qi * kHeadDim;
+#pragma unroll
+    for (int ob = 0; ob < 2; ++ob) {
+      const f32x16& o = ob ? o1 : o0;
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) {
+        uint2 w;
+        w.x = live ? pack_bf16x2(o[4 * gg + 0] * inv, o[4 * gg + 1] * inv) : 0u;
+        w.y = live ? pack_bf16x2(o[4 * gg + 2] * inv, o[4 * gg + 3] * inv) : 0u;
+        *reinterpret_cast<uint2*>(orow + 32 * ob + 8 * gg + 4 * hh) = w;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_fwd_bf16_short(const FwdArgs& a, hipStream_t s) {
+  const int n_qt = (a.n_q + kBM - 1) / kBM;
+  const long long blocks = (long long)n_qt * a.H * a.B;
+  FwdArgs args = a;
+  void* kargs[] = {&args};
+  const void* fn = a.causal ? reinterpret_cast<const void*>(&attn_fwd_bf16_short_kernel<true>)
+                            : reinterpret_cast<const void*>(&attn_fwd_bf16_short_kernel<false>);
+  return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(kThreads), kargs, 0, s);
+}
+
+}  // namespace headattn

@@ -58,6 +58,11 @@ inline int decode_splits(int n_max) {
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s);
 hipError_t launch_fwd_bf16_pair(const FwdArgs& a, hipStream_t s);
+hipError_t launch_fwd_bf16_short(const FwdArgs& a, hipStream_t s);
+
+// bf16 forward: calls whose key range fits LDS whole (n_k <= 256) run on the
+// short-sequence kernel, which loads all of a (b, h)'s K and V at once.
+constexpr int kShortMaxKeys = 256;
 
 // bf16 forward: calls with at least this many query rows run on the paired
 // 8-wave kernel (256 rows per workgroup); shorter ones on the 4-wave kernel

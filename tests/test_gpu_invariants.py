@@ -28,28 +28,35 @@ def _rand(seed, shape, dtype):
     return workloads.randn(workloads.generator(seed), shape, dtype).cuda()
 
 
+# Sequence lengths that reach each bf16 kernel: short key range (n_k <= 256),
+# 4-wave (n_k > 256, n_q < 512) and paired (n_q >= 512).
+SIZES = pytest.mark.parametrize("n", [150, 333, 520])
+
+
 @DTYPES
+@SIZES
 @pytest.mark.parametrize("mask", [0, 1, 2, 3])
-def test_ones_column_sums_to_one(dtype, mask):
-    B, H, n = 3, 4, 333
+def test_ones_column_sums_to_one(dtype, mask, n):
+    B, H = 3, 4
     Q, K, V = (_rand(s, (B, H, n, 64), dtype) for s in (1, 2, 3))
     V[..., 5] = 1.0
-    kl = torch.tensor([333, 100, 1], dtype=torch.int32, device="cuda") if mask & 1 else None
-    say(f"[ones column {dtype} mask{mask}]")
+    kl = torch.tensor([n, 100, 1], dtype=torch.int32, device="cuda") if mask & 1 else None
+    say(f"[ones column {dtype} mask{mask} n{n}]")
     O = ha.forward(Q, K, V, mask_kind=mask, kv_lens=kl, scale=0.125).float()
     tol = 2.0 ** -7 if dtype == BF16 else 1e-6
     assert torch.all((O[..., 5] - 1).abs() <= tol), (O[..., 5] - 1).abs().max()
 
 
 @DTYPES
+@pytest.mark.parametrize("n", [200, 300, 600])
 @pytest.mark.parametrize("mask", [1, 3])
-def test_nan_padding_is_invisible(dtype, mask):
-    B, H, n = 4, 2, 300
+def test_nan_padding_is_invisible(dtype, mask, n):
+    B, H = 4, 2
     Q, K, V = (_rand(s, (B, H, n, 64), dtype) for s in (4, 5, 6))
-    lens = [300, 65, 1, 199]
+    lens = [n, 65, 1, (2 * n) // 3]
     kl = torch.tensor(lens, dtype=torch.int32, device="cuda")
     ql = kl.clone()
-    say(f"[NaN padding {dtype} mask{mask}]")
+    say(f"[NaN padding {dtype} mask{mask} n{n}]")
     O1 = ha.forward(Q, K, V, mask_kind=mask, q_lens=ql, kv_lens=kl, scale=0.125)
     Q2, K2, V2 = Q.clone(), K.clone(), V.clone()
     for b, L in enumerate(lens):
@@ -82,12 +89,15 @@ def test_nan_padding_is_invisible_decode(dtype):
 
 
 @DTYPES
-def test_causal_future_is_invisible(dtype):
-    B, H, n = 2, 3, 400
+@pytest.mark.parametrize("n", [200, 400, 600])
+def test_causal_future_is_invisible(dtype, n):
+    B, H = 2, 3
     Q, K, V = (_rand(s, (B, H, n, 64), dtype) for s in (10, 11, 12))
-    say(f"[causal future {dtype}]")
+    say(f"[causal future {dtype} n{n}]")
     O1 = ha.forward(Q, K, V, mask_kind=2, scale=0.125)
-    for i in (0, 63, 64, 127, 128, 250):
+    for i in (0, 63, 64, 127, 128, 199, 250, 511):
+        if i >= n - 1:
+            continue
         Q2, K2, V2 = Q.clone(), K.clone(), V.clone()
         Q2[:, :, i + 1:] = 1000.0
         K2[:, :, i + 1:] = -3000.0
@@ -98,11 +108,12 @@ def test_causal_future_is_invisible(dtype):
 
 
 @DTYPES
-def test_single_allowed_key_returns_its_value(dtype):
-    B, H, n = 3, 2, 130
+@pytest.mark.parametrize("n", [130, 300, 530])
+def test_single_allowed_key_returns_its_value(dtype, n):
+    B, H = 3, 2
     Q, K, V = (_rand(s, (B, H, n, 64), dtype) for s in (13, 14, 15))
     kl = torch.ones(B, dtype=torch.int32, device="cuda")
-    say(f"[one key {dtype}]")
+    say(f"[one key {dtype} n{n}]")
     O = ha.forward(Q, K, V, mask_kind=1, kv_lens=kl, scale=0.125)
     torch.cuda.synchronize()
     assert torch.equal(O, V[:, :, :1].expand_as(O))
@@ -138,7 +149,7 @@ def test_joint_key_value_permutation(dtype):
     assert (O1 - O2).abs().max() <= tol
 
 
-@pytest.mark.parametrize("which", ["forward_causal", "forward_kpad", "decode"])
+@pytest.mark.parametrize("which", ["forward_causal", "forward_kpad", "forward_short", "decode"])
 def test_bitwise_determinism(which):
     say(f"[determinism {which}]")
     if which == "decode":
@@ -147,6 +158,10 @@ def test_bitwise_determinism(which):
         kl = torch.tensor([2000, 1, 3, 999, 1024, 1025, 64, 1500], dtype=torch.int32,
                           device="cuda")
         runs = [ha.decode(q, Kc, Vc, kl, scale=0.125) for _ in range(5)]
+    elif which == "forward_short":
+        Q, K, V = (_rand(s, (32, 8, 128, 64), BF16) for s in (27, 28, 29))
+        kl = torch.randint(8, 129, (32,), generator=torch.Generator().manual_seed(4)).to(torch.int32).cuda()
+        runs = [ha.forward(Q, K, V, mask_kind=1, q_lens=kl, kv_lens=kl, scale=0.125) for _ in range(5)]
     else:
         Q, K, V = (_rand(s, (2, 8, 1024, 64), BF16) for s in (24, 25, 26))
         mask = 2 if which == "forward_causal" else 1

@@ -10,7 +10,8 @@ same seeded inputs.
   span several tiles and a ragged tail, in both dtypes: n not a multiple of
   the tile sizes, lengths 0 / 1 / n, padded query rows, n_k = 0, negative
   and zero scale, out-of-range lengths (clamped), B*h divisible by 8 or not
-  (the two workgroup orders).
+  (the two workgroup orders), and shapes that reach each bf16 kernel (short
+  key range, 4-wave, paired).
 """
 import zlib
 
@@ -110,14 +111,24 @@ RAGGED = {
     "zero_scale": (2, 2, 40, 90, 1, None, [90, 17], 0.0),
     "big_scale": (1, 2, 70, 70, 0, None, None, 2.0),
     "cross_128x160": (4, 2, 128, 160, 1, None, [16, 160, 99, 128], 0.125),
+    # n_k <= 256: the short-key-range bf16 kernel (all of K/V loaded at once)
+    "short_causal_256": (2, 2, 256, 256, 2, None, None, 0.125),
+    "short_kpad_77x255": (3, 2, 77, 255, 1, [77, 10, 0], [255, 193, 1], 0.125),
+    "short_long_q_900x256": (1, 2, 900, 256, 1, [900], [200], 0.125),
+    "short_big_scale_150": (1, 2, 150, 150, 3, [150], [150], 2.0),
+    "short_single_key_col_300x1": (2, 2, 300, 1, 0, None, None, 0.125),
+    "short_one_tile_512x64": (1, 2, 512, 64, 0, None, None, 0.125),
+    "short_k_600x5": (1, 2, 600, 5, 0, None, None, 0.125),
+    # 256 < n_k, n_q < 512: the 4-wave bf16 kernel (keys streamed in tiles)
+    "fourwave_causal_384": (1, 2, 384, 384, 2, None, None, 0.125),
+    "fourwave_kpad_200x400": (2, 2, 200, 400, 1, [200, 50], [400, 257], 0.125),
     # n_q >= 512: the paired 8-wave bf16 kernel (256 query rows per workgroup)
     "pair_causal_1000": (1, 2, 1000, 1000, 2, None, None, 0.125),
     "pair_none_600x700": (2, 2, 600, 700, 0, None, None, 0.125),
     "pair_kpad_520x777": (3, 2, 520, 777, 1, [520, 300, 0], [777, 65, 1], 0.125),
     "pair_causal_kpad_768": (2, 2, 768, 768, 3, [768, 700], [768, 129], 0.125),
     "pair_xcd_causal_512": (8, 1, 512, 512, 2, None, None, 0.125),
-    "pair_one_tile_512x64": (1, 2, 512, 64, 0, None, None, 0.125),
-    "pair_short_k_600x5": (1, 2, 600, 5, 0, None, None, 0.125),
+    "pair_kv_257_600x257": (1, 2, 600, 257, 1, [600], [257], 0.125),
     "pair_big_scale_600": (1, 2, 600, 600, 0, None, None, 2.0),
     "pair_negative_scale_540": (1, 2, 540, 540, 2, None, None, -0.3),
     "pair_zero_scale_530x300": (2, 1, 530, 300, 1, None, [300, 44], 0.0),
