@@ -207,6 +207,33 @@ def decode(q, Kcache, Vcache, kv_lens, scale: float | None = None, pairs=None):
     return O
 
 
+def cache_append(Kcache, Vcache, Knew, Vnew, kv_lens):
+    """Append the K/V rows of new tokens to a decoder's caches (sj-techlog
+    page, KV cache section: the cache holds the K, V of tokens 0..t-1 and a
+    step adds the new token's K, V; kimjiil page §3.7: only the new token's
+    projections are computed per step).
+
+    Kcache, Vcache: [B, h, n_max, d]; Knew, Vnew: [B, h, n_new, d];
+    kv_lens[b]: valid cache rows of entry b *after* the append (the lengths
+    the following decode step reads).  New row r of entry b lands in cache
+    row kv_lens[b] - n_new + r; a row that falls outside [0, n_max) is not
+    written.  Returns new (Kcache, Vcache) arrays; the inputs are unchanged.
+    """
+    Kc = np.array(Kcache, copy=True)
+    Vc = np.array(Vcache, copy=True)
+    Kn = np.asarray(Knew)
+    Vn = np.asarray(Vnew)
+    B, H, n_max, _ = Kc.shape
+    n_new = Kn.shape[2]
+    for b in range(B):
+        for r in range(n_new):
+            row = int(kv_lens[b]) - n_new + r
+            if 0 <= row < n_max:
+                Kc[b, :, row] = Kn[b, :, r]
+                Vc[b, :, row] = Vn[b, :, r]
+    return Kc, Vc
+
+
 def sinusoidal_pe(pos: int, d_model: int) -> np.ndarray:
     """PE(pos, 2i) = sin(pos / 10000^(2i/d_model)), PE(pos, 2i+1) = cos(same).
 

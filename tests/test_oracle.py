@@ -302,6 +302,86 @@ def pin_decode_equals_recompute(orc):
         assert np.allclose(out[b, :, 0], full[b, :, lens[b] - 1], atol=1e-13)
 
 
+def pin_incremental_decode_equals_recompute(orc):
+    """sj-techlog page, KV cache section (and kimjiil page §3.7): a decoder
+    that appends each new token's K/V to its cache and attends from that
+    token alone computes, step by step, the rows of causal self-attention
+    over the whole sequence.  Caches start as NaN garbage; some entries are
+    fed one token per step, one with a first block of 3 (a prefill), so the
+    append's row placement and the decode's length rule are both pinned."""
+    n, d, B, H, n_max = 9, 8, 3, 2, 12
+    Q, K, V = (RNG.standard_normal((B, H, n, d)) for _ in range(3))
+    full = orc.attention(Q, K, V, mask_kind=orc.MASK_CAUSAL)
+    Kc = np.full((B, H, n_max, d), np.nan)
+    Vc = np.full((B, H, n_max, d), np.nan)
+    # entry 0 and 1: one token per step; entry 2: tokens 0-2 at once, then one per step
+    for t in range(n):
+        if t < 2:
+            new_rows = {0: [t], 1: [t], 2: []}
+        else:
+            new_rows = {0: [t], 1: [t], 2: [0, 1, 2] if t == 2 else [t]}
+        for b in range(B):
+            rows = new_rows[b]
+            if not rows:
+                continue
+            lens = np.zeros(B, dtype=np.int64)
+            lens[b] = rows[-1] + 1
+            Kn = np.zeros((B, H, len(rows), d))
+            Vn = np.zeros((B, H, len(rows), d))
+            Kn[b] = K[b][:, rows]
+            Vn[b] = V[b][:, rows]
+            Kb, Vb = orc.cache_append(Kc[b:b + 1], Vc[b:b + 1], Kn[b:b + 1], Vn[b:b + 1], lens[b:b + 1])
+            Kc[b:b + 1], Vc[b:b + 1] = Kb, Vb
+        lens = np.array([t + 1, t + 1, t + 1 if t >= 2 else 0])
+        for b in range(B):
+            if lens[b] == 0:
+                continue
+            out = orc.decode(Q[b:b + 1, :, t:t + 1], Kc[b:b + 1], Vc[b:b + 1], lens[b:b + 1])
+            assert np.allclose(out[0, :, 0], full[b, :, t], atol=1e-13), (t, b)
+
+
+def pin_cache_append_rows(orc):
+    """The append writes exactly the new rows: row r of the block lands at
+    cache row kv_len - n_new + r; every other cache row is unchanged, and a
+    row that would fall outside [0, n_max) is not written."""
+    B, H, n_max, d, n_new = 4, 2, 6, 3, 2
+    Kc = RNG.standard_normal((B, H, n_max, d))
+    Vc = RNG.standard_normal((B, H, n_max, d))
+    Kn = RNG.standard_normal((B, H, n_new, d))
+    Vn = RNG.standard_normal((B, H, n_new, d))
+    lens = np.array([2, 6, 1, 7])  # 1: first new row would be row -1; 7: last would be row 6
+    K2, V2 = orc.cache_append(Kc, Vc, Kn, Vn, lens)
+    for b in range(B):
+        for row in range(n_max):
+            r = row - (lens[b] - n_new)
+            if 0 <= r < n_new:
+                assert np.array_equal(K2[b, :, row], Kn[b, :, r]) and np.array_equal(V2[b, :, row], Vn[b, :, r])
+            else:
+                assert np.array_equal(K2[b, :, row], Kc[b, :, row]) and np.array_equal(V2[b, :, row], Vc[b, :, row])
+    assert np.array_equal(K2[2, :, 0], Kn[2, :, 1]) and np.array_equal(K2[3, :, 5], Kn[3, :, 0])
+
+
+def pin_cross_attention_decode(orc):
+    """kimjiil page §3.2.3 (encoder-decoder attention: queries from the
+    decoder, keys and values from the encoder output) with §3.7's cache: a
+    decode step against a fixed encoder cache is the key-padded cross
+    attention of that one query, and does not depend on the cache rows past
+    the source length."""
+    B, H, n_src, d = 3, 2, 7, 5
+    q = RNG.standard_normal((B, H, 1, d))
+    Ke, Ve = RNG.standard_normal((B, H, n_src, d)), RNG.standard_normal((B, H, n_src, d))
+    src = np.array([7, 1, 4])
+    out = orc.decode(q, Ke, Ve, src)
+    ref = orc.attention(q, Ke, Ve, mask_kind=orc.MASK_KEY_PADDING, kv_lens=src)
+    assert np.allclose(out, ref, atol=1e-14)
+    # one query, so the weights are softmax(K q s) over the first src rows
+    for b in range(B):
+        for h in range(H):
+            s = Ke[b, h, :src[b]] @ q[b, h, 0] / math.sqrt(d)
+            w = np.exp(s - s.max())
+            assert np.allclose(out[b, h, 0], (w / w.sum()) @ Ve[b, h, :src[b]], atol=1e-13)
+
+
 def pin_kv_cache_size(orc):
     """sj-techlog page KV cache arithmetic: 2 x 6 x 128 x 512 scalars,
     3.0 MiB in fp32 and 1.5 MiB in fp16."""

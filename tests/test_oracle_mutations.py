@@ -21,6 +21,7 @@ _allowed = orc.allowed_keys
 _attention = orc.attention
 _decode = orc.decode
 _pe = orc.sinusoidal_pe
+_append = orc.cache_append
 
 
 def m_causal_strict(i, n_k, kv_len, causal):
@@ -118,6 +119,22 @@ def m_decode_without_new_token(q, Kc, Vc, kv_lens, scale=None, pairs=None):
     return _decode(q, Kc, Vc, np.maximum(np.asarray(kv_lens) - 1, 1), scale, pairs)
 
 
+def m_append_one_row_late(Kc, Vc, Kn, Vn, kv_lens):
+    # off by one: the block lands one row past where the lengths put it
+    return _append(Kc, Vc, Kn, Vn, np.asarray(kv_lens) + 1)
+
+
+def m_append_reversed(Kc, Vc, Kn, Vn, kv_lens):
+    # the new block written in reverse row order
+    return _append(Kc, Vc, np.asarray(Kn)[:, :, ::-1], np.asarray(Vn)[:, :, ::-1], kv_lens)
+
+
+def m_append_k_only(Kc, Vc, Kn, Vn, kv_lens):
+    # the V row never reaches the cache
+    K2, _ = _append(Kc, Vc, Kn, Vn, kv_lens)
+    return K2, np.array(Vc, copy=True)
+
+
 def m_pe_swapped(pos, d_model):
     out = np.zeros(d_model)
     for dim in range(d_model):
@@ -147,6 +164,9 @@ MUTANTS = {
     "scale_1_over_dk": ("attention", m_scale_one_over_dk),
     "q_lens_ignored": ("attention", m_ignore_q_lens),
     "decode_drops_new_token": ("decode", m_decode_without_new_token),
+    "append_one_row_late": ("cache_append", m_append_one_row_late),
+    "append_block_reversed": ("cache_append", m_append_reversed),
+    "append_drops_v": ("cache_append", m_append_k_only),
     "pe_sin_cos_swapped": ("sinusoidal_pe", m_pe_swapped),
     "pe_exponent_i": ("sinusoidal_pe", m_pe_exponent),
 }
