@@ -8,6 +8,10 @@ decode HBM GB/s"):
   decoder_big   bf16 causal self-attention n128 + cross-attention 128->160
                 with source padding, B32 h16
   long_causal   bf16 causal self-attention B1 h16 n8192
+  kv_append     bf16 KV-cache append of one token per sequence at the decode
+                shape (the cache update of a decode step; it writes row L-1
+                with the values the cache holds there, so the decode's
+                inputs do not change)
   kv_decode     bf16 KV-cache decode, B64 h16, cache 4096, L in [1, 4096]
 Inputs are the seeded synthetic tensors of workloads.py, resident in HBM
 before timing starts.  Each leg is bracketed by HIP events on the stream
@@ -56,10 +60,11 @@ def kernel_source_hash() -> str:
 
 # ------------------------------------------------------------------ legs
 class Leg:
-    def __init__(self, name, calls=None, decode=None):
+    def __init__(self, name, calls=None, decode=None, append=None):
         self.name = name
         self.calls = calls or []   # forward calls (dicts of CPU tensors)
         self.decode = decode       # decode call (dict of CPU tensors)
+        self.append = append       # cache-append call (dict of CPU tensors)
         self.flops = 0
         self.bytes = 0
 
@@ -84,13 +89,26 @@ class Leg:
             L = int(d["kv_lens"].sum())
             self.flops += 4 * D * L * H
             self.bytes += 2 * L * H * D * el + 2 * B * H * D * el + 4 * B
+        if self.append is not None:
+            a = self.append
+            B, H, n_new, _ = a["Knew"].shape
+            el = a["Knew"].element_size()
+            # K and V rows read from the new block and written to the caches
+            self.bytes += 2 * 2 * B * H * n_new * D * el + 4 * B
 
 
 def make_legs():
     legs = []
     for name in ("encoder_base", "decoder_big", "long_causal"):
         legs.append(Leg(name, calls=workloads.make(name)["calls"]))
-    legs.append(Leg("kv_decode", decode=workloads.make("kv_decode")))
+    kd = workloads.make("kv_decode")
+    rows = (kd["kv_lens"] - 1).long()
+    bi = torch.arange(kd["q"].shape[0])
+    append = {"Knew": kd["Kcache"][bi, :, rows].unsqueeze(2).contiguous(),
+              "Vnew": kd["Vcache"][bi, :, rows].unsqueeze(2).contiguous(),
+              "kv_lens": kd["kv_lens"]}
+    legs.append(Leg("kv_append", append=append))
+    legs.append(Leg("kv_decode", decode=kd))
     for leg in legs:
         leg.count()
     return legs
@@ -104,6 +122,9 @@ def to_device(legs):
             dc = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in c.items()}
             dc["O"] = torch.empty_like(dc["Q"])
             leg.dev_calls.append(dc)
+        leg.dev_append = None
+        if leg.append is not None:
+            leg.dev_append = {k: v.cuda() for k, v in leg.append.items()}
         if leg.decode is not None:
             d = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in leg.decode.items()}
             B, H, _, _ = d["q"].shape
@@ -116,8 +137,11 @@ def to_device(legs):
             leg.dev_decode = None
 
 
-def run_leg(leg):
+def run_leg(leg, caches=None):
     import head_attention_amd as ha
+    a = leg.dev_append
+    if a is not None:
+        ha.cache_append(a["Knew"], a["Vnew"], caches["Kcache"], caches["Vcache"], a["kv_lens"])
     for c in leg.dev_calls:
         ha.forward(c["Q"], c["K"], c["V"], mask_kind=c["mask"], q_lens=c["q_lens"],
                    kv_lens=c["kv_lens"], scale=c["scale"], out=c["O"])
@@ -334,11 +358,13 @@ def main():
     legs = make_legs()
     to_device(legs)
     stream = torch.cuda.current_stream()
+    dd = next(leg.dev_decode for leg in legs if leg.dev_decode is not None)
+    caches = {"Kcache": dd["Kcache"], "Vcache": dd["Vcache"]}  # the append writes the decode's caches
     torch.cuda.synchronize()
 
     for _ in range(args.warmup):
         for leg in legs:
-            run_leg(leg)
+            run_leg(leg, caches)
     torch.cuda.synchronize()
 
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -347,7 +373,7 @@ def main():
     for s in range(args.steps):
         for j, leg in enumerate(legs):
             ev[s][j][0].record(stream)
-            run_leg(leg)
+            run_leg(leg, caches)
             ev[s][j][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -355,7 +381,7 @@ def main():
     leg_ms = [sum(ev[s][j][0].elapsed_time(ev[s][j][1]) for s in range(args.steps)) / args.steps
               for j in range(len(legs))]
     step_ms = sum(leg_ms)
-    fwd = [j for j, leg in enumerate(legs) if leg.dev_decode is None]
+    fwd = [j for j, leg in enumerate(legs) if leg.dev_calls]
     fwd_flops = sum(legs[j].flops for j in fwd)
     fwd_ms = sum(leg_ms[j] for j in fwd)
     value = fwd_flops / (fwd_ms * 1e-3) / 1e12
@@ -435,6 +461,12 @@ def main():
         out["copy_probe_bytes_each_way"] = args.copy_probe_mib * 2 ** 20
     if not args.no_sanity:
         out["sanity_max_abs_err_vs_oracle"] = round(sanity_check(legs), 6)
+        ap = next(leg.dev_append for leg in legs if leg.dev_append is not None)
+        rows = (ap["kv_lens"] - 1).long()
+        bi = torch.arange(rows.shape[0], device=rows.device)
+        out["sanity_append_rows_exact"] = bool(
+            torch.equal(caches["Kcache"][bi, :, rows], ap["Knew"][:, :, 0])
+            and torch.equal(caches["Vcache"][bi, :, rows], ap["Vnew"][:, :, 0]))
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)

@@ -1,7 +1,8 @@
 """MI355X-native scaled dot-product attention (gfx950 HIP kernels behind a C ABI).
 
-    from head_attention_amd import forward, decode
+    from head_attention_amd import forward, decode, cache_append
     O = forward(Q, K, V, mask_kind=ATTN_MASK_CAUSAL, scale=0.125)
+    cache_append(k_new, v_new, Kcache, Vcache, kv_lens)   # then decode(...)
 
 The C ABI is include/headattn.h; libheadattn.so is built in-tree with
 `python -m head_attention_amd.build`.
@@ -15,6 +16,7 @@ from ._binding import (  # noqa: F401
     LIB_PATH,
     AttnError,
     attn_layout,
+    cache_append,
     decode,
     decode_workspace_bytes,
     forward,

@@ -63,6 +63,8 @@ def lib() -> ctypes.CDLL:
         L.attn_decode.argtypes = [vp, vp, vp, attn_layout, i32p, ctypes.c_float, vp, vp,
                                   ctypes.c_size_t, vp]
         L.attn_decode.restype = ctypes.c_int
+        L.attn_cache_append.argtypes = [vp, vp, vp, vp, attn_layout, i32p, vp]
+        L.attn_cache_append.restype = ctypes.c_int
         L.attn_decode_workspace_bytes.argtypes = [attn_layout]
         L.attn_decode_workspace_bytes.restype = ctypes.c_size_t
         L.attn_status_string.argtypes = [ctypes.c_int]
@@ -195,3 +197,26 @@ def decode(q: torch.Tensor, Kcache: torch.Tensor, Vcache: torch.Tensor, kv_lens:
     if st != 0:
         raise AttnError(st, "attn_decode")
     return out
+
+
+def cache_append(Knew: torch.Tensor, Vnew: torch.Tensor, Kcache: torch.Tensor, Vcache: torch.Tensor,
+                 kv_lens: torch.Tensor, stream=None) -> None:
+    """attn_cache_append: write the new tokens' K/V rows into the caches.
+
+    Knew, Vnew [B, h, n_new, 64]; Kcache, Vcache [B, h, n_max, 64] (written in
+    place); kv_lens int32 GPU [B] = valid rows of each entry after the append.
+    Row r of the new block lands in cache row kv_lens[b] - n_new + r; rows
+    that would fall outside the cache are skipped (see include/headattn.h).
+    """
+    dt = Knew.dtype
+    for n, t in (("Knew", Knew), ("Vnew", Vnew), ("Kcache", Kcache), ("Vcache", Vcache)):
+        _check_tensor(n, t, dt)
+    B, H, n_new, d = Knew.shape
+    n_max = Kcache.shape[2]
+    if Vnew.shape != Knew.shape or Kcache.shape != (B, H, n_max, d) or Vcache.shape != Kcache.shape:
+        raise ValueError("new rows must be [B, h, n_new, d] and the caches [B, h, n_max, d]")
+    layout = attn_layout(B, H, n_new, n_max, d, _dtype_code(Knew))
+    st = lib().attn_cache_append(Knew.data_ptr(), Vnew.data_ptr(), Kcache.data_ptr(), Vcache.data_ptr(),
+                                 layout, _lens_ptr("kv_lens", kv_lens, B), _stream_handle(stream, Knew))
+    if st != 0:
+        raise AttnError(st, "attn_cache_append")

@@ -140,6 +140,49 @@ attn_status attn_forward(const void* Q, const void* K, const void* V, attn_layou
   return ATTN_OK;
 }
 
+attn_status attn_cache_append(const void* Knew, const void* Vnew, void* Kcache, void* Vcache,
+                              attn_layout L, const int32_t* kv_lens, void* stream) {
+  attn_status st = check_layout(L);
+  if (st != ATTN_OK) return st;
+  if (L.B == 0 || L.h == 0 || L.n_q == 0) return ATTN_OK;  // nothing to append
+  if (!Knew || !Vnew || !Kcache || !Vcache || !kv_lens) return ATTN_ERR_NULL_POINTER;
+  if (Knew == Kcache || Knew == Vcache || Vnew == Kcache || Vnew == Vcache || Kcache == Vcache)
+    return ATTN_ERR_BAD_SHAPE;
+  const int row_bytes = kHeadDim * (L.dtype == ATTN_BF16 ? 2 : 4);
+  const int64_t chunks = (int64_t)L.B * L.h * L.n_q * (row_bytes / 16);
+  if ((chunks + 255) / 256 > kMaxGrid) return ATTN_ERR_BAD_SHAPE;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (length_check_enabled()) {
+    std::vector<int32_t> h;
+    const hipError_t e = read_lengths(kv_lens, L.B, s, h);
+    if (e != hipSuccess) {
+      g_last_hip = e;
+      return ATTN_ERR_HIP;
+    }
+    for (int32_t v : h)
+      if (v < L.n_q || v > L.n_k) return ATTN_ERR_BAD_LENGTHS;
+  }
+
+  AppendArgs a;
+  a.Kn = Knew;
+  a.Vn = Vnew;
+  a.Kc = Kcache;
+  a.Vc = Vcache;
+  a.kv_lens = kv_lens;
+  a.B = L.B;
+  a.H = L.h;
+  a.n_new = L.n_q;
+  a.n_max = L.n_k;
+  a.row_bytes = row_bytes;
+  const hipError_t e = launch_cache_append(a, s);
+  if (e != hipSuccess) {
+    g_last_hip = e;
+    return ATTN_ERR_HIP;
+  }
+  return ATTN_OK;
+}
+
 size_t attn_decode_workspace_bytes(attn_layout L) {
   if (check_layout(L) != ATTN_OK || L.n_q != 1) return 0;
   return (size_t)L.B * L.h * decode_splits(L.n_k) * kPartialStride * sizeof(float);

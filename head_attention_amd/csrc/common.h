@@ -40,6 +40,18 @@ struct DecodeArgs {
   float scale;
 };
 
+// One KV-cache append: n_new rows per (b, h) copied into the caches.
+struct AppendArgs {
+  const void* Kn;
+  const void* Vn;
+  void* Kc;
+  void* Vc;
+  const int32_t* kv_lens;  // device int32[B], lengths after the append
+  int B, H, n_new, n_max;
+  int row_bytes;           // 64 * element size
+};
+hipError_t launch_cache_append(const AppendArgs& a, hipStream_t s);
+
 // Decode: keys per split (one workgroup of 4 waves x 64 keys).
 constexpr int kDecodeWaves = 4;
 constexpr int kDecodeChunk = 64 * kDecodeWaves;

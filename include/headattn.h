@@ -36,6 +36,8 @@
  *   ATTN_ERR_BAD_LENGTHS when one is out of range.
  * Allocation.  Entry points allocate no memory; decode's scratch is a
  *   caller-provided workspace.
+ * Lengths of attn_cache_append are the one exception to clamping: a row
+ *   whose destination falls outside the cache is skipped instead.
  * Empty calls.  B = 0, h = 0 or n_q = 0 is a valid call that does nothing.
  *   n_k = 0 (no keys) writes every row of O as 0; K and V may then be NULL.
  */
@@ -147,6 +149,34 @@ attn_status attn_decode(const void* q, const void* Kcache, const void* Vcache,
                         attn_layout cache_layout, const int32_t* kv_lens,
                         float scale, void* O, void* workspace,
                         size_t workspace_bytes, void* stream);
+
+/*
+ * attn_cache_append -- write the K/V rows of new tokens into a decoder's
+ * caches: the cache update that precedes attn_decode (sj-techlog page, KV
+ * cache section: a step's cache holds the K, V of tokens 0..t-1 plus the new
+ * token's; kimjiil page §3.7: per step only the new token's K, V are
+ * computed).  A block of n_new > 1 rows is a prefill of several tokens.
+ *
+ *   Knew, Vnew     [B, h, n_new, 64]  device, read
+ *   Kcache, Vcache [B, h, n_max, 64]  device, written in place: only the
+ *                  rows the block lands on change
+ *   cache_layout   B, h, n_q = n_new (rows appended per (b, h)),
+ *                  n_k = n_max, d = 64, dtype
+ *   kv_lens        device int32[B], required: the valid rows of entry b
+ *                  AFTER the append, i.e. the lengths the following
+ *                  attn_decode reads.  Row r of the block lands in cache row
+ *                  kv_lens[b] - n_new + r; a row that would fall outside
+ *                  [0, n_max) is not written, so no length can cause an
+ *                  out-of-bounds write.  With ATTN_CHECK=1 a length outside
+ *                  [n_new, n_max] returns ATTN_ERR_BAD_LENGTHS.
+ *   stream         hipStream_t or NULL.
+ * A pure copy: the written cache rows are bit-identical to the new rows.
+ * The new rows must not overlap the caches (ATTN_ERR_BAD_SHAPE when a base
+ * pointer coincides).  n_new = 0, B = 0 or h = 0 does nothing.
+ */
+attn_status attn_cache_append(const void* Knew, const void* Vnew, void* Kcache,
+                              void* Vcache, attn_layout cache_layout,
+                              const int32_t* kv_lens, void* stream);
 
 /* Bytes of fp32 split partials attn_decode needs for this cache layout; 0 if
  * the layout is invalid.  Pure host arithmetic. */

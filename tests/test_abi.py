@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("attn_forward", "attn_decode", "attn_decode_workspace_bytes",
+    for n in ("attn_forward", "attn_decode", "attn_cache_append", "attn_decode_workspace_bytes",
               "attn_status_string", "attn_last_hip_error"):
         assert n in names, names
 
@@ -121,6 +121,24 @@ def test_decode_validation():
     assert dec(L, wsb=ha.lib().attn_decode_workspace_bytes(L) - 1) == WORK
     assert dec(L, o=FAKE) == SHAPE
     assert dec(attn_layout(0, 2, 1, 300, 64, BF16), q=None, o=None, kl=None) == OK
+
+
+def app(layout, kn=FAKE, vn=FAKE + 32, kc=FAKE + 64, vc=FAKE + 96, kl=FAKE + 128):
+    return ha.lib().attn_cache_append(kn, vn, kc, vc, layout, kl, None)
+
+
+def test_cache_append_validation():
+    L = attn_layout(4, 2, 1, 300, 64, BF16)
+    assert app(attn_layout(4, 2, 1, 300, 16, BF16)) == SHAPE
+    assert app(attn_layout(4, 2, -1, 300, 64, BF16)) == SHAPE
+    assert app(attn_layout(4, 2, 1, 300, 64, 5)) == DTYPE
+    for kw in ("kn", "vn", "kc", "vc", "kl"):
+        assert app(L, **{kw: None}) == NULLP, kw
+    assert app(L, kc=FAKE) == SHAPE        # new rows alias the cache
+    assert app(L, vc=FAKE + 64) == SHAPE   # K and V caches alias
+    # nothing to append: OK without touching any pointer or the device
+    assert app(attn_layout(0, 2, 1, 300, 64, BF16), kn=None, vn=None, kc=None, vc=None, kl=None) == OK
+    assert app(attn_layout(4, 2, 0, 300, 64, F32), kn=None, vn=None, kc=None, vc=None, kl=None) == OK
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
