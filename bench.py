@@ -47,7 +47,10 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E
 D = 64
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
-KERNEL_SOURCES = ["attn_fwd_bf16.hip", "attn_decode.hip", "common.h"]
+# Sources of every kernel the bench launches: the traffic figures are reported
+# only while these are unchanged since the counters were taken.
+KERNEL_SOURCES = ["attn_fwd_bf16_pair.hip", "attn_fwd_bf16_short.hip", "attn_fwd_bf16.hip",
+                  "attn_decode.hip", "attn_cache.hip", "common.h"]
 
 
 def kernel_source_hash() -> str:
@@ -233,16 +236,16 @@ def cpu_baseline(target_s: float = 25.0):
 
 # ------------------------------------------------------- rocprof summaries
 def _short_kernel(name: str) -> str:
-    """attn_fwd_bf16[_pair]_kernel<causal, ...> -> ..._kernel<true|false>; other
-    kernels of the library by their plain name."""
+    """attn_fwd_bf16[_pair|_short]_kernel<causal, ...> -> ..._kernel<true|false>;
+    other kernels of the library by their plain name."""
     import re
-    m = re.search(r"(attn_fwd_bf16(?:_pair)?_kernel)<(true|false)", name) or \
-        re.search(r"(attn_fwd_bf16(?:_pair)?_kernel)ILb(\d)", name)
+    m = re.search(r"(attn_fwd_bf16(?:_pair|_short)?_kernel)<(true|false)", name) or \
+        re.search(r"(attn_fwd_bf16(?:_pair|_short)?_kernel)ILb(\d)", name)
     if m:
         causal = m.group(2) in ("true", "1")
         return f"{m.group(1)}<{'true' if causal else 'false'}>"
     for key in ("attn_fwd_f32_kernel", "decode_partial_kernel", "decode_merge_kernel",
-                "copyBuffer", "elementwise"):
+                "cache_append_kernel", "copyBuffer", "elementwise"):
         if key in name:
             return key
     return name[:60]
@@ -250,9 +253,10 @@ def _short_kernel(name: str) -> str:
 
 # Grid sizes (threads) of each leg's launches, to tell apart launches of the
 # same kernel in a trace of the default bench command.
-LEG_GRIDS = {("attn_fwd_bf16_kernel<false>", 65536): "encoder_base",
-             ("attn_fwd_bf16_kernel<true>", 131072): "decoder_big (causal self)",
-             ("attn_fwd_bf16_kernel<false>", 131072): "decoder_big (cross)",
+LEG_GRIDS = {("attn_fwd_bf16_short_kernel<false>", 65536): "encoder_base",
+             ("attn_fwd_bf16_short_kernel<true>", 131072): "decoder_big (causal self)",
+             ("attn_fwd_bf16_short_kernel<false>", 131072): "decoder_big (cross)",
+             ("cache_append_kernel", 8192): "kv_append",
              ("attn_fwd_bf16_pair_kernel<true>", 262144): "long_causal",
              ("decode_partial_kernel", 4194304): "kv_decode",
              ("decode_merge_kernel", 65536): "kv_decode"}
