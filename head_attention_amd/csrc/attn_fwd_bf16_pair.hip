@@ -23,8 +23,13 @@
 // the other issues the exponentials: the two kinds of work overlap across the
 // two waves instead of alternating inside one.  (Measured on MI355X: MFMA
 // and fma/exp/cvt work from two waves of one SIMD overlap, while v_dot2
-// waits for the matrix pipe -- so the row sums, v_dot2 of the bf16 weights
-// with ones, run in the MFMA phase of the wave that owns that pipe.)
+// waits for the matrix pipe -- so the row sums run on the matrix cores
+// themselves, as 16x16x32 products of the weights with a 0/1 selector, in
+// the MFMA phase: 8 small products per tile instead of 32 v_dot2.)
+//
+// The MFMA phase is one straight block: its LDS fragment reads go out in the
+// order of use, at most 12 in flight, so each group of products waits only
+// for its own fragments while the rest arrive.
 //
 // 64 rows per wave means each K or V fragment read from LDS feeds two query
 // blocks, half the LDS traffic per flop of 32-row waves; the per-wave state
@@ -63,6 +68,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
@@ -154,37 +160,6 @@ __device__ __forceinline__ float max32(const f32x16& a, const f32x16& b) {
   const float n2 = fmaxf(fmaxf(m[6], m[7]), m[8]);
   const float n3 = fmaxf(m[9], m[10]);
   return fmaxf(fmaxf(fmaxf(n0, n1), n2), n3);
-}
-
-// Sum of the 32 bf16 weights of one query block held by this lane, in fp32
-// (v_dot2 with ones: each bf16 is exact in fp32, and the adds are fp32 adds).
-__device__ __forceinline__ float bf16_sum(const uint32_t (&pk)[16]) {
-  const bf16x2 ones = __builtin_bit_cast(bf16x2, 0x3f803f80u);
-  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    a0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[i]), ones, a0, false);
-    a1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[4 + i]), ones, a1, false);
-    a2 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[8 + i]), ones, a2, false);
-    a3 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[12 + i]), ones, a3, false);
-  }
-  return (a0 + a1) + (a2 + a3);
-}
-
-// End the live range of registers whose value no later path reads, at no
-// cost: an empty volatile asm that "writes" them.  A plain assignment would
-// do the same, but the compiler hoists it onto the hot path (64 moves per
-// phase) or folds it into the accumulator initialisation.
-__device__ __forceinline__ void retire(f32x16& a, f32x16& b, f32x16& c, f32x16& d) {
-  asm volatile("" : "=v"(a), "=v"(b), "=v"(c), "=v"(d));
-}
-__device__ __forceinline__ void retire_frag(bf16x8 (&f)[2][4]) {
-  asm volatile("" : "=v"(f[0][0]), "=v"(f[0][1]), "=v"(f[0][2]), "=v"(f[0][3]));
-  asm volatile("" : "=v"(f[1][0]), "=v"(f[1][1]), "=v"(f[1][2]), "=v"(f[1][3]));
-}
-__device__ __forceinline__ void retire_pk(uint32_t (&p)[16]) {
-  asm volatile("" : "=v"(p[0]), "=v"(p[1]), "=v"(p[2]), "=v"(p[3]), "=v"(p[4]), "=v"(p[5]), "=v"(p[6]), "=v"(p[7]));
-  asm volatile("" : "=v"(p[8]), "=v"(p[9]), "=v"(p[10]), "=v"(p[11]), "=v"(p[12]), "=v"(p[13]), "=v"(p[14]), "=v"(p[15]));
 }
 
 __device__ __forceinline__ void barrier_lds() {
@@ -282,7 +257,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_pair_kernel(FwdArgs
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       uint4 v = make_uint4(0, 0, 0, 0);
-      if (qi < a.n_q) v = *reinterpret_cast<const uint4*>(Q + (size_t)qi * kHeadDim + 16 * s + 8 * hh);
+      // Padded query rows (i >= q_len, written as zeros) enter as zeros: the
+      // row-sum products multiply other rows' weights by 0, which must not
+      // meet NaN from padded memory.
+      if (qi < q_len) v = *reinterpret_cast<const uint4*>(Q + (size_t)qi * kHeadDim + 16 * s + 8 * hh);
       v.x ^= sign;
       v.y ^= sign;
       v.z ^= sign;
@@ -298,7 +276,23 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_pair_kernel(FwdArgs
   f32x16 sc[2][2];   // S^T[key block][query block] of the current tile
   uint32_t pk[2][16];  // bf16 weights [query block][8 key block + pair]
   float mc[2] = {0.f, 0.f};  // pivot term m * c per query block
-  float l[2] = {0.f, 0.f};   // this half-wave's partial row sums
+  // Row sums of the bf16 weights, accumulated on the matrix cores: one
+  // v_mfma_f32_16x16x32_bf16 per key step and query block takes the weights
+  // as they sit in the P registers (B operand: lane l supplies 8 values of
+  // column l % 16 in k group l / 16, i.e. of query l % 32 -- the groups of
+  // odd index hold queries 16..31) against a constant 0/1 A operand whose
+  // row 0 selects the even k groups and row 1 the odd ones.  Row 0 of the
+  // 16 x 16 result then holds the sums of queries 0..15 and row 1 those of
+  // queries 16..31: lanes 0..15, registers 0 and 1 (rows 2..15 stay 0).
+  // Each product is an exact bf16 value times 1, summed in fp32.
+  f32x4 ls[2] = {f32x4{}, f32x4{}};
+  const bf16x8 sel = __builtin_bit_cast(
+      bf16x8, (((lane & 15) == 0 && ((lane >> 4) & 1) == 0) || ((lane & 15) == 1 && ((lane >> 4) & 1) == 1))
+                  ? make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u)
+                  : make_uint4(0u, 0u, 0u, 0u));
+  // Whether a row has summed a nonzero weight yet (the pivot may move down
+  // only before that); both half-waves of a row agree.
+  bool seen[2] = {false, false};
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -311,20 +305,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_pair_kernel(FwdArgs
 #pragma unroll
     for (int i = 0; i < 16; ++i) pk[qb][i] = 0u;
 
-  // MFMA operand fragments, read from LDS at the start of the MFMA phase.
-  // K: [key block][d-step]; lane (ln, hh) holds K[32 kb + ln][16 s + 8 hh +
-  // 0..7].
-  auto load_k = [&](auto slot_tag, bf16x8 (&ka)[2][4]) __attribute__((always_inline)) {
-    constexpr int S = decltype(slot_tag)::value;
-    const uint4* kt = kslot<S>();
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int row = 32 * kb + ln;
-        ka[kb][s] = __builtin_bit_cast(bf16x8, kt[row * 8 + ((2 * s + hh) ^ (row & 7))]);
-      }
-  };
+  // MFMA operand fragments, read from LDS in the MFMA phase in the order
+  // of use with at most 12 reads in flight, so each group of products waits
+  // only for its own fragments (the LDS counter tracks 15 outstanding reads;
+  // past that every wait becomes a wait for all of them).
+  //
   // V^T: [d block][key step].  Key step j (16 keys) of key block kb = j / 2
   // takes, in MFMA k order, keys 16 (j % 2) + {0..3, 8..11} + 4 hh of the
   // block -- the order the S accumulators hold them in, so P feeds the B
@@ -332,50 +317,59 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_pair_kernel(FwdArgs
   // of 4 keys: lane i of 16-lane group g names row (key) kr and 8-byte chunk
   // h, and the read returns to lane i the 4 keys kr - i/4 .. +3 of d = dbase
   // + i.
-  auto load_v = [&](auto slot_tag, bf16x8 (&va)[2][4]) __attribute__((always_inline)) {
+  auto load_v_step = [&](auto slot_tag, auto j_tag, bf16x8 (&va)[2][4]) __attribute__((always_inline)) {
     constexpr int S = decltype(slot_tag)::value;
+    constexpr int j = decltype(j_tag)::value;
     const char* vt = reinterpret_cast<const char*>(vslot<S>());
     const int g = lane >> 4;
     const int i = lane & 15;
 #pragma unroll
-    for (int db = 0; db < 2; ++db)
+    for (int db = 0; db < 2; ++db) {
+      s16x4 part[2];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        s16x4 part[2];
-#pragma unroll
-        for (int x = 0; x < 2; ++x) {
-          const int kr = 16 * j + 8 * x + 4 * (g >> 1) + (i >> 2);
-          const int h = 8 * db + 4 * (g & 1) + (i & 3);
-          const int byte = kr * (int)kRowBytes + 16 * ((h >> 1) ^ (2 * (kr & 3))) + 8 * (h & 1);
-          part[x] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vt + byte));
-        }
-        va[db][j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
+      for (int x = 0; x < 2; ++x) {
+        const int kr = 16 * j + 8 * x + 4 * (g >> 1) + (i >> 2);
+        const int h = 8 * db + 4 * (g & 1) + (i & 3);
+        const int byte = kr * (int)kRowBytes + 16 * ((h >> 1) ^ (2 * (kr & 3))) + 8 * (h & 1);
+        part[x] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vt + byte));
       }
+      va[db][j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
+    }
   };
-
-  // S^T = K Q^T: 2 key blocks x 2 query blocks x 4 d-steps.
-  auto qk = [&](const bf16x8 (&ka)[2][4]) __attribute__((always_inline)) {
+  // K: [key block][d-step]; lane (ln, hh) holds K[32 kb + ln][16 s + 8 hh +
+  // 0..7].
+  auto load_k_step = [&](auto slot_tag, auto s_tag, bf16x8 (&ka)[2][4]) __attribute__((always_inline)) {
+    constexpr int S = decltype(slot_tag)::value;
+    constexpr int s = decltype(s_tag)::value;
+    const uint4* kt = kslot<S>();
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        f32x16 acc = f32x16{};
-#pragma unroll
-        for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kb][s], qf[qb][s], acc, 0, 0, 0);
-        sc[kb][qb] = acc;
-      }
+    for (int kb = 0; kb < 2; ++kb) {
+      const int row = 32 * kb + ln;
+      ka[kb][s] = __builtin_bit_cast(bf16x8, kt[row * 8 + ((2 * s + hh) ^ (row & 7))]);
+    }
   };
-  // O^T += V^T P^T.
-  auto pv = [&](const bf16x8 (&va)[2][4]) __attribute__((always_inline)) {
+  // O^T += V^T P^T for key step j, and the row sums of that step's weights.
+  auto pv_step = [&](auto j_tag, const bf16x8 (&va)[2][4]) __attribute__((always_inline)) {
+    constexpr int j = decltype(j_tag)::value;
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+    for (int qb = 0; qb < 2; ++qb) {
+      const bf16x8 pb = __builtin_bit_cast(
+          bf16x8, make_uint4(pk[qb][4 * j], pk[qb][4 * j + 1], pk[qb][4 * j + 2], pk[qb][4 * j + 3]));
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const bf16x8 pb = __builtin_bit_cast(
-            bf16x8, make_uint4(pk[qb][4 * j], pk[qb][4 * j + 1], pk[qb][4 * j + 2], pk[qb][4 * j + 3]));
+      for (int db = 0; db < 2; ++db) o[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db][j], pb, o[db][qb], 0, 0, 0);
+      ls[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sel, pb, ls[qb], 0, 0, 0);
+    }
+  };
+  // S^T = K Q^T: 2 key blocks x 2 query blocks x 4 d-steps, d-steps
+  // outermost so four independent accumulation chains interleave.
+  auto qk_smajor = [&](const bf16x8 (&ka)[2][4]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int db = 0; db < 2; ++db) o[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[db][j], pb, o[db][qb], 0, 0, 0);
-      }
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+          sc[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kb][s], qf[qb][s], s == 0 ? f32x16{} : sc[kb][qb], 0, 0, 0);
   };
 
   // Weights of tile t from sc into pk.  Masks only on the tiles that cross
@@ -417,10 +411,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_pair_kernel(FwdArgs
     bool move[2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) move[qb] = gap[qb] > kPivotUp;
-    if (__builtin_amdgcn_ballot_w64(l[0] == 0.f || l[1] == 0.f) != 0) {
+    if (__builtin_amdgcn_ballot_w64(!seen[0] || !seen[1]) != 0) {
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-        move[qb] = move[qb] || (gap[qb] < kPivotDown && gap[qb] > -INFINITY && half_swap_sum(l[qb]) == 0.f);
+      for (int qb = 0; qb < 2; ++qb) {
+        move[qb] = move[qb] || (gap[qb] < kPivotDown && gap[qb] > -INFINITY && !seen[qb]);
+        seen[qb] = seen[qb] || gap[qb] > -INFINITY;  // after this tile the row holds a weight >= 2^-64
+      }
     }
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
@@ -430,7 +426,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_pair_kernel(FwdArgs
         // l is 0 (nothing to rescale).
         const float shift = move[qb] ? gap[qb] : 0.f;
         const float alpha = shift > 0.f ? __builtin_amdgcn_exp2f(-shift) : 1.f;
-        l[qb] *= alpha;
+        // Row sums: lanes 0..15 hold query n in register 0 and query n + 16
+        // in register 1; the factor of query n + 16 comes from lane n + 16.
+        const auto hi = __builtin_amdgcn_permlane16_swap(__float_as_uint(alpha), __float_as_uint(alpha), false, false);
+        ls[qb][0] *= alpha;
+        ls[qb][1] *= __uint_as_float(hi[1]);
         o[0][qb] *= alpha;
         o[1][qb] *= alpha;
         mc[qb] += shift;
@@ -459,39 +459,58 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_pair_kernel(FwdArgs
     barrier_lds();
   };
   // MFMA phase at phase p (slot J = p % 4): P.V of tile p - 2, then S of
-  // tile p.  Both fragment reads are issued first, so the K reads arrive
-  // while the P.V products run.  Both branches define sc, so the scores
-  // live only until the next vector phase.
-  auto mphase = [&](auto j_tag, int t_pv, int t_qk) __attribute__((always_inline)) {
+  // tile p.  It runs unconditionally, so the phase is one straight block:
+  // before a wave's first tile and past its last one the weights are zero
+  // and the V slot holds finite values (zeroed at start, or a tile read
+  // through the range check), so P.V adds exact zeros; scores of a tile
+  // past the end are never turned into weights.  V reads of key steps 0-2
+  // go out first, each P.V step issues the next reads before its products,
+  // and the K reads go out during the last P.V steps, arriving before S
+  // needs them.  All of P.V comes before any of S: the weights and V
+  // fragments die before the scores are born.
+  auto mphase = [&](auto j_tag) __attribute__((always_inline)) {
     constexpr int J = decltype(j_tag)::value;
+    using SV = std::integral_constant<int, (J + 2) & 3>;
+    using SK = std::integral_constant<int, J>;
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
     __builtin_amdgcn_s_setprio(1);
-    const bool do_pv = t_pv >= 0 && t_pv < wave_tiles;
-    const bool do_qk = t_qk < wave_tiles;
     bf16x8 va[2][4], ka[2][4];
-    if (do_pv) load_v(std::integral_constant<int, (J + 2) & 3>(), va);
-    if (do_qk) load_k(std::integral_constant<int, J>(), ka);
-    if (do_pv) {
-      pv(va);
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) l[qb] += bf16_sum(pk[qb]);
-    }
-    // All of P.V before any of S: the weights and V fragments die before the
-    // scores are born.
+    load_v_step(SV(), I0(), va);
+    load_v_step(SV(), I1(), va);
+    load_v_step(SV(), I2(), va);
     __builtin_amdgcn_sched_barrier(0);
-    if (do_qk) {
-      qk(ka);
-    } else {
-      retire(sc[0][0], sc[0][1], sc[1][0], sc[1][1]);
-    }
+    pv_step(I0(), va);
+    __builtin_amdgcn_sched_barrier(0);
+    load_v_step(SV(), I3(), va);
+    __builtin_amdgcn_sched_barrier(0);
+    pv_step(I1(), va);
+    __builtin_amdgcn_sched_barrier(0);
+    load_k_step(SK(), I0(), ka);
+    load_k_step(SK(), I1(), ka);
+    __builtin_amdgcn_sched_barrier(0);
+    pv_step(I2(), va);
+    __builtin_amdgcn_sched_barrier(0);
+    load_k_step(SK(), I2(), ka);
+    load_k_step(SK(), I3(), ka);
+    __builtin_amdgcn_sched_barrier(0);
+    pv_step(I3(), va);
+    __builtin_amdgcn_sched_barrier(0);
+    qk_smajor(ka);
     __builtin_amdgcn_s_setprio(0);
   };
-  // Vector phase of tile t; both branches define pk.
+  // Vector phase of tile t: the weights of tile t, or zero weights for a
+  // phase before this wave's first tile or past its last.
   auto vphase = [&](int t) __attribute__((always_inline)) {
     if (t >= 0 && t < wave_tiles) {
       softmax(t);
     } else {
-      retire_pk(pk[0]);
-      retire_pk(pk[1]);
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) pk[qb][i] = 0u;
     }
   };
   using J0 = std::integral_constant<int, 0>;
@@ -506,7 +525,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_pair_kernel(FwdArgs
     fill_k(J1(), 1);
     fill_k(J2(), 2);
     fill_v(J0(), 0);
-    __builtin_amdgcn_s_waitcnt(0x0F70 | 2);
+    // The first MFMA phases of the two waves of a pair (p = 0, 1) read V
+    // slots 2 and 3 with zero weights: zero them, since 0 * NaN of stale LDS
+    // contents would not be zero.
+    g_v2[tid] = make_uint4(0, 0, 0, 0);
+    g_v3[tid] = make_uint4(0, 0, 0, 0);
+    __builtin_amdgcn_s_waitcnt(0x0070 | 2);  // vmcnt(2), lgkmcnt(0)
     barrier_lds();
     // Even-tile waves run MFMA phases at even p, odd-tile waves at odd p;
     // both run the same number of phases (and barriers).
@@ -514,18 +538,18 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_pair_kernel(FwdArgs
     if (par == 0) {
 #pragma nounroll
       for (int p = 0; p < n_phases; p += 4) {
-        fills(J0(), p);     mphase(J0(), p - 2, p); sync();
+        fills(J0(), p);     mphase(J0()); sync();
         fills(J1(), p + 1); vphase(p);              sync();
-        fills(J2(), p + 2); mphase(J2(), p, p + 2); sync();
+        fills(J2(), p + 2); mphase(J2()); sync();
         fills(J3(), p + 3); vphase(p + 2);          sync();
       }
     } else {
 #pragma nounroll
       for (int p = 0; p < n_phases; p += 4) {
         fills(J0(), p);     vphase(p - 1);              sync();
-        fills(J1(), p + 1); mphase(J1(), p - 1, p + 1); sync();
+        fills(J1(), p + 1); mphase(J1()); sync();
         fills(J2(), p + 2); vphase(p + 1);              sync();
-        fills(J3(), p + 3); mphase(J3(), p + 1, p + 3); sync();
+        fills(J3(), p + 3); mphase(J3()); sync();
       }
     }
     __builtin_amdgcn_s_waitcnt(0x0F70 | 0);  // no fill may land in the merge area
@@ -540,6 +564,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_pair_kernel(FwdArgs
     constexpr int VG = decltype(vg_tag)::value;
     return reinterpret_cast<float4*>(mslot<VG / 2>()) + ((VG & 1) * 4 + rg) * 64 + lane;
   };
+  // Full row sums in the row layout: lane (ln, hh) takes query ln's sum from
+  // lane ln % 16, register ln / 16.
+  float l[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const float v0 = __int_as_float(__builtin_amdgcn_ds_bpermute((lane & 15) * 4, __float_as_int(ls[qb][0])));
+    const float v1 = __int_as_float(__builtin_amdgcn_ds_bpermute((lane & 15) * 4, __float_as_int(ls[qb][1])));
+    l[qb] = (ln < 16) ? v0 : v1;
+  }
   if (par == 1) {
     static_for<16>([&](auto vg_tag) {
       constexpr int VG = decltype(vg_tag)::value;
@@ -562,7 +595,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_pair_kernel(FwdArgs
     const float M = fmaxf(mc[qb], lm.y);
     fa[qb] = __builtin_amdgcn_exp2f(mc[qb] - M);
     fb[qb] = __builtin_amdgcn_exp2f(lm.y - M);
-    const float l_row = half_swap_sum(fa[qb] * l[qb] + fb[qb] * lm.x);
+    const float l_row = fa[qb] * l[qb] + fb[qb] * lm.x;
     const int qi = qw0 + 32 * qb + ln;
     live[qb] = qi < q_len && l_row > 0.f;
     inv[qb] = live[qb] ? 1.f / l_row : 0.f;
