@@ -12,7 +12,8 @@ purpose and does no blocking, fusion or reordering beyond what the definition
 states.  Page citations name the page title and its section:
 
 * "[논문 리뷰]Attention Is All You Need" (kimjiil.github.io), §3.2.1 Eq. for
-  Attention(Q,K,V); §3.2.3 "Attention이 쓰이는 3곳" (masking sets illegal
+  Attention(Q,K,V); §3.2.2 multi-head attention (per-head projections W_i,
+  Concat(head_1..head_h) W^O); §3.2.3 "Attention이 쓰이는 3곳" (masking sets illegal
   logits to -inf before softmax, weight exactly 0); §3.5 Positional Encoding;
   §3.7 KV cache note.
 * "Attention Is All You Need를 지금 다시 읽는 법" (eightmm.github.io), the
@@ -232,6 +233,59 @@ def cache_append(Kcache, Vcache, Knew, Vnew, kv_lens):
                 Kc[b, :, row] = Kn[b, :, r]
                 Vc[b, :, row] = Vn[b, :, r]
     return Kc, Vc
+
+
+def head_projection(X, W, h: int):
+    """Multi-head input projections, split into heads (kimjiil page §3.2.2:
+    head_i = Attention(Q W_i^Q, K W_i^K, V W_i^V), W_i of shape d_model x d_k
+    with d_k = d_model / h; "Attention Is All You Need를 지금 다시 읽는 법",
+    multi-head section).
+
+    X: [B, n, d_model].  W: [n_out * d_model, d_model], one block of d_model
+    rows per projection (Q, K, V, or any subset in that order), each row one
+    output feature -- a projection is Y = X W^T, so block j's rows 64 i ..
+    64 i + 63 are head i's W_i (transposed).  Returns a list of n_out arrays
+    [B, h, n, d_model / h] in fp64: output head i, position t, dimension c
+    is sum_k X[b, t, k] W[j * d_model + i * d_k + c, k].
+    """
+    X = _f64(X)
+    W = _f64(W)
+    B, n, d_model = X.shape
+    d_k = d_model // h
+    n_out = W.shape[0] // d_model
+    Y = X @ W.T  # [B, n, n_out * d_model]
+    outs = []
+    for j in range(n_out):
+        Yj = Y[:, :, j * d_model:(j + 1) * d_model].reshape(B, n, h, d_k)
+        outs.append(np.ascontiguousarray(Yj.transpose(0, 2, 1, 3)))
+    return outs
+
+
+def output_projection(O, Wo):
+    """MultiHead = Concat(head_1, ..., head_h) W^O (kimjiil page §3.2.2):
+    O [B, h, n, d_k] is concatenated along the feature axis (head i fills
+    features i d_k .. (i + 1) d_k - 1) and multiplied by Wo^T, Wo being
+    [d_model, h d_k] with one row per output feature.  Returns [B, n, d_model]
+    in fp64."""
+    O = _f64(O)
+    Wo = _f64(Wo)
+    B, h, n, d_k = O.shape
+    concat = O.transpose(0, 2, 1, 3).reshape(B, n, h * d_k)
+    return concat @ Wo.T
+
+
+def multi_head_attention(Xq, Xkv, Wq, Wkv, Wo, h: int, mask_kind: int = MASK_NONE, q_lens=None,
+                         kv_lens=None, scale: float | None = None):
+    """The pages' multi-head attention sub-layer: queries projected from Xq,
+    keys and values from Xkv (the same tensor for self-attention, the encoder
+    output for encoder-decoder attention, kimjiil page §3.2.3 table),
+    scaled dot-product attention per head with the given mask, then the
+    output projection.  Wq [d_model, d_model], Wkv [2 d_model, d_model] (K
+    block then V block), Wo [d_model, d_model].  Returns [B, n_q, d_model]."""
+    (Q,) = head_projection(Xq, Wq, h)
+    K, V = head_projection(Xkv, Wkv, h)
+    O = attention(Q, K, V, mask_kind=mask_kind, q_lens=q_lens, kv_lens=kv_lens, scale=scale)
+    return output_projection(O, Wo)
 
 
 def sinusoidal_pe(pos: int, d_model: int) -> np.ndarray:

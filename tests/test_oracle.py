@@ -382,6 +382,66 @@ def pin_cross_attention_decode(orc):
             assert np.allclose(out[b, h, 0], (w / w.sum()) @ Ve[b, h, :src[b]], atol=1e-13)
 
 
+def pin_multi_head_vs_torch(orc):
+    """kimjiil page §3.2.2 multi-head attention, end to end (input
+    projections split into h heads of d_k = d_model / h, attention per head,
+    concatenation, output projection) against torch's own implementation of
+    the same sub-layer (torch.nn.functional.multi_head_attention_forward,
+    fp64, no biases), for self-attention with key padding, causal
+    self-attention, and cross attention with different query and key
+    lengths."""
+    rng = np.random.default_rng(77)
+    B, h, d_k = 2, 4, 4
+    d = h * d_k
+    Wq = rng.standard_normal((d, d)) / math.sqrt(d)
+    Wkv = rng.standard_normal((2 * d, d)) / math.sqrt(d)
+    Wo = rng.standard_normal((d, d)) / math.sqrt(d)
+    in_w = torch.from_numpy(np.concatenate([Wq, Wkv]))
+    for case in ("self_kpad", "causal", "cross"):
+        n_q, n_k = (5, 7) if case == "cross" else (6, 6)
+        Xq = rng.standard_normal((B, n_q, d))
+        Xkv = Xq if case != "cross" else rng.standard_normal((B, n_k, d))
+        kv_lens = np.array([n_k, 3]) if case != "causal" else None
+        mask = {"self_kpad": orc.MASK_KEY_PADDING, "causal": orc.MASK_CAUSAL,
+                "cross": orc.MASK_KEY_PADDING}[case]
+        got = orc.multi_head_attention(Xq, Xkv, Wq, Wkv, Wo, h, mask_kind=mask, kv_lens=kv_lens)
+        kpm = None
+        if kv_lens is not None:
+            kpm = torch.from_numpy(np.arange(n_k)[None, :] >= kv_lens[:, None])
+        am = torch.triu(torch.ones(n_q, n_k, dtype=torch.bool), 1) if case == "causal" else None
+        ref, _ = torch.nn.functional.multi_head_attention_forward(
+            torch.from_numpy(Xq).transpose(0, 1), torch.from_numpy(Xkv).transpose(0, 1),
+            torch.from_numpy(Xkv).transpose(0, 1), d, h, in_w, None, None, None, False, 0.0,
+            torch.from_numpy(Wo), None, training=False, key_padding_mask=kpm,
+            need_weights=False, attn_mask=am)
+        assert np.allclose(got, ref.transpose(0, 1).numpy(), atol=1e-12), case
+
+
+def pin_head_split_and_concat(orc):
+    """Head i of a projection uses rows i d_k .. (i + 1) d_k - 1 of its weight
+    block (brute force over every output element), and the concatenation is
+    the exact inverse of the split: projecting with the identity and
+    concatenating with the identity returns X."""
+    rng = np.random.default_rng(78)
+    B, n, h, d_k = 2, 3, 3, 2
+    d = h * d_k
+    X = rng.standard_normal((B, n, d))
+    W = rng.standard_normal((2 * d, d))
+    A, C = orc.head_projection(X, W, h)
+    for j, out in enumerate((A, C)):
+        for b in range(B):
+            for i in range(h):
+                for t in range(n):
+                    for c in range(d_k):
+                        ref = sum(X[b, t, k] * W[j * d + i * d_k + c, k] for k in range(d))
+                        assert abs(out[b, i, t, c] - ref) < 1e-12
+    (I,) = orc.head_projection(X, np.eye(d), h)
+    assert np.array_equal(orc.output_projection(I, np.eye(d)), X)
+    # one head with identity projections is plain attention (kimjiil page §3.2.2 with h = 1)
+    Y = orc.multi_head_attention(X, X, np.eye(d), np.vstack([np.eye(d), np.eye(d)]), np.eye(d), 1)
+    assert np.allclose(Y, orc.attention(X[:, None], X[:, None], X[:, None])[:, 0], atol=1e-13)
+
+
 def pin_kv_cache_size(orc):
     """sj-techlog page KV cache arithmetic: 2 x 6 x 128 x 512 scalars,
     3.0 MiB in fp32 and 1.5 MiB in fp16."""

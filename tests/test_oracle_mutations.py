@@ -22,6 +22,8 @@ _attention = orc.attention
 _decode = orc.decode
 _pe = orc.sinusoidal_pe
 _append = orc.cache_append
+_proj = orc.head_projection
+_oproj = orc.output_projection
 
 
 def m_causal_strict(i, n_k, kv_len, causal):
@@ -135,6 +137,32 @@ def m_append_k_only(Kc, Vc, Kn, Vn, kv_lens):
     return K2, np.array(Vc, copy=True)
 
 
+def m_heads_interleaved(X, W, h):
+    # head i takes every h-th feature instead of a contiguous block of d_k
+    X = np.asarray(X, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float64)
+    B, n, d = X.shape
+    d_k = d // h
+    Y = X @ W.T
+    outs = []
+    for j in range(W.shape[0] // d):
+        Yj = Y[:, :, j * d:(j + 1) * d].reshape(B, n, d_k, h).transpose(0, 3, 1, 2)
+        outs.append(np.ascontiguousarray(Yj))
+    return outs
+
+
+def m_proj_untransposed(X, W, h):
+    # X W instead of X W^T (square blocks only)
+    W = np.asarray(W, dtype=np.float64)
+    d = np.shape(X)[2]
+    Wt = np.vstack([W[j * d:(j + 1) * d].T for j in range(W.shape[0] // d)])
+    return _proj(X, Wt, h)
+
+
+def m_concat_heads_reversed(O, Wo):
+    return _oproj(np.asarray(O)[:, ::-1], Wo)
+
+
 def m_pe_swapped(pos, d_model):
     out = np.zeros(d_model)
     for dim in range(d_model):
@@ -167,6 +195,9 @@ MUTANTS = {
     "append_one_row_late": ("cache_append", m_append_one_row_late),
     "append_block_reversed": ("cache_append", m_append_reversed),
     "append_drops_v": ("cache_append", m_append_k_only),
+    "heads_interleaved": ("head_projection", m_heads_interleaved),
+    "projection_untransposed": ("head_projection", m_proj_untransposed),
+    "concat_heads_reversed": ("output_projection", m_concat_heads_reversed),
     "pe_sin_cos_swapped": ("sinusoidal_pe", m_pe_swapped),
     "pe_exponent_i": ("sinusoidal_pe", m_pe_exponent),
 }
