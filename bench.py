@@ -13,6 +13,11 @@ decode HBM GB/s"):
                 with the values the cache holds there, so the decode's
                 inputs do not change)
   kv_decode     bf16 KV-cache decode, B64 h16, cache 4096, L in [1, 4096]
+  mha_proj      the multi-head projections of decoder_big's layer (d_model
+                1024, h 16, B32): self-attention Q/K/V and output, cross
+                attention Q (128 decoder rows), K/V (160 encoder rows) and
+                output; seeded N(0, 1/d_model) weights.  Reported beside the
+                attention figures, not in `value`.
 Inputs are the seeded synthetic tensors of workloads.py, resident in HBM
 before timing starts.  Each leg is bracketed by HIP events on the stream
 the library launches on (torch's current stream); the step is bracketed by
@@ -50,7 +55,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 # Sources of every kernel the bench launches: the traffic figures are reported
 # only while these are unchanged since the counters were taken.
 KERNEL_SOURCES = ["attn_fwd_bf16_pair.hip", "attn_fwd_bf16_short.hip", "attn_fwd_bf16.hip",
-                  "attn_decode.hip", "attn_cache.hip", "common.h"]
+                  "attn_decode.hip", "attn_cache.hip", "attn_proj.hip", "common.h"]
 
 
 def kernel_source_hash() -> str:
@@ -63,8 +68,9 @@ def kernel_source_hash() -> str:
 
 # ------------------------------------------------------------------ legs
 class Leg:
-    def __init__(self, name, calls=None, decode=None, append=None):
+    def __init__(self, name, calls=None, decode=None, append=None, proj=None):
         self.name = name
+        self.proj = proj           # projection calls (list of dicts of CPU tensors)
         self.calls = calls or []   # forward calls (dicts of CPU tensors)
         self.decode = decode       # decode call (dict of CPU tensors)
         self.append = append       # cache-append call (dict of CPU tensors)
@@ -92,6 +98,17 @@ class Leg:
             L = int(d["kv_lens"].sum())
             self.flops += 4 * D * L * H
             self.bytes += 2 * L * H * D * el + 2 * B * H * D * el + 4 * B
+        for pc in self.proj or []:
+            if pc["kind"] == "head":
+                B, n, d_model = pc["X"].shape
+                n_out = pc["W"].shape[0] // d_model
+                self.flops += 2 * B * n * n_out * d_model * d_model
+                self.bytes += 2 * (B * n * d_model * (1 + n_out) + n_out * d_model * d_model)
+            else:
+                B, h, n, _ = pc["O"].shape
+                d_model = h * D
+                self.flops += 2 * B * n * d_model * d_model
+                self.bytes += 2 * (2 * B * n * d_model + d_model * d_model)
         if self.append is not None:
             a = self.append
             B, H, n_new, _ = a["Knew"].shape
@@ -112,6 +129,19 @@ def make_legs():
               "kv_lens": kd["kv_lens"]}
     legs.append(Leg("kv_append", append=append))
     legs.append(Leg("kv_decode", decode=kd))
+    g = workloads.generator(1100)
+    B, h, d_model, n_t, n_s = 32, 16, 1024, 128, 160
+    wts = lambda rows: (torch.randn((rows, d_model), generator=g) / d_model ** 0.5).to(torch.bfloat16)
+    x_dec = workloads.randn(g, (B, n_t, d_model), torch.bfloat16)
+    x_enc = workloads.randn(g, (B, n_s, d_model), torch.bfloat16)
+    o_self = workloads.randn(g, (B, h, n_t, D), torch.bfloat16)
+    o_cross = workloads.randn(g, (B, h, n_t, D), torch.bfloat16)
+    proj = [{"kind": "head", "X": x_dec, "W": wts(3 * d_model), "h": h},   # self Q, K, V
+            {"kind": "out", "O": o_self, "W": wts(d_model)},               # self output
+            {"kind": "head", "X": x_dec, "W": wts(d_model), "h": h},       # cross Q
+            {"kind": "head", "X": x_enc, "W": wts(2 * d_model), "h": h},   # cross K, V
+            {"kind": "out", "O": o_cross, "W": wts(d_model)}]              # cross output
+    legs.append(Leg("mha_proj", proj=proj))
     for leg in legs:
         leg.count()
     return legs
@@ -125,6 +155,17 @@ def to_device(legs):
             dc = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in c.items()}
             dc["O"] = torch.empty_like(dc["Q"])
             leg.dev_calls.append(dc)
+        leg.dev_proj = []
+        for pc in leg.proj or []:
+            dp = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in pc.items()}
+            if pc["kind"] == "head":
+                B, n, d_model = pc["X"].shape
+                dp["outs"] = [torch.empty((B, pc["h"], n, D), dtype=torch.bfloat16, device="cuda")
+                              for _ in range(pc["W"].shape[0] // d_model)]
+            else:
+                B, h, n, _ = pc["O"].shape
+                dp["Y"] = torch.empty((B, n, h * D), dtype=torch.bfloat16, device="cuda")
+            leg.dev_proj.append(dp)
         leg.dev_append = None
         if leg.append is not None:
             leg.dev_append = {k: v.cuda() for k, v in leg.append.items()}
@@ -142,6 +183,11 @@ def to_device(legs):
 
 def run_leg(leg, caches=None):
     import head_attention_amd as ha
+    for dp in leg.dev_proj:
+        if dp["kind"] == "head":
+            ha.head_projection(dp["X"], dp["W"], dp["h"], dp["outs"])
+        else:
+            ha.output_projection(dp["O"], dp["W"], dp["Y"])
     a = leg.dev_append
     if a is not None:
         ha.cache_append(a["Knew"], a["Vnew"], caches["Kcache"], caches["Vcache"], a["kv_lens"])
@@ -239,8 +285,8 @@ def _short_kernel(name: str) -> str:
     """attn_fwd_bf16[_pair|_short]_kernel<causal, ...> -> ..._kernel<true|false>;
     other kernels of the library by their plain name."""
     import re
-    m = re.search(r"(attn_fwd_bf16(?:_pair|_short)?_kernel)<(true|false)", name) or \
-        re.search(r"(attn_fwd_bf16(?:_pair|_short)?_kernel)ILb(\d)", name)
+    m = re.search(r"(attn_fwd_bf16(?:_pair|_short)?_kernel|proj_gemm_kernel)<(true|false)", name) or \
+        re.search(r"(attn_fwd_bf16(?:_pair|_short)?_kernel|proj_gemm_kernel)ILb(\d)", name)
     if m:
         causal = m.group(2) in ("true", "1")
         return f"{m.group(1)}<{'true' if causal else 'false'}>"
@@ -257,6 +303,10 @@ LEG_GRIDS = {("attn_fwd_bf16_short_kernel<false>", 65536): "encoder_base",
              ("attn_fwd_bf16_short_kernel<true>", 131072): "decoder_big (causal self)",
              ("attn_fwd_bf16_short_kernel<false>", 131072): "decoder_big (cross)",
              ("cache_append_kernel", 8192): "kv_append",
+             ("proj_gemm_kernel<true>", 196608): "mha_proj (self Q, K, V)",
+             ("proj_gemm_kernel<true>", 65536): "mha_proj (cross Q)",
+             ("proj_gemm_kernel<true>", 163840): "mha_proj (cross K, V)",
+             ("proj_gemm_kernel<false>", 65536): "mha_proj (self and cross output)",
              ("attn_fwd_bf16_pair_kernel<true>", 262144): "long_causal",
              ("decode_partial_kernel", 4194304): "kv_decode",
              ("decode_merge_kernel", 65536): "kv_decode"}
@@ -447,6 +497,14 @@ def main():
             "frac": round(lc_tflops / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
         },
+        "roofline_proj": {
+            "bound": "mfma",
+            "kernel": "proj_gemm_kernel on mha_proj (decoder_big layer projections)",
+            "achieved": round(legs[[l.name for l in legs].index("mha_proj")].flops
+                              / (leg_ms[[l.name for l in legs].index("mha_proj")] * 1e-3) / 1e12, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+        },
         "roofline_decode": {
             "bound": "hbm",
             "kernel": "decode_partial_kernel + decode_merge_kernel on kv_decode",
@@ -456,6 +514,7 @@ def main():
             "frac": round(kd_gbps / PEAK_HBM_GBPS, 4),
         },
     }
+    out["roofline_proj"]["frac"] = round(out["roofline_proj"]["achieved"] / PEAK_BF16_TFLOPS, 4)
     if args.copy_probe_mib:
         src = torch.ones(args.copy_probe_mib * 2 ** 18, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)

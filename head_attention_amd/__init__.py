@@ -20,6 +20,8 @@ from ._binding import (  # noqa: F401
     decode,
     decode_workspace_bytes,
     forward,
+    head_projection,
     lib,
+    output_projection,
     status_string,
 )

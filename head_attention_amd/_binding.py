@@ -65,6 +65,10 @@ def lib() -> ctypes.CDLL:
         L.attn_decode.restype = ctypes.c_int
         L.attn_cache_append.argtypes = [vp, vp, vp, vp, attn_layout, i32p, vp]
         L.attn_cache_append.restype = ctypes.c_int
+        L.attn_head_projection.argtypes = [vp, vp, attn_layout, ctypes.c_int32, vp, vp, vp, vp]
+        L.attn_head_projection.restype = ctypes.c_int
+        L.attn_output_projection.argtypes = [vp, vp, attn_layout, vp, vp]
+        L.attn_output_projection.restype = ctypes.c_int
         L.attn_decode_workspace_bytes.argtypes = [attn_layout]
         L.attn_decode_workspace_bytes.restype = ctypes.c_size_t
         L.attn_status_string.argtypes = [ctypes.c_int]
@@ -87,15 +91,15 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError(f"attention tensors must be bfloat16 or float32, got {t.dtype}")
 
 
-def _check_tensor(name: str, t: torch.Tensor, dtype) -> None:
+def _check_tensor(name: str, t: torch.Tensor, dtype, ndim: int = 4) -> None:
     # Cheap attribute reads only: this runs on every call, and at n = 128 a
     # call's Python time is comparable to the kernel's.
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if not t.is_cuda:
         raise ValueError(f"{name} must be on the GPU, got {t.device}")
-    if t.dim() != 4:
-        raise ValueError(f"{name} must be [B, h, n, d], got shape {tuple(t.shape)}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got shape {tuple(t.shape)}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if t.dtype != dtype:
@@ -220,3 +224,58 @@ def cache_append(Knew: torch.Tensor, Vnew: torch.Tensor, Kcache: torch.Tensor, V
                                  layout, _lens_ptr("kv_lens", kv_lens, B), _stream_handle(stream, Knew))
     if st != 0:
         raise AttnError(st, "attn_cache_append")
+
+
+def head_projection(X: torch.Tensor, W: torch.Tensor, h: int, outs=None, stream=None) -> list:
+    """attn_head_projection: the multi-head input projections X W_j^T, split
+    into heads.
+
+    X [B, n, d_model] bf16 (d_model = 64 h); W [n_out * d_model, d_model] bf16
+    (one block of d_model rows per projection, a linear layer's weight
+    layout).  Returns n_out tensors [B, h, n, 64] (or fills `outs`).
+    """
+    _check_tensor("X", X, torch.bfloat16, 3)
+    _check_tensor("W", W, torch.bfloat16, 2)
+    B, n, d_model = X.shape
+    if d_model != 64 * h or W.shape[1] != d_model or W.shape[0] % d_model != 0:
+        raise ValueError(f"X {tuple(X.shape)} / W {tuple(W.shape)} do not fit h = {h} heads of 64")
+    n_out = W.shape[0] // d_model
+    if outs is None:
+        outs = [torch.empty((B, h, n, 64), dtype=torch.bfloat16, device=X.device) for _ in range(n_out)]
+    if len(outs) != n_out:
+        raise ValueError(f"W holds {n_out} projections but {len(outs)} outputs were given")
+    for j, o in enumerate(outs):
+        _check_tensor(f"out{j}", o, torch.bfloat16)
+        if o.shape != (B, h, n, 64):
+            raise ValueError(f"out{j} must be [B, h, n, 64]")
+    ptrs = [o.data_ptr() for o in outs] + [None] * (3 - n_out)
+    st = lib().attn_head_projection(X.data_ptr(), W.data_ptr(), attn_layout(B, h, n, 0, 64, ATTN_BF16), n_out,
+                                    ptrs[0], ptrs[1], ptrs[2], _stream_handle(stream, X))
+    if st != 0:
+        raise AttnError(st, "attn_head_projection")
+    return outs
+
+
+def output_projection(O: torch.Tensor, Wo: torch.Tensor, out: torch.Tensor | None = None,
+                      stream=None) -> torch.Tensor:
+    """attn_output_projection: Concat(heads of O) Wo^T.
+
+    O [B, h, n, 64] bf16 (the attention output); Wo [d_model, d_model] bf16.
+    Returns Y [B, n, d_model].
+    """
+    _check_tensor("O", O, torch.bfloat16)
+    _check_tensor("Wo", Wo, torch.bfloat16, 2)
+    B, h, n, d = O.shape
+    d_model = h * d
+    if d != 64 or Wo.shape != (d_model, d_model):
+        raise ValueError(f"O {tuple(O.shape)} / Wo {tuple(Wo.shape)} do not fit")
+    if out is None:
+        out = torch.empty((B, n, d_model), dtype=torch.bfloat16, device=O.device)
+    _check_tensor("out", out, torch.bfloat16, 3)
+    if out.shape != (B, n, d_model):
+        raise ValueError("out must be [B, n, d_model]")
+    st = lib().attn_output_projection(O.data_ptr(), Wo.data_ptr(), attn_layout(B, h, n, 0, 64, ATTN_BF16),
+                                      out.data_ptr(), _stream_handle(stream, O))
+    if st != 0:
+        raise AttnError(st, "attn_output_projection")
+    return out

@@ -183,6 +183,81 @@ attn_status attn_cache_append(const void* Knew, const void* Vnew, void* Kcache, 
   return ATTN_OK;
 }
 
+attn_status attn_head_projection(const void* X, const void* W, attn_layout L, int32_t n_out,
+                                 void* out0, void* out1, void* out2, void* stream) {
+  attn_status st = check_layout(L);
+  if (st != ATTN_OK) return st;
+  if (L.dtype != ATTN_BF16) return ATTN_ERR_BAD_DTYPE;
+  if (n_out < 1 || n_out > 3) return ATTN_ERR_BAD_SHAPE;
+  if (L.B == 0 || L.n_q == 0 || L.h == 0) return ATTN_OK;  // nothing to write
+  void* outs[3] = {out0, out1, out2};
+  if (!X || !W) return ATTN_ERR_NULL_POINTER;
+  for (int j = 0; j < n_out; ++j) {
+    if (!outs[j]) return ATTN_ERR_NULL_POINTER;
+    if (outs[j] == X || outs[j] == W) return ATTN_ERR_BAD_SHAPE;
+    for (int k = 0; k < j; ++k)
+      if (outs[k] == outs[j]) return ATTN_ERR_BAD_SHAPE;
+  }
+  const int64_t d_model = (int64_t)L.h * kHeadDim;
+  const int64_t M = (int64_t)L.B * L.n_q;
+  const int64_t x_bytes = M * d_model * 2, w_bytes = (int64_t)n_out * d_model * d_model * 2;
+  if (x_bytes >= (1LL << 31) || w_bytes >= (1LL << 31)) return ATTN_ERR_BAD_SHAPE;
+  const int64_t blocks = ((n_out * d_model + 127) / 128) * ((M + 127) / 128);
+  if (blocks > kMaxGrid) return ATTN_ERR_BAD_SHAPE;
+  ProjArgs a;
+  a.W = W;
+  a.A = X;
+  a.out[0] = out0;
+  a.out[1] = n_out > 1 ? out1 : nullptr;
+  a.out[2] = n_out > 2 ? out2 : nullptr;
+  a.M = (int)M;
+  a.N = (int)(n_out * d_model);
+  a.K = (int)d_model;
+  a.H = L.h;
+  a.n_seq = L.n_q;
+  a.w_bytes = (uint32_t)w_bytes;
+  a.a_bytes = (uint32_t)x_bytes;
+  const hipError_t e = launch_proj(a, true, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    g_last_hip = e;
+    return ATTN_ERR_HIP;
+  }
+  return ATTN_OK;
+}
+
+attn_status attn_output_projection(const void* O, const void* Wo, attn_layout L, void* Y, void* stream) {
+  attn_status st = check_layout(L);
+  if (st != ATTN_OK) return st;
+  if (L.dtype != ATTN_BF16) return ATTN_ERR_BAD_DTYPE;
+  if (L.B == 0 || L.n_q == 0 || L.h == 0) return ATTN_OK;
+  if (!O || !Wo || !Y) return ATTN_ERR_NULL_POINTER;
+  if (Y == O || Y == Wo) return ATTN_ERR_BAD_SHAPE;
+  const int64_t d_model = (int64_t)L.h * kHeadDim;
+  const int64_t M = (int64_t)L.B * L.n_q;
+  const int64_t o_bytes = M * d_model * 2, w_bytes = d_model * d_model * 2;
+  if (o_bytes >= (1LL << 31) || w_bytes >= (1LL << 31)) return ATTN_ERR_BAD_SHAPE;
+  const int64_t blocks = ((d_model + 127) / 128) * ((M + 127) / 128);
+  if (blocks > kMaxGrid) return ATTN_ERR_BAD_SHAPE;
+  ProjArgs a;
+  a.W = Wo;
+  a.A = O;
+  a.out[0] = Y;
+  a.out[1] = a.out[2] = nullptr;
+  a.M = (int)M;
+  a.N = (int)d_model;
+  a.K = (int)d_model;
+  a.H = L.h;
+  a.n_seq = L.n_q;
+  a.w_bytes = (uint32_t)w_bytes;
+  a.a_bytes = (uint32_t)o_bytes;
+  const hipError_t e = launch_proj(a, false, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    g_last_hip = e;
+    return ATTN_ERR_HIP;
+  }
+  return ATTN_OK;
+}
+
 size_t attn_decode_workspace_bytes(attn_layout L) {
   if (check_layout(L) != ATTN_OK || L.n_q != 1) return 0;
   return (size_t)L.B * L.h * decode_splits(L.n_k) * kPartialStride * sizeof(float);

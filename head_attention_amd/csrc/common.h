@@ -52,6 +52,20 @@ struct AppendArgs {
 };
 hipError_t launch_cache_append(const AppendArgs& a, hipStream_t s);
 
+// One projection GEMM: C^T = W A^T, W [N, K] and A [M, K] bf16 (A given as
+// X [M, K] row-major, or as the heads of O [B, H, n_seq, 64] for the output
+// projection); the output is split into heads ([B, H, n_seq, 64] per block of
+// H * 64 features) or written row-major [M, N].
+struct ProjArgs {
+  const void* W;
+  const void* A;
+  void* out[3];
+  int M, N, K;   // M = B * n_seq tokens, N output features, K = H * 64
+  int H, n_seq;
+  uint32_t w_bytes, a_bytes;
+};
+hipError_t launch_proj(const ProjArgs& a, bool head_out, hipStream_t s);
+
 // Decode: keys per split (one workgroup of 4 waves x 64 keys).
 constexpr int kDecodeWaves = 4;
 constexpr int kDecodeChunk = 64 * kDecodeWaves;

@@ -178,6 +178,51 @@ attn_status attn_cache_append(const void* Knew, const void* Vnew, void* Kcache,
                               void* Vcache, attn_layout cache_layout,
                               const int32_t* kv_lens, void* stream);
 
+/*
+ * attn_head_projection -- the multi-head input projections, written straight
+ * into the per-head layout the attention calls read ("[논문 리뷰]Attention Is
+ * All You Need", §3.2.2: head_i = Attention(Q W_i^Q, K W_i^K, V W_i^V) with
+ * W_i of shape d_model x d_k, d_k = d_model / h = 64).
+ *
+ *   X       [B, n, d_model] bf16, device, read (d_model = 64 h)
+ *   W       [n_out * d_model, d_model] bf16, device, read: n_out blocks of
+ *           d_model rows, one row per output feature (a projection is
+ *           Y = X W^T, the convention of a linear layer's weight), in the
+ *           order the outputs are given; rows 64 i .. 64 i + 63 of a block
+ *           are head i's projection
+ *   layout  B, h, n_q = n (rows of X per batch entry), n_k ignored, d = 64,
+ *           dtype = ATTN_BF16 (the only type of this entry point)
+ *   n_out   1, 2 or 3: how many projections (Q; K and V; or Q, K and V)
+ *   out0..2 [B, h, n, 64] bf16, device, written: out_j[b, i, t, c] =
+ *           sum_k X[b, t, k] W[j d_model + 64 i + c, k]; unused ones NULL
+ *   stream  hipStream_t or NULL.
+ * fp32 accumulation, outputs rounded to bf16 (nearest even).  Self-attention
+ * projects Q, K, V of one X (n_out = 3); encoder-decoder attention projects
+ * Q from the decoder (n_out = 1) and K, V from the encoder output (n_out =
+ * 2).  No output may alias X or W.  Every tensor must be under 2 GiB.
+ */
+attn_status attn_head_projection(const void* X, const void* W, attn_layout layout,
+                                 int32_t n_out, void* out0, void* out1, void* out2,
+                                 void* stream);
+
+/*
+ * attn_output_projection -- MultiHead = Concat(head_1, ..., head_h) W^O
+ * (kimjiil page §3.2.2), reading the attention output O in its per-head
+ * layout (no concatenation copy).
+ *
+ *   O       [B, h, n, 64] bf16, device, read (the attn_forward output)
+ *   Wo      [d_model, d_model] bf16, device, read: one row per output
+ *           feature; input feature 64 i + c is dimension c of head i
+ *   layout  B, h, n_q = n, n_k ignored, d = 64, dtype = ATTN_BF16
+ *   Y       [B, n, d_model] bf16, device, written:
+ *           Y[b, t, f] = sum_{i, c} O[b, i, t, c] Wo[f, 64 i + c]
+ *   stream  hipStream_t or NULL.
+ * fp32 accumulation, Y rounded to bf16.  Y must not alias O or Wo.  Every
+ * tensor must be under 2 GiB.
+ */
+attn_status attn_output_projection(const void* O, const void* Wo, attn_layout layout, void* Y,
+                                   void* stream);
+
 /* Bytes of fp32 split partials attn_decode needs for this cache layout; 0 if
  * the layout is invalid.  Pure host arithmetic. */
 size_t attn_decode_workspace_bytes(attn_layout cache_layout);

@@ -29,7 +29,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("attn_forward", "attn_decode", "attn_cache_append", "attn_decode_workspace_bytes",
+    for n in ("attn_forward", "attn_decode", "attn_cache_append", "attn_head_projection",
+              "attn_output_projection", "attn_decode_workspace_bytes",
               "attn_status_string", "attn_last_hip_error"):
         assert n in names, names
 
@@ -139,6 +140,27 @@ def test_cache_append_validation():
     # nothing to append: OK without touching any pointer or the device
     assert app(attn_layout(0, 2, 1, 300, 64, BF16), kn=None, vn=None, kc=None, vc=None, kl=None) == OK
     assert app(attn_layout(4, 2, 0, 300, 64, F32), kn=None, vn=None, kc=None, vc=None, kl=None) == OK
+
+
+def test_projection_validation():
+    L = ha.lib()
+    lay_ = attn_layout(2, 8, 128, 0, 64, BF16)
+    hp = lambda lay, n_out=3, x=FAKE, w=FAKE + 16, o0=FAKE + 32, o1=FAKE + 48, o2=FAKE + 64: \
+        L.attn_head_projection(x, w, lay, n_out, o0, o1, o2, None)
+    assert hp(attn_layout(2, 8, 128, 0, 64, F32)) == DTYPE
+    assert hp(attn_layout(2, 8, 128, 0, 32, BF16)) == SHAPE
+    assert hp(lay_, n_out=0) == SHAPE and hp(lay_, n_out=4) == SHAPE
+    assert hp(lay_, x=None) == NULLP and hp(lay_, w=None) == NULLP
+    assert hp(lay_, o2=None) == NULLP
+    assert hp(lay_, o1=FAKE) == SHAPE          # output aliases X
+    assert hp(lay_, o2=FAKE + 32) == SHAPE     # two outputs alias
+    assert hp(attn_layout(2, 8, 1 << 24, 0, 64, BF16)) == SHAPE  # X over 2 GiB
+    assert hp(attn_layout(0, 8, 128, 0, 64, BF16), x=None, w=None, o0=None, o1=None, o2=None) == OK
+    op = lambda lay, o=FAKE, w=FAKE + 16, y=FAKE + 32: L.attn_output_projection(o, w, lay, y, None)
+    assert op(attn_layout(2, 8, 128, 0, 64, F32)) == DTYPE
+    assert op(lay_, y=None) == NULLP and op(lay_, o=None) == NULLP and op(lay_, w=None) == NULLP
+    assert op(lay_, y=FAKE) == SHAPE
+    assert op(attn_layout(2, 8, 0, 0, 64, BF16), o=None, w=None, y=None) == OK
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
