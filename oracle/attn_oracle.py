@@ -208,6 +208,73 @@ def decode(q, Kcache, Vcache, kv_lens, scale: float | None = None, pairs=None):
     return O
 
 
+def row_logsumexp(Q, K, mask_kind: int = MASK_NONE, q_lens=None, kv_lens=None, scale: float | None = None):
+    """Per query row, log(sum_j exp(s_ij)) over the allowed keys (natural
+    log), the normaliser of the softmax of kimjiil page §3.2.1; -inf for a
+    row with no allowed key or a padded query row.  Returns [B, h, n_q]."""
+    Q = _f64(Q)
+    K = _f64(K)
+    B, H, n_q, d = Q.shape
+    n_k = K.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    causal = bool(mask_kind & MASK_CAUSAL)
+    out = np.full((B, H, n_q), -np.inf)
+    for b in range(B):
+        kv_len = n_k if not (mask_kind & MASK_KEY_PADDING) else int(kv_lens[b])
+        q_len = n_q if q_lens is None else int(q_lens[b])
+        for h in range(H):
+            for i in range(min(q_len, n_q)):
+                idx = np.flatnonzero(allowed_keys(i, n_k, kv_len, causal))
+                if idx.size:
+                    s = scale * (K[b, h][idx] @ Q[b, h, i])
+                    m = s.max()
+                    out[b, h, i] = m + math.log(np.exp(s - m).sum())
+    return out
+
+
+def attention_backward(Q, K, V, dO, mask_kind: int = MASK_NONE, q_lens=None, kv_lens=None,
+                       scale: float | None = None):
+    """Gradients of L through O = softmax(Q K^T * scale + M) V, given dO =
+    dL/dO (the training the pages describe back-propagates through this
+    sub-layer; kimjiil page §3.2.1 defines the map).  Row by row, with the
+    softmax weights w of row i over its allowed keys (the forward's plain
+    definition):
+        dV[j]  += w_ij dO_i
+        dp_ij   = dO_i . V_j
+        ds_ij   = w_ij (dp_ij - sum_k w_ik dp_ik)      (softmax Jacobian)
+        dQ_i   += scale ds_ij K_j
+        dK[j]  += scale ds_ij Q_i
+    Excluded keys get no gradient; padded query rows (i >= q_len) contribute
+    nothing and get dQ = 0.  Returns (dQ, dK, dV) in fp64."""
+    Q, K, V, dO = (_f64(x) for x in (Q, K, V, dO))
+    B, H, n_q, d = Q.shape
+    n_k = K.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    causal = bool(mask_kind & MASK_CAUSAL)
+    dQ = np.zeros_like(Q)
+    dK = np.zeros_like(K)
+    dV = np.zeros_like(V)
+    for b in range(B):
+        kv_len = n_k if not (mask_kind & MASK_KEY_PADDING) else int(kv_lens[b])
+        q_len = n_q if q_lens is None else int(q_lens[b])
+        for h in range(H):
+            for i in range(min(q_len, n_q)):
+                idx = np.flatnonzero(allowed_keys(i, n_k, kv_len, causal))
+                if idx.size == 0:
+                    continue
+                s = scale * (K[b, h][idx] @ Q[b, h, i])
+                e = np.exp(s - s.max())
+                w = e / e.sum()
+                dp = V[b, h][idx] @ dO[b, h, i]
+                ds = w * (dp - (w * dp).sum())
+                dV[b, h][idx] += np.outer(w, dO[b, h, i])
+                dQ[b, h, i] += scale * (ds @ K[b, h][idx])
+                dK[b, h][idx] += scale * np.outer(ds, Q[b, h, i])
+    return dQ, dK, dV
+
+
 def cache_append(Kcache, Vcache, Knew, Vnew, kv_lens):
     """Append the K/V rows of new tokens to a decoder's caches (sj-techlog
     page, KV cache section: the cache holds the K, V of tokens 0..t-1 and a

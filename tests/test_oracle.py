@@ -442,6 +442,89 @@ def pin_head_split_and_concat(orc):
     assert np.allclose(Y, orc.attention(X[:, None], X[:, None], X[:, None])[:, 0], atol=1e-13)
 
 
+def pin_backward_vs_autograd(orc):
+    """The gradients of the attention map against torch autograd in fp64
+    (an independent differentiation of the forward definition), for every
+    mask kind, padded query rows and a row with no allowed key."""
+    rng = np.random.default_rng(91)
+    B, H, n, d = 3, 2, 7, 5
+    scale = 0.37
+    for mask in (0, 1, 2, 3):
+        Q, K, V, dO = (rng.standard_normal((B, H, n, d)) for _ in range(4))
+        kl = np.array([7, 3, 0]) if mask & 1 else None
+        ql = np.array([7, 5, 2])
+        dQ, dK, dV = orc.attention_backward(Q, K, V, dO, mask_kind=mask, q_lens=ql, kv_lens=kl, scale=scale)
+        tq, tk, tv = (torch.from_numpy(x.copy()).requires_grad_() for x in (Q, K, V))
+        allowed = np.zeros((B, 1, n, n), dtype=bool)
+        for b in range(B):
+            for i in range(n):
+                allowed[b, 0, i] = orc.allowed_keys(i, n, n if kl is None else kl[b], bool(mask & 2))
+        S = tq @ tk.transpose(-1, -2) * scale
+        S = S.masked_fill(~torch.from_numpy(allowed), float("-inf"))
+        P = torch.softmax(S, dim=-1).nan_to_num(0.0)   # rows with no key: weights 0
+        O = P @ tv
+        qmask = torch.from_numpy((np.arange(n)[None, :] < ql[:, None]).astype(np.float64))[:, None, :, None]
+        (O * torch.from_numpy(dO) * qmask).sum().backward()
+        for got, ref in ((dQ, tq.grad), (dK, tk.grad), (dV, tv.grad)):
+            assert np.allclose(got, ref.numpy(), atol=1e-12), mask
+
+
+def pin_backward_finite_differences(orc):
+    """Central differences of L = sum(O * dO) reproduce the analytic
+    gradients (a check of the formulas that uses only the forward)."""
+    rng = np.random.default_rng(92)
+    B, H, n, d = 1, 1, 5, 3
+    Q, K, V, dO = (rng.standard_normal((B, H, n, d)) for _ in range(4))
+    dQ, dK, dV = orc.attention_backward(Q, K, V, dO, mask_kind=orc.MASK_CAUSAL, scale=0.5)
+    L = lambda q, k, v: float((orc.attention(q, k, v, mask_kind=orc.MASK_CAUSAL, scale=0.5) * dO).sum())
+    eps = 1e-6
+    for X, G, which in ((Q, dQ, 0), (K, dK, 1), (V, dV, 2)):
+        for pos in ((0, 0, 0, 0), (0, 0, 2, 1), (0, 0, 4, 2)):
+            Xp, Xm = X.copy(), X.copy()
+            Xp[pos] += eps
+            Xm[pos] -= eps
+            args_p = [Q, K, V]
+            args_m = [Q, K, V]
+            args_p[which], args_m[which] = Xp, Xm
+            fd = (L(*args_p) - L(*args_m)) / (2 * eps)
+            assert abs(fd - G[pos]) < 1e-7, (which, pos)
+
+
+def pin_backward_shift_invariance(orc):
+    """Softmax ignores a constant added to every logit of a row, so adding
+    one vector to every key leaves O unchanged: the key gradients of each
+    (b, h) sum to zero.  Excluded keys and padded rows get exactly zero
+    gradient; the value gradients of a row's keys sum to that row's dO
+    (the weights sum to one)."""
+    rng = np.random.default_rng(93)
+    B, H, n, d = 2, 2, 6, 4
+    Q, K, V, dO = (rng.standard_normal((B, H, n, d)) for _ in range(4))
+    kl = np.array([6, 4])
+    dQ, dK, dV = orc.attention_backward(Q, K, V, dO, mask_kind=orc.MASK_KEY_PADDING, kv_lens=kl)
+    assert np.allclose(dK.sum(axis=2), 0.0, atol=1e-12)
+    assert np.all(dK[1, :, 4:] == 0) and np.all(dV[1, :, 4:] == 0)
+    assert np.allclose(dV.sum(axis=2), dO.sum(axis=2), atol=1e-12)
+    # a single allowed key: O = V_0 exactly, so dV_0 = dO and dQ = dK = 0
+    dQ1, dK1, dV1 = orc.attention_backward(Q, K, V, dO, mask_kind=orc.MASK_KEY_PADDING, kv_lens=np.array([1, 1]))
+    assert np.allclose(dV1[:, :, 0], dO.sum(axis=2)) and np.all(dQ1 == 0) and np.all(dK1 == 0)
+
+
+def pin_row_logsumexp(orc):
+    """The log-normaliser of each row: exp(s_ij - lse_i) are the softmax
+    weights (they sum to one), matching the weights of the forward."""
+    rng = np.random.default_rng(94)
+    Q, K, V = (rng.standard_normal((2, 2, 5, 3)) for _ in range(3))
+    kl = np.array([5, 2])
+    lse = orc.row_logsumexp(Q, K, mask_kind=3, kv_lens=kl, scale=0.7)
+    _, W = orc.attention(Q, K, V, mask_kind=3, kv_lens=kl, scale=0.7, return_weights=True)
+    for b in range(2):
+        for h in range(2):
+            for i in range(5):
+                s = 0.7 * (K[b, h] @ Q[b, h, i])
+                ok = orc.allowed_keys(i, 5, kl[b], True)
+                assert np.allclose(np.where(ok, np.exp(s - lse[b, h, i]), 0.0), W[b, h, i], atol=1e-14)
+
+
 def pin_kv_cache_size(orc):
     """sj-techlog page KV cache arithmetic: 2 x 6 x 128 x 512 scalars,
     3.0 MiB in fp32 and 1.5 MiB in fp16."""

@@ -24,6 +24,7 @@ _pe = orc.sinusoidal_pe
 _append = orc.cache_append
 _proj = orc.head_projection
 _oproj = orc.output_projection
+_bwd = orc.attention_backward
 
 
 def m_causal_strict(i, n_k, kv_len, causal):
@@ -163,6 +164,37 @@ def m_concat_heads_reversed(O, Wo):
     return _oproj(np.asarray(O)[:, ::-1], Wo)
 
 
+def _bwd_variant(kind):
+    def bwd(Q, K, V, dO, mask_kind=0, q_lens=None, kv_lens=None, scale=None):
+        Q, K, V, dO = (np.asarray(x, dtype=np.float64) for x in (Q, K, V, dO))
+        B, H, n_q, d = Q.shape
+        n_k = K.shape[2]
+        if scale is None:
+            scale = 1.0 / math.sqrt(d)
+        dQ, dK, dV = np.zeros_like(Q), np.zeros_like(K), np.zeros_like(V)
+        for b in range(B):
+            kv_len = n_k if not (mask_kind & 1) else int(kv_lens[b])
+            q_len = n_q if q_lens is None else int(q_lens[b])
+            for h in range(H):
+                for i in range(min(q_len, n_q)):
+                    idx = np.flatnonzero(orc.allowed_keys(i, n_k, kv_len, bool(mask_kind & 2)))
+                    if idx.size == 0:
+                        continue
+                    s = scale * (K[b, h][idx] @ Q[b, h, i])
+                    e = np.exp(s - s.max())
+                    w = e / e.sum()
+                    dp = V[b, h][idx] @ dO[b, h, i]
+                    ds = w * dp if kind == "no_rowsum" else w * (dp - (w * dp).sum())
+                    dV[b, h][idx] += np.outer(w, dO[b, h, i])
+                    dQ[b, h, i] += scale * (ds @ K[b, h][idx])
+                    kscale = 1.0 if kind == "dk_unscaled" else scale
+                    dK[b, h][idx] += kscale * np.outer(ds, Q[b, h, i])
+        if kind == "dv_transposed":
+            dV = dV[:, :, ::-1].copy()
+        return dQ, dK, dV
+    return bwd
+
+
 def m_pe_swapped(pos, d_model):
     out = np.zeros(d_model)
     for dim in range(d_model):
@@ -198,6 +230,9 @@ MUTANTS = {
     "heads_interleaved": ("head_projection", m_heads_interleaved),
     "projection_untransposed": ("head_projection", m_proj_untransposed),
     "concat_heads_reversed": ("output_projection", m_concat_heads_reversed),
+    "backward_drops_softmax_rowsum": ("attention_backward", _bwd_variant("no_rowsum")),
+    "backward_dk_unscaled": ("attention_backward", _bwd_variant("dk_unscaled")),
+    "backward_dv_keys_reversed": ("attention_backward", _bwd_variant("dv_transposed")),
     "pe_sin_cos_swapped": ("sinusoidal_pe", m_pe_swapped),
     "pe_exponent_i": ("sinusoidal_pe", m_pe_exponent),
 }
