@@ -13,6 +13,11 @@ decode HBM GB/s"):
                 with the values the cache holds there, so the decode's
                 inputs do not change)
   kv_decode     bf16 KV-cache decode, B64 h16, cache 4096, L in [1, 4096]
+  *_bwd         the backward pass (attn_backward, from the forward's saved
+                log-sum-exp) of encoder_base, decoder_big and long_causal
+                with a seeded N(0,1) dO; algorithmic flops 2.5x the
+                forward's (five products per allowed pair).  Reported beside
+                the forward figures, not in `value`.
   mha_proj      the multi-head projections of decoder_big's layer (d_model
                 1024, h 16, B32): self-attention Q/K/V and output, cross
                 attention Q (128 decoder rows), K/V (160 encoder rows) and
@@ -55,7 +60,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 # Sources of every kernel the bench launches: the traffic figures are reported
 # only while these are unchanged since the counters were taken.
 KERNEL_SOURCES = ["attn_fwd_bf16_pair.hip", "attn_fwd_bf16_short.hip", "attn_fwd_bf16.hip",
-                  "attn_decode.hip", "attn_cache.hip", "attn_proj.hip", "common.h"]
+                  "attn_decode.hip", "attn_cache.hip", "attn_proj.hip", "attn_bwd.hip", "common.h"]
 
 
 def kernel_source_hash() -> str:
@@ -68,8 +73,9 @@ def kernel_source_hash() -> str:
 
 # ------------------------------------------------------------------ legs
 class Leg:
-    def __init__(self, name, calls=None, decode=None, append=None, proj=None):
+    def __init__(self, name, calls=None, decode=None, append=None, proj=None, bwd=False):
         self.name = name
+        self.bwd = bwd             # time attn_backward of `calls` instead of the forward
         self.proj = proj           # projection calls (list of dicts of CPU tensors)
         self.calls = calls or []   # forward calls (dicts of CPU tensors)
         self.decode = decode       # decode call (dict of CPU tensors)
@@ -85,7 +91,7 @@ class Leg:
             n_k = c["K"].shape[2]
             el = c["Q"].element_size()
             pairs = workloads.allowed_pairs(c["mask"], n_q, n_k, B, c["q_lens"], c["kv_lens"])
-            self.flops += 4 * D * pairs * H
+            self.flops += (10 if self.bwd else 4) * D * pairs * H
             ql = n_q * B if c["q_lens"] is None else int(c["q_lens"].sum())
             kl = n_k * B if not (c["mask"] & 1) else int(c["kv_lens"].clamp(0, n_k).sum())
             row = H * D * el
@@ -121,6 +127,8 @@ def make_legs():
     legs = []
     for name in ("encoder_base", "decoder_big", "long_causal"):
         legs.append(Leg(name, calls=workloads.make(name)["calls"]))
+    for name in ("encoder_base", "decoder_big", "long_causal"):
+        legs.append(Leg(name + "_bwd", calls=workloads.make(name)["calls"], bwd=True))
     kd = workloads.make("kv_decode")
     rows = (kd["kv_lens"] - 1).long()
     bi = torch.arange(kd["q"].shape[0])
@@ -151,9 +159,18 @@ def to_device(legs):
     import head_attention_amd as ha
     for leg in legs:
         leg.dev_calls = []
-        for c in leg.calls:
+        for j, c in enumerate(leg.calls):
             dc = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in c.items()}
             dc["O"] = torch.empty_like(dc["Q"])
+            if leg.bwd:
+                B, H, n_q, _ = c["Q"].shape
+                g = workloads.generator(1200 + j)
+                dc["dO"] = workloads.randn(g, tuple(c["Q"].shape), torch.bfloat16).cuda()
+                dc["lse"] = torch.empty((B, H, n_q), dtype=torch.float32, device="cuda")
+                ha.forward(dc["Q"], dc["K"], dc["V"], mask_kind=dc["mask"], q_lens=dc["q_lens"],
+                           kv_lens=dc["kv_lens"], scale=dc["scale"], out=dc["O"], lse=dc["lse"])
+                dc["grads"] = (torch.empty_like(dc["Q"]), torch.empty_like(dc["K"]), torch.empty_like(dc["V"]))
+                dc["ws"] = torch.empty(B * H * n_q * 4, dtype=torch.uint8, device="cuda")
             leg.dev_calls.append(dc)
         leg.dev_proj = []
         for pc in leg.proj or []:
@@ -192,6 +209,11 @@ def run_leg(leg, caches=None):
     if a is not None:
         ha.cache_append(a["Knew"], a["Vnew"], caches["Kcache"], caches["Vcache"], a["kv_lens"])
     for c in leg.dev_calls:
+        if leg.bwd:
+            ha.backward(c["Q"], c["K"], c["V"], c["O"], c["dO"], c["lse"], mask_kind=c["mask"],
+                        q_lens=c["q_lens"], kv_lens=c["kv_lens"], scale=c["scale"], grads=c["grads"],
+                        workspace=c["ws"])
+            continue
         ha.forward(c["Q"], c["K"], c["V"], mask_kind=c["mask"], q_lens=c["q_lens"],
                    kv_lens=c["kv_lens"], scale=c["scale"], out=c["O"])
     d = leg.dev_decode
@@ -285,13 +307,13 @@ def _short_kernel(name: str) -> str:
     """attn_fwd_bf16[_pair|_short]_kernel<causal, ...> -> ..._kernel<true|false>;
     other kernels of the library by their plain name."""
     import re
-    m = re.search(r"(attn_fwd_bf16(?:_pair|_short)?_kernel|proj_gemm_kernel)<(true|false)", name) or \
-        re.search(r"(attn_fwd_bf16(?:_pair|_short)?_kernel|proj_gemm_kernel)ILb(\d)", name)
+    m = re.search(r"(attn_fwd_bf16(?:_pair|_short)?_kernel|proj_gemm_kernel|bwd_dkdv_kernel|bwd_dq_kernel)<(true|false)", name) or \
+        re.search(r"(attn_fwd_bf16(?:_pair|_short)?_kernel|proj_gemm_kernel|bwd_dkdv_kernel|bwd_dq_kernel)ILb(\d)", name)
     if m:
         causal = m.group(2) in ("true", "1")
         return f"{m.group(1)}<{'true' if causal else 'false'}>"
     for key in ("attn_fwd_f32_kernel", "decode_partial_kernel", "decode_merge_kernel",
-                "cache_append_kernel", "copyBuffer", "elementwise"):
+                "cache_append_kernel", "bwd_rowdot_kernel", "copyBuffer", "elementwise"):
         if key in name:
             return key
     return name[:60]
@@ -303,6 +325,9 @@ LEG_GRIDS = {("attn_fwd_bf16_short_kernel<false>", 65536): "encoder_base",
              ("attn_fwd_bf16_short_kernel<true>", 131072): "decoder_big (causal self)",
              ("attn_fwd_bf16_short_kernel<false>", 131072): "decoder_big (cross)",
              ("cache_append_kernel", 8192): "kv_append",
+             ("bwd_dkdv_kernel<true>", 16384): "long_causal_bwd",
+             ("bwd_dq_kernel<true>", 16384): "long_causal_bwd",
+             ("bwd_rowdot_kernel", 1048576): "long_causal_bwd",
              ("proj_gemm_kernel<true>", 196608): "mha_proj (self Q, K, V)",
              ("proj_gemm_kernel<true>", 65536): "mha_proj (cross Q)",
              ("proj_gemm_kernel<true>", 163840): "mha_proj (cross K, V)",
@@ -435,7 +460,7 @@ def main():
     leg_ms = [sum(ev[s][j][0].elapsed_time(ev[s][j][1]) for s in range(args.steps)) / args.steps
               for j in range(len(legs))]
     step_ms = sum(leg_ms)
-    fwd = [j for j, leg in enumerate(legs) if leg.dev_calls]
+    fwd = [j for j, leg in enumerate(legs) if leg.dev_calls and not leg.bwd]
     fwd_flops = sum(legs[j].flops for j in fwd)
     fwd_ms = sum(leg_ms[j] for j in fwd)
     value = fwd_flops / (fwd_ms * 1e-3) / 1e12
@@ -497,6 +522,14 @@ def main():
             "frac": round(lc_tflops / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
         },
+        "roofline_bwd": {
+            "bound": "mfma",
+            "kernel": "bwd_rowdot + bwd_dkdv + bwd_dq on long_causal_bwd (B1 h16 n8192)",
+            "achieved": round(legs[[l.name for l in legs].index("long_causal_bwd")].flops
+                              / (leg_ms[[l.name for l in legs].index("long_causal_bwd")] * 1e-3) / 1e12, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+        },
         "roofline_proj": {
             "bound": "mfma",
             "kernel": "proj_gemm_kernel on mha_proj (decoder_big layer projections)",
@@ -515,6 +548,7 @@ def main():
         },
     }
     out["roofline_proj"]["frac"] = round(out["roofline_proj"]["achieved"] / PEAK_BF16_TFLOPS, 4)
+    out["roofline_bwd"]["frac"] = round(out["roofline_bwd"]["achieved"] / PEAK_BF16_TFLOPS, 4)
     if args.copy_probe_mib:
         src = torch.ones(args.copy_probe_mib * 2 ** 18, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)

@@ -16,6 +16,7 @@ from ._binding import (  # noqa: F401
     LIB_PATH,
     AttnError,
     attn_layout,
+    backward,
     cache_append,
     decode,
     decode_workspace_bytes,

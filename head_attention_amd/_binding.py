@@ -69,6 +69,14 @@ def lib() -> ctypes.CDLL:
         L.attn_head_projection.restype = ctypes.c_int
         L.attn_output_projection.argtypes = [vp, vp, attn_layout, vp, vp]
         L.attn_output_projection.restype = ctypes.c_int
+        L.attn_forward_lse.argtypes = [vp, vp, vp, attn_layout, ctypes.c_int32, i32p, i32p,
+                                       ctypes.c_float, vp, vp, vp]
+        L.attn_forward_lse.restype = ctypes.c_int
+        L.attn_backward.argtypes = [vp, vp, vp, vp, vp, vp, attn_layout, ctypes.c_int32, i32p, i32p,
+                                    ctypes.c_float, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.attn_backward.restype = ctypes.c_int
+        L.attn_backward_workspace_bytes.argtypes = [attn_layout]
+        L.attn_backward_workspace_bytes.restype = ctypes.c_size_t
         L.attn_decode_workspace_bytes.argtypes = [attn_layout]
         L.attn_decode_workspace_bytes.restype = ctypes.c_size_t
         L.attn_status_string.argtypes = [ctypes.c_int]
@@ -131,12 +139,15 @@ def _stream_handle(stream, t: torch.Tensor) -> int | None:
 
 def forward(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, mask_kind: int = ATTN_MASK_NONE,
             q_lens: torch.Tensor | None = None, kv_lens: torch.Tensor | None = None,
-            scale: float | None = None, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+            scale: float | None = None, out: torch.Tensor | None = None, stream=None,
+            lse: torch.Tensor | None = None) -> torch.Tensor:
     """attn_forward: O = softmax(Q K^T * scale + M) V per (b, h), on the GPU.
 
     Q [B, h, n_q, 64]; K, V [B, h, n_k, 64]; all bf16 or all fp32, contiguous.
     q_lens / kv_lens: int32 GPU tensors [B] or None (see include/headattn.h).
     scale defaults to 1/sqrt(d).  Runs on torch's current stream (or `stream`).
+    lse: an fp32 GPU tensor [B, h, n_q] to receive each row's log-sum-exp
+    (attn_forward_lse), as attn_backward needs; None for the plain forward.
     """
     dt = Q.dtype
     for n, t in (("Q", Q), ("K", K), ("V", V)):
@@ -154,11 +165,21 @@ def forward(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, mask_kind: int = 
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     layout = attn_layout(B, H, n_q, n_k, d, _dtype_code(Q))
-    st = lib().attn_forward(Q.data_ptr(), K.data_ptr(), V.data_ptr(), layout, int(mask_kind),
-                            _lens_ptr("q_lens", q_lens, B), _lens_ptr("kv_lens", kv_lens, B),
-                            float(scale), out.data_ptr(), _stream_handle(stream, Q))
+    if lse is None:
+        st = lib().attn_forward(Q.data_ptr(), K.data_ptr(), V.data_ptr(), layout, int(mask_kind),
+                                _lens_ptr("q_lens", q_lens, B), _lens_ptr("kv_lens", kv_lens, B),
+                                float(scale), out.data_ptr(), _stream_handle(stream, Q))
+        if st != 0:
+            raise AttnError(st, "attn_forward")
+        return out
+    _check_tensor("lse", lse, torch.float32, 3)
+    if lse.shape != (B, H, n_q):
+        raise ValueError("lse must be [B, h, n_q]")
+    st = lib().attn_forward_lse(Q.data_ptr(), K.data_ptr(), V.data_ptr(), layout, int(mask_kind),
+                                _lens_ptr("q_lens", q_lens, B), _lens_ptr("kv_lens", kv_lens, B),
+                                float(scale), out.data_ptr(), lse.data_ptr(), _stream_handle(stream, Q))
     if st != 0:
-        raise AttnError(st, "attn_forward")
+        raise AttnError(st, "attn_forward_lse")
     return out
 
 
@@ -279,3 +300,45 @@ def output_projection(O: torch.Tensor, Wo: torch.Tensor, out: torch.Tensor | Non
     if st != 0:
         raise AttnError(st, "attn_output_projection")
     return out
+
+
+def backward(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, O: torch.Tensor, dO: torch.Tensor,
+             lse: torch.Tensor, mask_kind: int = ATTN_MASK_NONE, q_lens: torch.Tensor | None = None,
+             kv_lens: torch.Tensor | None = None, scale: float | None = None, grads=None,
+             workspace: torch.Tensor | None = None, stream=None):
+    """attn_backward: (dQ, dK, dV) of O = softmax(Q K^T * scale + M) V given dO.
+
+    Q, K, V, O, dO bf16 [B, h, n, 64] (the forward's tensors), lse the fp32
+    [B, h, n_q] log-sum-exp from forward(..., lse=...); the mask arguments and
+    scale must be those of the forward.  Returns three new tensors, or fills
+    `grads` = (dQ, dK, dV).
+    """
+    for n, t in (("Q", Q), ("K", K), ("V", V), ("O", O), ("dO", dO)):
+        _check_tensor(n, t, torch.bfloat16)
+    _check_tensor("lse", lse, torch.float32, 3)
+    B, H, n_q, d = Q.shape
+    n_k = K.shape[2]
+    if K.shape != (B, H, n_k, d) or V.shape != K.shape or O.shape != Q.shape or dO.shape != Q.shape \
+            or lse.shape != (B, H, n_q):
+        raise ValueError("shapes do not match the forward's")
+    if grads is None:
+        grads = (torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V))
+    dQ, dK, dV = grads
+    for n, t, ref in (("dQ", dQ, Q), ("dK", dK, K), ("dV", dV, V)):
+        _check_tensor(n, t, torch.bfloat16)
+        if t.shape != ref.shape:
+            raise ValueError(f"{n} must have the shape of its input")
+    layout = attn_layout(B, H, n_q, n_k, d, ATTN_BF16)
+    need = int(lib().attn_backward_workspace_bytes(layout))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=Q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = lib().attn_backward(Q.data_ptr(), K.data_ptr(), V.data_ptr(), O.data_ptr(), dO.data_ptr(),
+                             lse.data_ptr(), layout, int(mask_kind), _lens_ptr("q_lens", q_lens, B),
+                             _lens_ptr("kv_lens", kv_lens, B), float(scale), dQ.data_ptr(), dK.data_ptr(),
+                             dV.data_ptr(), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                             _stream_handle(stream, Q))
+    if st != 0:
+        raise AttnError(st, "attn_backward")
+    return dQ, dK, dV

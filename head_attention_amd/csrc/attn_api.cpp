@@ -4,6 +4,7 @@
 // Everything here is plain host code.  Validation happens before the first
 // HIP call, so a bad argument is reported without touching a device; a valid
 // call only enqueues work on the caller's stream.
+#include <algorithm>
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
@@ -87,9 +88,11 @@ const char* attn_status_string(attn_status status) {
 
 const char* attn_last_hip_error(void) { return hipGetErrorName(g_last_hip); }
 
-attn_status attn_forward(const void* Q, const void* K, const void* V, attn_layout layout,
+namespace {
+
+attn_status forward_impl(const void* Q, const void* K, const void* V, attn_layout layout,
                          int32_t mask_kind, const int32_t* q_lens, const int32_t* kv_lens,
-                         float scale, void* O, void* stream) {
+                         float scale, void* O, float* lse, void* stream) {
   attn_status st = check_layout(layout);
   if (st != ATTN_OK) return st;
   if (mask_kind & ~(ATTN_MASK_KEY_PADDING | ATTN_MASK_CAUSAL)) return ATTN_ERR_BAD_MASK;
@@ -104,6 +107,7 @@ attn_status attn_forward(const void* Q, const void* K, const void* V, attn_layou
   if (layout.n_k > 0 && (!K || !V)) return ATTN_ERR_NULL_POINTER;
   if (kpad && !kv_lens) return ATTN_ERR_NULL_POINTER;
   if (Q == O || K == O || V == O) return ATTN_ERR_BAD_SHAPE;  // inputs must not alias O
+  if (lse && (lse == O || lse == Q || lse == K || lse == V)) return ATTN_ERR_BAD_SHAPE;
 
   const int bm = layout.dtype == ATTN_BF16 ? 128 : 64;  // query rows per workgroup
   const int64_t blocks = (int64_t)((layout.n_q + bm - 1) / bm) * layout.h * layout.B;
@@ -128,6 +132,7 @@ attn_status attn_forward(const void* Q, const void* K, const void* V, attn_layou
   a.n_k = layout.n_k;
   a.scale = scale;
   a.causal = causal;
+  a.lse = lse;
   hipError_t e;
   if (layout.dtype == ATTN_F32) e = launch_fwd_f32(a, s);
   else if (layout.n_k <= kShortMaxKeys) e = launch_fwd_bf16_short(a, s);
@@ -138,6 +143,22 @@ attn_status attn_forward(const void* Q, const void* K, const void* V, attn_layou
     return ATTN_ERR_HIP;
   }
   return ATTN_OK;
+}
+
+}  // namespace
+
+attn_status attn_forward(const void* Q, const void* K, const void* V, attn_layout layout,
+                         int32_t mask_kind, const int32_t* q_lens, const int32_t* kv_lens,
+                         float scale, void* O, void* stream) {
+  return forward_impl(Q, K, V, layout, mask_kind, q_lens, kv_lens, scale, O, nullptr, stream);
+}
+
+attn_status attn_forward_lse(const void* Q, const void* K, const void* V, attn_layout layout,
+                             int32_t mask_kind, const int32_t* q_lens, const int32_t* kv_lens,
+                             float scale, void* O, float* LSE, void* stream) {
+  if (!LSE && layout.B > 0 && layout.h > 0 && layout.n_q > 0 && check_layout(layout) == ATTN_OK)
+    return ATTN_ERR_NULL_POINTER;
+  return forward_impl(Q, K, V, layout, mask_kind, q_lens, kv_lens, scale, O, LSE, stream);
 }
 
 attn_status attn_cache_append(const void* Knew, const void* Vnew, void* Kcache, void* Vcache,
@@ -251,6 +272,73 @@ attn_status attn_output_projection(const void* O, const void* Wo, attn_layout L,
   a.w_bytes = (uint32_t)w_bytes;
   a.a_bytes = (uint32_t)o_bytes;
   const hipError_t e = launch_proj(a, false, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    g_last_hip = e;
+    return ATTN_ERR_HIP;
+  }
+  return ATTN_OK;
+}
+
+size_t attn_backward_workspace_bytes(attn_layout L) {
+  if (check_layout(L) != ATTN_OK) return 0;
+  return (size_t)L.B * L.h * L.n_q * sizeof(float);
+}
+
+attn_status attn_backward(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                          const float* LSE, attn_layout L, int32_t mask_kind, const int32_t* q_lens,
+                          const int32_t* kv_lens, float scale, void* dQ, void* dK, void* dV,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  attn_status st = check_layout(L);
+  if (st != ATTN_OK) return st;
+  if (L.dtype != ATTN_BF16) return ATTN_ERR_BAD_DTYPE;
+  if (mask_kind & ~(ATTN_MASK_KEY_PADDING | ATTN_MASK_CAUSAL)) return ATTN_ERR_BAD_MASK;
+  const bool kpad = (mask_kind & ATTN_MASK_KEY_PADDING) != 0;
+  const bool causal = (mask_kind & ATTN_MASK_CAUSAL) != 0;
+  if (causal && L.n_q != L.n_k) return ATTN_ERR_BAD_MASK;
+  if (!kpad && kv_lens != nullptr) return ATTN_ERR_BAD_MASK;
+  if (!std::isfinite(scale)) return ATTN_ERR_BAD_SCALE;
+  if (L.B == 0 || L.h == 0 || (L.n_q == 0 && L.n_k == 0)) return ATTN_OK;
+  if (kpad && !kv_lens) return ATTN_ERR_NULL_POINTER;
+  if (L.n_q > 0 && (!Q || !O || !dO || !LSE || !dQ)) return ATTN_ERR_NULL_POINTER;
+  if (L.n_k > 0 && (!K || !V || !dK || !dV)) return ATTN_ERR_NULL_POINTER;
+  const void* ins[6] = {Q, K, V, O, dO, LSE};
+  const void* outs[3] = {dQ, dK, dV};
+  for (const void* o : outs) {
+    if (!o) continue;
+    for (const void* in : ins)
+      if (in == o) return ATTN_ERR_BAD_SHAPE;
+  }
+  if ((dQ && (dQ == dK || dQ == dV)) || (dK && dK == dV)) return ATTN_ERR_BAD_SHAPE;
+  const size_t need = attn_backward_workspace_bytes(L);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return ATTN_ERR_WORKSPACE;
+  const int64_t blocks = (int64_t)((std::max(L.n_q, L.n_k) + 127) / 128) * L.h * L.B;
+  if (blocks > kMaxGrid || ((int64_t)L.B * L.h * L.n_q + 31) / 32 > kMaxGrid) return ATTN_ERR_BAD_SHAPE;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (length_check_enabled()) {
+    if ((st = check_lengths(q_lens, L.B, L.n_q, s)) != ATTN_OK) return st;
+    if ((st = check_lengths(kv_lens, L.B, L.n_k, s)) != ATTN_OK) return st;
+  }
+  BwdArgs a;
+  a.Q = Q;
+  a.K = K;
+  a.V = V;
+  a.O = O;
+  a.dO = dO;
+  a.lse = LSE;
+  a.D = static_cast<float*>(workspace);
+  a.dQ = dQ;
+  a.dK = dK;
+  a.dV = dV;
+  a.q_lens = q_lens;
+  a.kv_lens = kv_lens;
+  a.B = L.B;
+  a.H = L.h;
+  a.n_q = L.n_q;
+  a.n_k = L.n_k;
+  a.scale = scale;
+  a.causal = causal;
+  const hipError_t e = launch_backward(a, s);
   if (e != hipSuccess) {
     g_last_hip = e;
     return ATTN_ERR_HIP;

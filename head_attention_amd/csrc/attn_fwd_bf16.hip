@@ -461,6 +461,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
   const float l_row = half_swap_sum(l);
   const bool live = qi < q_len && l_row > 0.f;
   const float inv = live ? 1.f / l_row : 0.f;
+  // Row log-sum-exp ln(sum_j exp(s_ij)) = (m c + log2 l) ln 2; -inf for a
+  // padded row or a row with no allowed key (one lane per row writes).
+  if (a.lse && hh == 0 && qi < a.n_q)
+    a.lse[(size_t)bh * a.n_q + qi] = live ? (mc + __builtin_amdgcn_logf(l_row)) * kLn2 : -INFINITY;
   if (qi < a.n_q) {
     __bf16* orow = O + (size_t)qi * kHeadDim;
 #pragma unroll

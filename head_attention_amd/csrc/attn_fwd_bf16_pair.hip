@@ -599,6 +599,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_pair_kernel(FwdArgs
     const int qi = qw0 + 32 * qb + ln;
     live[qb] = qi < q_len && l_row > 0.f;
     inv[qb] = live[qb] ? 1.f / l_row : 0.f;
+    // Row log-sum-exp (M + log2 l) ln 2; -inf for padded or keyless rows.
+    if (a.lse && hh == 0 && qi < a.n_q)
+      a.lse[(size_t)bh * a.n_q + qi] = live[qb] ? (M + __builtin_amdgcn_logf(l_row)) * kLn2 : -INFINITY;
   }
   // Register r of block (db, qb) holds d = 32 db + 8 (r / 4) + 4 hh + r % 4
   // of query row qw0 + 32 qb + ln: four consecutive d per 8-byte store.

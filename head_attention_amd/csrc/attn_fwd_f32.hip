@@ -124,6 +124,8 @@ __global__ __launch_bounds__(64) void attn_fwd_f32_kernel(FwdArgs a) {
   if (i < a.n_q) {
     // A row with no allowed key, or a padded query row, is written as 0.
     const float inv = (row_ok && l > 0.f) ? 1.f / l : 0.f;
+    // Row log-sum-exp (m + log2 l) ln 2 in fp32; -inf for padded or keyless rows.
+    if (a.lse) a.lse[bh * (size_t)a.n_q + i] = (row_ok && l > 0.f) ? (m + log2f(l)) * kLn2 : -INFINITY;
     float4* o4 = reinterpret_cast<float4*>(O + (size_t)i * kHeadDim);
 #pragma unroll
     for (int e = 0; e < kHeadDim / 4; ++e)

@@ -25,7 +25,12 @@ struct FwdArgs {
   int B, H, n_q, n_k;
   float scale;             // multiplies Q K^T; finite
   bool causal;
+  float* lse;              // device fp32 [B*H*n_q] or nullptr: per-row log-sum-exp
 };
+
+// ln(2): a row's log-sum-exp in natural units from its log2-domain pivot m
+// and sum l is (m + log2 l) ln 2.
+constexpr float kLn2 = 0.69314718055994531f;
 
 // One decode call.
 struct DecodeArgs {
@@ -65,6 +70,26 @@ struct ProjArgs {
   uint32_t w_bytes, a_bytes;
 };
 hipError_t launch_proj(const ProjArgs& a, bool head_out, hipStream_t s);
+
+// One backward call (bf16): gradients of O = softmax(Q K^T scale + M) V.
+struct BwdArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  const void* O;
+  const void* dO;
+  const float* lse;        // [B*H*n_q] natural-log row normalisers from the forward
+  float* D;                // workspace [B*H*n_q]: dO . O per row
+  void* dQ;
+  void* dK;
+  void* dV;
+  const int32_t* q_lens;
+  const int32_t* kv_lens;
+  int B, H, n_q, n_k;
+  float scale;
+  bool causal;
+};
+hipError_t launch_backward(const BwdArgs& a, hipStream_t s);
 
 // Decode: keys per split (one workgroup of 4 waves x 64 keys).
 constexpr int kDecodeWaves = 4;

@@ -124,6 +124,22 @@ attn_status attn_forward(const void* Q, const void* K, const void* V,
                          float scale, void* O, void* stream);
 
 /*
+ * attn_forward_lse -- attn_forward that also writes each query row's
+ * log-sum-exp, the normaliser of its softmax, which the backward pass
+ * (attn_backward) uses to recompute the weights without a second forward.
+ *
+ *   LSE  device fp32 [B, h, n_q], written: LSE[b, h, i] = ln sum_j
+ *        exp(scale q_i . k_j) over the allowed keys j (natural log); -inf
+ *        for a padded query row or a row with no allowed key.
+ * Every other argument, the output O and the error behaviour are those of
+ * attn_forward; LSE = NULL (with a non-empty call) is ATTN_ERR_NULL_POINTER.
+ */
+attn_status attn_forward_lse(const void* Q, const void* K, const void* V,
+                             attn_layout layout, int32_t mask_kind,
+                             const int32_t* q_lens, const int32_t* kv_lens,
+                             float scale, void* O, float* LSE, void* stream);
+
+/*
  * attn_decode -- one KV-cache decode step: for each (b, h) the single new
  * query attends to the kv_lens[b] valid rows of the cache, which already
  * include the new token's own K/V (the caller appends first; sj-techlog
@@ -222,6 +238,39 @@ attn_status attn_head_projection(const void* X, const void* W, attn_layout layou
  */
 attn_status attn_output_projection(const void* O, const void* Wo, attn_layout layout, void* Y,
                                    void* stream);
+
+/*
+ * attn_backward -- gradients of O = softmax(Q K^T * scale + M) V (the map of
+ * "[논문 리뷰]Attention Is All You Need", §3.2.1, trained end to end in §5):
+ * given dO = dL/dO, returns dL/dQ, dL/dK, dL/dV.  With the weights p_ij =
+ * exp(scale q_i . k_j - LSE_i) of the allowed keys:
+ *   dV_j = sum_i p_ij dO_i;   ds_ij = p_ij (dO_i . V_j - dO_i . O_i);
+ *   dQ_i = scale sum_j ds_ij K_j;   dK_j = scale sum_i ds_ij Q_i.
+ *
+ *   Q, K, V, O, dO  bf16 device tensors, read: the forward's inputs, its
+ *                   output O and the incoming gradient, all [B, h, n, 64]
+ *   LSE             fp32 [B, h, n_q] from attn_forward_lse of the same call
+ *   layout, mask_kind, q_lens, kv_lens, scale
+ *                   exactly as given to the forward (dtype must be ATTN_BF16)
+ *   dQ              [B, h, n_q, 64] bf16, written (padded rows as 0)
+ *   dK, dV          [B, h, n_k, 64] bf16, written (excluded keys as 0)
+ *   workspace       device buffer of at least attn_backward_workspace_bytes
+ *                   (fp32 dO . O per row); contents on entry do not matter
+ *   stream          hipStream_t or NULL.
+ * Three kernels on `stream` (row dots, key-major dK/dV, query-major dQ); no
+ * atomics, so the results are bitwise reproducible.  bf16 products, fp32
+ * accumulation; p and ds are rounded to bf16 once before their products.
+ * Outputs must not alias inputs or each other.
+ */
+attn_status attn_backward(const void* Q, const void* K, const void* V, const void* O,
+                          const void* dO, const float* LSE, attn_layout layout,
+                          int32_t mask_kind, const int32_t* q_lens, const int32_t* kv_lens,
+                          float scale, void* dQ, void* dK, void* dV, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace attn_backward needs (fp32 per query row); 0 if the
+ * layout is invalid.  Pure host arithmetic. */
+size_t attn_backward_workspace_bytes(attn_layout layout);
 
 /* Bytes of fp32 split partials attn_decode needs for this cache layout; 0 if
  * the layout is invalid.  Pure host arithmetic. */

@@ -1,0 +1,117 @@
+"""GPU parity of the training path: the per-row log-sum-exp the forward
+returns for the backward (attn_forward_lse), and attn_backward's dQ, dK, dV
+against the fp64 oracle (oracle.attention_backward, itself pinned against
+torch autograd and finite differences) on the same bf16 inputs, for every
+mask kind, padded query rows, cross attention with n_q != n_k, and shapes
+that span several tiles with a ragged tail.
+
+Bars.  LSE: |lse_gpu - lse_ref| <= 1e-2 on bf16 inputs (the row sum is
+taken over bf16-rounded weights, a relative error of at most 2^-8, i.e.
+4e-3 in the log) and <= 1e-5 on the fp32 path.  Gradients (bf16 outputs):
+relative L2 error <= 2e-2 and max |err| <= 2e-2 max(1, max |ref|) per
+tensor; the weights and ds are rounded to bf16 (2^-9 relative) before their
+products and D = dO . O uses the bf16-rounded O, so errors of a few 1e-3
+relative are expected.
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import head_attention_amd as ha
+import oracle.attn_oracle as orc
+import workloads
+from gpu_util import np64, say
+
+pytestmark = pytest.mark.gpu
+
+BF16, F32 = torch.bfloat16, torch.float32
+
+
+def _case(name, B, H, n_q, n_k, mask, ql, kl, dtype=BF16, scale=0.125):
+    g = workloads.generator(zlib.crc32(name.encode()) % 10000)
+    Q, K, V = (workloads.randn(g, (B, H, n, 64), dtype) for n in (n_q, n_k, n_k))
+    dO = workloads.randn(g, (B, H, n_q, 64), dtype)
+    ql = None if ql is None else torch.tensor(ql, dtype=torch.int32)
+    kl = None if kl is None else torch.tensor(kl, dtype=torch.int32)
+    return Q, K, V, dO, ql, kl, scale
+
+
+@pytest.mark.parametrize("dtype", [BF16, F32], ids=["bf16", "fp32"])
+@pytest.mark.parametrize("n_q,n_k,mask", [(128, 128, 3), (128, 160, 1), (300, 300, 2), (600, 600, 3)])
+def test_forward_lse(dtype, n_q, n_k, mask):
+    name = f"lse{n_q}x{n_k}m{mask}"
+    kl = [n_k, n_k // 3] if mask & 1 else None
+    Q, K, V, _, ql, kl, scale = _case(name, 2, 3, n_q, n_k, mask, [n_q, n_q - 7], kl, dtype)
+    say(f"[forward lse {dtype} {n_q}x{n_k} mask{mask}]")
+    lse = torch.empty((2, 3, n_q), dtype=torch.float32, device="cuda")
+    O = ha.forward(Q.cuda(), K.cuda(), V.cuda(), mask_kind=mask, q_lens=ql.cuda(),
+                   kv_lens=None if kl is None else kl.cuda(), scale=scale, lse=lse)
+    O_plain = ha.forward(Q.cuda(), K.cuda(), V.cuda(), mask_kind=mask, q_lens=ql.cuda(),
+                         kv_lens=None if kl is None else kl.cuda(), scale=scale)
+    torch.cuda.synchronize()
+    assert torch.equal(O, O_plain)  # the lse output does not change O
+    ref = orc.row_logsumexp(np64(Q), np64(K), mask_kind=mask, q_lens=ql.numpy(),
+                            kv_lens=None if kl is None else kl.numpy(), scale=scale)
+    got = lse.cpu().double().numpy()
+    assert np.array_equal(np.isinf(got), np.isinf(ref))
+    fin = np.isfinite(ref)
+    err = float(np.abs(got[fin] - ref[fin]).max())
+    say(f"  lse max err {err:.3e}")
+    assert err <= (1e-2 if dtype == BF16 else 1e-5)
+
+
+BWD = {
+    # name: (B, H, n_q, n_k, mask, q_lens, kv_lens, scale)
+    "none_128": (2, 4, 128, 128, 0, None, None, 0.125),
+    "kpad_128": (3, 2, 128, 128, 1, [128, 90, 17], [128, 90, 17], 0.125),
+    "causal_128": (2, 4, 128, 128, 2, None, None, 0.125),
+    "causal_kpad_200": (2, 2, 200, 200, 3, [200, 131], [200, 131], 0.125),
+    "cross_128x160": (3, 2, 128, 160, 1, None, [160, 16, 99], 0.125),
+    "causal_330": (1, 2, 330, 330, 2, None, None, 0.125),
+    "none_70x257": (1, 2, 70, 257, 0, None, None, 0.125),
+    "negative_scale_96": (1, 2, 96, 96, 2, None, None, -0.3),
+    "one_key": (2, 1, 40, 40, 1, [40, 40], [1, 2], 0.125),
+}
+
+
+def _check_grad(got, ref, what):
+    got = np.asarray(got, dtype=np.float64)
+    err = np.abs(got - ref)
+    nref = float(np.linalg.norm(ref))
+    rel = float(np.linalg.norm(got - ref)) / nref if nref > 0 else float(np.linalg.norm(got))
+    bound = 2e-2 * max(1.0, float(np.abs(ref).max()))
+    say(f"  {what}: max_abs={float(err.max()):.3e} (bound {bound:.2e}) rel_l2={rel:.3e}")
+    assert np.all(np.isfinite(got)), what
+    assert float(err.max()) <= bound, what
+    assert rel <= 2e-2, what
+
+
+@pytest.mark.parametrize("cid", sorted(BWD))
+def test_backward(cid):
+    B, H, n_q, n_k, mask, ql, kl, scale = BWD[cid]
+    Q, K, V, dO, ql, kl, scale = _case(cid, B, H, n_q, n_k, mask, ql, kl, BF16, scale)
+    say(f"[backward {cid}]")
+    d = lambda t: None if t is None else t.cuda()
+    Qd, Kd, Vd, dOd = d(Q), d(K), d(V), d(dO)
+    lse = torch.empty((B, H, n_q), dtype=torch.float32, device="cuda")
+    O = ha.forward(Qd, Kd, Vd, mask_kind=mask, q_lens=d(ql), kv_lens=d(kl), scale=scale, lse=lse)
+    dQ, dK, dV = ha.backward(Qd, Kd, Vd, O, dOd, lse, mask_kind=mask, q_lens=d(ql), kv_lens=d(kl),
+                             scale=scale)
+    dQ2, dK2, dV2 = ha.backward(Qd, Kd, Vd, O, dOd, lse, mask_kind=mask, q_lens=d(ql), kv_lens=d(kl),
+                                scale=scale)
+    torch.cuda.synchronize()
+    assert torch.equal(dQ, dQ2) and torch.equal(dK, dK2) and torch.equal(dV, dV2)  # deterministic
+    rQ, rK, rV = orc.attention_backward(np64(Q), np64(K), np64(V), np64(dO), mask_kind=mask,
+                                        q_lens=None if ql is None else ql.numpy(),
+                                        kv_lens=None if kl is None else kl.numpy(), scale=scale)
+    _check_grad(np64(dQ), rQ, "dQ")
+    _check_grad(np64(dK), rK, "dK")
+    _check_grad(np64(dV), rV, "dV")
+    if ql is not None:  # padded query rows: zero dQ
+        for b in range(B):
+            assert torch.all(dQ[b, :, int(ql[b]):] == 0)
+    if kl is not None:  # excluded keys: zero dK, dV
+        for b in range(B):
+            assert torch.all(dK[b, :, int(kl[b]):] == 0) and torch.all(dV[b, :, int(kl[b]):] == 0)
