@@ -29,7 +29,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("attn_forward", "attn_decode", "attn_cache_append", "attn_head_projection",
+    for n in ("attn_forward", "attn_forward_lse", "attn_backward", "attn_backward_workspace_bytes",
+              "attn_decode", "attn_cache_append", "attn_head_projection",
               "attn_output_projection", "attn_decode_workspace_bytes",
               "attn_status_string", "attn_last_hip_error"):
         assert n in names, names
@@ -161,6 +162,42 @@ def test_projection_validation():
     assert op(lay_, y=None) == NULLP and op(lay_, o=None) == NULLP and op(lay_, w=None) == NULLP
     assert op(lay_, y=FAKE) == SHAPE
     assert op(attn_layout(2, 8, 0, 0, 64, BF16), o=None, w=None, y=None) == OK
+
+
+def test_forward_lse_and_backward_validation():
+    L = ha.lib()
+    lay_ = attn_layout(2, 3, 16, 16, 64, BF16)
+    # forward_lse: LSE required for a non-empty call; LSE must not alias O
+    assert L.attn_forward_lse(FAKE, FAKE + 16, FAKE + 32, lay_, 0, None, None, 0.125, FAKE + 48, None, None) == NULLP
+    assert L.attn_forward_lse(FAKE, FAKE + 16, FAKE + 32, lay_, 0, None, None, 0.125, FAKE + 48, FAKE + 48,
+                              None) == SHAPE
+    assert L.attn_forward_lse(None, None, None, attn_layout(0, 3, 16, 16, 64, BF16), 0, None, None, 0.125,
+                              None, None, None) == OK
+    assert L.attn_backward_workspace_bytes(lay_) == 2 * 3 * 16 * 4
+    assert L.attn_backward_workspace_bytes(attn_layout(2, 3, 16, 16, 32, BF16)) == 0
+
+    def bwd(lay, mask=0, ql=None, kl=None, scale=0.125, ws_bytes=None, **ptrs):
+        p = dict(q=FAKE, k=FAKE + 16, v=FAKE + 32, o=FAKE + 48, do=FAKE + 64, lse=FAKE + 80,
+                 dq=FAKE + 96, dk=FAKE + 112, dv=FAKE + 128, ws=FAKE + 144)
+        p.update(ptrs)
+        wsb = L.attn_backward_workspace_bytes(lay) if ws_bytes is None else ws_bytes
+        return L.attn_backward(p["q"], p["k"], p["v"], p["o"], p["do"], p["lse"], lay, mask, ql, kl, scale,
+                               p["dq"], p["dk"], p["dv"], p["ws"], wsb, None)
+    assert bwd(attn_layout(2, 3, 16, 16, 64, F32)) == DTYPE
+    assert bwd(attn_layout(2, 3, 16, 16, 48, BF16)) == SHAPE
+    assert bwd(lay_, mask=4) == MASK
+    assert bwd(attn_layout(2, 3, 16, 20, 64, BF16), mask=2) == MASK   # causal needs n_q == n_k
+    assert bwd(lay_, mask=0, kl=FAKE) == MASK                           # kv_lens without padding
+    assert bwd(lay_, scale=float("nan")) == SCALE
+    for name in ("q", "k", "v", "o", "do", "lse", "dq", "dk", "dv"):
+        assert bwd(lay_, **{name: None}) == NULLP, name
+    assert bwd(lay_, mask=1) == NULLP                                   # padding without kv_lens
+    assert bwd(lay_, ws=None) == WORK
+    assert bwd(lay_, ws_bytes=L.attn_backward_workspace_bytes(lay_) - 1) == WORK
+    assert bwd(lay_, dq=FAKE) == SHAPE                                  # output aliases Q
+    assert bwd(lay_, dk=FAKE + 96) == SHAPE                             # dK aliases dQ
+    assert bwd(attn_layout(0, 3, 16, 16, 64, BF16), q=None, k=None, v=None, o=None, do=None, lse=None,
+               dq=None, dk=None, dv=None, ws=None) == OK
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
