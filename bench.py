@@ -325,9 +325,17 @@ LEG_GRIDS = {("attn_fwd_bf16_short_kernel<false>", 65536): "encoder_base",
              ("attn_fwd_bf16_short_kernel<true>", 131072): "decoder_big (causal self)",
              ("attn_fwd_bf16_short_kernel<false>", 131072): "decoder_big (cross)",
              ("cache_append_kernel", 8192): "kv_append",
-             ("bwd_dkdv_kernel<true>", 16384): "long_causal_bwd",
-             ("bwd_dq_kernel<true>", 16384): "long_causal_bwd",
+             ("bwd_dkdv_kernel<true>", 262144): "long_causal_bwd",
+             ("bwd_dq_kernel<true>", 262144): "long_causal_bwd",
              ("bwd_rowdot_kernel", 1048576): "long_causal_bwd",
+             ("bwd_dkdv_kernel<false>", 65536): "encoder_base_bwd",
+             ("bwd_dq_kernel<false>", 65536): "encoder_base_bwd",
+             ("bwd_rowdot_kernel", 262144): "encoder_base_bwd",
+             ("bwd_dkdv_kernel<true>", 131072): "decoder_big_bwd (causal self)",
+             ("bwd_dq_kernel<true>", 131072): "decoder_big_bwd (causal self)",
+             ("bwd_dkdv_kernel<false>", 262144): "decoder_big_bwd (cross)",
+             ("bwd_dq_kernel<false>", 131072): "decoder_big_bwd (cross)",
+             ("bwd_rowdot_kernel", 524288): "decoder_big_bwd (self and cross)",
              ("proj_gemm_kernel<true>", 196608): "mha_proj (self Q, K, V)",
              ("proj_gemm_kernel<true>", 65536): "mha_proj (cross Q)",
              ("proj_gemm_kernel<true>", 163840): "mha_proj (cross K, V)",
