@@ -27,7 +27,9 @@ states.  Page citations name the page title and its section:
 Readings where the pages are silent (the same list is kept with the design
 notes):
 * Mask kinds are exclusion sets: a key is *allowed* iff j < kv_len[b] (key
-  padding) and, for causal, j <= i (top-left aligned, n_q == n_k).  Excluded
+  padding), for causal j <= i (top-left aligned, n_q == n_k), and for
+  restricted self-attention |i - j| <= radius (j >= i - radius under the
+  causal mask as well; n_q == n_k).  Excluded
   keys never enter the sum, so their weight is exactly 0 and their K/V
   contents (even NaN) cannot reach the output.
 * A query row i >= q_len[b] (a padded query position) is written as 0.
@@ -36,6 +38,12 @@ notes):
   same choice the verification script on the sj-techlog page makes.
 * Decode: the single new query sits at position kv_len-1 and sees every one of
   the kv_len cached keys; the caller has already appended the new token's K/V.
+* Restricted self-attention (kimjiil page §4, Table 1 and the note after it:
+  each position looks only at its r surrounding positions, O(r n d) work)
+  leaves the shape of the neighbourhood open.  Reading: a window centred on
+  the query, r = 2 radius + 1 keys i - radius .. i + radius, clipped to the
+  sequence; with the decoder's causal mask only its past half remains,
+  i - radius .. i (radius + 1 keys).
 
 parity pinned: every function below is checked against page values, closed
 forms, invariants or an independent library routine in tests/test_oracle.py.
@@ -50,11 +58,13 @@ import numpy as np
 MASK_NONE = 0
 MASK_KEY_PADDING = 1
 MASK_CAUSAL = 2
+MASK_RESTRICTED = 4
 
 __all__ = [
     "MASK_NONE",
     "MASK_KEY_PADDING",
     "MASK_CAUSAL",
+    "MASK_RESTRICTED",
     "allowed_keys",
     "attention_row",
     "attention",
@@ -70,18 +80,34 @@ def _f64(x) -> np.ndarray:
     return np.asarray(x, dtype=np.float64)
 
 
-def allowed_keys(i: int, n_k: int, kv_len: int, causal: bool) -> np.ndarray:
+def _radius_of(mask_kind: int, radius, n_q: int, n_k: int):
+    """The window radius of a call: None unless mask_kind has MASK_RESTRICTED,
+    which is self-attention (n_q == n_k) and needs an integer radius >= 0."""
+    if not mask_kind & MASK_RESTRICTED:
+        return None
+    if radius is None or int(radius) < 0:
+        raise ValueError("restricted attention needs a radius >= 0")
+    if n_q != n_k:
+        raise ValueError("restricted self-attention needs n_q == n_k")
+    return int(radius)
+
+
+def allowed_keys(i: int, n_k: int, kv_len: int, causal: bool, radius=None) -> np.ndarray:
     """Boolean vector over the n_k keys: which keys query row i may attend to.
 
     Key padding ("pad token에 attention이 가지 않는가", sj-techlog page,
     failure section 2) excludes j >= kv_len.  The causal mask of the decoder
     self-attention (kimjiil page §3.2.3; the 4x4 table on the sj-techlog page)
-    excludes j > i.
+    excludes j > i.  Restricted self-attention (kimjiil page §4, Table 1:
+    a neighbourhood of r positions around the query) with radius w excludes
+    |i - j| > w; None means unrestricted.
     """
     j = np.arange(n_k)
     ok = j < kv_len
     if causal:
         ok &= j <= i
+    if radius is not None:
+        ok &= np.abs(j - i) <= radius
     return ok
 
 
@@ -117,13 +143,15 @@ def attention_row(q, K, V, allowed, scale: float, return_weights: bool = False):
 
 
 def attention(Q, K, V, mask_kind: int = MASK_NONE, q_lens=None, kv_lens=None,
-              scale: float | None = None, rows=None, return_weights: bool = False):
+              scale: float | None = None, rows=None, return_weights: bool = False,
+              radius=None):
     """Multi-head scaled dot-product attention, heads batched as [B, h, n, d].
 
     Q: [B, h, n_q, d_k]; K: [B, h, n_k, d_k]; V: [B, h, n_k, d_v]
     (sj-techlog page, "식 (1)의 모든 기호"; each head is an independent
     Attention(QW^Q, KW^K, VW^V), kimjiil page §3.2.2).
-    mask_kind: bit 1 = key padding by kv_lens[b]; bit 2 = causal (n_q == n_k).
+    mask_kind: bit 1 = key padding by kv_lens[b]; bit 2 = causal (n_q == n_k);
+    bit 4 = restricted to |i - j| <= radius (n_q == n_k; needs radius >= 0).
     q_lens[b]: rows i >= q_lens[b] are written as 0 (None = all rows valid).
     scale: defaults to 1/sqrt(d_k) (kimjiil page §3.2.1).
     rows: optional iterable of (b, h, i) to evaluate only those rows; then a
@@ -144,6 +172,7 @@ def attention(Q, K, V, mask_kind: int = MASK_NONE, q_lens=None, kv_lens=None,
     kpad = bool(mask_kind & MASK_KEY_PADDING)
     if kpad and kv_lens is None:
         raise ValueError("key padding needs kv_lens")
+    radius = _radius_of(mask_kind, radius, n_q, n_k)
 
     def kv_len_of(b):
         return int(kv_lens[b]) if kpad else n_k
@@ -157,7 +186,7 @@ def attention(Q, K, V, mask_kind: int = MASK_NONE, q_lens=None, kv_lens=None,
             if i >= q_len_of(b):
                 res[(b, h, i)] = np.zeros(V.shape[3])
                 continue
-            ok = allowed_keys(i, n_k, kv_len_of(b), causal)
+            ok = allowed_keys(i, n_k, kv_len_of(b), causal, radius)
             res[(b, h, i)] = attention_row(Q[b, h, i], K[b, h], V[b, h], ok, scale)
         return res
 
@@ -168,7 +197,7 @@ def attention(Q, K, V, mask_kind: int = MASK_NONE, q_lens=None, kv_lens=None,
         q_len = q_len_of(b)
         for h in range(H):
             for i in range(min(q_len, n_q)):
-                ok = allowed_keys(i, n_k, kv_len, causal)
+                ok = allowed_keys(i, n_k, kv_len, causal, radius)
                 if return_weights:
                     O[b, h, i], W[b, h, i] = attention_row(
                         Q[b, h, i], K[b, h], V[b, h], ok, scale, True)
@@ -208,7 +237,8 @@ def decode(q, Kcache, Vcache, kv_lens, scale: float | None = None, pairs=None):
     return O
 
 
-def row_logsumexp(Q, K, mask_kind: int = MASK_NONE, q_lens=None, kv_lens=None, scale: float | None = None):
+def row_logsumexp(Q, K, mask_kind: int = MASK_NONE, q_lens=None, kv_lens=None, scale: float | None = None,
+                  radius=None):
     """Per query row, log(sum_j exp(s_ij)) over the allowed keys (natural
     log), the normaliser of the softmax of kimjiil page §3.2.1; -inf for a
     row with no allowed key or a padded query row.  Returns [B, h, n_q]."""
@@ -219,13 +249,14 @@ def row_logsumexp(Q, K, mask_kind: int = MASK_NONE, q_lens=None, kv_lens=None, s
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     causal = bool(mask_kind & MASK_CAUSAL)
+    radius = _radius_of(mask_kind, radius, n_q, n_k)
     out = np.full((B, H, n_q), -np.inf)
     for b in range(B):
         kv_len = n_k if not (mask_kind & MASK_KEY_PADDING) else int(kv_lens[b])
         q_len = n_q if q_lens is None else int(q_lens[b])
         for h in range(H):
             for i in range(min(q_len, n_q)):
-                idx = np.flatnonzero(allowed_keys(i, n_k, kv_len, causal))
+                idx = np.flatnonzero(allowed_keys(i, n_k, kv_len, causal, radius))
                 if idx.size:
                     s = scale * (K[b, h][idx] @ Q[b, h, i])
                     m = s.max()
@@ -234,7 +265,7 @@ def row_logsumexp(Q, K, mask_kind: int = MASK_NONE, q_lens=None, kv_lens=None, s
 
 
 def attention_backward(Q, K, V, dO, mask_kind: int = MASK_NONE, q_lens=None, kv_lens=None,
-                       scale: float | None = None):
+                       scale: float | None = None, radius=None):
     """Gradients of L through O = softmax(Q K^T * scale + M) V, given dO =
     dL/dO (the training the pages describe back-propagates through this
     sub-layer; kimjiil page §3.2.1 defines the map).  Row by row, with the
@@ -253,6 +284,7 @@ def attention_backward(Q, K, V, dO, mask_kind: int = MASK_NONE, q_lens=None, kv_
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     causal = bool(mask_kind & MASK_CAUSAL)
+    radius = _radius_of(mask_kind, radius, n_q, n_k)
     dQ = np.zeros_like(Q)
     dK = np.zeros_like(K)
     dV = np.zeros_like(V)
@@ -261,7 +293,7 @@ def attention_backward(Q, K, V, dO, mask_kind: int = MASK_NONE, q_lens=None, kv_
         q_len = n_q if q_lens is None else int(q_lens[b])
         for h in range(H):
             for i in range(min(q_len, n_q)):
-                idx = np.flatnonzero(allowed_keys(i, n_k, kv_len, causal))
+                idx = np.flatnonzero(allowed_keys(i, n_k, kv_len, causal, radius))
                 if idx.size == 0:
                     continue
                 s = scale * (K[b, h][idx] @ Q[b, h, i])

@@ -525,6 +525,103 @@ def pin_row_logsumexp(orc):
                 assert np.allclose(np.where(ok, np.exp(s - lse[b, h, i]), 0.0), W[b, h, i], atol=1e-14)
 
 
+def _band(n, radius, causal):
+    """Allowed (query, key) pairs of restricted self-attention built with
+    torch's own band routines: keys i - radius .. i + radius (kimjiil page
+    §4, Table 1's neighbourhood of r = 2 radius + 1 positions), only the
+    past half under the causal mask."""
+    ones = torch.ones(n, n, dtype=torch.bool)
+    band = torch.triu(ones, -radius) & torch.tril(ones, 0 if causal else radius)
+    return band.numpy()
+
+
+def pin_restricted_slices(orc):
+    """Each row of restricted self-attention is plain attention of its query
+    over the contiguous slice of keys around it (cut by index arithmetic,
+    clipped at both ends of the sequence and at kv_len), computed by torch's
+    scaled_dot_product_attention in fp64 with no mask at all."""
+    rng = np.random.default_rng(95)
+    B, H, n, d = 2, 2, 11, 4
+    Q, K, V = (rng.standard_normal((B, H, n, d)) for _ in range(3))
+    kl = np.array([11, 6])
+    for causal in (False, True):
+        for radius in (0, 1, 3, 10, 25):
+            mask = orc.MASK_RESTRICTED | orc.MASK_KEY_PADDING | (orc.MASK_CAUSAL if causal else 0)
+            O = orc.attention(Q, K, V, mask_kind=mask, kv_lens=kl, scale=0.4, radius=radius)
+            for b in range(B):
+                for i in range(n):
+                    lo = max(0, i - radius)
+                    hi = min(i + 1 if causal else i + radius + 1, kl[b])
+                    if lo >= hi:
+                        assert np.all(O[b, :, i] == 0.0), (causal, radius, b, i)
+                        continue
+                    ref = torch.nn.functional.scaled_dot_product_attention(
+                        torch.from_numpy(Q[b, :, i:i + 1]), torch.from_numpy(K[b, :, lo:hi]),
+                        torch.from_numpy(V[b, :, lo:hi]), scale=0.4).numpy()
+                    assert np.allclose(O[b, :, i], ref[:, 0], atol=1e-12), (causal, radius, b, i)
+
+
+def pin_restricted_vs_torch_band(orc):
+    """Whole-matrix restricted self-attention against torch's fp64 attention
+    with a boolean band mask from triu/tril, for radii from 0 to beyond the
+    sequence, with and without the causal mask."""
+    rng = np.random.default_rng(96)
+    B, H, n, d = 1, 3, 9, 8
+    Q, K, V = (rng.standard_normal((B, H, n, d)) for _ in range(3))
+    for causal in (False, True):
+        for radius in (0, 2, 4, 8, 100):
+            mask = orc.MASK_RESTRICTED | (orc.MASK_CAUSAL if causal else 0)
+            O = orc.attention(Q, K, V, mask_kind=mask, scale=0.3, radius=radius)
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                torch.from_numpy(Q), torch.from_numpy(K), torch.from_numpy(V),
+                attn_mask=torch.from_numpy(_band(n, radius, causal)), scale=0.3).numpy()
+            assert np.allclose(O, ref, atol=1e-12), (causal, radius)
+
+
+def pin_restricted_closed_forms(orc):
+    """kimjiil page §4, Table 1: a query sees r = 2 radius + 1 neighbours
+    (radius + 1 under the causal mask), fewer only at the sequence ends.
+    Radius 0 leaves each position only itself, so O = V exactly; a radius
+    that spans the sequence is plain (or causal) self-attention."""
+    rng = np.random.default_rng(97)
+    n, d, radius = 12, 4, 3
+    Q, K, V = (rng.standard_normal((1, 2, n, d)) for _ in range(3))
+    for causal in (False, True):
+        cm = orc.MASK_CAUSAL if causal else 0
+        _, W = orc.attention(Q, K, V, mask_kind=orc.MASK_RESTRICTED | cm, radius=radius, return_weights=True)
+        for i in range(n):
+            want = (min(i, radius) + 1) if causal else (min(i, radius) + min(n - 1 - i, radius) + 1)
+            assert np.count_nonzero(W[0, 0, i]) == want, (causal, i)
+            if radius <= i <= n - 1 - radius:
+                assert want == (radius + 1 if causal else 2 * radius + 1)
+        O0 = orc.attention(Q, K, V, mask_kind=orc.MASK_RESTRICTED | cm, radius=0)
+        assert np.array_equal(O0, V)
+        full = orc.attention(Q, K, V, mask_kind=cm)
+        wide = orc.attention(Q, K, V, mask_kind=orc.MASK_RESTRICTED | cm, radius=n - 1)
+        assert np.allclose(full, wide, atol=1e-14)
+
+
+def pin_restricted_backward_and_lse(orc):
+    """Gradients and row log-normalisers under the restricted mask against
+    torch autograd and torch.logsumexp in fp64, with the band built by
+    torch's triu/tril."""
+    rng = np.random.default_rng(98)
+    B, H, n, d, scale = 1, 2, 8, 3, 0.6
+    for causal in (False, True):
+        for radius in (0, 1, 3):
+            mask = orc.MASK_RESTRICTED | (orc.MASK_CAUSAL if causal else 0)
+            Q, K, V, dO = (rng.standard_normal((B, H, n, d)) for _ in range(4))
+            dQ, dK, dV = orc.attention_backward(Q, K, V, dO, mask_kind=mask, scale=scale, radius=radius)
+            lse = orc.row_logsumexp(Q, K, mask_kind=mask, scale=scale, radius=radius)
+            tq, tk, tv = (torch.from_numpy(x.copy()).requires_grad_() for x in (Q, K, V))
+            S = (tq @ tk.transpose(-1, -2) * scale).masked_fill(
+                ~torch.from_numpy(_band(n, radius, causal)), float("-inf"))
+            (torch.softmax(S, dim=-1) @ tv * torch.from_numpy(dO)).sum().backward()
+            for got, ref in ((dQ, tq.grad), (dK, tk.grad), (dV, tv.grad)):
+                assert np.allclose(got, ref.numpy(), atol=1e-12), (causal, radius)
+            assert np.allclose(lse, torch.logsumexp(S, dim=-1).detach().numpy(), atol=1e-12)
+
+
 def pin_kv_cache_size(orc):
     """sj-techlog page KV cache arithmetic: 2 x 6 x 128 x 512 scalars,
     3.0 MiB in fp32 and 1.5 MiB in fp16."""

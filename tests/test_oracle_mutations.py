@@ -27,28 +27,59 @@ _oproj = orc.output_projection
 _bwd = orc.attention_backward
 
 
-def m_causal_strict(i, n_k, kv_len, causal):
+def _window(ok, i, j, radius):
+    if radius is not None:
+        ok &= np.abs(j - i) <= radius
+    return ok
+
+
+def m_causal_strict(i, n_k, kv_len, causal, radius=None):
     j = np.arange(n_k)
     ok = j < kv_len
     if causal:
         ok &= j < i  # off by one: excludes the diagonal
-    return ok
+    return _window(ok, i, j, radius)
 
 
-def m_padding_inclusive(i, n_k, kv_len, causal):
+def m_padding_inclusive(i, n_k, kv_len, causal, radius=None):
     j = np.arange(n_k)
     ok = j <= kv_len  # off by one: admits the first pad
     if causal:
         ok &= j <= i
-    return ok
+    return _window(ok, i, j, radius)
 
 
-def m_causal_transposed(i, n_k, kv_len, causal):
+def m_causal_transposed(i, n_k, kv_len, causal, radius=None):
     j = np.arange(n_k)
     ok = j < kv_len
     if causal:
         ok &= j >= i  # upper instead of lower triangle
-    return ok
+    return _window(ok, i, j, radius)
+
+
+def _window_variant(kind):
+    def allowed(i, n_k, kv_len, causal, radius=None):
+        j = np.arange(n_k)
+        ok = j < kv_len
+        if causal:
+            ok &= j <= i
+        if radius is None:
+            return ok
+        if kind == "strict":
+            ok &= np.abs(j - i) < radius  # off by one: drops both edges
+        elif kind == "past_only":
+            ok &= j >= i - radius  # no upper limit without the causal mask
+        elif kind == "wide_past":
+            ok &= (j >= i - radius - 1) & (j <= i + radius)  # one extra key behind
+        elif kind == "radius_as_r":
+            ok &= np.abs(j - i) <= radius // 2  # radius read as the window size r
+        return ok
+    return allowed
+
+
+def m_bwd_ignores_radius(Q, K, V, dO, mask_kind=0, q_lens=None, kv_lens=None, scale=None, radius=None):
+    return _bwd(Q, K, V, dO, mask_kind=mask_kind & ~orc.MASK_RESTRICTED, q_lens=q_lens,
+                kv_lens=kv_lens, scale=scale)
 
 
 def m_no_max_shift(q, K, V, allowed, scale, return_weights=False):
@@ -165,8 +196,9 @@ def m_concat_heads_reversed(O, Wo):
 
 
 def _bwd_variant(kind):
-    def bwd(Q, K, V, dO, mask_kind=0, q_lens=None, kv_lens=None, scale=None):
+    def bwd(Q, K, V, dO, mask_kind=0, q_lens=None, kv_lens=None, scale=None, radius=None):
         Q, K, V, dO = (np.asarray(x, dtype=np.float64) for x in (Q, K, V, dO))
+        radius = radius if mask_kind & orc.MASK_RESTRICTED else None
         B, H, n_q, d = Q.shape
         n_k = K.shape[2]
         if scale is None:
@@ -177,7 +209,7 @@ def _bwd_variant(kind):
             q_len = n_q if q_lens is None else int(q_lens[b])
             for h in range(H):
                 for i in range(min(q_len, n_q)):
-                    idx = np.flatnonzero(orc.allowed_keys(i, n_k, kv_len, bool(mask_kind & 2)))
+                    idx = np.flatnonzero(orc.allowed_keys(i, n_k, kv_len, bool(mask_kind & 2), radius))
                     if idx.size == 0:
                         continue
                     s = scale * (K[b, h][idx] @ Q[b, h, i])
@@ -215,6 +247,11 @@ MUTANTS = {
     "causal_excludes_diagonal": ("allowed_keys", m_causal_strict),
     "padding_admits_first_pad": ("allowed_keys", m_padding_inclusive),
     "causal_upper_triangle": ("allowed_keys", m_causal_transposed),
+    "window_excludes_edges": ("allowed_keys", _window_variant("strict")),
+    "window_past_only": ("allowed_keys", _window_variant("past_only")),
+    "window_one_extra_past_key": ("allowed_keys", _window_variant("wide_past")),
+    "window_radius_read_as_size": ("allowed_keys", _window_variant("radius_as_r")),
+    "backward_ignores_radius": ("attention_backward", m_bwd_ignores_radius),
     "no_max_shift": ("attention_row", m_no_max_shift),
     "mask_after_softmax": ("attention_row", _row_variant("mask_after_softmax")),
     "no_normalisation": ("attention_row", _row_variant("no_normalise")),
