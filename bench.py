@@ -73,8 +73,10 @@ def kernel_source_hash() -> str:
 
 # ------------------------------------------------------------------ legs
 class Leg:
-    def __init__(self, name, calls=None, decode=None, append=None, proj=None, bwd=False):
+    def __init__(self, name, calls=None, decode=None, append=None, proj=None, bwd=False,
+                 in_value=True):
         self.name = name
+        self.in_value = in_value   # a forward leg that counts towards the headline value
         self.bwd = bwd             # time attn_backward of `calls` instead of the forward
         self.proj = proj           # projection calls (list of dicts of CPU tensors)
         self.calls = calls or []   # forward calls (dicts of CPU tensors)
@@ -90,7 +92,8 @@ class Leg:
             B, H, n_q, _ = c["Q"].shape
             n_k = c["K"].shape[2]
             el = c["Q"].element_size()
-            pairs = workloads.allowed_pairs(c["mask"], n_q, n_k, B, c["q_lens"], c["kv_lens"])
+            pairs = workloads.allowed_pairs(c["mask"], n_q, n_k, B, c["q_lens"], c["kv_lens"],
+                                            radius=c.get("radius"))
             self.flops += (10 if self.bwd else 4) * D * pairs * H
             ql = n_q * B if c["q_lens"] is None else int(c["q_lens"].sum())
             kl = n_k * B if not (c["mask"] & 1) else int(c["kv_lens"].clamp(0, n_k).sum())
@@ -129,6 +132,7 @@ def make_legs():
         legs.append(Leg(name, calls=workloads.make(name)["calls"]))
     for name in ("encoder_base", "decoder_big", "long_causal"):
         legs.append(Leg(name + "_bwd", calls=workloads.make(name)["calls"], bwd=True))
+    legs.append(Leg("long_restricted", calls=workloads.make("long_restricted")["calls"], in_value=False))
     kd = workloads.make("kv_decode")
     rows = (kd["kv_lens"] - 1).long()
     bi = torch.arange(kd["q"].shape[0])
@@ -214,6 +218,10 @@ def run_leg(leg, caches=None):
                         q_lens=c["q_lens"], kv_lens=c["kv_lens"], scale=c["scale"], grads=c["grads"],
                         workspace=c["ws"])
             continue
+        if "radius" in c:
+            ha.forward_restricted(c["Q"], c["K"], c["V"], c["radius"], mask_kind=c["mask"],
+                                  q_lens=c["q_lens"], kv_lens=c["kv_lens"], scale=c["scale"], out=c["O"])
+            continue
         ha.forward(c["Q"], c["K"], c["V"], mask_kind=c["mask"], q_lens=c["q_lens"],
                    kv_lens=c["kv_lens"], scale=c["scale"], out=c["O"])
     d = leg.dev_decode
@@ -240,7 +248,7 @@ def sanity_check(legs):
             ref = orc.attention(np64(c["Q"]), np64(c["K"]), np64(c["V"]), mask_kind=c["mask"],
                                 q_lens=None if c["q_lens"] is None else c["q_lens"].numpy(),
                                 kv_lens=None if c["kv_lens"] is None else c["kv_lens"].numpy(),
-                                scale=c["scale"], rows=rows)
+                                scale=c["scale"], rows=rows, radius=c.get("radius"))
             out = np64(dc["O"])
             worst = max(worst, max(float(np.abs(out[r] - ref[r]).max()) for r in rows))
         if leg.decode is not None:
@@ -303,10 +311,17 @@ def cpu_baseline(target_s: float = 25.0):
 
 
 # ------------------------------------------------------- rocprof summaries
+FWD_MODES = {"0": "none", "1": "causal", "2": "band"}
+
+
 def _short_kernel(name: str) -> str:
-    """attn_fwd_bf16[_pair|_short]_kernel<causal, ...> -> ..._kernel<true|false>;
-    other kernels of the library by their plain name."""
+    """attn_fwd_bf16[_pair|_short]_kernel<mode> -> ..._kernel<none|causal|band>;
+    the bool-templated kernels -> <true|false>; other kernels of the library by
+    their plain name."""
     import re
+    m = re.search(r"(attn_fwd_bf16(?:_pair|_short)?_kernel)(?:<|ILi)(\d)", name)
+    if m:
+        return f"{m.group(1)}<{FWD_MODES[m.group(2)]}>"
     m = re.search(r"(attn_fwd_bf16(?:_pair|_short)?_kernel|proj_gemm_kernel|bwd_dkdv_kernel|bwd_dq_kernel)<(true|false)", name) or \
         re.search(r"(attn_fwd_bf16(?:_pair|_short)?_kernel|proj_gemm_kernel|bwd_dkdv_kernel|bwd_dq_kernel)ILb(\d)", name)
     if m:
@@ -321,9 +336,10 @@ def _short_kernel(name: str) -> str:
 
 # Grid sizes (threads) of each leg's launches, to tell apart launches of the
 # same kernel in a trace of the default bench command.
-LEG_GRIDS = {("attn_fwd_bf16_short_kernel<false>", 65536): "encoder_base",
-             ("attn_fwd_bf16_short_kernel<true>", 131072): "decoder_big (causal self)",
-             ("attn_fwd_bf16_short_kernel<false>", 131072): "decoder_big (cross)",
+LEG_GRIDS = {("attn_fwd_bf16_short_kernel<none>", 65536): "encoder_base",
+             ("attn_fwd_bf16_short_kernel<causal>", 131072): "decoder_big (causal self)",
+             ("attn_fwd_bf16_short_kernel<none>", 131072): "decoder_big (cross)",
+             ("attn_fwd_bf16_pair_kernel<band>", 262144): "long_restricted",
              ("cache_append_kernel", 8192): "kv_append",
              ("bwd_dkdv_kernel<true>", 262144): "long_causal_bwd",
              ("bwd_dq_kernel<true>", 262144): "long_causal_bwd",
@@ -340,7 +356,7 @@ LEG_GRIDS = {("attn_fwd_bf16_short_kernel<false>", 65536): "encoder_base",
              ("proj_gemm_kernel<true>", 65536): "mha_proj (cross Q)",
              ("proj_gemm_kernel<true>", 163840): "mha_proj (cross K, V)",
              ("proj_gemm_kernel<false>", 65536): "mha_proj (self and cross output)",
-             ("attn_fwd_bf16_pair_kernel<true>", 262144): "long_causal",
+             ("attn_fwd_bf16_pair_kernel<causal>", 262144): "long_causal",
              ("decode_partial_kernel", 4194304): "kv_decode",
              ("decode_merge_kernel", 65536): "kv_decode"}
 
@@ -396,7 +412,7 @@ def summarize_counters(fetch_csv: str, write_csv: str, copy_mib: int, out_json: 
                      f"{write.get(k, 0.0):.1f} | {rd:.2f} | {wr:.2f} |")
         res[f"{k[0]}@{k[1]}"] = {"read_bytes": rd * 1e6, "write_bytes": wr * 1e6}
     if out_json:
-        lc = res.get("attn_fwd_bf16_pair_kernel<true>@262144")
+        lc = res.get("attn_fwd_bf16_pair_kernel<causal>@262144")
         with open(out_json, "w") as f:
             json.dump({"kernel_source_hash": kernel_source_hash(),
                        "fetch_scale": f_fetch, "write_scale": f_write,
@@ -468,7 +484,7 @@ def main():
     leg_ms = [sum(ev[s][j][0].elapsed_time(ev[s][j][1]) for s in range(args.steps)) / args.steps
               for j in range(len(legs))]
     step_ms = sum(leg_ms)
-    fwd = [j for j, leg in enumerate(legs) if leg.dev_calls and not leg.bwd]
+    fwd = [j for j, leg in enumerate(legs) if leg.dev_calls and not leg.bwd and leg.in_value]
     fwd_flops = sum(legs[j].flops for j in fwd)
     fwd_ms = sum(leg_ms[j] for j in fwd)
     value = fwd_flops / (fwd_ms * 1e-3) / 1e12
@@ -546,6 +562,14 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
         },
+        "roofline_restricted": {
+            "bound": "mfma",
+            "kernel": "attn_fwd_bf16_pair_kernel<band> on long_restricted (B1 h16 n8192, radius 256)",
+            "achieved": round(legs[[l.name for l in legs].index("long_restricted")].flops
+                              / (leg_ms[[l.name for l in legs].index("long_restricted")] * 1e-3) / 1e12, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+        },
         "roofline_decode": {
             "bound": "hbm",
             "kernel": "decode_partial_kernel + decode_merge_kernel on kv_decode",
@@ -557,6 +581,7 @@ def main():
     }
     out["roofline_proj"]["frac"] = round(out["roofline_proj"]["achieved"] / PEAK_BF16_TFLOPS, 4)
     out["roofline_bwd"]["frac"] = round(out["roofline_bwd"]["achieved"] / PEAK_BF16_TFLOPS, 4)
+    out["roofline_restricted"]["frac"] = round(out["roofline_restricted"]["achieved"] / PEAK_BF16_TFLOPS, 4)
     if args.copy_probe_mib:
         src = torch.ones(args.copy_probe_mib * 2 ** 18, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)

@@ -13,6 +13,7 @@ from ._binding import (  # noqa: F401
     ATTN_MASK_CAUSAL,
     ATTN_MASK_KEY_PADDING,
     ATTN_MASK_NONE,
+    ATTN_MASK_RESTRICTED,
     LIB_PATH,
     AttnError,
     attn_layout,
@@ -21,6 +22,7 @@ from ._binding import (  # noqa: F401
     decode,
     decode_workspace_bytes,
     forward,
+    forward_restricted,
     head_projection,
     lib,
     output_projection,

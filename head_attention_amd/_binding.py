@@ -22,6 +22,7 @@ ATTN_F32 = 1
 ATTN_MASK_NONE = 0
 ATTN_MASK_KEY_PADDING = 1
 ATTN_MASK_CAUSAL = 2
+ATTN_MASK_RESTRICTED = 4
 
 STATUS_NAMES = {
     0: "ATTN_OK", 1: "ATTN_ERR_NULL_POINTER", 2: "ATTN_ERR_BAD_SHAPE", 3: "ATTN_ERR_BAD_DTYPE",
@@ -72,6 +73,9 @@ def lib() -> ctypes.CDLL:
         L.attn_forward_lse.argtypes = [vp, vp, vp, attn_layout, ctypes.c_int32, i32p, i32p,
                                        ctypes.c_float, vp, vp, vp]
         L.attn_forward_lse.restype = ctypes.c_int
+        L.attn_forward_restricted.argtypes = [vp, vp, vp, attn_layout, ctypes.c_int32, i32p, i32p,
+                                              ctypes.c_int32, ctypes.c_float, vp, vp, vp]
+        L.attn_forward_restricted.restype = ctypes.c_int
         L.attn_backward.argtypes = [vp, vp, vp, vp, vp, vp, attn_layout, ctypes.c_int32, i32p, i32p,
                                     ctypes.c_float, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.attn_backward.restype = ctypes.c_int
@@ -180,6 +184,46 @@ def forward(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, mask_kind: int = 
                                 float(scale), out.data_ptr(), lse.data_ptr(), _stream_handle(stream, Q))
     if st != 0:
         raise AttnError(st, "attn_forward_lse")
+    return out
+
+
+def forward_restricted(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, radius: int,
+                       mask_kind: int = ATTN_MASK_RESTRICTED, q_lens: torch.Tensor | None = None,
+                       kv_lens: torch.Tensor | None = None, scale: float | None = None,
+                       out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                       stream=None) -> torch.Tensor:
+    """attn_forward_restricted: restricted self-attention, query i sees keys
+    i - radius .. i + radius (i - radius .. i when mask_kind has
+    ATTN_MASK_CAUSAL).  mask_kind must hold ATTN_MASK_RESTRICTED; n_q == n_k.
+    Tensors as for forward(); lse (fp32 [B, h, n_q]) is optional."""
+    dt = Q.dtype
+    for n, t in (("Q", Q), ("K", K), ("V", V)):
+        _check_tensor(n, t, dt)
+    B, H, n_q, d = Q.shape
+    n_k = K.shape[2]
+    if K.shape != (B, H, n_k, d) or V.shape != (B, H, n_k, d):
+        raise ValueError(f"K {tuple(K.shape)} / V {tuple(V.shape)} do not match Q {tuple(Q.shape)}")
+    if out is None:
+        out = torch.empty_like(Q)
+    else:
+        _check_tensor("out", out, dt)
+        if out.shape != Q.shape:
+            raise ValueError("out must have Q's shape")
+    lse_ptr = None
+    if lse is not None:
+        _check_tensor("lse", lse, torch.float32, 3)
+        if lse.shape != (B, H, n_q):
+            raise ValueError("lse must be [B, h, n_q]")
+        lse_ptr = lse.data_ptr()
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    layout = attn_layout(B, H, n_q, n_k, d, _dtype_code(Q))
+    st = lib().attn_forward_restricted(Q.data_ptr(), K.data_ptr(), V.data_ptr(), layout, int(mask_kind),
+                                       _lens_ptr("q_lens", q_lens, B), _lens_ptr("kv_lens", kv_lens, B),
+                                       int(radius), float(scale), out.data_ptr(), lse_ptr,
+                                       _stream_handle(stream, Q))
+    if st != 0:
+        raise AttnError(st, "attn_forward_restricted")
     return out
 
 

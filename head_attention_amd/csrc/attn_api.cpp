@@ -76,7 +76,8 @@ const char* attn_status_string(attn_status status) {
     case ATTN_ERR_BAD_SHAPE: return "ATTN_ERR_BAD_SHAPE: negative size, d != 64, or size overflow";
     case ATTN_ERR_BAD_DTYPE: return "ATTN_ERR_BAD_DTYPE: dtype must be ATTN_BF16 or ATTN_F32";
     case ATTN_ERR_BAD_MASK:
-      return "ATTN_ERR_BAD_MASK: unknown mask bits, causal with n_q != n_k, or kv_lens "
+      return "ATTN_ERR_BAD_MASK: unknown mask bits, causal or restricted with n_q != n_k, a "
+             "negative radius or ATTN_MASK_RESTRICTED outside attn_forward_restricted, or kv_lens "
              "given/missing against ATTN_MASK_KEY_PADDING";
     case ATTN_ERR_BAD_LENGTHS: return "ATTN_ERR_BAD_LENGTHS: a length is outside [0, n]";
     case ATTN_ERR_BAD_SCALE: return "ATTN_ERR_BAD_SCALE: scale must be finite";
@@ -90,15 +91,19 @@ const char* attn_last_hip_error(void) { return hipGetErrorName(g_last_hip); }
 
 namespace {
 
+// radius < 0: no restriction (mask_kind must not hold ATTN_MASK_RESTRICTED);
+// radius >= 0: restricted self-attention (mask_kind must hold it).
 attn_status forward_impl(const void* Q, const void* K, const void* V, attn_layout layout,
                          int32_t mask_kind, const int32_t* q_lens, const int32_t* kv_lens,
-                         float scale, void* O, float* lse, void* stream) {
+                         float scale, void* O, float* lse, int32_t radius, void* stream) {
   attn_status st = check_layout(layout);
   if (st != ATTN_OK) return st;
-  if (mask_kind & ~(ATTN_MASK_KEY_PADDING | ATTN_MASK_CAUSAL)) return ATTN_ERR_BAD_MASK;
+  if (mask_kind & ~(ATTN_MASK_KEY_PADDING | ATTN_MASK_CAUSAL | ATTN_MASK_RESTRICTED)) return ATTN_ERR_BAD_MASK;
   const bool kpad = (mask_kind & ATTN_MASK_KEY_PADDING) != 0;
   const bool causal = (mask_kind & ATTN_MASK_CAUSAL) != 0;
-  if (causal && layout.n_q != layout.n_k) return ATTN_ERR_BAD_MASK;
+  const bool restricted = (mask_kind & ATTN_MASK_RESTRICTED) != 0;
+  if (restricted != (radius >= 0)) return ATTN_ERR_BAD_MASK;
+  if ((causal || restricted) && layout.n_q != layout.n_k) return ATTN_ERR_BAD_MASK;
   if (!kpad && kv_lens != nullptr) return ATTN_ERR_BAD_MASK;
   if (!std::isfinite(scale)) return ATTN_ERR_BAD_SCALE;
   const bool empty_out = layout.B == 0 || layout.h == 0 || layout.n_q == 0;
@@ -133,10 +138,12 @@ attn_status forward_impl(const void* Q, const void* K, const void* V, attn_layou
   a.scale = scale;
   a.causal = causal;
   a.lse = lse;
+  // A radius of n_k or more already spans every key.
+  a.radius = restricted ? std::min(radius, layout.n_k) : -1;
   hipError_t e;
   if (layout.dtype == ATTN_F32) e = launch_fwd_f32(a, s);
   else if (layout.n_k <= kShortMaxKeys) e = launch_fwd_bf16_short(a, s);
-  else if (layout.n_q >= kPairMinRows) e = launch_fwd_bf16_pair(a, s);
+  else if (layout.n_q >= kPairMinRows || restricted) e = launch_fwd_bf16_pair(a, s);
   else e = launch_fwd_bf16(a, s);
   if (e != hipSuccess) {
     g_last_hip = e;
@@ -150,7 +157,7 @@ attn_status forward_impl(const void* Q, const void* K, const void* V, attn_layou
 attn_status attn_forward(const void* Q, const void* K, const void* V, attn_layout layout,
                          int32_t mask_kind, const int32_t* q_lens, const int32_t* kv_lens,
                          float scale, void* O, void* stream) {
-  return forward_impl(Q, K, V, layout, mask_kind, q_lens, kv_lens, scale, O, nullptr, stream);
+  return forward_impl(Q, K, V, layout, mask_kind, q_lens, kv_lens, scale, O, nullptr, -1, stream);
 }
 
 attn_status attn_forward_lse(const void* Q, const void* K, const void* V, attn_layout layout,
@@ -158,7 +165,14 @@ attn_status attn_forward_lse(const void* Q, const void* K, const void* V, attn_l
                              float scale, void* O, float* LSE, void* stream) {
   if (!LSE && layout.B > 0 && layout.h > 0 && layout.n_q > 0 && check_layout(layout) == ATTN_OK)
     return ATTN_ERR_NULL_POINTER;
-  return forward_impl(Q, K, V, layout, mask_kind, q_lens, kv_lens, scale, O, LSE, stream);
+  return forward_impl(Q, K, V, layout, mask_kind, q_lens, kv_lens, scale, O, LSE, -1, stream);
+}
+
+attn_status attn_forward_restricted(const void* Q, const void* K, const void* V, attn_layout layout,
+                                    int32_t mask_kind, const int32_t* q_lens, const int32_t* kv_lens,
+                                    int32_t radius, float scale, void* O, float* LSE, void* stream) {
+  if (radius < 0) return ATTN_ERR_BAD_MASK;
+  return forward_impl(Q, K, V, layout, mask_kind, q_lens, kv_lens, scale, O, LSE, radius, stream);
 }
 
 attn_status attn_cache_append(const void* Knew, const void* Vnew, void* Kcache, void* Vcache,

@@ -172,8 +172,10 @@ __device__ __forceinline__ void barrier_lds() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <bool CAUSAL>
+template <int MODE>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_pair_kernel(FwdArgs a) {
+  constexpr bool CAUSAL = MODE == kModeCausal;
+  constexpr bool BAND = MODE == kModeBand;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
@@ -211,16 +213,28 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_pair_kernel(FwdArgs
   const int q0 = qt * kBM;
   const int qw0 = q0 + kWaveRows * rg;  // first query row of this wave
 
+  // Restricted self-attention: row i sees keys i - wl .. i + wr.  The
+  // workgroup then starts at key tile t0 (tile indices below are relative
+  // to it) and a row group skips the tiles wholly before its rows' windows.
+  const int wl = BAND ? a.radius : 0;
+  const int wr = BAND ? (a.causal ? 0 : a.radius) : 0;
+  const int t0 = BAND ? max(0, q0 - wl) / kBN : 0;
   int end = kv_lim;  // keys the workgroup needs
   if (CAUSAL) end = min(end, q0 + kBM);
+  if (BAND) end = min(end, q0 + kBM + wr);
   if (q0 >= q_len) end = 0;
-  const int n_tiles = (end + kBN - 1) / kBN;
+  const int n_tiles = max(0, (end + kBN - 1) / kBN - t0);
   int wave_end = end;  // keys this row group needs
   if (CAUSAL) wave_end = min(wave_end, qw0 + kWaveRows);
+  if (BAND) wave_end = min(wave_end, qw0 + kWaveRows + wr);
   if (qw0 >= q_len) wave_end = 0;
-  const int wave_tiles = (wave_end + kBN - 1) / kBN;
+  const int wave_tiles = max(0, (wave_end + kBN - 1) / kBN - t0);
+  const int wave_first = BAND ? max(0, qw0 - wl) / kBN - t0 : 0;
 
-  const uint32_t n_bytes = (uint32_t)kv_lim * kRowBytes;
+  const int k_base = t0 * kBN;  // first key of relative tile 0
+  K += (size_t)k_base * kHeadDim;
+  V += (size_t)k_base * kHeadDim;
+  const uint32_t n_bytes = (uint32_t)max(0, kv_lim - k_base) * kRowBytes;
   const __amdgpu_buffer_rsrc_t rk =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(K), (short)0, (int)n_bytes, kBufferWord3);
   const __amdgpu_buffer_rsrc_t rv =
@@ -382,18 +396,23 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_pair_kernel(FwdArgs
   // A fully masked row (max -inf) and NaN (garbage in padded query rows)
   // never move.
   auto softmax = [&](int t) __attribute__((always_inline)) {
-    const int k0 = t * kBN;
-    const bool need_mask = (k0 + kBN > kv_lim) || (CAUSAL && k0 + kBN - 1 > qw0);
+    const int k0 = k_base + t * kBN;
+    bool need_mask = (k0 + kBN > kv_lim) || (CAUSAL && k0 + kBN - 1 > qw0);
+    if (BAND) need_mask = need_mask || (k0 + kBN - 1 > qw0 + wr) || (k0 < qw0 + kWaveRows - 1 - wl);
     if (need_mask) {
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         const int qi = qw0 + 32 * qb + ln;
-        const int lim = (CAUSAL ? min(kv_lim, qi + 1) : kv_lim) - k0 - 4 * hh;
+        int hi = kv_lim;  // keys below hi and at or above lo are allowed
+        if (CAUSAL) hi = min(hi, qi + 1);
+        if (BAND) hi = min(hi, qi + wr + 1);
+        const int lim = hi - k0 - 4 * hh;
+        const int lo = BAND ? qi - wl - k0 - 4 * hh : INT_MIN;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int off = 8 * (r >> 2) + (r & 3);
-          sc[0][qb][r] = off < lim ? sc[0][qb][r] : -INFINITY;
-          sc[1][qb][r] = off + 32 < lim ? sc[1][qb][r] : -INFINITY;
+          sc[0][qb][r] = (off < lim && off >= lo) ? sc[0][qb][r] : -INFINITY;
+          sc[1][qb][r] = (off + 32 < lim && off + 32 >= lo) ? sc[1][qb][r] : -INFINITY;
         }
       }
     }
@@ -504,7 +523,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_pair_kernel(FwdArgs
   // Vector phase of tile t: the weights of tile t, or zero weights for a
   // phase before this wave's first tile or past its last.
   auto vphase = [&](int t) __attribute__((always_inline)) {
-    if (t >= 0 && t < wave_tiles) {
+    if (t >= wave_first && t < wave_tiles) {
       softmax(t);
     } else {
 #pragma unroll
@@ -631,8 +650,10 @@ hipError_t launch_fwd_bf16_pair(const FwdArgs& a, hipStream_t s) {
   const long long blocks = (long long)n_qt * a.H * a.B;
   FwdArgs args = a;
   void* kargs[] = {&args};
-  const void* fn = a.causal ? reinterpret_cast<const void*>(&attn_fwd_bf16_pair_kernel<true>)
-                            : reinterpret_cast<const void*>(&attn_fwd_bf16_pair_kernel<false>);
+  const int mode = fwd_mode(a);
+  const void* fn = mode == kModeBand     ? reinterpret_cast<const void*>(&attn_fwd_bf16_pair_kernel<kModeBand>)
+                   : mode == kModeCausal ? reinterpret_cast<const void*>(&attn_fwd_bf16_pair_kernel<kModeCausal>)
+                                         : reinterpret_cast<const void*>(&attn_fwd_bf16_pair_kernel<kModeNone>);
   return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(kThreads), kargs, 0, s);
 }
 

@@ -92,8 +92,10 @@ __device__ __forceinline__ float exp_pack_sum(const f32x16& s0, const f32x16& s1
   return acc0 + acc1;
 }
 
-template <bool CAUSAL>
+template <int MODE>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_short_kernel(FwdArgs a) {
+  constexpr bool CAUSAL = MODE == kModeCausal;
+  constexpr bool BAND = MODE == kModeBand;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
@@ -130,14 +132,21 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_short_kernel(FwdArg
   const int qw0 = q0 + 32 * wave;  // first query row of this wave
   const int qi = qw0 + ln;         // query row of this lane
 
+  // Restricted self-attention: row i sees keys i - wl .. i + wr; a wave
+  // starts at the first tile its rows' windows reach.
+  const int wl = BAND ? a.radius : 0;
+  const int wr = BAND ? (a.causal ? 0 : a.radius) : 0;
   int end = kv_lim;  // keys the workgroup needs (at most n_k <= 256)
   if (CAUSAL) end = min(end, q0 + kBM);
+  if (BAND) end = min(end, q0 + kBM + wr);
   if (q0 >= q_len) end = 0;
   const int n_tiles = min((end + kBN - 1) / kBN, kMaxTiles);  // the host sends n_k <= 256 only
   int wave_end = min(end, kShortMaxKeys);  // keys this wave needs
   if (CAUSAL) wave_end = min(wave_end, qw0 + 32);
+  if (BAND) wave_end = min(wave_end, qw0 + 32 + wr);
   if (qw0 >= q_len) wave_end = 0;
   const int wave_tiles = (wave_end + kBN - 1) / kBN;
+  const int wave_first = BAND ? max(0, qw0 - wl) / kBN : 0;
 
   // ---- all loads at once.  Q: B operand of S^T = K Q^T, lane (ln, hh)
   // holds Q[qi][16 s + 8 hh + 0..7], sign of scale folded in; c = |scale|
@@ -189,9 +198,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_short_kernel(FwdArg
   float mc = 0.f;           // pivot term of the exponent, m * c
   float l = 0.f;            // this half-wave's partial row sum of bf16 weights
 
+  // Band mode: whether the row has summed a nonzero weight yet (its pivot
+  // may move down only before that); both half-waves of a row agree.  The
+  // other modes need no flag: tile 0 holds key 0, which every row with a key
+  // may see.
+  bool seen = false;
+
   const int g = lane >> 4;
   const int i16 = lane & 15;
-  for (int t = 0; t < wave_tiles; ++t) {
+  for (int t = wave_first; t < wave_tiles; ++t) {
     // S^T = K Q^T: lane (ln, hh) of key block kb reads K[64 t + 32 kb + ln]
     // [16 s + 8 hh + 0..7].
     const uint4* kt = s_k + t * kTileChunks;
@@ -230,13 +245,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_short_kernel(FwdArg
     // key-length boundary: register r of block kb holds key 64 t + 32 kb +
     // 8 (r / 4) + 4 hh + r % 4.
     const int k0 = t * kBN;
-    if ((k0 + kBN > kv_lim) || (CAUSAL && k0 + kBN - 1 > qw0)) {
-      const int lim = (CAUSAL ? min(kv_lim, qi + 1) : kv_lim) - k0 - 4 * hh;
+    bool need_mask = (k0 + kBN > kv_lim) || (CAUSAL && k0 + kBN - 1 > qw0);
+    if (BAND) need_mask = need_mask || (k0 + kBN - 1 > qw0 + wr) || (k0 < qw0 + 31 - wl);
+    if (need_mask) {
+      int hi = kv_lim;  // keys below hi and at or above lo are allowed
+      if (CAUSAL) hi = min(hi, qi + 1);
+      if (BAND) hi = min(hi, qi + wr + 1);
+      const int lim = hi - k0 - 4 * hh;
+      const int lo = BAND ? qi - wl - k0 - 4 * hh : INT_MIN;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int off = 8 * (r >> 2) + (r & 3);
-        s0[r] = off < lim ? s0[r] : -INFINITY;
-        s1[r] = off + 32 < lim ? s1[r] : -INFINITY;
+        s0[r] = (off < lim && off >= lo) ? s0[r] : -INFINITY;
+        s1[r] = (off + 32 < lim && off + 32 >= lo) ? s1[r] : -INFINITY;
       }
     }
     uint32_t pk[16];
@@ -248,7 +269,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_short_kernel(FwdArg
     // and l are 0: scale 1), and the tile's weights are recomputed.  NaN
     // (garbage in padded rows) triggers neither check.
     bool move = lt > kPivotHigh;
-    if (t == 0) move = move || half_swap_sum(lt) < kPivotLow;
+    if (!BAND && t == 0) move = move || half_swap_sum(lt) < kPivotLow;
+    if (BAND && __builtin_amdgcn_ballot_w64(!seen) != 0) {
+      // A row that has summed nothing yet: a sum this small would be lost
+      // to underflow (all-masked tiles give 0 and a max of -inf: no move).
+      const float row_lt = half_swap_sum(lt);
+      move = move || (!seen && row_lt < kPivotLow);
+      seen = seen || row_lt > 0.f;
+    }
     if (__builtin_amdgcn_ballot_w64(move) != 0) {
       move = half_swap_or(move);  // both half-waves of a row must agree
       float tmax = fmaxf(s0[0], s1[0]);
@@ -262,6 +290,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_short_kernel(FwdArg
       o1 *= alpha;
       mc = m_new;
       lt = exp_pack_sum(s0, s1, c, mc, pk);
+      if (BAND) seen = seen || tm > -INFINITY;  // the tile max now weighs 1
     }
     l += lt;
 
@@ -308,8 +337,10 @@ hipError_t launch_fwd_bf16_short(const FwdArgs& a, hipStream_t s) {
   const long long blocks = (long long)n_qt * a.H * a.B;
   FwdArgs args = a;
   void* kargs[] = {&args};
-  const void* fn = a.causal ? reinterpret_cast<const void*>(&attn_fwd_bf16_short_kernel<true>)
-                            : reinterpret_cast<const void*>(&attn_fwd_bf16_short_kernel<false>);
+  const int mode = fwd_mode(a);
+  const void* fn = mode == kModeBand     ? reinterpret_cast<const void*>(&attn_fwd_bf16_short_kernel<kModeBand>)
+                   : mode == kModeCausal ? reinterpret_cast<const void*>(&attn_fwd_bf16_short_kernel<kModeCausal>)
+                                         : reinterpret_cast<const void*>(&attn_fwd_bf16_short_kernel<kModeNone>);
   return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(kThreads), kargs, 0, s);
 }
 

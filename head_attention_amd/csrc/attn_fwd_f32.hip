@@ -39,11 +39,17 @@ __global__ __launch_bounds__(64) void attn_fwd_f32_kernel(FwdArgs a) {
   const int q_len = a.q_lens ? clamp_len(a.q_lens[b], a.n_q) : a.n_q;
   const int kv_lim = a.kv_lens ? clamp_len(a.kv_lens[b], a.n_k) : a.n_k;
   const bool row_ok = i < q_len;  // q_len <= n_q
-  // Keys any row of this tile may attend to.
+  // Restricted self-attention: row i sees keys i - wl .. i + wr.
+  const bool band = a.radius >= 0;
+  const int wl = band ? a.radius : 0;
+  const int wr = band ? (a.causal ? 0 : a.radius) : 0;
+  // Keys any row of this tile may attend to: [start, end).
   int end = kv_lim;
   if (a.causal) end = min(end, qt * kRows + kRows);
+  if (band) end = min(end, qt * kRows + kRows + wr);
   // Whole tile padded (all rows >= q_len): nothing to compute.
   if (qt * kRows >= q_len) end = 0;
+  const int start = band ? max(0, qt * kRows - wl) : 0;
 
   __shared__ float4 Ks[kKeys * kHeadDim / 4];
   __shared__ float4 Vs[kKeys * kHeadDim / 4];
@@ -66,7 +72,7 @@ __global__ __launch_bounds__(64) void attn_fwd_f32_kernel(FwdArgs a) {
   const float c = a.scale * kLog2e;  // logits in the log2 domain
   float m = -INFINITY, l = 0.f;
 
-  for (int k0 = 0; k0 < end; k0 += kKeys) {
+  for (int k0 = start; k0 < end; k0 += kKeys) {
     __syncthreads();  // previous tile fully consumed
     // Coalesced tile load: 64 lanes x 16 B per step, 16 steps per tensor.
     // Rows at or beyond kv_lim are zero-filled and never read from memory.
@@ -89,7 +95,8 @@ __global__ __launch_bounds__(64) void attn_fwd_f32_kernel(FwdArgs a) {
     const int n_here = min(kKeys, end - k0);
     for (int j = 0; j < n_here; ++j) {
       const int key = k0 + j;
-      const bool ok = row_ok && key < kv_lim && (!a.causal || key <= i);
+      const bool ok = row_ok && key < kv_lim && (!a.causal || key <= i) &&
+                      (!band || (key >= i - wl && key <= i + wr));
       if (!ok) continue;
       float dot = 0.f;
 #pragma unroll

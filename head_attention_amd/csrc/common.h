@@ -3,6 +3,8 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include <climits>
 #include <stdint.h>
 
 namespace headattn {
@@ -26,7 +28,18 @@ struct FwdArgs {
   float scale;             // multiplies Q K^T; finite
   bool causal;
   float* lse;              // device fp32 [B*H*n_q] or nullptr: per-row log-sum-exp
+  // Restricted self-attention: -1 = off; else row i sees only keys
+  // i - radius .. i + radius (i - radius .. i with causal), 0 <= radius <= n_k.
+  int radius;
 };
+
+// Mask shapes the bf16 forward kernels are specialised for: none (key
+// padding only), the causal triangle, and the band of restricted
+// self-attention (keys i - radius .. i + radius, or i - radius .. i).
+enum FwdMode : int { kModeNone = 0, kModeCausal = 1, kModeBand = 2 };
+inline int fwd_mode(const FwdArgs& a) {
+  return a.radius >= 0 ? kModeBand : (a.causal ? kModeCausal : kModeNone);
+}
 
 // ln(2): a row's log-sum-exp in natural units from its log2-domain pivot m
 // and sum l is (m + log2 l) ln 2.

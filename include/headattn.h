@@ -75,12 +75,18 @@ typedef struct {
  * Causal (kimjiil page §3.2.3 and §3.1; sj-techlog page, section "mask는
  * softmax 전에 더해야 한다", 4x4 table): key j is excluded for query i when
  * j > i (top-left aligned; requires n_q == n_k).
+ * Restricted (attn_forward_restricted only; kimjiil page §4, Table 1: each
+ * position attends to a neighbourhood of r positions around it, O(r n d)
+ * work): key j is excluded for query i when |i - j| > radius, so a row sees
+ * r = 2 radius + 1 keys, or radius + 1 (i - radius .. i) together with
+ * causal; requires n_q == n_k.
  * An excluded key gets logit -inf before the softmax: its weight is exactly 0
  * and its K/V contents (even NaN) never reach O. */
 enum {
   ATTN_MASK_NONE = 0,
   ATTN_MASK_KEY_PADDING = 1,
-  ATTN_MASK_CAUSAL = 2
+  ATTN_MASK_CAUSAL = 2,
+  ATTN_MASK_RESTRICTED = 4
 };
 
 typedef enum {
@@ -89,8 +95,11 @@ typedef enum {
   ATTN_ERR_BAD_SHAPE = 2,    /* negative size, d != 64, size overflow, n_q != 1
                                 for decode, or an input pointer equal to O    */
   ATTN_ERR_BAD_DTYPE = 3,    /* dtype not an attn_dtype                       */
-  ATTN_ERR_BAD_MASK = 4,     /* unknown bits; causal with n_q != n_k; kv_lens
-                                given without ATTN_MASK_KEY_PADDING           */
+  ATTN_ERR_BAD_MASK = 4,     /* unknown bits; causal or restricted with
+                                n_q != n_k; ATTN_MASK_RESTRICTED outside
+                                attn_forward_restricted (or missing there);
+                                radius < 0; kv_lens given without
+                                ATTN_MASK_KEY_PADDING                         */
   ATTN_ERR_BAD_LENGTHS = 5,  /* (ATTN_CHECK=1 only) a length outside [0, n]   */
   ATTN_ERR_BAD_SCALE = 6,    /* scale is not finite                           */
   ATTN_ERR_WORKSPACE = 7,    /* decode workspace NULL or smaller than needed  */
@@ -138,6 +147,28 @@ attn_status attn_forward_lse(const void* Q, const void* K, const void* V,
                              attn_layout layout, int32_t mask_kind,
                              const int32_t* q_lens, const int32_t* kv_lens,
                              float scale, void* O, float* LSE, void* stream);
+
+/*
+ * attn_forward_restricted -- restricted self-attention (kimjiil page §4,
+ * Table 1 and the note under it): attn_forward where query i attends only
+ * to keys i - radius .. i + radius (i - radius .. i with ATTN_MASK_CAUSAL),
+ * so the work per row is O(r d) with r = 2 radius + 1 instead of O(n d).
+ *
+ *   mask_kind  ATTN_MASK_RESTRICTED, optionally with ATTN_MASK_KEY_PADDING
+ *              and ATTN_MASK_CAUSAL; n_q must equal n_k.
+ *   radius     >= 0; a radius of n_k - 1 or more is plain (or causal)
+ *              self-attention.  radius 0 gives O = V on every valid row.
+ *   LSE        device fp32 [B, h, n_q] or NULL; when given, written as by
+ *              attn_forward_lse (over the row's window).
+ * Q, K, V, layout, q_lens, kv_lens, scale, O and stream are those of
+ * attn_forward; so are the numerics and the error behaviour.  A row whose
+ * window holds no valid key (key padding) is written as 0.
+ */
+attn_status attn_forward_restricted(const void* Q, const void* K, const void* V,
+                                    attn_layout layout, int32_t mask_kind,
+                                    const int32_t* q_lens, const int32_t* kv_lens,
+                                    int32_t radius, float scale, void* O,
+                                    float* LSE, void* stream);
 
 /*
  * attn_decode -- one KV-cache decode step: for each (b, h) the single new

@@ -29,7 +29,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("attn_forward", "attn_forward_lse", "attn_backward", "attn_backward_workspace_bytes",
+    for n in ("attn_forward", "attn_forward_lse", "attn_forward_restricted",
+              "attn_backward", "attn_backward_workspace_bytes",
               "attn_decode", "attn_cache_append", "attn_head_projection",
               "attn_output_projection", "attn_decode_workspace_bytes",
               "attn_status_string", "attn_last_hip_error"):
@@ -217,3 +218,32 @@ def test_header_is_plain_c():
                         "-x", "c", "-", "-o", os.devnull], input=src.encode(),
                        capture_output=True)
     assert r.returncode == 0, r.stderr.decode()
+
+
+def test_forward_restricted_validation():
+    """Argument checks of attn_forward_restricted; every call here is
+    rejected (or empty) before any launch."""
+    L = ha.lib()
+    lay_ = attn_layout(2, 3, 16, 16, 64, BF16)
+
+    def rf(lay, mask=4, radius=3, ql=None, kl=None, scale=0.125, q=FAKE, k=FAKE + 16, v=FAKE + 32,
+           o=FAKE + 48, lse=None):
+        return L.attn_forward_restricted(q, k, v, lay, mask, ql, kl, radius, scale, o, lse, None)
+    assert rf(lay_, mask=0) == MASK                                  # the restricted bit is required
+    assert rf(lay_, mask=2) == MASK
+    assert rf(lay_, radius=-1) == MASK
+    assert rf(lay_, mask=4 | 8) == MASK                              # unknown bit
+    assert rf(attn_layout(2, 3, 16, 20, 64, BF16)) == MASK           # self-attention only: n_q == n_k
+    assert rf(lay_, mask=4, kl=FAKE) == MASK                         # kv_lens without padding
+    assert rf(lay_, mask=5) == NULLP                                 # padding without kv_lens
+    assert rf(lay_, scale=float("inf")) == SCALE
+    assert rf(attn_layout(2, 3, 16, 16, 32, BF16)) == SHAPE
+    assert rf(attn_layout(2, 3, 16, 16, 64, 7)) == DTYPE
+    assert rf(lay_, q=None) == NULLP and rf(lay_, o=None) == NULLP and rf(lay_, k=None) == NULLP
+    assert rf(lay_, o=FAKE) == SHAPE                                 # O aliases Q
+    assert rf(lay_, lse=FAKE + 48) == SHAPE                          # LSE aliases O
+    assert rf(attn_layout(0, 3, 16, 16, 64, BF16), q=None, k=None, v=None, o=None) == OK
+    # the restricted bit is refused by the entry points without a radius
+    assert L.attn_forward(FAKE, FAKE + 16, FAKE + 32, lay_, 4, None, None, 0.125, FAKE + 48, None) == MASK
+    assert L.attn_forward_lse(FAKE, FAKE + 16, FAKE + 32, lay_, 6, None, None, 0.125, FAKE + 48, FAKE + 64,
+                              None) == MASK

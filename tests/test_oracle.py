@@ -664,3 +664,25 @@ def test_flop_model_long_causal():
     pairs = workloads.allowed_pairs(2, 8192, 8192, 1)
     assert pairs == 8192 * 8193 // 2
     assert orc_mod.attention_flops(pairs * 16, 64) == 137_455_730_688
+
+
+def test_pair_count_restricted():
+    """The counting of the flop model for restricted self-attention agrees
+    with the oracle's own masks by brute force (kimjiil page §4 Table 1:
+    O(r n d) work with r = 2 radius + 1), including key padding, query
+    padding and the causal half-window."""
+    import workloads
+    rng = np.random.default_rng(99)
+    for trial in range(30):
+        B, n = int(rng.integers(1, 4)), int(rng.integers(1, 40))
+        radius = int(rng.integers(0, 45))
+        mask = 4 | int(rng.integers(0, 4))
+        kl = rng.integers(0, n + 1, size=B) if mask & 1 else None
+        ql = rng.integers(0, n + 1, size=B)
+        want = 0
+        for b in range(B):
+            for i in range(int(ql[b])):
+                want += int(orc_mod.allowed_keys(i, n, n if kl is None else int(kl[b]), bool(mask & 2),
+                                                 radius).sum())
+        assert workloads.allowed_pairs(mask, n, n, B, ql, kl, radius=radius) == want, trial
+    assert workloads.allowed_pairs(4, 8192, 8192, 1, radius=256) == 8192 * 513 - 256 * 257

@@ -33,9 +33,11 @@ WORKLOADS = {
                        "source L in [16,160], B32 h16 d64, bf16"),
     "long_causal": (4, "causal self-attention B1 h16 n8192 d64, bf16"),
     "kv_decode": (5, "KV-cache decode, B64 h16, cache 4096, L in [1,4096], d64, bf16"),
+    "long_restricted": (6, "restricted self-attention B1 h16 n8192 d64, radius 256 "
+                           "(r = 513 keys per row), bf16"),
 }
 
-MASK_NONE, MASK_KEY_PADDING, MASK_CAUSAL = 0, 1, 2
+MASK_NONE, MASK_KEY_PADDING, MASK_CAUSAL, MASK_RESTRICTED = 0, 1, 2, 4
 
 
 def generator(seed: int) -> torch.Generator:
@@ -58,6 +60,7 @@ def make(name: str) -> dict:
 
     Each entry of the returned dict is one attention call:
       {"calls": [ {"Q","K","V","mask","q_lens","kv_lens","scale"} ... ]}
+    (restricted calls also carry "radius"),
     or, for the decode workload, {"q","Kcache","Vcache","kv_lens","scale"}.
     """
     num, _ = WORKLOADS[name]
@@ -94,13 +97,20 @@ def make(name: str) -> dict:
         Kc = randn(g, (64, 16, 4096, D))
         Vc = randn(g, (64, 16, 4096, D))
         return dict(q=q, Kcache=Kc, Vcache=Vc, kv_lens=L, scale=0.125)
+    if name == "long_restricted":
+        shp = (1, 16, 8192, D)
+        Q, K, V = (randn(g, shp) for _ in range(3))
+        return {"calls": [dict(Q=Q, K=K, V=V, mask=MASK_RESTRICTED, q_lens=None,
+                               kv_lens=None, scale=0.125, radius=256)]}
     raise KeyError(name)
 
 
-def allowed_pairs(mask: int, n_q: int, n_k: int, B: int, q_lens=None, kv_lens=None) -> int:
+def allowed_pairs(mask: int, n_q: int, n_k: int, B: int, q_lens=None, kv_lens=None,
+                  radius=None) -> int:
     """Number of (query, key) pairs a call actually computes, summed over the
-    batch (per head).  Counting only: rows beyond q_len and keys beyond kv_len
-    or in the causal future are excluded.  Used for the flop and byte models.
+    batch (per head).  Counting only: rows beyond q_len and keys beyond kv_len,
+    in the causal future or (restricted) farther than radius from the query
+    are excluded.  Used for the flop and byte models.
     """
     total = 0
     for b in range(B):
@@ -108,7 +118,12 @@ def allowed_pairs(mask: int, n_q: int, n_k: int, B: int, q_lens=None, kv_lens=No
         kl = n_k if not (mask & MASK_KEY_PADDING) else int(kv_lens[b])
         ql = max(0, min(ql, n_q))
         kl = max(0, min(kl, n_k))
-        if mask & MASK_CAUSAL:
+        if mask & MASK_RESTRICTED:
+            # row i sees keys max(0, i - radius) .. min(i or i + radius, kl - 1)
+            for i in range(ql):
+                hi = min(i if mask & MASK_CAUSAL else i + radius, kl - 1)
+                total += max(0, hi - max(0, i - radius) + 1)
+        elif mask & MASK_CAUSAL:
             # row i sees keys j <= i and j < kl
             total += sum(min(i + 1, kl) for i in range(ql))
         else:
