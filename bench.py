@@ -174,7 +174,9 @@ def to_device(legs):
                 ha.forward(dc["Q"], dc["K"], dc["V"], mask_kind=dc["mask"], q_lens=dc["q_lens"],
                            kv_lens=dc["kv_lens"], scale=dc["scale"], out=dc["O"], lse=dc["lse"])
                 dc["grads"] = (torch.empty_like(dc["Q"]), torch.empty_like(dc["K"]), torch.empty_like(dc["V"]))
-                dc["ws"] = torch.empty(B * H * n_q * 4, dtype=torch.uint8, device="cuda")
+                n_k = c["K"].shape[2]
+                dc["ws"] = torch.empty(ha.backward_workspace_bytes(B, H, n_q, n_k), dtype=torch.uint8,
+                                       device="cuda")
             leg.dev_calls.append(dc)
         leg.dev_proj = []
         for pc in leg.proj or []:
@@ -315,11 +317,12 @@ FWD_MODES = {"0": "none", "1": "causal", "2": "band"}
 
 
 def _short_kernel(name: str) -> str:
-    """attn_fwd_bf16[_pair|_short]_kernel<mode> -> ..._kernel<none|causal|band>;
+    """attn_fwd_bf16[_pair|_short]_kernel<mode> and the backward's dK/dV and dQ
+    kernels -> ..._kernel<none|causal|band>;
     the bool-templated kernels -> <true|false>; other kernels of the library by
     their plain name."""
     import re
-    m = re.search(r"(attn_fwd_bf16(?:_pair|_short)?_kernel)(?:<|ILi)(\d)", name)
+    m = re.search(r"(attn_fwd_bf16(?:_pair|_short)?_kernel|bwd_dkdv_kernel|bwd_dq_kernel)(?:<|ILi)(\d)", name)
     if m:
         return f"{m.group(1)}<{FWD_MODES[m.group(2)]}>"
     m = re.search(r"(attn_fwd_bf16(?:_pair|_short)?_kernel|proj_gemm_kernel|bwd_dkdv_kernel|bwd_dq_kernel)<(true|false)", name) or \
@@ -341,16 +344,16 @@ LEG_GRIDS = {("attn_fwd_bf16_short_kernel<none>", 65536): "encoder_base",
              ("attn_fwd_bf16_short_kernel<none>", 131072): "decoder_big (cross)",
              ("attn_fwd_bf16_pair_kernel<band>", 262144): "long_restricted",
              ("cache_append_kernel", 8192): "kv_append",
-             ("bwd_dkdv_kernel<true>", 262144): "long_causal_bwd",
-             ("bwd_dq_kernel<true>", 262144): "long_causal_bwd",
+             ("bwd_dkdv_kernel<causal>", 262144): "long_causal_bwd",
+             ("bwd_dq_kernel<causal>", 262144): "long_causal_bwd",
              ("bwd_rowdot_kernel", 1048576): "long_causal_bwd",
-             ("bwd_dkdv_kernel<false>", 65536): "encoder_base_bwd",
-             ("bwd_dq_kernel<false>", 65536): "encoder_base_bwd",
+             ("bwd_dkdv_kernel<none>", 65536): "encoder_base_bwd",
+             ("bwd_dq_kernel<none>", 65536): "encoder_base_bwd",
              ("bwd_rowdot_kernel", 262144): "encoder_base_bwd",
-             ("bwd_dkdv_kernel<true>", 131072): "decoder_big_bwd (causal self)",
-             ("bwd_dq_kernel<true>", 131072): "decoder_big_bwd (causal self)",
-             ("bwd_dkdv_kernel<false>", 262144): "decoder_big_bwd (cross)",
-             ("bwd_dq_kernel<false>", 131072): "decoder_big_bwd (cross)",
+             ("bwd_dkdv_kernel<causal>", 131072): "decoder_big_bwd (causal self)",
+             ("bwd_dq_kernel<causal>", 131072): "decoder_big_bwd (causal self)",
+             ("bwd_dkdv_kernel<none>", 262144): "decoder_big_bwd (cross)",
+             ("bwd_dq_kernel<none>", 131072): "decoder_big_bwd (cross)",
              ("bwd_rowdot_kernel", 524288): "decoder_big_bwd (self and cross)",
              ("proj_gemm_kernel<true>", 196608): "mha_proj (self Q, K, V)",
              ("proj_gemm_kernel<true>", 65536): "mha_proj (cross Q)",

@@ -18,6 +18,7 @@ from ._binding import (  # noqa: F401
     AttnError,
     attn_layout,
     backward,
+    backward_workspace_bytes,
     cache_append,
     decode,
     decode_workspace_bytes,

@@ -79,6 +79,10 @@ def lib() -> ctypes.CDLL:
         L.attn_backward.argtypes = [vp, vp, vp, vp, vp, vp, attn_layout, ctypes.c_int32, i32p, i32p,
                                     ctypes.c_float, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.attn_backward.restype = ctypes.c_int
+        L.attn_backward_restricted.argtypes = [vp, vp, vp, vp, vp, vp, attn_layout, ctypes.c_int32, i32p, i32p,
+                                               ctypes.c_int32, ctypes.c_float, vp, vp, vp, vp, ctypes.c_size_t,
+                                               vp]
+        L.attn_backward_restricted.restype = ctypes.c_int
         L.attn_backward_workspace_bytes.argtypes = [attn_layout]
         L.attn_backward_workspace_bytes.restype = ctypes.c_size_t
         L.attn_decode_workspace_bytes.argtypes = [attn_layout]
@@ -227,6 +231,10 @@ def forward_restricted(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, radius
     return out
 
 
+def backward_workspace_bytes(B: int, h: int, n_q: int, n_k: int, d: int = 64) -> int:
+    return int(lib().attn_backward_workspace_bytes(attn_layout(B, h, n_q, n_k, d, ATTN_BF16)))
+
+
 def decode_workspace_bytes(B: int, h: int, n_max: int, dtype=torch.bfloat16, d: int = 64) -> int:
     code = ATTN_BF16 if dtype == torch.bfloat16 else ATTN_F32
     return int(lib().attn_decode_workspace_bytes(attn_layout(B, h, 1, n_max, d, code)))
@@ -349,13 +357,15 @@ def output_projection(O: torch.Tensor, Wo: torch.Tensor, out: torch.Tensor | Non
 def backward(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, O: torch.Tensor, dO: torch.Tensor,
              lse: torch.Tensor, mask_kind: int = ATTN_MASK_NONE, q_lens: torch.Tensor | None = None,
              kv_lens: torch.Tensor | None = None, scale: float | None = None, grads=None,
-             workspace: torch.Tensor | None = None, stream=None):
+             workspace: torch.Tensor | None = None, stream=None, radius: int | None = None):
     """attn_backward: (dQ, dK, dV) of O = softmax(Q K^T * scale + M) V given dO.
 
     Q, K, V, O, dO bf16 [B, h, n, 64] (the forward's tensors), lse the fp32
     [B, h, n_q] log-sum-exp from forward(..., lse=...); the mask arguments and
     scale must be those of the forward.  Returns three new tensors, or fills
-    `grads` = (dQ, dK, dV).
+    `grads` = (dQ, dK, dV).  With `radius` (and ATTN_MASK_RESTRICTED in
+    mask_kind) it calls attn_backward_restricted, the backward of
+    forward_restricted.
     """
     for n, t in (("Q", Q), ("K", K), ("V", V), ("O", O), ("dO", dO)):
         _check_tensor(n, t, torch.bfloat16)
@@ -378,11 +388,14 @@ def backward(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, O: torch.Tensor,
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=Q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    st = lib().attn_backward(Q.data_ptr(), K.data_ptr(), V.data_ptr(), O.data_ptr(), dO.data_ptr(),
-                             lse.data_ptr(), layout, int(mask_kind), _lens_ptr("q_lens", q_lens, B),
-                             _lens_ptr("kv_lens", kv_lens, B), float(scale), dQ.data_ptr(), dK.data_ptr(),
-                             dV.data_ptr(), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                             _stream_handle(stream, Q))
+    common = (Q.data_ptr(), K.data_ptr(), V.data_ptr(), O.data_ptr(), dO.data_ptr(), lse.data_ptr(), layout,
+              int(mask_kind), _lens_ptr("q_lens", q_lens, B), _lens_ptr("kv_lens", kv_lens, B))
+    tail = (float(scale), dQ.data_ptr(), dK.data_ptr(), dV.data_ptr(), workspace.data_ptr(),
+            workspace.numel() * workspace.element_size(), _stream_handle(stream, Q))
+    if radius is None:
+        st, where = lib().attn_backward(*common, *tail), "attn_backward"
+    else:
+        st, where = lib().attn_backward_restricted(*common, int(radius), *tail), "attn_backward_restricted"
     if st != 0:
-        raise AttnError(st, "attn_backward")
+        raise AttnError(st, where)
     return dQ, dK, dV

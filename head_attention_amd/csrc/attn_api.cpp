@@ -295,20 +295,28 @@ attn_status attn_output_projection(const void* O, const void* Wo, attn_layout L,
 
 size_t attn_backward_workspace_bytes(attn_layout L) {
   if (check_layout(L) != ATTN_OK) return 0;
-  return (size_t)L.B * L.h * L.n_q * sizeof(float);
+  // Two fp32 values per query row, rows rounded up to a multiple of 64.
+  const size_t n_pad = ((size_t)L.n_q + 63) / 64 * 64;
+  return (size_t)L.B * L.h * n_pad * 2 * sizeof(float);
 }
 
-attn_status attn_backward(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+namespace {
+
+// radius < 0: no restriction (mask_kind must not hold ATTN_MASK_RESTRICTED);
+// radius >= 0: restricted self-attention (mask_kind must hold it).
+attn_status backward_impl(const void* Q, const void* K, const void* V, const void* O, const void* dO,
                           const float* LSE, attn_layout L, int32_t mask_kind, const int32_t* q_lens,
-                          const int32_t* kv_lens, float scale, void* dQ, void* dK, void* dV,
-                          void* workspace, size_t workspace_bytes, void* stream) {
+                          const int32_t* kv_lens, int32_t radius, float scale, void* dQ, void* dK,
+                          void* dV, void* workspace, size_t workspace_bytes, void* stream) {
   attn_status st = check_layout(L);
   if (st != ATTN_OK) return st;
   if (L.dtype != ATTN_BF16) return ATTN_ERR_BAD_DTYPE;
-  if (mask_kind & ~(ATTN_MASK_KEY_PADDING | ATTN_MASK_CAUSAL)) return ATTN_ERR_BAD_MASK;
+  if (mask_kind & ~(ATTN_MASK_KEY_PADDING | ATTN_MASK_CAUSAL | ATTN_MASK_RESTRICTED)) return ATTN_ERR_BAD_MASK;
   const bool kpad = (mask_kind & ATTN_MASK_KEY_PADDING) != 0;
   const bool causal = (mask_kind & ATTN_MASK_CAUSAL) != 0;
-  if (causal && L.n_q != L.n_k) return ATTN_ERR_BAD_MASK;
+  const bool restricted = (mask_kind & ATTN_MASK_RESTRICTED) != 0;
+  if (restricted != (radius >= 0)) return ATTN_ERR_BAD_MASK;
+  if ((causal || restricted) && L.n_q != L.n_k) return ATTN_ERR_BAD_MASK;
   if (!kpad && kv_lens != nullptr) return ATTN_ERR_BAD_MASK;
   if (!std::isfinite(scale)) return ATTN_ERR_BAD_SCALE;
   if (L.B == 0 || L.h == 0 || (L.n_q == 0 && L.n_k == 0)) return ATTN_OK;
@@ -325,8 +333,11 @@ attn_status attn_backward(const void* Q, const void* K, const void* V, const voi
   if ((dQ && (dQ == dK || dQ == dV)) || (dK && dK == dV)) return ATTN_ERR_BAD_SHAPE;
   const size_t need = attn_backward_workspace_bytes(L);
   if (need > 0 && (!workspace || workspace_bytes < need)) return ATTN_ERR_WORKSPACE;
+  // The kernels address the workspace with 32-bit byte offsets.
+  if (need >= ((size_t)1 << 31)) return ATTN_ERR_BAD_SHAPE;
   const int64_t blocks = (int64_t)((std::max(L.n_q, L.n_k) + 127) / 128) * L.h * L.B;
-  if (blocks > kMaxGrid || ((int64_t)L.B * L.h * L.n_q + 31) / 32 > kMaxGrid) return ATTN_ERR_BAD_SHAPE;
+  const int64_t n_pad = ((int64_t)L.n_q + 63) / 64 * 64;
+  if (blocks > kMaxGrid || ((int64_t)L.B * L.h * n_pad + 31) / 32 > kMaxGrid) return ATTN_ERR_BAD_SHAPE;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (length_check_enabled()) {
@@ -341,6 +352,7 @@ attn_status attn_backward(const void* Q, const void* K, const void* V, const voi
   a.dO = dO;
   a.lse = LSE;
   a.D = static_cast<float*>(workspace);
+  a.L = a.D + (size_t)L.B * L.h * n_pad;
   a.dQ = dQ;
   a.dK = dK;
   a.dV = dV;
@@ -350,14 +362,36 @@ attn_status attn_backward(const void* Q, const void* K, const void* V, const voi
   a.H = L.h;
   a.n_q = L.n_q;
   a.n_k = L.n_k;
+  a.n_pad = (int)n_pad;
   a.scale = scale;
   a.causal = causal;
+  a.radius = restricted ? std::min(radius, L.n_k) : -1;
   const hipError_t e = launch_backward(a, s);
   if (e != hipSuccess) {
     g_last_hip = e;
     return ATTN_ERR_HIP;
   }
   return ATTN_OK;
+}
+
+}  // namespace
+
+attn_status attn_backward(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                          const float* LSE, attn_layout L, int32_t mask_kind, const int32_t* q_lens,
+                          const int32_t* kv_lens, float scale, void* dQ, void* dK, void* dV,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  return backward_impl(Q, K, V, O, dO, LSE, L, mask_kind, q_lens, kv_lens, -1, scale, dQ, dK, dV, workspace,
+                       workspace_bytes, stream);
+}
+
+attn_status attn_backward_restricted(const void* Q, const void* K, const void* V, const void* O,
+                                     const void* dO, const float* LSE, attn_layout L, int32_t mask_kind,
+                                     const int32_t* q_lens, const int32_t* kv_lens, int32_t radius,
+                                     float scale, void* dQ, void* dK, void* dV, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  if (radius < 0) return ATTN_ERR_BAD_MASK;
+  return backward_impl(Q, K, V, O, dO, LSE, L, mask_kind, q_lens, kv_lens, radius, scale, dQ, dK, dV,
+                       workspace, workspace_bytes, stream);
 }
 
 size_t attn_decode_workspace_bytes(attn_layout L) {

@@ -6,12 +6,16 @@
 //   dV_j = sum_i p_ij dO_i          dp_ij = dO_i . V_j
 //   ds_ij = p_ij (dp_ij - D_i),     D_i = dO_i . O_i = sum_j p_ij dp_ij
 //   dQ_i = scale sum_j ds_ij K_j    dK_j = scale sum_i ds_ij Q_i
+// The masks are the forward's: key padding, causal, and the band of
+// restricted self-attention (§4, Table 1: keys i - radius .. i + radius, or
+// i - radius .. i with the causal mask).
 //
 // Three kernels on the caller's stream:
-//   bwd_rowdot:  D_i = dO_i . O_i in fp32 (0 for padded rows), into the
-//                workspace;
+//   bwd_rowdot:  per row, D_i = dO_i . O_i in fp32 and L_i = lse_i log2(e),
+//                into the workspace; padded rows (and rows up to the next
+//                multiple of 64) get D = 0 and L = +inf, i.e. weight 0;
 //   bwd_dkdv:    key-major.  A workgroup owns 128 keys of one (b, h), 32 per
-//                wave; query tiles of 64 rows (Q, dO, lse, D) stream through
+//                wave; query tiles of 64 rows (Q, dO, L, D) stream through
 //                LDS.  Per tile a wave computes S = Q K^T and dP = dO V^T
 //                with the keys on the lanes (its K and V fragments stay in
 //                registers for the whole loop), forms P and dS in registers,
@@ -27,11 +31,20 @@
 //                the tile.  No atomics: every output element has one owner,
 //                so the gradients are bitwise reproducible.
 //
+// Streaming: tiles reach LDS by buffer loads that write LDS directly, into a
+// ring of three slots, two tiles ahead of use; one barrier per tile both
+// publishes the tile in use and frees the slot of the tile before it.  Rows
+// at or beyond a valid length read as zero through the descriptor's range
+// check, so padded memory is never read.  Workgroups of one head share an
+// XCD (its L2 then serves the re-reads of that head's Q, dO or K, V), and
+// under the causal mask the longest ones start first.
+//
 // Numerics: bf16 inputs, fp32 accumulation; P and dS are rounded to bf16
-// once before their products; D from the bf16 O and dO in fp32.  Masks are
-// the forward's (exclusion before the softmax): an excluded key has p = 0
-// and gets no gradient; padded query rows (i >= q_len) read as zero rows
-// and carry lse = +inf internally, so they contribute nothing.
+// once before their products; D from the bf16 O and dO in fp32.  An
+// excluded key has p = 0 and gets no gradient; padded query rows read as
+// zero rows with L = +inf, so they contribute nothing.
+#include <type_traits>
+
 #include "common.h"
 
 namespace headattn {
@@ -46,9 +59,11 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 
 constexpr int kThreads = 256;
-constexpr int kTile = 64;  // rows per streamed tile
+constexpr int kTile = 64;   // rows per streamed tile
+constexpr int kSlots = 3;   // LDS ring: the tile in use and two in flight
 constexpr uint32_t kRowBytes = kHeadDim * 2;
 constexpr uint32_t kBufferWord3 = 0x00020000u;  // raw buffer, 32-bit elements (gfx9 family)
+constexpr uint32_t kOutOfRange = 0x80000000u;   // an offset the range check always rejects
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   f32x2 v = {lo, hi};
@@ -63,7 +78,8 @@ struct Tile {
 };
 
 // Fill rows [r0, r0 + 64) of a [rows][64] bf16 tensor into t; rows at or
-// beyond the descriptor's range read as zero.  256 threads, 2 instructions.
+// beyond the descriptor's range read as zero.  256 threads, 2 instructions
+// per wave.
 __device__ __forceinline__ void fill_tile(Tile& t, __amdgpu_buffer_rsrc_t r, int r0, int wave, int lane) {
   const int fpos = lane & 7;
 #pragma unroll
@@ -101,28 +117,89 @@ __device__ __forceinline__ bf16x8 tr_frag(const Tile& t, int db, int j, int lane
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// (b, h) of a workgroup and its block index along the owned axis.
-__device__ __forceinline__ void bh_block(int bid, int n_blocks, int& bh, int& blk) {
-  blk = bid % n_blocks;
-  bh = bid / n_blocks;
+// Ring slots.  Distinct objects, so the compiler tracks the asynchronous LDS
+// writes of the fills per slot and waits only where the code does.  The
+// dK/dV kernel streams Q (a), dO (b) and L, D (ld); the dQ kernel K (a) and
+// V (b).  Per ld slot: L of the tile's 64 rows in floats 0..63, D in
+// 64..127; the buffer load that fills them writes 1 KB, the rest is a
+// landing area.
+struct Slot {
+  Tile a, b;
+  float4 ld[64];
+};
+__shared__ Slot g_s0, g_s1, g_s2;
+
+template <int S>
+__device__ __forceinline__ Slot& slot() {
+  return S == 0 ? g_s0 : S == 1 ? g_s1 : g_s2;
+}
+template <int S>
+__device__ __forceinline__ Tile& aslot() {
+  return slot<S>().a;
+}
+template <int S>
+__device__ __forceinline__ Tile& bslot() {
+  return slot<S>().b;
+}
+template <int S>
+__device__ __forceinline__ float4* ldslot() {
+  return slot<S>().ld;
 }
 
-// ---------------------------------------------------------------- D = rowdot
+// (b, h) of a workgroup and its block index along the owned axis.  The 8
+// XCDs take workgroup ids round robin; when B*h divides by 8 each XCD gets
+// whole heads.  Blocks of equal rank run together, rank 0 first; `reverse`
+// gives rank 0 to the last block.
+__device__ __forceinline__ void bh_block(int bid, int n_blocks, int HB, bool reverse, int& bh, int& blk) {
+  int rank;
+  if ((HB & 7) == 0) {
+    const int per = HB >> 3;
+    const int slot = bid >> 3;
+    rank = slot / per;
+    bh = (bid & 7) * per + slot % per;
+  } else {
+    bh = bid % HB;
+    rank = bid / HB;
+  }
+  blk = reverse ? n_blocks - 1 - rank : rank;
+}
+
+// Wait until at most N of this wave's buffer loads are outstanding and all
+// its LDS operations are done, then the workgroup barrier -- a bare
+// s_barrier: a workgroup fence would add a wait for every fill in flight.
+template <int N>
+__device__ __forceinline__ void wait_barrier() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0070 | N);  // vmcnt(N), lgkmcnt(0)
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+using Slot0 = std::integral_constant<int, 0>;
+using Slot1 = std::integral_constant<int, 1>;
+using Slot2 = std::integral_constant<int, 2>;
+
+// ---------------------------------------------------------------- D, L = rowdot
 __global__ __launch_bounds__(kThreads) void bwd_rowdot_kernel(BwdArgs a) {
-  // 8 lanes per row, 16 bytes each: 32 rows per workgroup.
+  // 8 lanes per row, 16 bytes each: 32 rows per workgroup, over the padded
+  // row range [0, n_pad) of each (b, h).
   const int64_t row = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);
   const int part = threadIdx.x & 7;
-  const int64_t rows = (int64_t)a.B * a.H * a.n_q;
+  const int64_t rows = (int64_t)a.B * a.H * a.n_pad;
   float acc = 0.f;
   bool valid = false;
+  int64_t src = 0;
   if (row < rows) {
-    const int i = (int)(row % a.n_q);
-    const int b = (int)(row / ((int64_t)a.H * a.n_q));
+    const int i = (int)(row % a.n_pad);
+    const int64_t bh = row / a.n_pad;
+    const int b = (int)(bh / a.H);
     const int q_len = a.q_lens ? clamp_len(a.q_lens[b], a.n_q) : a.n_q;
     valid = i < q_len;
+    src = bh * a.n_q + i;
     if (valid) {
-      const bf16x8 o = *reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(a.O) + row * kHeadDim + 8 * part);
-      const bf16x8 g = *reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(a.dO) + row * kHeadDim + 8 * part);
+      const bf16x8 o = *reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(a.O) + src * kHeadDim + 8 * part);
+      const bf16x8 g = *reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(a.dO) + src * kHeadDim + 8 * part);
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc = fmaf((float)o[e], (float)g[e], acc);
     }
@@ -131,14 +208,22 @@ __global__ __launch_bounds__(kThreads) void bwd_rowdot_kernel(BwdArgs a) {
   acc += __shfl_xor(acc, 1);
   acc += __shfl_xor(acc, 2);
   acc += __shfl_xor(acc, 4);
-  if (row < rows && part == 0) a.D[row] = valid ? acc : 0.f;
+  if (row < rows && part == 0) {
+    float l = INFINITY;  // weight exp2(s c - L) = 0
+    if (valid) {
+      const float v = a.lse[src];
+      l = v == -INFINITY ? INFINITY : v * kLog2e;  // -inf: a row with no allowed key
+    }
+    a.D[row] = valid ? acc : 0.f;
+    a.L[row] = l;
+  }
 }
 
 // ---------------------------------------------------------------- dK, dV
-template <bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
-  __shared__ Tile sq, sdo;
-  __shared__ float s_lse[kTile], s_d[kTile];
+template <int MODE>
+__global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
+  constexpr bool CAUSAL = MODE == kModeCausal;
+  constexpr bool BAND = MODE == kModeBand;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -148,26 +233,37 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
 
   const int n_kb = (a.n_k + 127) / 128;
   int bh, kb;
-  bh_block(blockIdx.x, n_kb, bh, kb);
+  bh_block(blockIdx.x, n_kb, a.B * a.H, false, bh, kb);
   const int b = bh / a.H;
   const int q_len = __builtin_amdgcn_readfirstlane(a.q_lens ? clamp_len(a.q_lens[b], a.n_q) : a.n_q);
   const int kv_lim = __builtin_amdgcn_readfirstlane(a.kv_lens ? clamp_len(a.kv_lens[b], a.n_k) : a.n_k);
   const int kb0 = kb * 128;
   const int kw0 = kb0 + 32 * wave;  // this wave's first key
   const int key = kw0 + ln;          // this lane's key
+  // Restricted: query i sees keys i - wl .. i + wr, so key j is seen by
+  // queries j - wr .. j + wl.
+  const int wl = BAND ? a.radius : 0;
+  const int wr = BAND ? (a.causal ? 0 : a.radius) : 0;
 
   const __bf16* Q = static_cast<const __bf16*>(a.Q) + (size_t)bh * a.n_q * kHeadDim;
   const __bf16* K = static_cast<const __bf16*>(a.K) + (size_t)bh * a.n_k * kHeadDim;
   const __bf16* V = static_cast<const __bf16*>(a.V) + (size_t)bh * a.n_k * kHeadDim;
   const __bf16* dO = static_cast<const __bf16*>(a.dO) + (size_t)bh * a.n_q * kHeadDim;
-  const float* LSE = a.lse + (size_t)bh * a.n_q;
-  const float* Dv = a.D + (size_t)bh * a.n_q;
 
   // Query rows below q_len only: padded rows read as zeros.
   const __amdgpu_buffer_rsrc_t rq =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(Q), (short)0, (int)((uint32_t)q_len * kRowBytes), kBufferWord3);
   const __amdgpu_buffer_rsrc_t rdo =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(dO), (short)0, (int)((uint32_t)q_len * kRowBytes), kBufferWord3);
+  // D then L, n_pad rows per (b, h) each, n_pad a multiple of 64, so a tile
+  // never reaches the next head's rows.  Lanes 0..15 of wave 0 load 4 rows
+  // of L each, lanes 16..31 4 rows of D; the other lanes read nothing (zeros
+  // into the landing area).
+  const uint32_t bhp = (uint32_t)a.B * a.H * a.n_pad;
+  const __amdgpu_buffer_rsrc_t rld = __builtin_amdgcn_make_buffer_rsrc(a.D, (short)0, (int)(bhp * 8u), kBufferWord3);
+  const uint32_t ld_base = lane < 16   ? (bhp + (uint32_t)bh * a.n_pad + 4u * lane) * 4u
+                           : lane < 32 ? ((uint32_t)bh * a.n_pad + 4u * (lane - 16)) * 4u
+                                       : kOutOfRange;
 
   // K and V fragments of this lane's key (B operands of S = Q K^T and
   // dP = dO V^T), for the whole loop; sign of scale folded into K.
@@ -191,24 +287,52 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
 
   f32x16 dk[2] = {f32x16{}, f32x16{}};  // dK^T [d block], column = key ln
   f32x16 dv[2] = {f32x16{}, f32x16{}};  // dV^T [d block]
-  const bool wave_live = kw0 < kv_lim && (!CAUSAL || kw0 < q_len);
+  bool wave_live = kw0 < kv_lim;
+  if (CAUSAL) wave_live = wave_live && kw0 < q_len;
+  if (BAND) wave_live = wave_live && kw0 - wr < q_len;
 
-  int q_start = CAUSAL ? (kb0 / kTile) * kTile : 0;
-  const int q_end = (kb0 < kv_lim) ? q_len : 0;  // no key of the block is valid: nothing to do
-  for (int q0 = q_start; q0 < q_end; q0 += kTile) {
-    __syncthreads();  // the previous tile is consumed
-    fill_tile(sq, rq, q0, wave, lane);
-    fill_tile(sdo, rdo, q0, wave, lane);
-    if (tid < kTile) {
-      const int i = q0 + tid;
-      const float l = i < q_len ? LSE[i] : -INFINITY;
-      // Padded rows and rows with no key: weight 0 through lse = +inf.
-      s_lse[tid] = l == -INFINITY ? INFINITY : l * kLog2e;
-      s_d[tid] = i < q_len ? Dv[i] : 0.f;
+  // Query tiles of the workgroup: [q_start, q_end) in steps of 64.
+  int q_start = 0, q_end = q_len;
+  if (CAUSAL) q_start = (kb0 / kTile) * kTile;
+  if (BAND) {
+    q_start = (max(0, kb0 - wr) / kTile) * kTile;
+    q_end = min(q_end, kb0 + 128 + wl);
+  }
+  if (kb0 >= kv_lim) q_end = 0;  // no key of the block is valid: nothing to do
+  const int n_tiles = q_end > q_start ? (q_end - q_start + kTile - 1) / kTile : 0;
+
+  // Fill of tile u into slot S (= u % 3): Q and dO (2 + 2 loads per wave),
+  // and from wave 0 one load of L and D.
+  auto fill = [&](auto slot_tag, int u) __attribute__((always_inline)) {
+    constexpr int S = decltype(slot_tag)::value;
+    const int q0 = q_start + u * kTile;
+    fill_tile(aslot<S>(), rq, q0, wave, lane);
+    fill_tile(bslot<S>(), rdo, q0, wave, lane);
+    if (wave == 0) {
+      const uint32_t off = ld_base == kOutOfRange ? kOutOfRange : ld_base + (uint32_t)q0 * 4u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rld, (lds_void_t*)ldslot<S>(), 16, off, 0, 0, 0);
     }
-    __syncthreads();
+  };
+
+  // One tile: S = u % 3 is its slot.  Tile u has landed (the only loads
+  // allowed in flight are tile u + 1's) and every wave is done with tile
+  // u - 1, whose slot tile u + 2 takes.
+  auto step = [&](auto slot_tag, int u) __attribute__((always_inline)) {
+    constexpr int S = decltype(slot_tag)::value;
+    using S2 = std::integral_constant<int, (S + 2) % kSlots>;
+    if (u >= n_tiles) return;
+    if (wave == 0) wait_barrier<5>();
+    else wait_barrier<4>();
+    fill(S2(), u + 2);
+
+    const int q0 = q_start + u * kTile;
     // Does any query of the tile see any key of this wave?
-    if (!wave_live || (CAUSAL && q0 + kTile - 1 < kw0)) continue;
+    if (!wave_live) return;
+    if (CAUSAL && q0 + kTile - 1 < kw0) return;
+    if (BAND && (q0 + kTile - 1 < kw0 - wr || q0 > kw0 + 31 + wl)) return;
+    const Tile& tq = aslot<S>();
+    const Tile& tdo = bslot<S>();
+    const float* tld = reinterpret_cast<const float*>(ldslot<S>());
 
     // S[q][key] and dP[q][key] for query blocks qb (32 rows each): lane
     // (ln, hh) register r holds query q0 + 32 qb + 8 (r / 4) + 4 hh + r % 4.
@@ -218,23 +342,24 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
       f32x16 sa = f32x16{}, pa = f32x16{};
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(sq, 32 * qb + ln, s, hh), kf[s], sa, 0, 0, 0);
-        pa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(sdo, 32 * qb + ln, s, hh), vf[s], pa, 0, 0, 0);
+        sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(tq, 32 * qb + ln, s, hh), kf[s], sa, 0, 0, 0);
+        pa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(tdo, 32 * qb + ln, s, hh), vf[s], pa, 0, 0, 0);
       }
       s_[qb] = sa;
       dp[qb] = pa;
     }
-    // P = exp2(s c - lse2) with the mask, dS = P (dP - D); both packed to
+    // P = exp2(s c - L) with the mask, dS = P (dP - D); both packed to
     // bf16 in the register order the k slots of the next products use.
-    const bool need_mask = (kw0 + 32 > kv_lim) || (CAUSAL && q0 < kw0 + 32);
+    bool need_mask = (kw0 + 32 > kv_lim) || (CAUSAL && q0 < kw0 + 32);
+    if (BAND) need_mask = need_mask || !(q0 + kTile - 1 - wl <= kw0 && kw0 + 31 <= q0 + wr);
     uint32_t pp[16], ps[16];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
         const int ql = 32 * qb + 8 * gq + 4 * hh;  // first of this group's 4 queries
-        const float4 l4 = *reinterpret_cast<const float4*>(&s_lse[ql]);
-        const float4 d4 = *reinterpret_cast<const float4*>(&s_d[ql]);
+        const float4 l4 = *reinterpret_cast<const float4*>(&tld[ql]);
+        const float4 d4 = *reinterpret_cast<const float4*>(&tld[kTile + ql]);
         const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
         const float dvv[4] = {d4.x, d4.y, d4.z, d4.w};
         float p[4], g[4];
@@ -244,7 +369,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
           float x = fmaf(s_[qb][r], c, -lv[e]);
           if (need_mask) {
             const int qi = q0 + ql + e;
-            const bool ok = key < kv_lim && (!CAUSAL || key <= qi);
+            bool ok = key < kv_lim;
+            if (CAUSAL) ok = ok && key <= qi;
+            if (BAND) ok = ok && key >= qi - wl && key <= qi + wr;
             x = ok ? x : -INFINITY;
           }
           p[e] = __builtin_amdgcn_exp2f(x);
@@ -264,10 +391,23 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
       const bf16x8 sb = __builtin_bit_cast(bf16x8, make_uint4(ps[4 * j], ps[4 * j + 1], ps[4 * j + 2], ps[4 * j + 3]));
 #pragma unroll
       for (int db = 0; db < 2; ++db) {
-        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(sdo, db, j, lane), pb, dv[db], 0, 0, 0);
-        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(sq, db, j, lane), sb, dk[db], 0, 0, 0);
+        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(tdo, db, j, lane), pb, dv[db], 0, 0, 0);
+        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(tq, db, j, lane), sb, dk[db], 0, 0, 0);
       }
     }
+  };
+
+  if (n_tiles > 0) {
+    fill(Slot0(), 0);
+    fill(Slot1(), 1);
+    for (int u = 0; u < n_tiles; u += kSlots) {
+      step(Slot0(), u);
+      step(Slot1(), u + 1);
+      step(Slot2(), u + 2);
+    }
+    // The last two fills (past the end: zeros, never read) land before the
+    // workgroup's LDS is released.
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0)
   }
 
   // ---- store: register r of block db holds d = 32 db + 8 (r / 4) + 4 hh +
@@ -293,9 +433,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------- dQ
-template <bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdArgs a) {
-  __shared__ Tile sk, sv;
+template <int MODE>
+__global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
+  constexpr bool CAUSAL = MODE == kModeCausal;
+  constexpr bool BAND = MODE == kModeBand;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -305,13 +446,15 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdArgs a) {
 
   const int n_qb = (a.n_q + 127) / 128;
   int bh, qblk;
-  bh_block(blockIdx.x, n_qb, bh, qblk);
+  bh_block(blockIdx.x, n_qb, a.B * a.H, CAUSAL, bh, qblk);
   const int b = bh / a.H;
   const int q_len = __builtin_amdgcn_readfirstlane(a.q_lens ? clamp_len(a.q_lens[b], a.n_q) : a.n_q);
   const int kv_lim = __builtin_amdgcn_readfirstlane(a.kv_lens ? clamp_len(a.kv_lens[b], a.n_k) : a.n_k);
   const int q0 = qblk * 128;
   const int qw0 = q0 + 32 * wave;
   const int qi = qw0 + ln;
+  const int wl = BAND ? a.radius : 0;
+  const int wr = BAND ? (a.causal ? 0 : a.radius) : 0;
 
   const __bf16* Q = static_cast<const __bf16*>(a.Q) + (size_t)bh * a.n_q * kHeadDim;
   const __bf16* K = static_cast<const __bf16*>(a.K) + (size_t)bh * a.n_k * kHeadDim;
@@ -343,27 +486,52 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdArgs a) {
     qf[s] = __builtin_bit_cast(bf16x8, qv);
     gf[s] = __builtin_bit_cast(bf16x8, gv);
   }
-  float lse2 = INFINITY, dval = 0.f;
-  if (row_live) {
-    const float l = a.lse[(size_t)bh * a.n_q + qi];
-    lse2 = l == -INFINITY ? INFINITY : l * kLog2e;
-    dval = a.D[(size_t)bh * a.n_q + qi];
+  // L and D of this row (rows below n_pad exist for every qi < n_q).
+  float lrow = INFINITY, dval = 0.f;
+  if (qi < a.n_q) {
+    lrow = a.L[(size_t)bh * a.n_pad + qi];
+    dval = a.D[(size_t)bh * a.n_pad + qi];
   }
 
   f32x16 dq[2] = {f32x16{}, f32x16{}};  // dQ^T [d block], column = query ln
-  int end = kv_lim;
+  // Key tiles of the workgroup: [k_start, end) in steps of 64.
+  int k_start = 0, end = kv_lim;
   if (CAUSAL) end = min(end, q0 + 128);
+  if (BAND) {
+    k_start = (max(0, q0 - wl) / kTile) * kTile;
+    end = min(end, q0 + 128 + wr);
+  }
   if (q0 >= q_len) end = 0;
-  int wave_end = end;
+  const int n_tiles = end > k_start ? (end - k_start + kTile - 1) / kTile : 0;
+  // Keys this wave needs: [wave_start, wave_end).
+  int wave_start = 0, wave_end = end;
   if (CAUSAL) wave_end = min(wave_end, qw0 + 32);
+  if (BAND) {
+    wave_start = max(0, qw0 - wl);
+    wave_end = min(wave_end, qw0 + 32 + wr);
+  }
   if (qw0 >= q_len) wave_end = 0;
 
-  for (int k0 = 0; k0 < end; k0 += kTile) {
-    __syncthreads();
-    fill_tile(sk, rk, k0, wave, lane);
-    fill_tile(sv, rv, k0, wave, lane);
-    __syncthreads();
-    if (k0 >= wave_end) continue;
+  // Fill of tile u into slot S (= u % 3): K and V, 2 + 2 loads per wave.
+  auto fill = [&](auto slot_tag, int u) __attribute__((always_inline)) {
+    constexpr int S = decltype(slot_tag)::value;
+    const int k0 = k_start + u * kTile;
+    fill_tile(aslot<S>(), rk, k0, wave, lane);
+    fill_tile(bslot<S>(), rv, k0, wave, lane);
+  };
+
+  // One tile, as in the dK/dV kernel.
+  auto step = [&](auto slot_tag, int u) __attribute__((always_inline)) {
+    constexpr int S = decltype(slot_tag)::value;
+    using S2 = std::integral_constant<int, (S + 2) % kSlots>;
+    if (u >= n_tiles) return;
+    wait_barrier<4>();
+    fill(S2(), u + 2);
+
+    const int k0 = k_start + u * kTile;
+    if (k0 >= wave_end || k0 + kTile <= wave_start) return;
+    const Tile& tk = aslot<S>();
+    const Tile& tv = bslot<S>();
     // S^T[key][q], dP^T[key][q] for key blocks kb: register r holds key
     // k0 + 32 kb + 8 (r / 4) + 4 hh + r % 4 of query ln.
     f32x16 st[2], dpt[2];
@@ -372,13 +540,14 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdArgs a) {
       f32x16 sa = f32x16{}, pa = f32x16{};
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(sk, 32 * kb + ln, s, hh), qf[s], sa, 0, 0, 0);
-        pa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(sv, 32 * kb + ln, s, hh), gf[s], pa, 0, 0, 0);
+        sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(tk, 32 * kb + ln, s, hh), qf[s], sa, 0, 0, 0);
+        pa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(tv, 32 * kb + ln, s, hh), gf[s], pa, 0, 0, 0);
       }
       st[kb] = sa;
       dpt[kb] = pa;
     }
-    const bool need_mask = (k0 + kTile > kv_lim) || (CAUSAL && k0 + kTile - 1 > qw0);
+    bool need_mask = (k0 + kTile > kv_lim) || (CAUSAL && k0 + kTile - 1 > qw0);
+    if (BAND) need_mask = need_mask || (k0 + kTile - 1 > qw0 + wr) || (k0 < qw0 + 31 - wl);
     uint32_t ps[16];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -388,10 +557,12 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
           const int r = 2 * r2 + e;
-          float x = fmaf(st[kb][r], c, -lse2);
+          float x = fmaf(st[kb][r], c, -lrow);
           if (need_mask) {
             const int kj = k0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
-            const bool ok = kj < kv_lim && (!CAUSAL || kj <= qi);
+            bool ok = kj < kv_lim;
+            if (CAUSAL) ok = ok && kj <= qi;
+            if (BAND) ok = ok && kj >= qi - wl && kj <= qi + wr;
             x = ok ? x : -INFINITY;
           }
           const float p = __builtin_amdgcn_exp2f(x);
@@ -405,8 +576,21 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdArgs a) {
       const bf16x8 sb = __builtin_bit_cast(bf16x8, make_uint4(ps[4 * j], ps[4 * j + 1], ps[4 * j + 2], ps[4 * j + 3]));
 #pragma unroll
       for (int db = 0; db < 2; ++db)
-        dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(sk, db, j, lane), sb, dq[db], 0, 0, 0);
+        dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(tk, db, j, lane), sb, dq[db], 0, 0, 0);
     }
+  };
+
+  if (n_tiles > 0) {
+    fill(Slot0(), 0);
+    fill(Slot1(), 1);
+    for (int u = 0; u < n_tiles; u += kSlots) {
+      step(Slot0(), u);
+      step(Slot1(), u + 1);
+      step(Slot2(), u + 2);
+    }
+    // The last two fills (past the end: zeros, never read) land before the
+    // workgroup's LDS is released.
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0)
   }
 
   // dQ = scale sum ds K: the sign of scale sits in Q', not in K, so apply
@@ -426,12 +610,25 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dq_kernel(BwdArgs a) {
   }
 }
 
+const void* dkdv_fn(int mode) {
+  return mode == kModeBand     ? reinterpret_cast<const void*>(&bwd_dkdv_kernel<kModeBand>)
+         : mode == kModeCausal ? reinterpret_cast<const void*>(&bwd_dkdv_kernel<kModeCausal>)
+                               : reinterpret_cast<const void*>(&bwd_dkdv_kernel<kModeNone>);
+}
+
+const void* dq_fn(int mode) {
+  return mode == kModeBand     ? reinterpret_cast<const void*>(&bwd_dq_kernel<kModeBand>)
+         : mode == kModeCausal ? reinterpret_cast<const void*>(&bwd_dq_kernel<kModeCausal>)
+                               : reinterpret_cast<const void*>(&bwd_dq_kernel<kModeNone>);
+}
+
 }  // namespace
 
 hipError_t launch_backward(const BwdArgs& a, hipStream_t s) {
   BwdArgs args = a;
   void* kargs[] = {&args};
-  const int64_t rows = (int64_t)a.B * a.H * a.n_q;
+  const int mode = a.radius >= 0 ? kModeBand : (a.causal ? kModeCausal : kModeNone);
+  const int64_t rows = (int64_t)a.B * a.H * a.n_pad;
   hipError_t e = hipSuccess;
   if (rows > 0) {
     e = hipLaunchKernel(reinterpret_cast<const void*>(&bwd_rowdot_kernel), dim3((unsigned)((rows + 31) / 32)),
@@ -440,16 +637,12 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t s) {
   }
   if (a.n_k > 0) {
     const int64_t blocks = (int64_t)((a.n_k + 127) / 128) * a.H * a.B;
-    const void* fn = a.causal ? reinterpret_cast<const void*>(&bwd_dkdv_kernel<true>)
-                              : reinterpret_cast<const void*>(&bwd_dkdv_kernel<false>);
-    e = hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(kThreads), kargs, 0, s);
+    e = hipLaunchKernel(dkdv_fn(mode), dim3((unsigned)blocks), dim3(kThreads), kargs, 0, s);
     if (e != hipSuccess) return e;
   }
-  if (rows == 0) return hipSuccess;
+  if (a.n_q == 0) return hipSuccess;
   const int64_t blocks = (int64_t)((a.n_q + 127) / 128) * a.H * a.B;
-  const void* fn = a.causal ? reinterpret_cast<const void*>(&bwd_dq_kernel<true>)
-                            : reinterpret_cast<const void*>(&bwd_dq_kernel<false>);
-  return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(kThreads), kargs, 0, s);
+  return hipLaunchKernel(dq_fn(mode), dim3((unsigned)blocks), dim3(kThreads), kargs, 0, s);
 }
 
 }  // namespace headattn

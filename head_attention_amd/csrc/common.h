@@ -92,15 +92,18 @@ struct BwdArgs {
   const void* O;
   const void* dO;
   const float* lse;        // [B*H*n_q] natural-log row normalisers from the forward
-  float* D;                // workspace [B*H*n_q]: dO . O per row
+  float* D;                // workspace [B*H*n_pad]: dO . O per row (0 for padded rows)
+  float* L;                // workspace [B*H*n_pad]: lse log2(e) per row (+inf for padded rows)
   void* dQ;
   void* dK;
   void* dV;
   const int32_t* q_lens;
   const int32_t* kv_lens;
   int B, H, n_q, n_k;
+  int n_pad;               // n_q rounded up to a multiple of 64
   float scale;
   bool causal;
+  int radius;              // restricted self-attention radius, -1 = off (0 <= radius <= n_k)
 };
 hipError_t launch_backward(const BwdArgs& a, hipStream_t s);
 

@@ -286,7 +286,9 @@ attn_status attn_output_projection(const void* O, const void* Wo, attn_layout la
  *   dQ              [B, h, n_q, 64] bf16, written (padded rows as 0)
  *   dK, dV          [B, h, n_k, 64] bf16, written (excluded keys as 0)
  *   workspace       device buffer of at least attn_backward_workspace_bytes
- *                   (fp32 dO . O per row); contents on entry do not matter
+ *                   (per query row, padded to a multiple of 64 rows: fp32
+ *                   dO . O, then fp32 LSE log2(e)); contents on entry do not
+ *                   matter; calls that share it must be ordered (same stream)
  *   stream          hipStream_t or NULL.
  * Three kernels on `stream` (row dots, key-major dK/dV, query-major dQ); no
  * atomics, so the results are bitwise reproducible.  bf16 products, fp32
@@ -299,8 +301,26 @@ attn_status attn_backward(const void* Q, const void* K, const void* V, const voi
                           float scale, void* dQ, void* dK, void* dV, void* workspace,
                           size_t workspace_bytes, void* stream);
 
-/* Bytes of workspace attn_backward needs (fp32 per query row); 0 if the
- * layout is invalid.  Pure host arithmetic. */
+/*
+ * attn_backward_restricted -- attn_backward of attn_forward_restricted:
+ * the same gradients over the band of restricted self-attention (kimjiil
+ * page §4, Table 1), keys i - radius .. i + radius (i - radius .. i with
+ * ATTN_MASK_CAUSAL).  mask_kind must hold ATTN_MASK_RESTRICTED, radius >= 0
+ * and n_q == n_k; LSE comes from attn_forward_restricted with the same
+ * radius.  Every other argument and the error behaviour are those of
+ * attn_backward, which refuses ATTN_MASK_RESTRICTED.
+ */
+attn_status attn_backward_restricted(const void* Q, const void* K, const void* V,
+                                     const void* O, const void* dO, const float* LSE,
+                                     attn_layout layout, int32_t mask_kind,
+                                     const int32_t* q_lens, const int32_t* kv_lens,
+                                     int32_t radius, float scale, void* dQ, void* dK,
+                                     void* dV, void* workspace, size_t workspace_bytes,
+                                     void* stream);
+
+/* Bytes of workspace attn_backward and attn_backward_restricted need: two
+ * fp32 values per query row, rows of each (b, h) rounded up to a multiple
+ * of 64; 0 if the layout is invalid.  Pure host arithmetic. */
 size_t attn_backward_workspace_bytes(attn_layout layout);
 
 /* Bytes of fp32 split partials attn_decode needs for this cache layout; 0 if

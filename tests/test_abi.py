@@ -30,7 +30,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("attn_forward", "attn_forward_lse", "attn_forward_restricted",
-              "attn_backward", "attn_backward_workspace_bytes",
+              "attn_backward", "attn_backward_restricted", "attn_backward_workspace_bytes",
               "attn_decode", "attn_cache_append", "attn_head_projection",
               "attn_output_projection", "attn_decode_workspace_bytes",
               "attn_status_string", "attn_last_hip_error"):
@@ -174,7 +174,10 @@ def test_forward_lse_and_backward_validation():
                               None) == SHAPE
     assert L.attn_forward_lse(None, None, None, attn_layout(0, 3, 16, 16, 64, BF16), 0, None, None, 0.125,
                               None, None, None) == OK
-    assert L.attn_backward_workspace_bytes(lay_) == 2 * 3 * 16 * 4
+    # per (b, h): n_q rounded up to 64 rows, two fp32 values per row
+    assert L.attn_backward_workspace_bytes(lay_) == 2 * 3 * 64 * 8
+    assert L.attn_backward_workspace_bytes(attn_layout(1, 2, 130, 16, 64, BF16)) == 2 * 192 * 8
+    assert L.attn_backward_workspace_bytes(attn_layout(1, 2, 0, 16, 64, BF16)) == 0
     assert L.attn_backward_workspace_bytes(attn_layout(2, 3, 16, 16, 32, BF16)) == 0
 
     def bwd(lay, mask=0, ql=None, kl=None, scale=0.125, ws_bytes=None, **ptrs):
@@ -247,3 +250,33 @@ def test_forward_restricted_validation():
     assert L.attn_forward(FAKE, FAKE + 16, FAKE + 32, lay_, 4, None, None, 0.125, FAKE + 48, None) == MASK
     assert L.attn_forward_lse(FAKE, FAKE + 16, FAKE + 32, lay_, 6, None, None, 0.125, FAKE + 48, FAKE + 64,
                               None) == MASK
+
+
+def test_backward_restricted_validation():
+    """attn_backward_restricted takes the restricted mask and a radius;
+    attn_backward refuses the restricted bit.  Every call is rejected before
+    any launch."""
+    L = ha.lib()
+    lay_ = attn_layout(2, 3, 16, 16, 64, BF16)
+
+    def rb(lay, mask=4, radius=2, kl=None, scale=0.125, ws_bytes=None, **ptrs):
+        p = dict(q=FAKE, k=FAKE + 16, v=FAKE + 32, o=FAKE + 48, do=FAKE + 64, lse=FAKE + 80,
+                 dq=FAKE + 96, dk=FAKE + 112, dv=FAKE + 128, ws=FAKE + 144)
+        p.update(ptrs)
+        wsb = L.attn_backward_workspace_bytes(lay) if ws_bytes is None else ws_bytes
+        return L.attn_backward_restricted(p["q"], p["k"], p["v"], p["o"], p["do"], p["lse"], lay, mask, None, kl,
+                                          radius, scale, p["dq"], p["dk"], p["dv"], p["ws"], wsb, None)
+    assert rb(lay_, mask=0) == MASK
+    assert rb(lay_, mask=2) == MASK
+    assert rb(lay_, radius=-3) == MASK
+    assert rb(attn_layout(2, 3, 16, 24, 64, BF16)) == MASK
+    assert rb(attn_layout(2, 3, 16, 16, 64, F32)) == DTYPE
+    assert rb(lay_, mask=5) == NULLP                       # padding without kv_lens
+    assert rb(lay_, scale=float("nan")) == SCALE
+    assert rb(lay_, ws=None) == WORK
+    assert rb(lay_, dv=FAKE + 32) == SHAPE                  # dV aliases V
+    assert rb(attn_layout(0, 3, 16, 16, 64, BF16), q=None, k=None, v=None, o=None, do=None, lse=None,
+              dq=None, dk=None, dv=None, ws=None) == OK
+    wsb = L.attn_backward_workspace_bytes(lay_)
+    assert L.attn_backward(FAKE, FAKE + 16, FAKE + 32, FAKE + 48, FAKE + 64, FAKE + 80, lay_, 4, None, None, 0.125,
+                           FAKE + 96, FAKE + 112, FAKE + 128, FAKE + 144, wsb, None) == MASK

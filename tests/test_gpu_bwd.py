@@ -73,6 +73,11 @@ BWD = {
     "none_70x257": (1, 2, 70, 257, 0, None, None, 0.125),
     "negative_scale_96": (1, 2, 96, 96, 2, None, None, -0.3),
     "one_key": (2, 1, 40, 40, 1, [40, 40], [1, 2], 0.125),
+    # several ring wraps of the streamed tiles, B*h a multiple of 8 (heads
+    # grouped per XCD) and not
+    "causal_2000_h8": (1, 8, 2000, 2000, 2, None, None, 0.125),
+    "causal_kpad_1100": (2, 4, 1100, 1100, 3, [1100, 517], [1100, 517], 0.125),
+    "none_700x1300": (1, 3, 700, 1300, 0, None, None, 0.125),
 }
 
 
@@ -115,3 +120,46 @@ def test_backward(cid):
     if kl is not None:  # excluded keys: zero dK, dV
         for b in range(B):
             assert torch.all(dK[b, :, int(kl[b]):] == 0) and torch.all(dV[b, :, int(kl[b]):] == 0)
+
+
+BWD_RESTRICTED = {
+    # name: (B, H, n, radius, causal, key padding, query padding)
+    "r17_pad_300": (1, 4, 300, 17, False, True, True),
+    "r100_causal_700_h8": (2, 4, 700, 100, True, False, False),
+    "r0_kpad_520": (1, 2, 520, 0, False, True, False),
+    "r300_causal_200": (1, 2, 200, 300, True, False, True),
+    "r64_1000": (1, 3, 1000, 64, False, False, False),
+    "r1_causal_kpad_333": (2, 2, 333, 1, True, True, True),
+}
+
+
+@pytest.mark.parametrize("cid", sorted(BWD_RESTRICTED))
+def test_backward_restricted(cid):
+    """attn_backward_restricted against the oracle's backward over the band
+    of restricted self-attention (kimjiil page §4, Table 1), from the LSE of
+    attn_forward_restricted with the same radius."""
+    B, H, n, radius, causal, kpad, qpad = BWD_RESTRICTED[cid]
+    mask = ha.ATTN_MASK_RESTRICTED | (ha.ATTN_MASK_CAUSAL if causal else 0) | (ha.ATTN_MASK_KEY_PADDING if kpad else 0)
+    ql = [n - 13 * (b + 1) for b in range(B)] if qpad else None
+    kl = [max(1, n // (b + 2)) for b in range(B)] if kpad else None
+    Q, K, V, dO, ql, kl, scale = _case(cid, B, H, n, n, mask, ql, kl, BF16, 0.125)
+    say(f"[backward restricted {cid}] B{B} h{H} n{n} radius {radius} mask {mask}")
+    d = lambda t: None if t is None else t.cuda()
+    Qd, Kd, Vd, dOd = d(Q), d(K), d(V), d(dO)
+    lse = torch.empty((B, H, n), dtype=torch.float32, device="cuda")
+    O = ha.forward_restricted(Qd, Kd, Vd, radius, mask_kind=mask, q_lens=d(ql), kv_lens=d(kl), scale=scale,
+                              lse=lse)
+    grads = ha.backward(Qd, Kd, Vd, O, dOd, lse, mask_kind=mask, q_lens=d(ql), kv_lens=d(kl), scale=scale,
+                        radius=radius)
+    again = ha.backward(Qd, Kd, Vd, O, dOd, lse, mask_kind=mask, q_lens=d(ql), kv_lens=d(kl), scale=scale,
+                        radius=radius)
+    torch.cuda.synchronize()
+    assert all(torch.equal(x, y) for x, y in zip(grads, again))  # deterministic
+    refs = orc.attention_backward(np64(Q), np64(K), np64(V), np64(dO), mask_kind=mask,
+                                  q_lens=None if ql is None else ql.numpy(),
+                                  kv_lens=None if kl is None else kl.numpy(), scale=scale, radius=radius)
+    for name, got, ref in zip(("dQ", "dK", "dV"), grads, refs):
+        _check_grad(np64(got), ref, name)
+    if kl is not None:  # keys past kv_len: zero dK, dV
+        for b in range(B):
+            assert torch.all(grads[1][b, :, int(kl[b]):] == 0) and torch.all(grads[2][b, :, int(kl[b]):] == 0)
