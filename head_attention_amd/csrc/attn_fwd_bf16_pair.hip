@@ -86,22 +86,31 @@ constexpr uint32_t kBufferWord3 = 0x00020000u;  // raw buffer, 32-bit elements (
 constexpr float kPivotUp = 64.f;
 constexpr float kPivotDown = -64.f;
 
-// Ring slots, 8 KB each (64 rows x 8 chunks of 16 B).  Distinct objects, so
-// the compiler tracks the asynchronous LDS writes of the fills per slot.
-__shared__ uint4 g_k0[512], g_k1[512], g_k2[512], g_k3[512];
-__shared__ uint4 g_v0[512], g_v1[512], g_v2[512], g_v3[512];
+// Ring of 8 slots, each the K and the V tile of one 64-key tile (8 KB each:
+// 64 rows x 8 chunks of 16 B).  Every tile is its own object, so the
+// compiler tracks the asynchronous LDS writes of the fills per tile (a slot
+// as one object holding K and V made it wait for every fill in flight
+// before each V read).
+__shared__ uint4 g_k0[512], g_k1[512], g_k2[512], g_k3[512], g_k4[512], g_k5[512], g_k6[512], g_k7[512];
+__shared__ uint4 g_v0[512], g_v1[512], g_v2[512], g_v3[512], g_v4[512], g_v5[512], g_v6[512], g_v7[512];
+constexpr int kSlots = 8;
+// Fills run this many phases ahead: the fill at phase p is tile p + 5,
+// into the slot of tile p - 3, whose V was last read at phase p - 1.
+constexpr int kAhead = 5;
 // Row sums and pivots of the odd-tile waves for the final merge.
 __shared__ float2 g_lm[4][2][64];
 
 template <int S>
 __device__ __forceinline__ uint4* kslot() {
-  return S == 0 ? g_k0 : S == 1 ? g_k1 : S == 2 ? g_k2 : g_k3;
+  return S == 0 ? g_k0 : S == 1 ? g_k1 : S == 2 ? g_k2 : S == 3 ? g_k3
+       : S == 4 ? g_k4 : S == 5 ? g_k5 : S == 6 ? g_k6 : g_k7;
 }
 template <int S>
 __device__ __forceinline__ uint4* vslot() {
-  return S == 0 ? g_v0 : S == 1 ? g_v1 : S == 2 ? g_v2 : g_v3;
+  return S == 0 ? g_v0 : S == 1 ? g_v1 : S == 2 ? g_v2 : S == 3 ? g_v3
+       : S == 4 ? g_v4 : S == 5 ? g_v5 : S == 6 ? g_v6 : g_v7;
 }
-// The 8 slots in order, as the 64 KB merge area.
+// Tiles K0 .. K3 and V0 .. V3 as the 8 KB parts of the 64 KB merge area.
 template <int S>
 __device__ __forceinline__ uint4* mslot() {
   return S < 4 ? (S == 0 ? g_k0 : S == 1 ? g_k1 : S == 2 ? g_k2 : g_k3)
@@ -464,20 +473,24 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_pair_kernel(FwdArgs
   };
 
   // Phases.  A phase p begins with this wave's share of the fills of
-  // K(p + 3) and V(p + 1) (tiles past the end read as zeros and are never
-  // used) and ends with a wait for this wave's fills of phase p - 2 and a
-  // barrier, which publishes K(p + 1) and V(p - 1).  Slot of tile t: t % 4;
-  // a slot is refilled only after the phase that last read it has ended.
+  // K(p + 5) and V(p + 5) into slot (p + 5) % 8 (tiles past the end read
+  // real rows or zeros and are never used), and ends with a wait for this
+  // wave's fills of four phases ago and a barrier, which publishes K(p + 1)
+  // (and V(p - 1), filled two phases earlier still).  The slot of tile t
+  // holds its K and its V; it is refilled only after the phase that last
+  // read it (the P.V of tile t, at phase t + 2) has ended.
   auto fills = [&](auto j_tag, int p) __attribute__((always_inline)) {
     constexpr int J = decltype(j_tag)::value;
-    fill_k(std::integral_constant<int, (J + 3) & 3>(), p + 3);
-    fill_v(std::integral_constant<int, (J + 1) & 3>(), p + 1);
+    using SF = std::integral_constant<int, (J + kAhead) % kSlots>;
+    fill_k(SF(), p + kAhead);
+    fill_v(SF(), p + kAhead);
   };
   auto sync = [&]() __attribute__((always_inline)) {
-    __builtin_amdgcn_s_waitcnt(0x0F70 | 4);  // vmcnt(4): this and the previous phase's fills may fly
+    // vmcnt(8): the fills of this and the three previous phases may fly.
+    __builtin_amdgcn_s_waitcnt(0x0F70 | 8);
     barrier_lds();
   };
-  // MFMA phase at phase p (slot J = p % 4): P.V of tile p - 2, then S of
+  // MFMA phase at phase p (slot J = p % 8): P.V of tile p - 2, then S of
   // tile p.  It runs unconditionally, so the phase is one straight block:
   // before a wave's first tile and past its last one the weights are zero
   // and the V slot holds finite values (zeroed at start, or a tile read
@@ -489,7 +502,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_pair_kernel(FwdArgs
   // fragments die before the scores are born.
   auto mphase = [&](auto j_tag) __attribute__((always_inline)) {
     constexpr int J = decltype(j_tag)::value;
-    using SV = std::integral_constant<int, (J + 2) & 3>;
+    using SV = std::integral_constant<int, (J + kSlots - 2) % kSlots>;
     using SK = std::integral_constant<int, J>;
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
@@ -536,39 +549,62 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_pair_kernel(FwdArgs
   using J1 = std::integral_constant<int, 1>;
   using J2 = std::integral_constant<int, 2>;
   using J3 = std::integral_constant<int, 3>;
+  using J4 = std::integral_constant<int, 4>;
+  using J5 = std::integral_constant<int, 5>;
+  using J6 = std::integral_constant<int, 6>;
+  using J7 = std::integral_constant<int, 7>;
 
   if (n_tiles > 0) {
-    // Prologue: K(0), K(1) as if filled two and three phases before phase 0,
-    // K(2), V(0) as the fills of phase -1.
+    // Prologue: tiles 0 .. 4 (K and V) as if filled at phases -5 .. -1.
     fill_k(J0(), 0);
-    fill_k(J1(), 1);
-    fill_k(J2(), 2);
     fill_v(J0(), 0);
-    // The first MFMA phases of the two waves of a pair (p = 0, 1) read V
-    // slots 2 and 3 with zero weights: zero them, since 0 * NaN of stale LDS
-    // contents would not be zero.
-    g_v2[tid] = make_uint4(0, 0, 0, 0);
-    g_v3[tid] = make_uint4(0, 0, 0, 0);
-    __builtin_amdgcn_s_waitcnt(0x0070 | 2);  // vmcnt(2), lgkmcnt(0)
+    fill_k(J1(), 1);
+    fill_v(J1(), 1);
+    fill_k(J2(), 2);
+    fill_v(J2(), 2);
+    fill_k(J3(), 3);
+    fill_v(J3(), 3);
+    fill_k(J4(), 4);
+    fill_v(J4(), 4);
+    // The first MFMA phases of the two waves of a pair (p = 0, 1) read the
+    // V tiles of slots 6 and 7 with zero weights: zero them, since 0 * NaN
+    // of stale LDS contents would not be zero.
+    g_v6[tid] = make_uint4(0, 0, 0, 0);
+    g_v7[tid] = make_uint4(0, 0, 0, 0);
+    __builtin_amdgcn_s_waitcnt(0x0070 | 8);  // vmcnt(8), lgkmcnt(0): tile 0 has landed
     barrier_lds();
     // Even-tile waves run MFMA phases at even p, odd-tile waves at odd p;
     // both run the same number of phases (and barriers).
     const int n_phases = n_tiles + 2;
     if (par == 0) {
 #pragma nounroll
-      for (int p = 0; p < n_phases; p += 4) {
+      for (int p = 0; p < n_phases; p += 8) {
         fills(J0(), p);     mphase(J0()); sync();
         fills(J1(), p + 1); vphase(p);              sync();
+        if (p + 2 >= n_phases) break;
         fills(J2(), p + 2); mphase(J2()); sync();
         fills(J3(), p + 3); vphase(p + 2);          sync();
+        if (p + 4 >= n_phases) break;
+        fills(J4(), p + 4); mphase(J4()); sync();
+        fills(J5(), p + 5); vphase(p + 4);          sync();
+        if (p + 6 >= n_phases) break;
+        fills(J6(), p + 6); mphase(J6()); sync();
+        fills(J7(), p + 7); vphase(p + 6);          sync();
       }
     } else {
 #pragma nounroll
-      for (int p = 0; p < n_phases; p += 4) {
+      for (int p = 0; p < n_phases; p += 8) {
         fills(J0(), p);     vphase(p - 1);              sync();
         fills(J1(), p + 1); mphase(J1()); sync();
+        if (p + 2 >= n_phases) break;
         fills(J2(), p + 2); vphase(p + 1);              sync();
         fills(J3(), p + 3); mphase(J3()); sync();
+        if (p + 4 >= n_phases) break;
+        fills(J4(), p + 4); vphase(p + 3);              sync();
+        fills(J5(), p + 5); mphase(J5()); sync();
+        if (p + 6 >= n_phases) break;
+        fills(J6(), p + 6); vphase(p + 5);              sync();
+        fills(J7(), p + 7); mphase(J7()); sync();
       }
     }
     __builtin_amdgcn_s_waitcnt(0x0F70 | 0);  // no fill may land in the merge area
@@ -576,9 +612,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_pair_kernel(FwdArgs
   }
 
   // ---- merge the pair: the odd-tile wave hands (O, l, m) to its partner
-  // through LDS.  The 64 KB of ring slots hold O as 16 vec4 groups
+  // through LDS.  Eight 8 KB tiles (64 KB) hold O as 16 vec4 groups
   // ([d block][query block][register / 4]) x 4 row groups x 64 lanes; group
-  // vg sits in slot vg / 2, so every index is a compile-time slot.
+  // vg sits in tile vg / 2, so every index is a compile-time tile.
   auto mptr = [&](auto vg_tag) -> float4* __attribute__((always_inline)) {
     constexpr int VG = decltype(vg_tag)::value;
     return reinterpret_cast<float4*>(mslot<VG / 2>()) + ((VG & 1) * 4 + rg) * 64 + lane;
