@@ -16,13 +16,18 @@
 // lane ends up holding four consecutive output features of one token -- one
 // 8-byte store, along a head's 64 dimensions or along Y's row.
 //
-// Workgroup: 4 waves, a 128 (features) x 128 (tokens) tile, each wave 64 x
-// 64 (2 x 2 blocks of 32 x 32).  K runs in steps of 64: W and A tiles of
-// 128 x 64 bf16 reach LDS by buffer loads that write LDS directly, double
-// buffered, one barrier per step; rows past the end of W or A read as zero
-// through the descriptor's range check.  For the output projection a K step
-// of 64 is exactly one head, so the A tile of a step is 128 rows of one
-// head's [n, 64] slab: a per-row offset, no gather of single elements.
+// Workgroup: 4 waves, 2 (features) x 2 (tokens); a wave owns 64 features x
+// 32 TB tokens (2 x TB blocks of 32 x 32), so per 16-wide k step it reads
+// 2 + TB fragments from LDS for 2 TB products.  TB = 4 (a 128 x 256 tile)
+// when the grid still fills the chip, else TB = 2 (128 x 128).  K runs in
+// steps of 32: the W and A tiles of a step reach LDS by buffer loads that
+// write LDS directly, into a ring of three slots two steps ahead of use, one
+// bare barrier per step.  Rows past the end of W or A read as zero through
+// the descriptor's range check.  For the output projection two K steps make
+// one head, so the A tile of a step is a 32-wide column band of one head's
+// [n, 64] slab: a per-row offset, no gather of single elements.
+#include <type_traits>
+
 #include "common.h"
 
 namespace headattn {
@@ -36,23 +41,65 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr int kThreads = 256;
 constexpr int kBN = 128;  // output features per workgroup
-constexpr int kBM = 128;  // tokens per workgroup
-constexpr int kBK = 64;   // k per step (= one head for the output projection)
-constexpr uint32_t kRowBytes = kBK * 2;
-constexpr int kTileChunks = 128 * 8;  // 16-byte chunks of a 128 x 64 tile
+constexpr int kBK = 32;   // k per step
+constexpr int kSlots = 3;
+constexpr uint32_t kStepBytes = kBK * 2;        // bytes of one row in one step
 constexpr uint32_t kBufferWord3 = 0x00020000u;  // raw buffer, 32-bit elements (gfx9 family)
 constexpr uint32_t kOutOfRange = 0x80000000u;   // an offset the range check always rejects
 
-__shared__ uint4 s_w[2][kTileChunks];
-__shared__ uint4 s_a[2][kTileChunks];
+// Ring slots: the W tile (128 rows) and the A tile (up to 256 rows) of one
+// step, rows of 64 B (4 chunks of 16 B; chunk c of row r at position
+// c ^ ((r / 2) % 4), so the 8 rows one read instruction touches per cycle hit
+// 8 different 16-byte bank groups).
+__shared__ uint4 g_w0[kBN * 4], g_w1[kBN * 4], g_w2[kBN * 4];
+__shared__ uint4 g_a0[256 * 4], g_a1[256 * 4], g_a2[256 * 4];
+
+template <int S>
+__device__ __forceinline__ uint4* wslot() {
+  return S == 0 ? g_w0 : S == 1 ? g_w1 : g_w2;
+}
+template <int S>
+__device__ __forceinline__ uint4* aslot() {
+  return S == 0 ? g_a0 : S == 1 ? g_a1 : g_a2;
+}
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   f32x2 v = {lo, hi};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
-template <bool HEAD_OUT>
+// One 16-byte-per-lane buffer load that writes LDS directly (lane l's 16
+// bytes at lds + 16 l), issued from inline assembly: the compiler then does
+// not track these asynchronous LDS writes and adds no waits of its own for
+// them; the ring's explicit vmcnt waits and barriers order them.
+// M0 is a reserved register, so its clobber below is documentation only:
+// nothing else in these kernels reads M0 (checked in the ISA).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_fill16(__amdgpu_buffer_rsrc_t rsrc, const void* lds, uint32_t voff) {
+  const uint32_t base = (uint32_t)(uintptr_t)(const lds_void_t*)lds;
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(base)), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Wait until at most N of this wave's buffer loads are outstanding and its
+// LDS operations are done, then a bare workgroup barrier (a workgroup fence
+// would add a wait for every fill in flight).
+template <int N>
+__device__ __forceinline__ void wait_barrier() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0070 | N);  // vmcnt(N), lgkmcnt(0)
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <bool HEAD_OUT, int TB>
 __global__ __launch_bounds__(kThreads, 2) void proj_gemm_kernel(ProjArgs a) {
+  constexpr int kBM = 64 * TB;  // tokens per workgroup
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
@@ -69,123 +116,165 @@ __global__ __launch_bounds__(kThreads, 2) void proj_gemm_kernel(ProjArgs a) {
   const int K = a.K;
   const int nk = K / kBK;
 
-  // ---- fills: one instruction of the workgroup covers 32 rows of a tile;
-  // lane l of wave w writes chunk 64 w + l of that quarter (row 8 w + l / 8,
-  // position l % 8), which receives the row's chunk (l % 8) ^ (row % 8).
+  // ---- fills: one instruction of a wave covers 16 rows of a tile; lane l
+  // writes position l % 4 of row l / 4, which receives the row's chunk
+  // (l % 4) ^ ((row / 2) % 4).  Per step a wave fills 32 rows of W
+  // (2 loads) and 16 TB rows of A (TB loads).
   const __amdgpu_buffer_rsrc_t rw =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.W), (short)0, (int)a.w_bytes, kBufferWord3);
   const __amdgpu_buffer_rsrc_t ra =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.A), (short)0, (int)a.a_bytes, kBufferWord3);
-  const int fpos = lane & 7;
-  uint32_t w_off[4], a_off[4], a_step;
+  const int fpos = lane & 3;
+  uint32_t w_off[2], a_off[TB];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int row = 32 * q + 8 * wave + (lane >> 3);
-    const uint32_t chunk = 16u * (uint32_t)(fpos ^ (row & 7));
+  for (int q = 0; q < 2; ++q) {
+    const int row = 32 * wave + 16 * q + (lane >> 2);
+    const uint32_t chunk = 16u * (uint32_t)(fpos ^ ((row >> 1) & 3));
     const int n = n0 + row;
     w_off[q] = n < a.N ? (uint32_t)n * (uint32_t)K * 2u + chunk : kOutOfRange;
+  }
+#pragma unroll
+  for (int q = 0; q < TB; ++q) {
+    const int row = 16 * TB * wave + 16 * q + (lane >> 2);
+    const uint32_t chunk = 16u * (uint32_t)(fpos ^ ((row >> 1) & 3));
     const int m = m0 + row;
     if (HEAD_OUT) {
       // A = X [M, K] row-major
       a_off[q] = m < a.M ? (uint32_t)m * (uint32_t)K * 2u + chunk : kOutOfRange;
     } else {
-      // A = Concat(heads of O): row m = (b, t), step s = head s of O[b, s, t, :]
+      // A = Concat(heads of O): row m = (b, t), head s of O[b, s, t, :]
       const int b = m / a.n_seq;
       const int t = m - b * a.n_seq;
-      a_off[q] = m < a.M ? ((uint32_t)b * (uint32_t)a.H * (uint32_t)a.n_seq + (uint32_t)t) * kRowBytes + chunk
+      a_off[q] = m < a.M ? ((uint32_t)b * (uint32_t)a.H * (uint32_t)a.n_seq + (uint32_t)t) * (kHeadDim * 2u) + chunk
                          : kOutOfRange;
     }
   }
-  // Byte advance of one K step along the A rows.
-  a_step = HEAD_OUT ? kRowBytes : (uint32_t)a.n_seq * kRowBytes;
-  auto fill = [&](int slot, int kt) __attribute__((always_inline)) {
+  // Byte offset of step kt along an A row: 64 B per step for X; for O, head
+  // kt / 2 (n_seq rows of 128 B further each) and half kt % 2 of its 64 d.
+  auto a_step = [&](int kt) __attribute__((always_inline)) -> uint32_t {
+    return HEAD_OUT ? (uint32_t)kt * kStepBytes
+                    : (uint32_t)(kt >> 1) * (uint32_t)a.n_seq * (kHeadDim * 2u) + (uint32_t)(kt & 1) * kStepBytes;
+  };
+  auto fill = [&](auto slot_tag, int kt) __attribute__((always_inline)) {
+    constexpr int S = decltype(slot_tag)::value;
+    const uint32_t ws = (uint32_t)kt * kStepBytes, as = a_step(kt);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t wo = w_off[q] == kOutOfRange ? kOutOfRange : w_off[q] + (uint32_t)kt * kRowBytes;
-      const uint32_t ao = a_off[q] == kOutOfRange ? kOutOfRange : a_off[q] + (uint32_t)kt * a_step;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_void_t*)(&s_w[slot][256 * q + 64 * wave]), 16, wo, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(&s_a[slot][256 * q + 64 * wave]), 16, ao, 0, 0, 0);
+    for (int q = 0; q < 2; ++q) {
+      const uint32_t wo = w_off[q] == kOutOfRange ? kOutOfRange : w_off[q] + ws;
+      lds_fill16(rw, wslot<S>() + 128 * wave + 64 * q, wo);
+    }
+#pragma unroll
+    for (int q = 0; q < TB; ++q) {
+      const uint32_t ao = a_off[q] == kOutOfRange ? kOutOfRange : a_off[q] + as;
+      lds_fill16(ra, aslot<S>() + 64 * TB * wave + 64 * q, ao);
     }
   };
 
-  f32x16 acc[2][2];  // [feature block][token block]
+  f32x16 acc[2][TB];  // [feature block][token block]
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < TB; ++j) acc[i][j] = f32x16{};
 
-  fill(0, 0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int slot = kt & 1;
-    if (kt + 1 < nk) fill(slot ^ 1, kt + 1);
-    // Fragments of k step s: lane (ln, hh) reads row 64 w + 32 blk + ln,
-    // chunk 2 s + hh (d / k 16 s + 8 hh .. + 7).
-    const uint4* wt = s_w[slot];
-    const uint4* at = s_a[slot];
+  // One step: S = kt % 3 is its slot.  Step kt has landed (only step kt + 1's
+  // loads may be in flight) and every wave is done with step kt - 1, whose
+  // slot step kt + 2 takes.  Fragments of k sub-step s: lane (ln, hh) reads
+  // row 64 wn + 32 blk + ln of W (32 TB wm + 32 blk + ln of A), chunk
+  // 2 s + hh (k 16 s + 8 hh .. + 7).
+  auto step = [&](auto slot_tag, int kt) __attribute__((always_inline)) {
+    constexpr int S = decltype(slot_tag)::value;
+    using S2 = std::integral_constant<int, (S + 2) % kSlots>;
+    if (kt >= nk) return;
+    wait_barrier<2 + TB>();
+    fill(S2(), kt + 2);
+    const uint4* wt = wslot<S>();
+    const uint4* at = aslot<S>();
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int s = 0; s < 2; ++s) {
       const int ch = 2 * s + hh;
-      bf16x8 wf[2], af[2];
+      bf16x8 wf[2], af[TB];
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk) {
-        const int rw_ = 64 * wn + 32 * blk + ln;
-        const int ra_ = 64 * wm + 32 * blk + ln;
-        wf[blk] = __builtin_bit_cast(bf16x8, wt[rw_ * 8 + (ch ^ (rw_ & 7))]);
-        af[blk] = __builtin_bit_cast(bf16x8, at[ra_ * 8 + (ch ^ (ra_ & 7))]);
+        const int r = 64 * wn + 32 * blk + ln;
+        wf[blk] = __builtin_bit_cast(bf16x8, wt[r * 4 + (ch ^ ((r >> 1) & 3))]);
+      }
+#pragma unroll
+      for (int blk = 0; blk < TB; ++blk) {
+        const int r = 32 * TB * wm + 32 * blk + ln;
+        af[blk] = __builtin_bit_cast(bf16x8, at[r * 4 + (ch ^ ((r >> 1) & 3))]);
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[i], af[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < TB; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[i], af[j], acc[i][j], 0, 0, 0);
     }
-    __syncthreads();  // the next step's tile has landed; this step's slot is free
+  };
+
+  using Slot0 = std::integral_constant<int, 0>;
+  using Slot1 = std::integral_constant<int, 1>;
+  using Slot2 = std::integral_constant<int, 2>;
+  fill(Slot0(), 0);
+  fill(Slot1(), 1);
+  for (int kt = 0; kt < nk; kt += kSlots) {
+    step(Slot0(), kt);
+    step(Slot1(), kt + 1);
+    step(Slot2(), kt + 2);
   }
+  // The last two fills (past the end of K: out of range, zeros, never read)
+  // land before the workgroup's LDS is released.
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0)
 
   // ---- epilogue.  Register r of block (i, j) holds feature n0 + 64 wn +
-  // 32 i + 8 (r / 4) + 4 hh + r % 4 of token m0 + 64 wm + 32 j + ln: four
-  // consecutive features per 8-byte store.
+  // 32 i + 8 (r / 4) + 4 hh + r % 4 of token m0 + 32 TB wm + 32 j + ln:
+  // four consecutive features per 8-byte store.  A wave's 64 features are
+  // one head of one projection (64-aligned), so the output tensor and head
+  // are wave-uniform.
+  const int nw = n0 + 64 * wn;  // first feature of this wave
+  if (nw >= a.N) return;
+  const int d_model = a.H * kHeadDim;
+  const int p = nw / d_model;
+  const int hd = (nw - p * d_model) / kHeadDim;
+  __bf16* const out = static_cast<__bf16*>(a.out[HEAD_OUT ? p : 0]);
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int m = m0 + 64 * wm + 32 * j + ln;
+  for (int j = 0; j < TB; ++j) {
+    const int m = m0 + 32 * TB * wm + 32 * j + ln;
     if (m >= a.M) continue;
+    const int b = m / a.n_seq;
+    const int t = m - b * a.n_seq;
+    __bf16* const row = HEAD_OUT ? out + (((size_t)b * a.H + hd) * a.n_seq + t) * kHeadDim
+                                 : out + (size_t)m * a.N + nw;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int n = n0 + 64 * wn + 32 * i + 8 * g + 4 * hh;
-        if (n >= a.N) continue;
         uint2 v;
         v.x = pack_bf16x2(acc[i][j][4 * g], acc[i][j][4 * g + 1]);
         v.y = pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
-        if (HEAD_OUT) {
-          // feature n = (projection p, head hd, dim c); token m = (b, t)
-          const int d_model = a.H * kHeadDim;
-          const int p = n / d_model;
-          const int hd = (n - p * d_model) / kHeadDim;
-          const int c = n % kHeadDim;
-          const int b = m / a.n_seq;
-          const int t = m - b * a.n_seq;
-          __bf16* out = static_cast<__bf16*>(a.out[p]);
-          *reinterpret_cast<uint2*>(out + (((size_t)b * a.H + hd) * a.n_seq + t) * kHeadDim + c) = v;
-        } else {
-          __bf16* y = static_cast<__bf16*>(a.out[0]);
-          *reinterpret_cast<uint2*>(y + (size_t)m * a.N + n) = v;
-        }
+        *reinterpret_cast<uint2*>(row + 32 * i + 8 * g + 4 * hh) = v;
       }
     }
   }
 }
 
+template <bool HEAD_OUT>
+hipError_t launch_tb(const ProjArgs& a, hipStream_t s) {
+  // 256-token tiles while they still give every compute unit a workgroup.
+  const long long n_blocks = (a.N + kBN - 1) / kBN;
+  const long long big = n_blocks * ((a.M + 255) / 256);
+  ProjArgs args = a;
+  void* kargs[] = {&args};
+  if (big >= 256)
+    return hipLaunchKernel(reinterpret_cast<const void*>(&proj_gemm_kernel<HEAD_OUT, 4>), dim3((unsigned)big),
+                           dim3(kThreads), kargs, 0, s);
+  const long long small = n_blocks * ((a.M + 127) / 128);
+  return hipLaunchKernel(reinterpret_cast<const void*>(&proj_gemm_kernel<HEAD_OUT, 2>), dim3((unsigned)small),
+                         dim3(kThreads), kargs, 0, s);
+}
+
 }  // namespace
 
 hipError_t launch_proj(const ProjArgs& a, bool head_out, hipStream_t s) {
-  const long long blocks = (long long)((a.N + kBN - 1) / kBN) * ((a.M + kBM - 1) / kBM);
-  ProjArgs args = a;
-  void* kargs[] = {&args};
-  const void* fn = head_out ? reinterpret_cast<const void*>(&proj_gemm_kernel<true>)
-                            : reinterpret_cast<const void*>(&proj_gemm_kernel<false>);
-  return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(kThreads), kargs, 0, s);
+  return head_out ? launch_tb<true>(a, s) : launch_tb<false>(a, s);
 }
 
 }  // namespace headattn
