@@ -355,9 +355,9 @@ LEG_GRIDS = {("attn_fwd_bf16_short_kernel<none>", 65536): "encoder_base",
              ("bwd_dkdv_kernel<none>", 262144): "decoder_big_bwd (cross)",
              ("bwd_dq_kernel<none>", 131072): "decoder_big_bwd (cross)",
              ("bwd_rowdot_kernel", 524288): "decoder_big_bwd (self and cross)",
-             ("proj_gemm_kernel<true>", 196608): "mha_proj (self Q, K, V)",
+             ("proj_gemm_kernel<true>", 98304): "mha_proj (self Q, K, V)",
              ("proj_gemm_kernel<true>", 65536): "mha_proj (cross Q)",
-             ("proj_gemm_kernel<true>", 163840): "mha_proj (cross K, V)",
+             ("proj_gemm_kernel<true>", 81920): "mha_proj (cross K, V)",
              ("proj_gemm_kernel<false>", 65536): "mha_proj (self and cross output)",
              ("attn_fwd_bf16_pair_kernel<causal>", 262144): "long_causal",
              ("decode_partial_kernel", 4194304): "kv_decode",

@@ -86,7 +86,7 @@ __device__ __forceinline__ void fill_tile(Tile& t, __amdgpu_buffer_rsrc_t r, int
   for (int half = 0; half < 2; ++half) {
     const int row = 32 * half + 8 * wave + (lane >> 3);
     const uint32_t off = (uint32_t)(r0 + row) * kRowBytes + 16u * (uint32_t)(fpos ^ (2 * (row & 3)));
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(&t.c[256 * half + 64 * wave]), 16, off, 0, 0, 0);
+    lds_fill16(r, &t.c[256 * half + 64 * wave], off);
   }
 }
 
@@ -117,9 +117,8 @@ __device__ __forceinline__ bf16x8 tr_frag(const Tile& t, int db, int j, int lane
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// Ring slots.  Distinct objects, so the compiler tracks the asynchronous LDS
-// writes of the fills per slot and waits only where the code does.  The
-// dK/dV kernel streams Q (a), dO (b) and L, D (ld); the dQ kernel K (a) and
+// Ring slots (fills issued with lds_fill16, ordered by the ring's own
+// waits).  The dK/dV kernel streams Q (a), dO (b) and L, D (ld); the dQ kernel K (a) and
 // V (b).  Per ld slot: L of the tile's 64 rows in floats 0..63, D in
 // 64..127; the buffer load that fills them writes 1 KB, the rest is a
 // landing area.
@@ -310,7 +309,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
     fill_tile(bslot<S>(), rdo, q0, wave, lane);
     if (wave == 0) {
       const uint32_t off = ld_base == kOutOfRange ? kOutOfRange : ld_base + (uint32_t)q0 * 4u;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rld, (lds_void_t*)ldslot<S>(), 16, off, 0, 0, 0);
+      lds_fill16(rld, ldslot<S>(), off);
     }
   };
 
@@ -400,6 +399,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
   if (n_tiles > 0) {
     fill(Slot0(), 0);
     fill(Slot1(), 1);
+    // Everything issued so far has landed: the register fragments loaded
+    // above, and the first two tiles.  (The compiler does not see the fills;
+    // without this wait it would re-wait for its own loads inside the loop
+    // with a vmcnt(0) that also drains the ring.)
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0), lgkmcnt(0)
     for (int u = 0; u < n_tiles; u += kSlots) {
       step(Slot0(), u);
       step(Slot1(), u + 1);
@@ -583,6 +587,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   if (n_tiles > 0) {
     fill(Slot0(), 0);
     fill(Slot1(), 1);
+    // Everything issued so far has landed: the register fragments loaded
+    // above, and the first two tiles.  (The compiler does not see the fills;
+    // without this wait it would re-wait for its own loads inside the loop
+    // with a vmcnt(0) that also drains the ring.)
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0), lgkmcnt(0)
     for (int u = 0; u < n_tiles; u += kSlots) {
       step(Slot0(), u);
       step(Slot1(), u + 1);

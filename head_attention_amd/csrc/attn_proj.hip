@@ -68,23 +68,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
-// One 16-byte-per-lane buffer load that writes LDS directly (lane l's 16
-// bytes at lds + 16 l), issued from inline assembly: the compiler then does
-// not track these asynchronous LDS writes and adds no waits of its own for
-// them; the ring's explicit vmcnt waits and barriers order them.
-// M0 is a reserved register, so its clobber below is documentation only:
-// nothing else in these kernels reads M0 (checked in the ISA).
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void lds_fill16(__amdgpu_buffer_rsrc_t rsrc, const void* lds, uint32_t voff) {
-  const uint32_t base = (uint32_t)(uintptr_t)(const lds_void_t*)lds;
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :
-               : "s"(__builtin_amdgcn_readfirstlane(base)), "v"(voff), "s"(rsrc)
-               : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
 // Wait until at most N of this wave's buffer loads are outstanding and its
 // LDS operations are done, then a bare workgroup barrier (a workgroup fence
 // would add a wait for every fill in flight).

@@ -33,6 +33,26 @@ struct FwdArgs {
   int radius;
 };
 
+// One 16-byte-per-lane buffer load that writes LDS directly (lane l's 16
+// bytes land at lds + 16 l; offsets outside the descriptor's range read as
+// zero), issued from inline assembly.  The compiler then does not track
+// these asynchronous LDS writes and adds no waits of its own for them (with
+// the builtin it could not tell some ring slots apart and drained the whole
+// ring before their reads); the caller's explicit vmcnt waits and barriers
+// order them.  Two rules follow: the compiler's own vector-memory loads must
+// have landed (an explicit vmcnt(0)) before a ring runs, or it re-waits for
+// them inside the ring with a vmcnt(0) that drains it; and nothing else in
+// these kernels may use M0, which the compiler is not told about (checked in
+// the ISA: M0 is a reserved register and cannot be named as a clobber).
+__device__ __forceinline__ void lds_fill16(__amdgpu_buffer_rsrc_t rsrc, const void* lds, uint32_t voff) {
+  typedef __attribute__((address_space(3))) const void lds_cvoid_t;
+  const uint32_t base = (uint32_t)(uintptr_t)(lds_cvoid_t*)lds;
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(base)), "v"(voff), "s"(rsrc)
+               : "memory");
+}
+
 // Mask shapes the bf16 forward kernels are specialised for: none (key
 // padding only), the causal triangle, and the band of restricted
 // self-attention (keys i - radius .. i + radius, or i - radius .. i).
