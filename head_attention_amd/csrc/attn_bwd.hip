@@ -465,11 +465,6 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   const __bf16* V = static_cast<const __bf16*>(a.V) + (size_t)bh * a.n_k * kHeadDim;
   const __bf16* dO = static_cast<const __bf16*>(a.dO) + (size_t)bh * a.n_q * kHeadDim;
 
-  const __amdgpu_buffer_rsrc_t rk =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(K), (short)0, (int)((uint32_t)kv_lim * kRowBytes), kBufferWord3);
-  const __amdgpu_buffer_rsrc_t rv =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(V), (short)0, (int)((uint32_t)kv_lim * kRowBytes), kBufferWord3);
-
   // Q and dO fragments of this lane's query (B operands of S^T = K Q^T and
   // dP^T = V dO^T), sign of scale folded into Q; zero for padded rows.
   const uint32_t sign = a.scale < 0.f ? 0x80008000u : 0u;
@@ -507,6 +502,14 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
   }
   if (q0 >= q_len) end = 0;
   const int n_tiles = end > k_start ? (end - k_start + kTile - 1) / kTile : 0;
+  // The descriptors end at the last key the workgroup may use (never past
+  // kv_len): the ring's fills past its last tile read zeros without touching
+  // memory.
+  const uint32_t k_bytes = (uint32_t)max(0, end) * kRowBytes;
+  const __amdgpu_buffer_rsrc_t rk =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(K), (short)0, (int)k_bytes, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rv =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(V), (short)0, (int)k_bytes, kBufferWord3);
   // Keys this wave needs: [wave_start, wave_end).
   int wave_start = 0, wave_end = end;
   if (CAUSAL) wave_end = min(wave_end, qw0 + 32);

@@ -243,7 +243,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_pair_kernel(FwdArgs
   const int k_base = t0 * kBN;  // first key of relative tile 0
   K += (size_t)k_base * kHeadDim;
   V += (size_t)k_base * kHeadDim;
-  const uint32_t n_bytes = (uint32_t)max(0, kv_lim - k_base) * kRowBytes;
+  // The descriptors end at the last key the workgroup may use: the ring's
+  // fills past its last tile read zeros without touching memory.
+  const uint32_t n_bytes = (uint32_t)max(0, end - k_base) * kRowBytes;
   const __amdgpu_buffer_rsrc_t rk =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(K), (short)0, (int)n_bytes, kBufferWord3);
   const __amdgpu_buffer_rsrc_t rv =
