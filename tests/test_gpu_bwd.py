@@ -163,3 +163,76 @@ def test_backward_restricted(cid):
     if kl is not None:  # keys past kv_len: zero dK, dV
         for b in range(B):
             assert torch.all(grads[1][b, :, int(kl[b]):] == 0) and torch.all(grads[2][b, :, int(kl[b]):] == 0)
+
+
+def _bench_dO(c):
+    """The incoming gradient the bench draws for a workload call (seeded,
+    same shape as O)."""
+    g = workloads.generator(1200)
+    return workloads.randn(g, tuple(c["Q"].shape), torch.bfloat16)
+
+
+def test_long_causal_backward_sampled():
+    """The bench's long_causal backward (B1 h16 n=8192 causal) at full size
+    in the launch configuration the bench times, on outputs the oracle can
+    compute alone: dQ of sampled rows (row i's gradient depends only on its
+    own row over keys 0..i), and dK, dV of the last 128 keys (only rows
+    8064..8191 see them), each from a batch of one-row problems with key
+    padding kv_len = i + 1 -- the causal row written as a padded one."""
+    c = workloads.make("long_causal")["calls"][0]
+    dO = _bench_dO(c)
+    Qd, Kd, Vd, dOd = (t.cuda() for t in (c["Q"], c["K"], c["V"], dO))
+    say("[long_causal backward] B1 h16 n8192 causal")
+    lse = torch.empty((1, 16, 8192), dtype=torch.float32, device="cuda")
+    O = ha.forward(Qd, Kd, Vd, mask_kind=2, scale=c["scale"], lse=lse)
+    dQ, dK, dV = (np64(t) for t in ha.backward(Qd, Kd, Vd, O, dOd, lse, mask_kind=2, scale=c["scale"]))
+    Q, K, V, G = (np64(t) for t in (c["Q"], c["K"], c["V"], dO))
+    n = 8192
+    heads = (0, 5, 15)
+    tail = list(range(n - 128, n))
+    rng = np.random.default_rng(12)
+    picks = sorted({0, 1, 63, 64, 4095, 4096} | {int(x) for x in rng.integers(0, n - 128, 10)})
+    for h in heads:
+        rows = picks + tail
+        # one batch entry per row i: its query, all keys, kv_len = i + 1
+        Qb = Q[0, h][rows][:, None, None, :]
+        Gb = G[0, h][rows][:, None, None, :]
+        Kb = np.broadcast_to(K[0, h], (len(rows), 1, n, 64))
+        Vb = np.broadcast_to(V[0, h], (len(rows), 1, n, 64))
+        kl = np.array([i + 1 for i in rows])
+        rQ, rK, rV = orc.attention_backward(Qb, Kb, Vb, Gb, mask_kind=orc.MASK_KEY_PADDING, kv_lens=kl,
+                                            scale=c["scale"])
+        _check_grad(dQ[0, h][rows], rQ[:, 0, 0], f"dQ head {h} ({len(rows)} rows)")
+        # the tail rows are all the rows that see the last 128 keys
+        nt = len(tail)
+        _check_grad(dK[0, h, n - 128:], rK[-nt:, 0].sum(axis=0)[n - 128:], f"dK head {h} (last 128 keys)")
+        _check_grad(dV[0, h, n - 128:], rV[-nt:, 0].sum(axis=0)[n - 128:], f"dV head {h} (last 128 keys)")
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["centred", "causal"])
+def test_long_restricted_backward_sampled(causal):
+    """Restricted backward at the long_restricted size (B1 h16 n=8192,
+    radius 256) on positions the oracle can isolate: around position j only
+    positions j - 2r .. j + 2r interact with j (its own window and the
+    windows of the rows that see it), so the oracle's restricted backward
+    on that slice gives dQ, dK and dV of j exactly."""
+    c = workloads.make("long_restricted")["calls"][0]
+    r = c["radius"]
+    mask = c["mask"] | (ha.ATTN_MASK_CAUSAL if causal else 0)
+    dO = _bench_dO(c)
+    Qd, Kd, Vd, dOd = (t.cuda() for t in (c["Q"], c["K"], c["V"], dO))
+    say(f"[long_restricted backward causal={causal}] B1 h16 n8192 radius {r}")
+    lse = torch.empty((1, 16, 8192), dtype=torch.float32, device="cuda")
+    O = ha.forward_restricted(Qd, Kd, Vd, r, mask_kind=mask, scale=c["scale"], lse=lse)
+    dQ, dK, dV = (np64(t) for t in ha.backward(Qd, Kd, Vd, O, dOd, lse, mask_kind=mask, scale=c["scale"],
+                                                 radius=r))
+    Q, K, V, G = (np64(t) for t in (c["Q"], c["K"], c["V"], dO))
+    n = 8192
+    for h, j in ((0, 0), (3, 300), (7, 4100), (15, n - 1), (9, 2 * r)):
+        lo, hi = max(0, j - 2 * r), min(n, j + 2 * r + 1)
+        sl = lambda x: x[:, h:h + 1, lo:hi]
+        rQ, rK, rV = orc.attention_backward(sl(Q), sl(K), sl(V), sl(G), mask_kind=mask, scale=c["scale"],
+                                            radius=r)
+        k = j - lo
+        for name, got, ref in (("dQ", dQ, rQ), ("dK", dK, rK), ("dV", dV, rV)):
+            _check_grad(got[0, h, j][None], ref[0, 0, k][None], f"{name} head {h} position {j}")
