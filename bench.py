@@ -64,10 +64,16 @@ KERNEL_SOURCES = ["attn_fwd_bf16_pair.hip", "attn_fwd_bf16_short.hip", "attn_fwd
 
 
 def kernel_source_hash() -> str:
+    """Hash of the kernels' code: the sources with comments and blank space
+    removed, so that a comment edit does not void the stored counters."""
+    import re
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "head_attention_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "head_attention_amd", "csrc", f), encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)   # block comments
+        text = re.sub(r"//[^\n]*", " ", text)                 # line comments
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

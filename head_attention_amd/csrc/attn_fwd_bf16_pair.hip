@@ -39,10 +39,11 @@
 //
 // K and V tiles reach LDS by buffer loads that write LDS directly (no VGPR
 // staging).  Every wave fills 1 KB of each tile; rows at or beyond the valid
-// length read as zero through the descriptor's range check, so padded K/V
-// memory (even NaN) is never read.  Tiles sit in 4-slot rings, K three phases
-// and V one phase ahead of use; a phase ends with a wait for this wave's
-// fills of two phases ago and a barrier.  K rows keep their 16-byte chunks
+// length (or past the last key the workgroup may use) read as zero through
+// the descriptor's range check, so padded K/V memory (even NaN) is never
+// read.  Tiles sit in an 8-slot ring, K five phases and V seven phases ahead
+// of use; a phase ends with a wait for this wave's fills of four phases ago
+// and a barrier.  K rows keep their 16-byte chunks
 // XOR-swizzled by row; V stays row-major (chunks swizzled by row % 4) and is
 // read transposed with ds_read_b64_tr_b16, which hands each lane four
 // consecutive keys of one d -- the A-operand order of O^T += V^T P^T.
