@@ -41,6 +41,8 @@ def _weights(g, rows, d_model):
     (32, 160, 16, 2),   # Transformer-big encoder output -> K, V of cross attention
     (3, 77, 3, 1),      # ragged tokens (M = 231) and features (N = 192)
     (1, 1, 1, 3),       # one token, one head
+    (32, 128, 16, 3),   # Transformer-big self-attention Q, K, V (256-token tiles)
+    (41, 97, 13, 3),    # 256-token tiles, ragged M = 3977 and N = 2496 (not a multiple of 128)
 ])
 def test_head_projection(B, n, h, n_out):
     g = workloads.generator(800 + n + h)
@@ -56,7 +58,9 @@ def test_head_projection(B, n, h, n_out):
         check_rounding(np64(o), r, f"projection {j}")
 
 
-@pytest.mark.parametrize("B,n,h", [(32, 128, 8), (32, 128, 16), (3, 77, 3), (1, 1, 1)])
+@pytest.mark.parametrize("B,n,h", [(32, 128, 8), (32, 128, 16), (3, 77, 3), (1, 1, 1),
+                                   (16, 257, 38),   # ragged M = 4112, N = 2432 (not a multiple of 128)
+                                   (64, 128, 32)])  # M = 8192, N = 2048
 def test_output_projection(B, n, h):
     g = workloads.generator(900 + n + h)
     d = 64 * h
