@@ -252,6 +252,7 @@ attn_status attn_head_projection(const void* X, const void* W, attn_layout L, in
   a.n_seq = L.n_q;
   a.w_bytes = (uint32_t)w_bytes;
   a.a_bytes = (uint32_t)x_bytes;
+  a.xcd_fp = 0;
   const hipError_t e = launch_proj(a, true, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) {
     g_last_hip = e;
@@ -285,6 +286,7 @@ attn_status attn_output_projection(const void* O, const void* Wo, attn_layout L,
   a.n_seq = L.n_q;
   a.w_bytes = (uint32_t)w_bytes;
   a.a_bytes = (uint32_t)o_bytes;
+  a.xcd_fp = 0;
   const hipError_t e = launch_proj(a, false, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) {
     g_last_hip = e;

@@ -91,9 +91,30 @@ __global__ __launch_bounds__(kThreads, 2) void proj_gemm_kernel(ProjArgs a) {
   const int wn = wave & 1;   // feature half of the tile
   const int wm = wave >> 1;  // token half of the tile
 
+  // Tile of this workgroup.  Workgroup ids go round robin over the 8 XCDs;
+  // with xcd_fp = f each XCD owns a rectangle of f/8 of the token blocks by
+  // 1/f of the feature blocks, so a tile's X rows and W rows are mostly
+  // already in that XCD's L2 (the plain order sends the 8 feature blocks of
+  // one token block to 8 different XCDs, each fetching the same X rows).
   const int n_blocks = (a.N + kBN - 1) / kBN;
-  const int nb = blockIdx.x % n_blocks;
-  const int mb = blockIdx.x / n_blocks;
+  int nb = blockIdx.x % n_blocks;
+  int mb = blockIdx.x / n_blocks;
+  if (a.xcd_fp > 0) {
+    const int fp = a.xcd_fp;
+    const int x = blockIdx.x & 7;
+    const int l = blockIdx.x >> 3;
+    const int nbr = n_blocks / fp;                               // feature blocks per rectangle
+    const int mbr = ((a.M + kBM - 1) / kBM) / (8 / fp);         // token blocks per rectangle
+    // Inside the rectangle, groups of up to 8 token blocks walk all its
+    // feature blocks, so the workgroups an XCD runs at once share X rows
+    // and W rows (a long rectangle walked row by row would stream all its W
+    // rows through L2 once per token block).
+    const int g0 = l / (8 * nbr) * 8;  // first token block of l's group
+    const int gs = min(8, mbr - g0);   // token blocks in the group
+    const int r = l - g0 * nbr;
+    nb = (x % fp) * nbr + r / gs;
+    mb = (x / fp) * mbr + g0 + r % gs;
+  }
   const int n0 = nb * kBN;
   const int m0 = mb * kBM;
   const int K = a.K;
@@ -239,6 +260,23 @@ __global__ __launch_bounds__(kThreads, 2) void proj_gemm_kernel(ProjArgs a) {
   }
 }
 
+// The XCD split with the fewest L2 fills, W rows read by 8/f XCDs and X rows
+// by f: f minimising w_bytes * 8/f + a_bytes * f among those that divide the
+// tile grid evenly; 0 (plain order) when none does.
+int xcd_split(const ProjArgs& a, long long n_blocks, long long m_blocks) {
+  int best = 0;
+  double best_cost = 0.0;
+  for (int f = 1; f <= 8; f *= 2) {
+    if (n_blocks % f != 0 || m_blocks % (8 / f) != 0) continue;
+    const double cost = (double)a.w_bytes * (8 / f) + (double)a.a_bytes * f;
+    if (best == 0 || cost < best_cost) {
+      best = f;
+      best_cost = cost;
+    }
+  }
+  return best;
+}
+
 template <bool HEAD_OUT>
 hipError_t launch_tb(const ProjArgs& a, hipStream_t s) {
   // 256-token tiles while they still give every compute unit a workgroup.
@@ -246,10 +284,13 @@ hipError_t launch_tb(const ProjArgs& a, hipStream_t s) {
   const long long big = n_blocks * ((a.M + 255) / 256);
   ProjArgs args = a;
   void* kargs[] = {&args};
-  if (big >= 256)
+  if (big >= 256) {
+    args.xcd_fp = xcd_split(a, n_blocks, (a.M + 255) / 256);
     return hipLaunchKernel(reinterpret_cast<const void*>(&proj_gemm_kernel<HEAD_OUT, 4>), dim3((unsigned)big),
                            dim3(kThreads), kargs, 0, s);
+  }
   const long long small = n_blocks * ((a.M + 127) / 128);
+  args.xcd_fp = xcd_split(a, n_blocks, (a.M + 127) / 128);
   return hipLaunchKernel(reinterpret_cast<const void*>(&proj_gemm_kernel<HEAD_OUT, 2>), dim3((unsigned)small),
                          dim3(kThreads), kargs, 0, s);
 }

@@ -101,6 +101,10 @@ struct ProjArgs {
   int M, N, K;   // M = B * n_seq tokens, N output features, K = H * 64
   int H, n_seq;
   uint32_t w_bytes, a_bytes;
+  // Tile order: 0 = feature block fastest over the whole grid; f in {1, 2,
+  // 4, 8} = each of the 8 XCDs takes a rectangle of 1/f of the feature
+  // blocks by f/8 of the token blocks (set by the launcher).
+  int xcd_fp;
 };
 hipError_t launch_proj(const ProjArgs& a, bool head_out, hipStream_t s);
 
