@@ -438,7 +438,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------- dQ
 template <int MODE>
-__global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kThreads, 3) void bwd_dq_kernel(BwdArgs a) {
   constexpr bool CAUSAL = MODE == kModeCausal;
   constexpr bool BAND = MODE == kModeBand;
 
@@ -555,6 +555,24 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
     }
     bool need_mask = (k0 + kTile > kv_lim) || (CAUSAL && k0 + kTile - 1 > qw0);
     if (BAND) need_mask = need_mask || (k0 + kTile - 1 > qw0 + wr) || (k0 < qw0 + 31 - wl);
+    if (need_mask) {
+      // Register r of key block kb holds key k0 + 32 kb + 4 hh + off(r),
+      // off(r) = 8 (r / 4) + r % 4; it is allowed when lo <= off(r) < lim.
+      int hi = kv_lim;
+      if (CAUSAL) hi = min(hi, qi + 1);
+      if (BAND) hi = min(hi, qi + wr + 1);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int base = k0 + 32 * kb + 4 * hh;
+        const int lim = hi - base;
+        const int lo = BAND ? qi - wl - base : INT_MIN;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int off = 8 * (r >> 2) + (r & 3);
+          st[kb][r] = (off < lim && off >= lo) ? st[kb][r] : -INFINITY;
+        }
+      }
+    }
     uint32_t ps[16];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -564,14 +582,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
           const int r = 2 * r2 + e;
-          float x = fmaf(st[kb][r], c, -lrow);
-          if (need_mask) {
-            const int kj = k0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
-            bool ok = kj < kv_lim;
-            if (CAUSAL) ok = ok && kj <= qi;
-            if (BAND) ok = ok && kj >= qi - wl && kj <= qi + wr;
-            x = ok ? x : -INFINITY;
-          }
+          const float x = fmaf(st[kb][r], c, -lrow);  // -inf for a masked key (c > 0)
           const float p = __builtin_amdgcn_exp2f(x);
           g[e] = p * (dpt[kb][r] - dval);
         }
