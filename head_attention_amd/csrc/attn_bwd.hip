@@ -28,8 +28,11 @@
 //                query rows, key tiles stream through LDS, S^T = K Q^T and
 //                dP^T = V dO^T put the queries on the lanes, and dQ^T +=
 //                K^T dS^T takes dS^T from registers and K^T transposed from
-//                the tile.  No atomics: every output element has one owner,
-//                so the gradients are bitwise reproducible.
+//                the tile.  Three workgroups share a CU (at most 168 VGPRs,
+//                3 x 51 KB of LDS): a third wave per SIMD covers the serial
+//                chain of products and exponentials.  No atomics: every
+//                output element has one owner, so the gradients are bitwise
+//                reproducible.
 //
 // Streaming: tiles reach LDS by buffer loads that write LDS directly, into a
 // ring of three slots, two tiles ahead of use; one barrier per tile both
