@@ -2,7 +2,10 @@
 fp64 oracle on the same bf16 inputs, and of the whole multi-head sub-layer
 (projections + attention + output projection) built from the library's
 entry points.  Weights are seeded N(0, 1/d_model) draws (no trained weights
-are needed: the projections are plain linear maps).
+are needed: the projections are plain linear maps).  The shapes reach both
+tile sizes and every tile order the launcher picks: XCD rectangles of all,
+1/2, 1/4 or 1/8 of the feature blocks, a last partial group of token blocks,
+and the plain order for grids the split does not divide.
 
 Bars: the attention bars of gpu_util (max abs <= 2e-2 and relative L2 <=
 1e-2), and for a projection alone the bound its arithmetic fixes: products of
@@ -43,6 +46,9 @@ def _weights(g, rows, d_model):
     (1, 1, 1, 3),       # one token, one head
     (32, 128, 16, 3),   # Transformer-big self-attention Q, K, V (256-token tiles)
     (41, 97, 13, 3),    # 256-token tiles, ragged M = 3977 and N = 2496 (not a multiple of 128)
+    (2, 128, 16, 3),    # few tokens: each XCD takes 1/8 of the feature blocks
+    (8, 128, 16, 2),    # XCD rectangles of 1/4 of the feature blocks by 1/2 of the tokens
+    (144, 128, 16, 1),  # 9 token blocks per XCD: a full group of 8 and a group of 1
 ])
 def test_head_projection(B, n, h, n_out):
     g = workloads.generator(800 + n + h)
