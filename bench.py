@@ -459,9 +459,9 @@ def main():
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print(json.dumps({"error": "this build runs on one GPU only: the attention path has no "
-                                   "multi-GPU mode (see the sharding notes in DESIGN.md); "
-                                   "run with --gpus 1"}))
+        print(json.dumps({"error": "this library runs on one GPU: its attention path has no "
+                                   "multi-GPU mode (each GPU would run the same kernels on its "
+                                   "share of heads or sequences); run with --gpus 1"}))
         sys.exit(2)
 
     import head_attention_amd as ha
