@@ -73,12 +73,22 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
-// A streamed 64-row tile in LDS: row-major, 16-byte chunks of row r at
-// position chunk ^ (2 (r % 4)) -- the layout the transposed reads below
-// are laid out for.
+// A streamed 64-row tile in LDS: row-major, 16-byte chunk c of row r at
+// position c ^ swz(r), swz(r) = 2 (r % 4) ^ (r / 4) % 4.  Row reads (16
+// bytes per lane, lanes on consecutive rows, 16 lanes served together) and
+// transposed reads (four rows from a multiple of 4, adjacent chunks) then
+// spread over all banks: 16 consecutive rows of one chunk take 8 positions
+// in each row parity (rows r and r + 8 of a 128-byte row pair no longer
+// share banks), and a transposed read's rows take distinct positions.
+// Measured with SQ_LDS_BANK_CONFLICT on the dK/dV and dQ kernels: with
+// 2 (r % 4), the layout the transposed reads first had, every row read was
+// 2-way conflicted; 2 (r % 4) + (r / 4) % 2 removed two thirds of the
+// conflict cycles, and this layout the rest.
 struct Tile {
   uint4 c[kTile * 8];
 };
+
+__device__ __forceinline__ int swz(int r) { return (2 * (r & 3)) ^ ((r >> 2) & 3); }
 
 // Fill rows [r0, r0 + 64) of a [rows][64] bf16 tensor into t; rows at or
 // beyond the descriptor's range read as zero.  256 threads, 2 instructions
@@ -88,14 +98,14 @@ __device__ __forceinline__ void fill_tile(Tile& t, __amdgpu_buffer_rsrc_t r, int
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
     const int row = 32 * half + 8 * wave + (lane >> 3);
-    const uint32_t off = (uint32_t)(r0 + row) * kRowBytes + 16u * (uint32_t)(fpos ^ (2 * (row & 3)));
+    const uint32_t off = (uint32_t)(r0 + row) * kRowBytes + 16u * (uint32_t)(fpos ^ swz(row));
     lds_fill16(r, &t.c[256 * half + 64 * wave], off);
   }
 }
 
 // Row fragment: lane (ln, hh) gets row `row`, d 16 s + 8 hh .. + 7.
 __device__ __forceinline__ bf16x8 row_frag(const Tile& t, int row, int s, int hh) {
-  return __builtin_bit_cast(bf16x8, t.c[row * 8 + ((2 * s + hh) ^ (2 * (row & 3)))]);
+  return __builtin_bit_cast(bf16x8, t.c[row * 8 + ((2 * s + hh) ^ swz(row))]);
 }
 
 // Transposed fragment (A operand of X^T[d][r] times registers holding rows
@@ -106,15 +116,17 @@ __device__ __forceinline__ bf16x8 row_frag(const Tile& t, int row, int s, int hh
 // and 8-byte chunk h; the read returns to lane i the 4 rows kr - i/4 .. +3
 // of d = dbase + i.
 __device__ __forceinline__ bf16x8 tr_frag(const Tile& t, int db, int j, int lane) {
-  const char* base = reinterpret_cast<const char*>(t.c);
+  // swz depends on the row mod 16 only, so the 16-row step j is a plain
+  // offset and the per-lane part is shared by every j.
+  const char* base = reinterpret_cast<const char*>(t.c) + 16 * j * (int)kRowBytes;
   const int g = lane >> 4;
   const int i = lane & 15;
   s16x4 part[2];
 #pragma unroll
   for (int x = 0; x < 2; ++x) {
-    const int kr = 16 * j + 8 * x + 4 * (g >> 1) + (i >> 2);
+    const int kr = 8 * x + 4 * (g >> 1) + (i >> 2);  // row within the step
     const int h = 8 * db + 4 * (g & 1) + (i & 3);
-    const int byte = kr * (int)kRowBytes + 16 * ((h >> 1) ^ (2 * (kr & 3))) + 8 * (h & 1);
+    const int byte = kr * (int)kRowBytes + 16 * ((h >> 1) ^ swz(kr)) + 8 * (h & 1);
     part[x] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(base + byte));
   }
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));

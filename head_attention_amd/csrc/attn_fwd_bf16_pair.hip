@@ -257,7 +257,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_pair_kernel(FwdArgs
   // (l % 8) ^ swizzle(row).
   const int frow = 8 * wave + (lane >> 3);
   const int fpos = lane & 7;
-  const uint32_t koff = (uint32_t)frow * kRowBytes + 16u * (uint32_t)(fpos ^ (frow & 7));
+  const uint32_t koff = (uint32_t)frow * kRowBytes + 16u * (uint32_t)(fpos ^ k_swz(frow));
   const uint32_t voff = (uint32_t)frow * kRowBytes + 16u * (uint32_t)(fpos ^ (2 * (frow & 3)));
   auto fill_k = [&](auto slot_tag, int t) __attribute__((always_inline)) {
     constexpr int S = decltype(slot_tag)::value;
@@ -371,7 +371,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_pair_kernel(FwdArgs
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int row = 32 * kb + ln;
-      ka[kb][s] = __builtin_bit_cast(bf16x8, kt[row * 8 + ((2 * s + hh) ^ (row & 7))]);
+      ka[kb][s] = __builtin_bit_cast(bf16x8, kt[row * 8 + ((2 * s + hh) ^ k_swz(row))]);
     }
   };
   // O^T += V^T P^T for key step j, and the row sums of that step's weights.

@@ -175,7 +175,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_short_kernel(FwdArg
     for (int half = 0; half < 2; ++half) {
       const int row = 32 * half + 8 * wave + (lane >> 3);
       const uint32_t base = (uint32_t)(t * kBN + row) * kRowBytes;
-      const uint32_t koff = base + 16u * (uint32_t)(fpos ^ (row & 7));
+      const uint32_t koff = base + 16u * (uint32_t)(fpos ^ k_swz(row));
       const uint32_t voff = base + 16u * (uint32_t)(fpos ^ (2 * (row & 3)));
       const uint32_t chunk0 = (uint32_t)t * kTileChunks + 256u * half + 64u * wave;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(s_k + chunk0), 16, koff, 0, 0, 0);
@@ -214,8 +214,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_short_kernel(FwdArg
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int ch = 2 * s + hh;
-      const bf16x8 k0 = __builtin_bit_cast(bf16x8, kt[ln * 8 + (ch ^ (ln & 7))]);
-      const bf16x8 k1 = __builtin_bit_cast(bf16x8, kt[(32 + ln) * 8 + (ch ^ ((32 + ln) & 7))]);
+      const bf16x8 k0 = __builtin_bit_cast(bf16x8, kt[ln * 8 + (ch ^ k_swz(ln))]);
+      const bf16x8 k1 = __builtin_bit_cast(bf16x8, kt[(32 + ln) * 8 + (ch ^ k_swz(32 + ln))]);
       s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[s], s0, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[s], s1, 0, 0, 0);
     }

@@ -53,6 +53,14 @@ __device__ __forceinline__ void lds_fill16(__amdgpu_buffer_rsrc_t rsrc, const vo
                : "memory");
 }
 
+// Position of the 16-byte chunks of row r of a K tile that is only read by
+// rows (16 bytes per lane, lanes on consecutive rows): chunk c sits at
+// c ^ k_swz(r), distinct over any 8 consecutive rows and, for 16
+// consecutive rows, within each row parity -- so the reads spread over all
+// banks whether the LDS serves 8 or 16 lanes per cycle (r % 8 alone left
+// rows r and r + 8 on the same banks).
+__device__ __forceinline__ int k_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
 // Mask shapes the bf16 forward kernels are specialised for: none (key
 // padding only), the causal triangle, and the band of restricted
 // self-attention (keys i - radius .. i + radius, or i - radius .. i).
