@@ -78,8 +78,9 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // bytes per lane, lanes on consecutive rows, 16 lanes served together) and
 // transposed reads (four rows from a multiple of 4, adjacent chunks) then
 // spread over all banks: 16 consecutive rows of one chunk take 8 positions
-// in each row parity (rows r and r + 8 of a 128-byte row pair no longer
-// share banks), and a transposed read's rows take distinct positions.
+// in each row parity (rows r and r + 8, 1 KB apart and so on the same
+// banks, no longer share them), and a transposed read's rows take distinct
+// positions.
 // Measured with SQ_LDS_BANK_CONFLICT on the dK/dV and dQ kernels: with
 // 2 (r % 4), the layout the transposed reads first had, every row read was
 // 2-way conflicted; 2 (r % 4) + (r / 4) % 2 removed two thirds of the
