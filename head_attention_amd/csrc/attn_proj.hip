@@ -49,8 +49,11 @@ constexpr uint32_t kOutOfRange = 0x80000000u;   // an offset the range check alw
 
 // Ring slots: the W tile (128 rows) and the A tile (up to 256 rows) of one
 // step, rows of 64 B (4 chunks of 16 B; chunk c of row r at position
-// c ^ ((r / 2) % 4), so the 8 rows one read instruction touches per cycle hit
-// 8 different 16-byte bank groups).
+// c ^ ((r / 4) % 4)).  A fragment read has its lanes on consecutive rows and
+// the LDS serves 16 lanes (256 bytes) per cycle: rows r, r + 4, r + 8,
+// r + 12 fall on the same banks and take 4 different positions, so the read
+// is free of bank conflicts.  ((r / 2) % 4 gave those rows 2 positions:
+// half of the kernel's active LDS cycles were conflict stalls.)
 __shared__ uint4 g_w0[kBN * 4], g_w1[kBN * 4], g_w2[kBN * 4];
 __shared__ uint4 g_a0[256 * 4], g_a1[256 * 4], g_a2[256 * 4];
 
@@ -122,7 +125,7 @@ __global__ __launch_bounds__(kThreads, 2) void proj_gemm_kernel(ProjArgs a) {
 
   // ---- fills: one instruction of a wave covers 16 rows of a tile; lane l
   // writes position l % 4 of row l / 4, which receives the row's chunk
-  // (l % 4) ^ ((row / 2) % 4).  Per step a wave fills 32 rows of W
+  // (l % 4) ^ ((row / 4) % 4).  Per step a wave fills 32 rows of W
   // (2 loads) and 16 TB rows of A (TB loads).
   const __amdgpu_buffer_rsrc_t rw =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.W), (short)0, (int)a.w_bytes, kBufferWord3);
@@ -133,14 +136,14 @@ __global__ __launch_bounds__(kThreads, 2) void proj_gemm_kernel(ProjArgs a) {
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int row = 32 * wave + 16 * q + (lane >> 2);
-    const uint32_t chunk = 16u * (uint32_t)(fpos ^ ((row >> 1) & 3));
+    const uint32_t chunk = 16u * (uint32_t)(fpos ^ ((row >> 2) & 3));
     const int n = n0 + row;
     w_off[q] = n < a.N ? (uint32_t)n * (uint32_t)K * 2u + chunk : kOutOfRange;
   }
 #pragma unroll
   for (int q = 0; q < TB; ++q) {
     const int row = 16 * TB * wave + 16 * q + (lane >> 2);
-    const uint32_t chunk = 16u * (uint32_t)(fpos ^ ((row >> 1) & 3));
+    const uint32_t chunk = 16u * (uint32_t)(fpos ^ ((row >> 2) & 3));
     const int m = m0 + row;
     if (HEAD_OUT) {
       // A = X [M, K] row-major
@@ -200,12 +203,12 @@ __global__ __launch_bounds__(kThreads, 2) void proj_gemm_kernel(ProjArgs a) {
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk) {
         const int r = 64 * wn + 32 * blk + ln;
-        wf[blk] = __builtin_bit_cast(bf16x8, wt[r * 4 + (ch ^ ((r >> 1) & 3))]);
+        wf[blk] = __builtin_bit_cast(bf16x8, wt[r * 4 + (ch ^ ((r >> 2) & 3))]);
       }
 #pragma unroll
       for (int blk = 0; blk < TB; ++blk) {
         const int r = 32 * TB * wm + 32 * blk + ln;
-        af[blk] = __builtin_bit_cast(bf16x8, at[r * 4 + (ch ^ ((r >> 1) & 3))]);
+        af[blk] = __builtin_bit_cast(bf16x8, at[r * 4 + (ch ^ ((r >> 2) & 3))]);
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
