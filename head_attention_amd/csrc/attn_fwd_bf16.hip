@@ -65,15 +65,16 @@ constexpr float kPivotHigh = 0x1p64f;  // a tile sum above this moves the pivot 
 constexpr float kPivotLow = 0x1p-64f;  // a first-tile row sum below this moves it down
 
 // One LDS tile: 64 rows x 128 B as 8 chunks of 16 B.  K tiles are stored
-// [key][chunk], V^T tiles [d][chunk of 8 keys].  Chunks are XOR-swizzled per
-// row so 8 lanes reading the same logical chunk of 8 consecutive rows hit 8
-// different chunk positions.  (Measured faster than padding the rows to
+// [key][chunk] (positions k_swz of the shared header), V^T tiles [d][chunk
+// of 8 keys].  Chunks are XOR-swizzled per row so the 16 lanes the LDS
+// serves together, reading one logical chunk of 16 consecutive rows, spread
+// over all banks (rows r and r + 8 are 1 KB apart, on the same banks, and
+// take different positions).  (Measured faster than padding the rows to
 // 144 B, although padding needs fewer address registers.)
 struct Tile {
   uint4 c[64 * 8];
 };
 
-__device__ __forceinline__ int k_swz(int key) { return key & 7; }
 __device__ __forceinline__ int vt_swz(int d) { return (d ^ (d >> 3)) & 7; }
 
 // Position of key group g (keys 4g..4g+3 of a tile) inside a V^T row.  A lane
