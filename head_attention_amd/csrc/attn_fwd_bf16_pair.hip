@@ -124,16 +124,6 @@ __device__ __forceinline__ float half_swap_max(float x) {
   const uint32_t a = r[0], b = r[1];
   return fmaxf(__uint_as_float(a), __uint_as_float(b));
 }
-__device__ __forceinline__ float half_swap_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  const uint32_t a = r[0], b = r[1];
-  return __uint_as_float(a) + __uint_as_float(b);
-}
-__device__ __forceinline__ bool half_swap_or(bool x) {
-  const auto r = __builtin_amdgcn_permlane32_swap((uint32_t)x, (uint32_t)x, false, false);
-  const uint32_t a = r[0], b = r[1];
-  return (a | b) != 0;
-}
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   f32x2 v = {lo, hi};
@@ -618,7 +608,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_pair_kernel(FwdArgs
   // through LDS.  Eight 8 KB tiles (64 KB) hold O as 16 vec4 groups
   // ([d block][query block][register / 4]) x 4 row groups x 64 lanes; group
   // vg sits in tile vg / 2, so every index is a compile-time tile.
-  auto mptr = [&](auto vg_tag) -> float4* __attribute__((always_inline)) {
+  auto mptr = [&](auto vg_tag) __attribute__((always_inline)) -> float4* {
     constexpr int VG = decltype(vg_tag)::value;
     return reinterpret_cast<float4*>(mslot<VG / 2>()) + ((VG & 1) * 4 + rg) * 64 + lane;
   };
