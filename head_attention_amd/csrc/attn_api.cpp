@@ -32,13 +32,19 @@ bool length_check_enabled() {
 
 constexpr int64_t kMaxGrid = 2147483647LL;
 
-// Shape checks common to both entry points.  Sizes must be non-negative and
-// d must be 64; every element count must fit comfortably in int64 and the
-// per-(b, h) row count in int32 (kernels index rows with int).
+// Rows per (b, h) slice.  The bf16 kernels address a slice through buffer
+// descriptors whose range and offsets are 32-bit byte counts of 128-byte
+// rows, kept below 2^31: longer slices would wrap and read as zeros.
+constexpr int32_t kMaxRows = (1 << 24) - 1;
+
+// Shape checks common to every entry point.  Sizes must be non-negative and
+// d must be 64; a (b, h) slice holds at most kMaxRows rows, and every element
+// count must fit comfortably in int64.
 attn_status check_layout(const attn_layout& L) {
   if (L.dtype != ATTN_BF16 && L.dtype != ATTN_F32) return ATTN_ERR_BAD_DTYPE;
   if (L.B < 0 || L.h < 0 || L.n_q < 0 || L.n_k < 0) return ATTN_ERR_BAD_SHAPE;
   if (L.d != kHeadDim) return ATTN_ERR_BAD_SHAPE;
+  if (L.n_q > kMaxRows || L.n_k > kMaxRows) return ATTN_ERR_BAD_SHAPE;
   const long double elems_q = (long double)L.B * L.h * L.n_q * L.d;
   const long double elems_k = (long double)L.B * L.h * L.n_k * L.d;
   if (elems_q > 4.0e18L || elems_k > 4.0e18L) return ATTN_ERR_BAD_SHAPE;
@@ -73,7 +79,9 @@ const char* attn_status_string(attn_status status) {
   switch (status) {
     case ATTN_OK: return "ATTN_OK: success";
     case ATTN_ERR_NULL_POINTER: return "ATTN_ERR_NULL_POINTER: a required pointer is NULL";
-    case ATTN_ERR_BAD_SHAPE: return "ATTN_ERR_BAD_SHAPE: negative size, d != 64, or size overflow";
+    case ATTN_ERR_BAD_SHAPE:
+      return "ATTN_ERR_BAD_SHAPE: negative size, d != 64, more than 2^24 - 1 rows per (b, h), or size "
+             "overflow";
     case ATTN_ERR_BAD_DTYPE: return "ATTN_ERR_BAD_DTYPE: dtype must be ATTN_BF16 or ATTN_F32";
     case ATTN_ERR_BAD_MASK:
       return "ATTN_ERR_BAD_MASK: unknown mask bits, causal or restricted with n_q != n_k, a "

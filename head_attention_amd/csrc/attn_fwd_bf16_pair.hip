@@ -100,6 +100,8 @@ constexpr int kSlots = 8;
 constexpr int kAhead = 5;
 // Row sums and pivots of the odd-tile waves for the final merge.
 __shared__ float2 g_lm[4][2][64];
+// Set when a row failed the fixed-pivot range check: the workgroup runs again.
+__shared__ int g_redo;
 
 template <int S>
 __device__ __forceinline__ uint4* kslot() {
@@ -172,8 +174,14 @@ __device__ __forceinline__ void barrier_lds() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int MODE>
-__global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_pair_kernel(FwdArgs a) {
+// One workgroup's whole computation, in one of two passes: FIXED = the
+// weights under the fixed pivot 0, followed by a range check (returns false,
+// writing nothing, when a row fails it); otherwise the moving pivot (always
+// succeeds).  The kernel inlines the first pass and calls the second, which is
+// rare, as a separate function: two copies of the pipeline in one function
+// spill the Q fragments inside the loop.
+template <int MODE, bool FIXED>
+__device__ __forceinline__ bool pair_pass(const FwdArgs& a) {
   constexpr bool CAUSAL = MODE == kModeCausal;
   constexpr bool BAND = MODE == kModeBand;
   const int tid = threadIdx.x;
@@ -291,7 +299,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_pair_kernel(FwdArgs
   f32x16 o[2][2];    // O^T[d block][query block]
   f32x16 sc[2][2];   // S^T[key block][query block] of the current tile
   uint32_t pk[2][16];  // bf16 weights [query block][8 key block + pair]
-  float mc[2] = {0.f, 0.f};  // pivot term m * c per query block
+  float mc[2];  // pivot term m * c per query block
   // Row sums of the bf16 weights, accumulated on the matrix cores: one
   // v_mfma_f32_16x16x32_bf16 per key step and query block takes the weights
   // as they sit in the P registers (B operand: lane l supplies 8 values of
@@ -301,25 +309,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_pair_kernel(FwdArgs
   // 16 x 16 result then holds the sums of queries 0..15 and row 1 those of
   // queries 16..31: lanes 0..15, registers 0 and 1 (rows 2..15 stay 0).
   // Each product is an exact bf16 value times 1, summed in fp32.
-  f32x4 ls[2] = {f32x4{}, f32x4{}};
+  f32x4 ls[2];
   const bf16x8 sel = __builtin_bit_cast(
       bf16x8, (((lane & 15) == 0 && ((lane >> 4) & 1) == 0) || ((lane & 15) == 1 && ((lane >> 4) & 1) == 1))
                   ? make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u)
                   : make_uint4(0u, 0u, 0u, 0u));
   // Whether a row has summed a nonzero weight yet (the pivot may move down
-  // only before that); both half-waves of a row agree.
-  bool seen[2] = {false, false};
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      o[i][j] = f32x16{};
-      sc[i][j] = f32x16{};
-    }
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) pk[qb][i] = 0u;
+  // only before that); both half-waves of a row agree.  (All of this state is
+  // reset at the start of each pass.)
+  bool seen[2];
 
   // MFMA operand fragments, read from LDS in the MFMA phase in the order
   // of use with at most 12 reads in flight, so each group of products waits
@@ -526,11 +524,46 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_pair_kernel(FwdArgs
     qk_smajor(ka);
     __builtin_amdgcn_s_setprio(0);
   };
+  // Weights of tile t under the fixed pivot 0 (the first pass): the same
+  // masks, then x = s c and 2^x straight away -- no row maxima, no pivot
+  // checks.  Whether the pivot was safe for every row is decided once, from
+  // the row sums at the end (see the range check after the loop).
+  auto softmax_fixed = [&](int t) __attribute__((always_inline)) {
+    const int k0 = k_base + t * kBN;
+    bool need_mask = (k0 + kBN > kv_lim) || (CAUSAL && k0 + kBN - 1 > qw0);
+    if (BAND) need_mask = need_mask || (k0 + kBN - 1 > qw0 + wr) || (k0 < qw0 + kWaveRows - 1 - wl);
+    if (need_mask) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const int qi = qw0 + 32 * qb + ln;
+        int hi = kv_lim;
+        if (CAUSAL) hi = min(hi, qi + 1);
+        if (BAND) hi = min(hi, qi + wr + 1);
+        const int lim = hi - k0 - 4 * hh;
+        const int lo = BAND ? qi - wl - k0 - 4 * hh : INT_MIN;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int off = 8 * (r >> 2) + (r & 3);
+          sc[0][qb][r] = (off < lim && off >= lo) ? sc[0][qb][r] : -INFINITY;
+          sc[1][qb][r] = (off + 32 < lim && off + 32 >= lo) ? sc[1][qb][r] : -INFINITY;
+        }
+      }
+    }
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sc[kb][qb][r] *= c;
+      exp_pack(sc[0][qb], sc[1][qb], pk[qb]);
+    }
+  };
   // Vector phase of tile t: the weights of tile t, or zero weights for a
   // phase before this wave's first tile or past its last.
   auto vphase = [&](int t) __attribute__((always_inline)) {
     if (t >= wave_first && t < wave_tiles) {
-      softmax(t);
+      if constexpr (FIXED) softmax_fixed(t);
+      else softmax(t);
     } else {
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
@@ -547,102 +580,161 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_pair_kernel(FwdArgs
   using J6 = std::integral_constant<int, 6>;
   using J7 = std::integral_constant<int, 7>;
 
-  if (n_tiles > 0) {
-    // Prologue: tiles 0 .. 4 (K and V) as if filled at phases -5 .. -1.
-    fill_k(J0(), 0);
-    fill_v(J0(), 0);
-    fill_k(J1(), 1);
-    fill_v(J1(), 1);
-    fill_k(J2(), 2);
-    fill_v(J2(), 2);
-    fill_k(J3(), 3);
-    fill_v(J3(), 3);
-    fill_k(J4(), 4);
-    fill_v(J4(), 4);
-    // The first MFMA phases of the two waves of a pair (p = 0, 1) read the
-    // V tiles of slots 6 and 7 with zero weights: zero them, since 0 * NaN
-    // of stale LDS contents would not be zero.
-    g_v6[tid] = make_uint4(0, 0, 0, 0);
-    g_v7[tid] = make_uint4(0, 0, 0, 0);
-    __builtin_amdgcn_s_waitcnt(0x0070 | 8);  // vmcnt(8), lgkmcnt(0): tile 0 has landed
-    barrier_lds();
-    // Even-tile waves run MFMA phases at even p, odd-tile waves at odd p;
-    // both run the same number of phases (and barriers).
-    const int n_phases = n_tiles + 2;
-    if (par == 0) {
-#pragma nounroll
-      for (int p = 0; p < n_phases; p += 8) {
-        fills(J0(), p);     mphase(J0()); sync();
-        fills(J1(), p + 1); vphase(p);              sync();
-        if (p + 2 >= n_phases) break;
-        fills(J2(), p + 2); mphase(J2()); sync();
-        fills(J3(), p + 3); vphase(p + 2);          sync();
-        if (p + 4 >= n_phases) break;
-        fills(J4(), p + 4); mphase(J4()); sync();
-        fills(J5(), p + 5); vphase(p + 4);          sync();
-        if (p + 6 >= n_phases) break;
-        fills(J6(), p + 6); mphase(J6()); sync();
-        fills(J7(), p + 7); vphase(p + 6);          sync();
+  // The pass over the tiles, from a reset state.
+  auto run = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        o[i][j] = f32x16{};
+        sc[i][j] = f32x16{};
       }
-    } else {
-#pragma nounroll
-      for (int p = 0; p < n_phases; p += 8) {
-        fills(J0(), p);     vphase(p - 1);              sync();
-        fills(J1(), p + 1); mphase(J1()); sync();
-        if (p + 2 >= n_phases) break;
-        fills(J2(), p + 2); vphase(p + 1);              sync();
-        fills(J3(), p + 3); mphase(J3()); sync();
-        if (p + 4 >= n_phases) break;
-        fills(J4(), p + 4); vphase(p + 3);              sync();
-        fills(J5(), p + 5); mphase(J5()); sync();
-        if (p + 6 >= n_phases) break;
-        fills(J6(), p + 6); vphase(p + 5);              sync();
-        fills(J7(), p + 7); mphase(J7()); sync();
-      }
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) pk[qb][i] = 0u;
+      mc[qb] = 0.f;
+      ls[qb] = f32x4{};
+      seen[qb] = false;
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70 | 0);  // no fill may land in the merge area
-    barrier_lds();
-  }
+    if (n_tiles > 0) {
+      // Prologue: tiles 0 .. 4 (K and V) as if filled at phases -5 .. -1.
+      fill_k(J0(), 0);
+      fill_v(J0(), 0);
+      fill_k(J1(), 1);
+      fill_v(J1(), 1);
+      fill_k(J2(), 2);
+      fill_v(J2(), 2);
+      fill_k(J3(), 3);
+      fill_v(J3(), 3);
+      fill_k(J4(), 4);
+      fill_v(J4(), 4);
+      // The first MFMA phases of the two waves of a pair (p = 0, 1) read the
+      // V tiles of slots 6 and 7 with zero weights: zero them, since 0 * NaN
+      // of stale LDS contents would not be zero.
+      g_v6[tid] = make_uint4(0, 0, 0, 0);
+      g_v7[tid] = make_uint4(0, 0, 0, 0);
+      __builtin_amdgcn_s_waitcnt(0x0070 | 8);  // vmcnt(8), lgkmcnt(0): tile 0 has landed
+      barrier_lds();
+      // Even-tile waves run MFMA phases at even p, odd-tile waves at odd p;
+      // both run the same number of phases (and barriers).
+      const int n_phases = n_tiles + 2;
+      if (par == 0) {
+  #pragma nounroll
+        for (int p = 0; p < n_phases; p += 8) {
+          fills(J0(), p);     mphase(J0()); sync();
+          fills(J1(), p + 1); vphase(p);              sync();
+          if (p + 2 >= n_phases) break;
+          fills(J2(), p + 2); mphase(J2()); sync();
+          fills(J3(), p + 3); vphase(p + 2);          sync();
+          if (p + 4 >= n_phases) break;
+          fills(J4(), p + 4); mphase(J4()); sync();
+          fills(J5(), p + 5); vphase(p + 4);          sync();
+          if (p + 6 >= n_phases) break;
+          fills(J6(), p + 6); mphase(J6()); sync();
+          fills(J7(), p + 7); vphase(p + 6);          sync();
+        }
+      } else {
+  #pragma nounroll
+        for (int p = 0; p < n_phases; p += 8) {
+          fills(J0(), p);     vphase(p - 1);              sync();
+          fills(J1(), p + 1); mphase(J1()); sync();
+          if (p + 2 >= n_phases) break;
+          fills(J2(), p + 2); vphase(p + 1);              sync();
+          fills(J3(), p + 3); mphase(J3()); sync();
+          if (p + 4 >= n_phases) break;
+          fills(J4(), p + 4); vphase(p + 3);              sync();
+          fills(J5(), p + 5); mphase(J5()); sync();
+          if (p + 6 >= n_phases) break;
+          fills(J6(), p + 6); vphase(p + 5);              sync();
+          fills(J7(), p + 7); mphase(J7()); sync();
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0x0F70 | 0);  // no fill may land in the merge area
+      barrier_lds();
+    }
+  };
 
-  // ---- merge the pair: the odd-tile wave hands (O, l, m) to its partner
-  // through LDS.  Eight 8 KB tiles (64 KB) hold O as 16 vec4 groups
-  // ([d block][query block][register / 4]) x 4 row groups x 64 lanes; group
-  // vg sits in tile vg / 2, so every index is a compile-time tile.
+  // ---- hand the odd-tile waves' (O, l, m) to their partners through LDS.
+  // Eight 8 KB tiles (64 KB) hold O as 16 vec4 groups ([d block][query
+  // block][register / 4]) x 4 row groups x 64 lanes; group vg sits in tile
+  // vg / 2, so every index is a compile-time tile.
   auto mptr = [&](auto vg_tag) __attribute__((always_inline)) -> float4* {
     constexpr int VG = decltype(vg_tag)::value;
     return reinterpret_cast<float4*>(mslot<VG / 2>()) + ((VG & 1) * 4 + rg) * 64 + lane;
   };
-  // Full row sums in the row layout: lane (ln, hh) takes query ln's sum from
-  // lane ln % 16, register ln / 16.
   float l[2];
+  auto handoff = [&]() __attribute__((always_inline)) {
+    // Full row sums in the row layout: lane (ln, hh) takes query ln's sum
+    // from lane ln % 16, register ln / 16.
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const float v0 = __int_as_float(__builtin_amdgcn_ds_bpermute((lane & 15) * 4, __float_as_int(ls[qb][0])));
-    const float v1 = __int_as_float(__builtin_amdgcn_ds_bpermute((lane & 15) * 4, __float_as_int(ls[qb][1])));
-    l[qb] = (ln < 16) ? v0 : v1;
-  }
-  if (par == 1) {
-    static_for<16>([&](auto vg_tag) {
-      constexpr int VG = decltype(vg_tag)::value;
-      constexpr int DB = VG / 8, QB = (VG / 4) % 2, R = 4 * (VG % 4);
-      *mptr(vg_tag) = make_float4(o[DB][QB][R], o[DB][QB][R + 1], o[DB][QB][R + 2], o[DB][QB][R + 3]);
-    });
+    for (int qb = 0; qb < 2; ++qb) {
+      const float v0 = __int_as_float(__builtin_amdgcn_ds_bpermute((lane & 15) * 4, __float_as_int(ls[qb][0])));
+      const float v1 = __int_as_float(__builtin_amdgcn_ds_bpermute((lane & 15) * 4, __float_as_int(ls[qb][1])));
+      l[qb] = (ln < 16) ? v0 : v1;
+    }
+    if (par == 1) {
+      static_for<16>([&](auto vg_tag) {
+        constexpr int VG = decltype(vg_tag)::value;
+        constexpr int DB = VG / 8, QB = (VG / 4) % 2, R = 4 * (VG % 4);
+        *mptr(vg_tag) = make_float4(o[DB][QB][R], o[DB][QB][R + 1], o[DB][QB][R + 2], o[DB][QB][R + 3]);
+      });
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) g_lm[rg][qb][lane] = make_float2(l[qb], mc[qb]);
+      for (int qb = 0; qb < 2; ++qb) g_lm[rg][qb][lane] = make_float2(l[qb], mc[qb]);
+    }
+    __syncthreads();
+  };
+
+  if constexpr (FIXED) {
+    if (tid == 0) g_redo = 0;
   }
-  __syncthreads();
-  if (par == 1) return;
+  run();
+  handoff();
+  if constexpr (FIXED) {
+    // Range check of the fixed pivot.  Under pivot 0 every weight of a row
+    // is at most its sum l, so l_A, l_B < 2^64 bounds every weight, partial
+    // sum and product below fp32 overflow (a weight of 2^128 or more shows
+    // as l = inf, NaN as a NaN sum).  l_A + l_B >= 2^-32 puts the row's
+    // largest weight at 2^-56 or more (a row has fewer than 2^24 keys), so a
+    // weight that fell into the subnormal range is below 2^-70 of it and
+    // changes no result.  A row with an allowed key that fails either bound
+    // -- logits far above 64 or far below -32 in log2 units -- sends the
+    // whole workgroup through the second pass.  Rows without an allowed key
+    // (padded, kv_len = 0, an empty window) are zeros either way.
+    if (par == 0) {
+      bool bad = false;
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const float2 lm = g_lm[rg][qb][lane];
+        const int qi = qw0 + 32 * qb + ln;
+        const int lo = BAND ? max(0, qi - wl) : 0;
+        const int hi = BAND ? min(kv_lim, qi + wr + 1) : kv_lim;
+        const bool keys = qi < q_len && lo < hi;
+        const bool ok = l[qb] + lm.x >= 0x1p-32f && l[qb] < 0x1p64f && lm.x < 0x1p64f;
+        bad = bad || (keys && !ok);
+      }
+      if (__builtin_amdgcn_ballot_w64(bad) != 0 && lane == 0) g_redo = 1;
+    }
+    __syncthreads();
+    if (__builtin_amdgcn_readfirstlane(g_redo) != 0) return false;
+  }
+  if (par == 1) return true;
 
   // O = (2^(mA - M) O_A + 2^(mB - M) O_B) / (2^(mA - M) l_A + 2^(mB - M) l_B)
-  // with M = max(mA, mB); 2^0 = 1 exactly, and both pivots are finite.
+  // with M the larger pivot of the waves that summed a weight (l > 0); 2^0 =
+  // 1 exactly.  A wave that saw no key of the row keeps its starting pivot 0,
+  // which says nothing about the row's scale: it takes factor 0 and no part
+  // in M (otherwise a partner pivot far below 0, moved down at its first
+  // key, would give 2^(mA - 0) = 0 and lose the row).
   float fa[2], fb[2], inv[2];
   bool live[2];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const float2 lm = g_lm[rg][qb][lane];
-    const float M = fmaxf(mc[qb], lm.y);
-    fa[qb] = __builtin_amdgcn_exp2f(mc[qb] - M);
-    fb[qb] = __builtin_amdgcn_exp2f(lm.y - M);
+    const bool ea = l[qb] > 0.f, eb = lm.x > 0.f;
+    const float M = ea ? (eb ? fmaxf(mc[qb], lm.y) : mc[qb]) : lm.y;
+    fa[qb] = ea ? __builtin_amdgcn_exp2f(mc[qb] - M) : 0.f;
+    fb[qb] = eb ? __builtin_amdgcn_exp2f(lm.y - M) : 0.f;
     const float l_row = fa[qb] * l[qb] + fb[qb] * lm.x;
     const int qi = qw0 + 32 * qb + ln;
     live[qb] = qi < q_len && l_row > 0.f;
@@ -670,6 +762,47 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_pair_kernel(FwdArgs
       *reinterpret_cast<uint2*>(O + (size_t)qi * kHeadDim + 32 * DB + 8 * G + 4 * hh) = w;
     }
   });
+  return true;
+}
+
+// Every lane holds the same value: take lane 0's, so that the compiler
+// treats it (and everything derived from it) as uniform.
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ float uni(float v) { return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v))); }
+template <typename T>
+__device__ __forceinline__ T* uni(T* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (T*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
+// The second pass.  The call's arguments come in by value, in per-lane
+// registers or memory, so each field is made uniform again first (the
+// buffer descriptors and every address derived from them must be scalar).
+template <int MODE>
+__device__ __attribute__((noinline)) void pair_pass_moving(FwdArgs v) {
+  FwdArgs a;
+  a.Q = uni(v.Q);
+  a.K = uni(v.K);
+  a.V = uni(v.V);
+  a.O = uni(v.O);
+  a.q_lens = uni(v.q_lens);
+  a.kv_lens = uni(v.kv_lens);
+  a.B = uni(v.B);
+  a.H = uni(v.H);
+  a.n_q = uni(v.n_q);
+  a.n_k = uni(v.n_k);
+  a.scale = uni(v.scale);
+  a.causal = uni((int)v.causal) != 0;
+  a.lse = uni(v.lse);
+  a.radius = uni(v.radius);
+  pair_pass<MODE, false>(a);
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_pair_kernel(FwdArgs a) {
+  if (!pair_pass<MODE, true>(a)) pair_pass_moving<MODE>(a);
 }
 
 }  // namespace

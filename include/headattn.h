@@ -62,8 +62,8 @@ typedef enum {
 typedef struct {
   int32_t B;     /* batch entries, >= 0                 */
   int32_t h;     /* heads, >= 0                         */
-  int32_t n_q;   /* query rows per (b, h), >= 0         */
-  int32_t n_k;   /* key/value rows per (b, h), >= 0     */
+  int32_t n_q;   /* query rows per (b, h), 0 .. 2^24-1  */
+  int32_t n_k;   /* key/value rows per (b, h), 0 .. 2^24-1 */
   int32_t d;     /* head dimension, must be 64          */
   int32_t dtype; /* attn_dtype                          */
 } attn_layout;
@@ -92,8 +92,10 @@ enum {
 typedef enum {
   ATTN_OK = 0,
   ATTN_ERR_NULL_POINTER = 1, /* a required pointer is NULL                    */
-  ATTN_ERR_BAD_SHAPE = 2,    /* negative size, d != 64, size overflow, n_q != 1
-                                for decode, or an input pointer equal to O    */
+  ATTN_ERR_BAD_SHAPE = 2,    /* negative size, d != 64, n_q or n_k above
+                                2^24 - 1 rows per (b, h), size overflow,
+                                n_q != 1 for decode, or an input pointer
+                                equal to O                                    */
   ATTN_ERR_BAD_DTYPE = 3,    /* dtype not an attn_dtype                       */
   ATTN_ERR_BAD_MASK = 4,     /* unknown bits; causal or restricted with
                                 n_q != n_k; ATTN_MASK_RESTRICTED outside

@@ -63,6 +63,9 @@ def lay(B=2, h=3, nq=16, nk=16, d=64, dt=BF16):
     (lay(d=32), SHAPE), (lay(d=128), SHAPE), (lay(B=-1), SHAPE), (lay(nq=-5), SHAPE),
     (lay(dt=2), DTYPE), (lay(dt=-1), DTYPE),
     (lay(B=2 ** 30, h=2 ** 30, nq=2 ** 20), SHAPE),
+    # a (b, h) slice holds at most 2^24 - 1 rows (32-bit byte ranges of 128 B rows)
+    (lay(B=1, h=1, nq=2 ** 24, nk=16), SHAPE), (lay(B=1, h=1, nq=16, nk=2 ** 24), SHAPE),
+    (lay(B=1, h=1, nq=2 ** 25, nk=2 ** 25), SHAPE),
 ])
 def test_forward_bad_layout(layout, code):
     assert fwd(layout) == code
@@ -114,6 +117,7 @@ def test_decode_validation():
     L = attn_layout(4, 2, 1, 300, 64, BF16)
     assert dec(attn_layout(4, 2, 2, 300, 64, BF16)) == SHAPE
     assert dec(attn_layout(4, 2, 1, 300, 16, BF16)) == SHAPE
+    assert dec(attn_layout(1, 1, 1, 2 ** 24, 64, BF16)) == SHAPE   # cache above 2^24 - 1 rows
     assert dec(attn_layout(4, 2, 1, 300, 64, 7)) == DTYPE
     assert dec(L, scale=float("-inf")) == SCALE
     assert dec(L, q=None) == NULLP

@@ -1,0 +1,124 @@
+"""GPU parity on rows whose every allowed logit lies far below zero.
+
+Softmax does not depend on a constant added to a row's logits ("[논문
+리뷰]Attention Is All You Need", §3.2.1 equation; the max shift of the
+sj-techlog page's verification script), so a row with logits near -100 or
+-200 has the same weights as one near 0.  A kernel that keeps a fixed pivot
+would underflow every weight of such a row (2^(-200 log2 e) is far below the
+smallest fp32), so the kernels must move their pivot down to the row's scale
+before the first weight is formed -- and every place where partial results
+under different pivots are combined (the paired kernel's two waves per row,
+the decode splits) must take its common pivot from the parts that saw a key.
+
+Inputs: every K row is 1 + 0.1 N(0,1) per element (a shared component plus
+noise), and query row i is -a_i/8 times the all-ones vector, so that
+scale q_i . k_j = -a_i (1 + N(0, 0.1^2/64)) ~ -a_i +- a_i/80: the weights of a row
+stay well spread while all of its logits sit near -a_i.  a_i cycles through
+100 and 200 (log2 exponents near -144 and -289).  The oracle sees exactly the
+bf16 values the GPU sees.
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import head_attention_amd as ha
+import oracle.attn_oracle as orc
+import workloads
+from gpu_util import F32_REL_MAX, check, dev, np64, say
+
+pytestmark = pytest.mark.gpu
+
+BF16, F32 = torch.bfloat16, torch.float32
+A_LEVELS = (100.0, 200.0)
+
+
+def _far_negative(seed, B, H, n_q, n_k, dtype):
+    g = workloads.generator(seed)
+    K = (1.0 + 0.1 * torch.randn((B, H, n_k, 64), generator=g)).to(dtype)
+    V = workloads.randn(g, (B, H, n_k, 64), dtype)
+    a = torch.tensor([A_LEVELS[i % len(A_LEVELS)] for i in range(n_q)])
+    Q = (-(a / 8.0)[None, None, :, None] * torch.ones((B, H, n_q, 64))).to(dtype)
+    return Q, K, V
+
+
+def _run(Q, K, V, mask, kv_lens=None, radius=None):
+    kl = None if kv_lens is None else torch.tensor(kv_lens, dtype=torch.int32)
+    if radius is None:
+        out = ha.forward(dev(Q), dev(K), dev(V), mask_kind=mask, kv_lens=dev(kl), scale=0.125)
+    else:
+        out = ha.forward_restricted(dev(Q), dev(K), dev(V), radius, mask_kind=mask,
+                                    kv_lens=dev(kl), scale=0.125)
+    torch.cuda.synchronize()
+    ref = orc.attention(np64(Q), np64(K), np64(V), mask_kind=mask,
+                        kv_lens=None if kl is None else kl.numpy(), scale=0.125, radius=radius)
+    return np64(out), ref
+
+
+CASES = {
+    # id: (B, H, n_q, n_k, mask, kv_lens, radius) -- kernels: short (n_k <= 256),
+    # 4-wave (256 < n_k, n_q < 512), paired (n_q >= 512, or any restricted call)
+    "short_none_150": (1, 2, 150, 150, 0, None, None),
+    "short_causal_150": (1, 2, 150, 150, 2, None, None),
+    "fourwave_none_300": (1, 2, 300, 300, 0, None, None),
+    "fourwave_causal_300": (1, 2, 300, 300, 2, None, None),
+    "pair_none_700": (1, 2, 700, 700, 0, None, None),
+    # causal rows 0..63 on the paired kernel: the odd-tile wave of each row
+    # sees no key, its partner moves its pivot far down
+    "pair_causal_520": (1, 2, 520, 520, 2, None, None),
+    "pair_causal_700": (1, 2, 700, 700, 2, None, None),
+    # key padding with kv_len <= 64 at n_q >= 512: every row's keys sit in the
+    # even wave's first tile
+    "pair_kpad_short_keys_600": (3, 2, 600, 600, 1, [64, 1, 33], None),
+    # restricted: radius 0 (one key per row, its own) and a narrow band
+    "band_r0_700": (1, 2, 700, 700, 4, None, 0),
+    "band_causal_r0_700": (1, 2, 700, 700, 6, None, 0),
+    "band_r20_700": (1, 2, 700, 700, 4, None, 20),
+    "band_causal_r40_600": (1, 2, 600, 600, 6, None, 40),
+    "short_band_r0_150": (1, 2, 150, 150, 4, None, 0),
+}
+
+
+@pytest.mark.parametrize("dtype", [BF16, F32], ids=["bf16", "fp32"])
+@pytest.mark.parametrize("cid", sorted(CASES))
+def test_far_negative_rows(cid, dtype):
+    B, H, n_q, n_k, mask, kl, radius = CASES[cid]
+    say(f"[far-negative {cid} {dtype}] B{B} H{H} nq{n_q} nk{n_k} mask{mask} radius{radius}")
+    Q, K, V = _far_negative(zlib.crc32(cid.encode()) % 1000 + 5000, B, H, n_q, n_k, dtype)
+    out, ref = _run(Q, K, V, mask, kl, radius)
+    if dtype == BF16:
+        check(out, ref, dtype, cid)
+    else:
+        # fp32 path: a score's rounding error is relative to the size of its
+        # terms, about 2^-24 sqrt(64) scale sum_d |q_d k_d| -- near 3e-5 for
+        # logits around -200 (terms of 25 each), against ~1e-6 for N(0,1)
+        # rows -- so the fp32 bar grows with the largest |logit|: 1e-5 times
+        # max(1, max|logit| / 8), 8 being about the largest logit of an
+        # N(0,1) row at the pages' scale.  (The bf16 bar is absolute and
+        # holds unchanged.)
+        big = max(A_LEVELS) * 1.05
+        tol = F32_REL_MAX * max(1.0, big / 8.0)
+        rel = float(np.abs(out - ref).max() / np.abs(ref).max())
+        say(f"  {cid}: max_rel={rel:.3e} (bar {tol:.2e})")
+        assert np.all(np.isfinite(out)) and rel <= tol, f"{cid}: relative max error {rel}"
+    # every row has an allowed key here, so no output row may be all zeros
+    norms = np.abs(out).reshape(-1, 64).max(axis=1)
+    rows_ref = np.abs(ref).reshape(-1, 64).max(axis=1)
+    assert np.all((norms > 0) == (rows_ref > 0)), f"{cid}: a row with keys came out zero"
+
+
+def test_far_negative_decode():
+    """Decode splits whose maxima are all far below zero merge as well."""
+    B, H, n_max = 4, 2, 1100
+    g = workloads.generator(5100)
+    Kc = (1.0 + 0.1 * torch.randn((B, H, n_max, 64), generator=g)).to(BF16)
+    Vc = workloads.randn(g, (B, H, n_max, 64), BF16)
+    q = (-(torch.tensor([100.0, 200.0, 150.0, 200.0]) / 8.0)[:, None, None, None]
+         * torch.ones((B, H, 1, 64))).to(BF16)
+    lens = torch.tensor([1100, 1, 257, 700], dtype=torch.int32)
+    say("[far-negative decode]")
+    out = ha.decode(dev(q), dev(Kc), dev(Vc), dev(lens), scale=0.125)
+    torch.cuda.synchronize()
+    ref = orc.decode(np64(q), np64(Kc), np64(Vc), lens.numpy(), scale=0.125)
+    check(np64(out), ref, BF16, "far-negative decode")
