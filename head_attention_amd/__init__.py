@@ -14,6 +14,7 @@ from ._binding import (  # noqa: F401
     ATTN_MASK_KEY_PADDING,
     ATTN_MASK_NONE,
     ATTN_MASK_RESTRICTED,
+    DECODE_NOALLOC_MAX_BYTES,
     LIB_PATH,
     AttnError,
     attn_layout,
@@ -21,6 +22,7 @@ from ._binding import (  # noqa: F401
     backward_workspace_bytes,
     cache_append,
     decode,
+    decode_noalloc,
     decode_workspace_bytes,
     forward,
     forward_restricted,

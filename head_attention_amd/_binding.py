@@ -27,8 +27,11 @@ ATTN_MASK_RESTRICTED = 4
 STATUS_NAMES = {
     0: "ATTN_OK", 1: "ATTN_ERR_NULL_POINTER", 2: "ATTN_ERR_BAD_SHAPE", 3: "ATTN_ERR_BAD_DTYPE",
     4: "ATTN_ERR_BAD_MASK", 5: "ATTN_ERR_BAD_LENGTHS", 6: "ATTN_ERR_BAD_SCALE",
-    7: "ATTN_ERR_WORKSPACE", 8: "ATTN_ERR_HIP",
+    7: "ATTN_ERR_WORKSPACE", 8: "ATTN_ERR_HIP", 9: "ATTN_ERR_SCRATCH_LIMIT",
 }
+
+# Scratch that attn_decode_noalloc holds per GPU (ATTN_DECODE_NOALLOC_MAX_BYTES).
+DECODE_NOALLOC_MAX_BYTES = 8 << 20
 
 
 class attn_layout(ctypes.Structure):
@@ -64,6 +67,8 @@ def lib() -> ctypes.CDLL:
         L.attn_decode.argtypes = [vp, vp, vp, attn_layout, i32p, ctypes.c_float, vp, vp,
                                   ctypes.c_size_t, vp]
         L.attn_decode.restype = ctypes.c_int
+        L.attn_decode_noalloc.argtypes = [vp, vp, vp, attn_layout, i32p, ctypes.c_float, vp, vp]
+        L.attn_decode_noalloc.restype = ctypes.c_int
         L.attn_cache_append.argtypes = [vp, vp, vp, vp, attn_layout, i32p, vp]
         L.attn_cache_append.restype = ctypes.c_int
         L.attn_head_projection.argtypes = [vp, vp, attn_layout, ctypes.c_int32, vp, vp, vp, vp]
@@ -273,6 +278,39 @@ def decode(q: torch.Tensor, Kcache: torch.Tensor, Vcache: torch.Tensor, kv_lens:
                            _stream_handle(stream, q))
     if st != 0:
         raise AttnError(st, "attn_decode")
+    return out
+
+
+def decode_noalloc(q: torch.Tensor, Kcache: torch.Tensor, Vcache: torch.Tensor, kv_lens: torch.Tensor,
+                   scale: float | None = None, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """attn_decode_noalloc: the decode step with its partials in the library's
+    static per-GPU scratch (no workspace, no device allocation by the call).
+
+    Arguments as for decode(); `out` is allocated with torch when not given
+    (pass it to keep the whole step allocation-free).  Raises AttnError
+    (ATTN_ERR_SCRATCH_LIMIT) when the layout needs more than
+    DECODE_NOALLOC_MAX_BYTES of partials.  Calls on one GPU share that
+    scratch: calls that could overlap must be ordered by the caller.
+    """
+    dt = q.dtype
+    for n, t in (("q", q), ("Kcache", Kcache), ("Vcache", Vcache)):
+        _check_tensor(n, t, dt)
+    B, H, one, d = q.shape
+    n_max = Kcache.shape[2]
+    if one != 1 or tuple(Kcache.shape) != (B, H, n_max, d) or Vcache.shape != Kcache.shape:
+        raise ValueError("q must be [B, h, 1, d] and the caches [B, h, n_max, d]")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_tensor("out", out, dt)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = lib().attn_decode_noalloc(q.data_ptr(), Kcache.data_ptr(), Vcache.data_ptr(),
+                                   attn_layout(B, H, 1, n_max, d, _dtype_code(q)),
+                                   _lens_ptr("kv_lens", kv_lens, B), float(scale), out.data_ptr(),
+                                   _stream_handle(stream, q))
+    if st != 0:
+        raise AttnError(st, "attn_decode_noalloc")
     return out
 
 

@@ -91,6 +91,9 @@ const char* attn_status_string(attn_status status) {
     case ATTN_ERR_BAD_SCALE: return "ATTN_ERR_BAD_SCALE: scale must be finite";
     case ATTN_ERR_WORKSPACE: return "ATTN_ERR_WORKSPACE: decode workspace missing or too small";
     case ATTN_ERR_HIP: return "ATTN_ERR_HIP: a HIP runtime call failed";
+    case ATTN_ERR_SCRATCH_LIMIT:
+      return "ATTN_ERR_SCRATCH_LIMIT: attn_decode_noalloc needs more than ATTN_DECODE_NOALLOC_MAX_BYTES "
+             "of scratch for this layout (use attn_decode with a workspace)";
   }
   return "unknown attn_status";
 }
@@ -409,9 +412,11 @@ size_t attn_decode_workspace_bytes(attn_layout L) {
   return (size_t)L.B * L.h * decode_splits(L.n_k) * kPartialStride * sizeof(float);
 }
 
-attn_status attn_decode(const void* q, const void* Kcache, const void* Vcache, attn_layout L,
-                        const int32_t* kv_lens, float scale, void* O, void* workspace,
-                        size_t workspace_bytes, void* stream) {
+namespace {
+
+// Checks shared by attn_decode and attn_decode_noalloc, before any HIP call.
+attn_status check_decode(const void* q, const void* Kcache, const void* Vcache, const attn_layout& L,
+                         const int32_t* kv_lens, float scale, const void* O) {
   attn_status st = check_layout(L);
   if (st != ATTN_OK) return st;
   if (L.n_q != 1) return ATTN_ERR_BAD_SHAPE;
@@ -420,28 +425,28 @@ attn_status attn_decode(const void* q, const void* Kcache, const void* Vcache, a
   if (!q || !O || !kv_lens) return ATTN_ERR_NULL_POINTER;
   if (L.n_k > 0 && (!Kcache || !Vcache)) return ATTN_ERR_NULL_POINTER;
   if (q == O || Kcache == O || Vcache == O) return ATTN_ERR_BAD_SHAPE;
-  const size_t need = attn_decode_workspace_bytes(L);
-  if (need > 0 && (!workspace || workspace_bytes < need)) return ATTN_ERR_WORKSPACE;
   const int64_t splits = decode_splits(L.n_k);
-  if ((int64_t)L.B * L.h * splits > kMaxGrid || (int64_t)L.B * L.h > kMaxGrid)
-    return ATTN_ERR_BAD_SHAPE;
+  if ((int64_t)L.B * L.h * splits > kMaxGrid || (int64_t)L.B * L.h > kMaxGrid) return ATTN_ERR_BAD_SHAPE;
+  return ATTN_OK;
+}
 
-  hipStream_t s = static_cast<hipStream_t>(stream);
+attn_status launch_decode(const void* q, const void* Kcache, const void* Vcache, const attn_layout& L,
+                          const int32_t* kv_lens, float scale, void* O, float* work, hipStream_t s) {
+  attn_status st;
   if (length_check_enabled()) {
     if ((st = check_lengths(kv_lens, L.B, L.n_k, s)) != ATTN_OK) return st;
   }
-
   DecodeArgs a;
   a.q = q;
   a.Kc = Kcache;
   a.Vc = Vcache;
   a.O = O;
   a.kv_lens = kv_lens;
-  a.work = static_cast<float*>(workspace);
+  a.work = work;
   a.B = L.B;
   a.H = L.h;
   a.n_max = L.n_k;
-  a.n_split = (int)splits;
+  a.n_split = decode_splits(L.n_k);
   a.scale = scale;
   const hipError_t e = L.dtype == ATTN_BF16 ? launch_decode_bf16(a, s) : launch_decode_f32(a, s);
   if (e != hipSuccess) {
@@ -449,6 +454,33 @@ attn_status attn_decode(const void* q, const void* Kcache, const void* Vcache, a
     return ATTN_ERR_HIP;
   }
   return ATTN_OK;
+}
+
+}  // namespace
+
+attn_status attn_decode(const void* q, const void* Kcache, const void* Vcache, attn_layout L,
+                        const int32_t* kv_lens, float scale, void* O, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  attn_status st = check_decode(q, Kcache, Vcache, L, kv_lens, scale, O);
+  if (st != ATTN_OK || L.B == 0 || L.h == 0) return st;
+  const size_t need = attn_decode_workspace_bytes(L);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return ATTN_ERR_WORKSPACE;
+  return launch_decode(q, Kcache, Vcache, L, kv_lens, scale, O, static_cast<float*>(workspace),
+                       static_cast<hipStream_t>(stream));
+}
+
+attn_status attn_decode_noalloc(const void* q, const void* Kcache, const void* Vcache, attn_layout L,
+                                const int32_t* kv_lens, float scale, void* O, void* stream) {
+  attn_status st = check_decode(q, Kcache, Vcache, L, kv_lens, scale, O);
+  if (st != ATTN_OK || L.B == 0 || L.h == 0) return st;
+  if (attn_decode_workspace_bytes(L) > kNoAllocScratchBytes) return ATTN_ERR_SCRATCH_LIMIT;
+  float* work = nullptr;
+  const hipError_t e = decode_scratch(&work);
+  if (e != hipSuccess) {
+    g_last_hip = e;
+    return ATTN_ERR_HIP;
+  }
+  return launch_decode(q, Kcache, Vcache, L, kv_lens, scale, O, work, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

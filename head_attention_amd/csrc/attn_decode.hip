@@ -22,6 +22,8 @@
 //   O = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s.
 // Both passes are the same exact identity the online softmax uses: partial
 // sums under different pivots combine after rescaling to a common pivot.
+#include <mutex>
+
 #include "common.h"
 
 namespace headattn {
@@ -299,5 +301,35 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
 
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t s) { return launch_decode<float>(a, s); }
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s) { return launch_decode<__bf16>(a, s); }
+
+// ---- the partials of attn_decode_noalloc: a file-scope device array that
+// each GPU holds for the life of the process, so that a call allocates
+// nothing.  Host code never passes `scratch` itself to a kernel (in host code
+// the name is a host-side stand-in, not a device address): the device address
+// comes from hipGetSymbolAddress, once per device with that device current.
+static __device__ __align__(256) float scratch[kNoAllocScratchBytes / sizeof(float)];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t decode_scratch(float** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = static_cast<float*>(p);
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 }  // namespace headattn

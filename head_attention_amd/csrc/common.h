@@ -170,6 +170,13 @@ constexpr int kPairMinRows = 512;
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s);
 
+// attn_decode_noalloc keeps its split partials in a static device array of
+// this many bytes per GPU (the ATTN_DECODE_NOALLOC_MAX_BYTES of the header).
+constexpr size_t kNoAllocScratchBytes = (size_t)8 << 20;
+// Device address of that array on the current device (looked up once per
+// device); never the array's host-side name.
+hipError_t decode_scratch(float** ptr);
+
 // Clamp a device-provided length into [0, n] so that a bad length can never
 // index outside the caller's buffers.
 __device__ __forceinline__ int clamp_len(int v, int n) { return v < 0 ? 0 : (v > n ? n : v); }

@@ -105,7 +105,9 @@ typedef enum {
   ATTN_ERR_BAD_LENGTHS = 5,  /* (ATTN_CHECK=1 only) a length outside [0, n]   */
   ATTN_ERR_BAD_SCALE = 6,    /* scale is not finite                           */
   ATTN_ERR_WORKSPACE = 7,    /* decode workspace NULL or smaller than needed  */
-  ATTN_ERR_HIP = 8           /* a HIP runtime call failed                     */
+  ATTN_ERR_HIP = 8,          /* a HIP runtime call failed                     */
+  ATTN_ERR_SCRATCH_LIMIT = 9 /* attn_decode_noalloc: the layout needs more
+                                than ATTN_DECODE_NOALLOC_MAX_BYTES of scratch */
 } attn_status;
 
 /*
@@ -328,6 +330,34 @@ size_t attn_backward_workspace_bytes(attn_layout layout);
 /* Bytes of fp32 split partials attn_decode needs for this cache layout; 0 if
  * the layout is invalid.  Pure host arithmetic. */
 size_t attn_decode_workspace_bytes(attn_layout cache_layout);
+
+/* Scratch that attn_decode_noalloc holds per GPU: 8 MiB. */
+#define ATTN_DECODE_NOALLOC_MAX_BYTES ((size_t)8 << 20)
+
+/*
+ * attn_decode_noalloc -- attn_decode for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): the same computation and kernels, with the split
+ * partials kept in a static device array of ATTN_DECODE_NOALLOC_MAX_BYTES
+ * that each GPU the library runs on holds until the process ends.  The call
+ * allocates and frees nothing; the caller still owns q, the caches, kv_lens
+ * and O.
+ *
+ *   q, Kcache, Vcache, cache_layout, kv_lens, scale, O, stream
+ *           exactly as for attn_decode.
+ * Errors: those of attn_decode (never ATTN_ERR_WORKSPACE), plus
+ * ATTN_ERR_SCRATCH_LIMIT when attn_decode_workspace_bytes(cache_layout)
+ * exceeds ATTN_DECODE_NOALLOC_MAX_BYTES (e.g. B 64, h 16 fits up to
+ * n_max = 7936; B 1, h 16 up to 508,160).  Every call on one GPU shares that
+ * GPU's array, whose contents carry no meaning between calls (each call
+ * writes every record it reads): calls that may overlap on one GPU -- on
+ * different streams, or from different threads without ordering -- race and
+ * must be serialised by the caller.  The first call on a device looks up the
+ * array's device address once (thread-safe).
+ */
+attn_status attn_decode_noalloc(const void* q, const void* Kcache, const void* Vcache,
+                                attn_layout cache_layout, const int32_t* kv_lens, float scale,
+                                void* O, void* stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* attn_status_string(attn_status status);

@@ -13,7 +13,7 @@ from head_attention_amd import attn_layout
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
-OK, NULLP, SHAPE, DTYPE, MASK, LENS, SCALE, WORK, HIP = range(9)
+OK, NULLP, SHAPE, DTYPE, MASK, LENS, SCALE, WORK, HIP, SCRATCH = range(10)
 BF16, F32 = 0, 1
 FAKE = 0x1000  # never dereferenced: every call below fails validation first
 
@@ -31,7 +31,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("attn_forward", "attn_forward_lse", "attn_forward_restricted",
               "attn_backward", "attn_backward_restricted", "attn_backward_workspace_bytes",
-              "attn_decode", "attn_cache_append", "attn_head_projection",
+              "attn_decode", "attn_decode_noalloc", "attn_cache_append", "attn_head_projection",
               "attn_output_projection", "attn_decode_workspace_bytes",
               "attn_status_string", "attn_last_hip_error"):
         assert n in names, names
@@ -44,7 +44,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in range(9):
+    for code in range(10):
         s = ha.status_string(code)
         assert s.startswith(ha._binding.STATUS_NAMES[code]), s
     assert "unknown" in ha.status_string(99)
@@ -128,6 +128,34 @@ def test_decode_validation():
     assert dec(L, wsb=ha.lib().attn_decode_workspace_bytes(L) - 1) == WORK
     assert dec(L, o=FAKE) == SHAPE
     assert dec(attn_layout(0, 2, 1, 300, 64, BF16), q=None, o=None, kl=None) == OK
+
+
+def dec_noalloc(layout, q=FAKE, k=FAKE, v=FAKE, kl=FAKE + 32, o=FAKE + 64, scale=0.125):
+    return ha.lib().attn_decode_noalloc(q, k, v, layout, kl, scale, o, None)
+
+
+def test_decode_noalloc_validation():
+    """The allocation-free decode validates like attn_decode, and rejects a
+    layout whose partials exceed the static scratch before any HIP call."""
+    L = attn_layout(4, 2, 1, 300, 64, BF16)
+    assert dec_noalloc(attn_layout(4, 2, 2, 300, 64, BF16)) == SHAPE
+    assert dec_noalloc(attn_layout(4, 2, 1, 300, 16, BF16)) == SHAPE
+    assert dec_noalloc(attn_layout(4, 2, 1, 300, 64, 7)) == DTYPE
+    assert dec_noalloc(L, scale=float("nan")) == SCALE
+    assert dec_noalloc(L, q=None) == NULLP
+    assert dec_noalloc(L, kl=None) == NULLP
+    assert dec_noalloc(L, o=FAKE) == SHAPE
+    assert dec_noalloc(attn_layout(0, 2, 1, 300, 64, BF16), q=None, o=None, kl=None) == OK
+    # 64 x 16 heads: partials fit up to n_max = 7936 (31 splits of 256 keys)
+    lim = ha.DECODE_NOALLOC_MAX_BYTES
+    assert ha.lib().attn_decode_workspace_bytes(attn_layout(64, 16, 1, 7936, 64, BF16)) <= lim
+    assert ha.lib().attn_decode_workspace_bytes(attn_layout(64, 16, 1, 7937, 64, BF16)) > lim
+    assert dec_noalloc(attn_layout(64, 16, 1, 7937, 64, BF16)) == SCRATCH
+    assert dec_noalloc(attn_layout(1, 16, 1, 508161, 64, F32)) == SCRATCH
+    assert "ATTN_ERR_SCRATCH_LIMIT" in ha.status_string(SCRATCH)
+    hdr = open(os.path.join(ROOT, "include", "headattn.h"), encoding="utf-8").read()
+    m = re.search(r"#define ATTN_DECODE_NOALLOC_MAX_BYTES \(\(size_t\)(\d+) << (\d+)\)", hdr)
+    assert m and int(m.group(1)) << int(m.group(2)) == lim
 
 
 def app(layout, kn=FAKE, vn=FAKE + 32, kc=FAKE + 64, vc=FAKE + 96, kl=FAKE + 128):
