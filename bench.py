@@ -104,7 +104,12 @@ class Leg:
             ql = n_q * B if c["q_lens"] is None else int(c["q_lens"].sum())
             kl = n_k * B if not (c["mask"] & 1) else int(c["kv_lens"].clamp(0, n_k).sum())
             row = H * D * el
-            self.bytes += (ql + 2 * kl + B * n_q) * row
+            if self.bwd:
+                # read Q, O, dO (valid query rows), K, V (valid key rows) and one
+                # fp32 log-sum-exp per query row; write dQ, dK, dV in full
+                self.bytes += (3 * ql + 2 * kl) * row + 4 * B * H * n_q + (B * n_q + 2 * B * n_k) * row
+            else:
+                self.bytes += (ql + 2 * kl + B * n_q) * row
             self.bytes += 4 * B * ((c["q_lens"] is not None) + (c["kv_lens"] is not None))
         if self.decode is not None:
             d = self.decode
@@ -272,50 +277,95 @@ def sanity_check(legs):
 
 
 # ------------------------------------------------------------ CPU baseline
-def cpu_baseline(target_s: float = 25.0):
-    """The fp64 oracle as it stands, single-threaded BLAS, on a bounded
-    sample of the long_causal workload: evenly spaced query rows of every
-    head (each row does its full causal prefix), sized from a short probe to
-    take about target_s.  Throughput in the same algorithmic flop units as
-    the GPU number."""
+# Worker state for the all-core run: the long_causal tensors in fp64, set in
+# the parent before the pool forks (the children read them copy-on-write).
+_CPU_QKV = None
+
+
+def _cpu_rows(rows):
+    """One worker of the all-core run: the oracle on its share of the rows,
+    one BLAS thread."""
     import oracle.attn_oracle as orc
+    from threadpoolctl import threadpool_limits
+    Q, K, V = _CPU_QKV
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        orc.attention(Q, K, V, mask_kind=orc.MASK_CAUSAL, scale=0.125, rows=rows)
+        return time.perf_counter() - t0
+
+
+def _cpu_model() -> str:
     try:
-        from threadpoolctl import threadpool_limits
-    except ImportError:  # pragma: no cover
-        threadpool_limits = None
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(target_1t_s: float = 8.0, max_workers: int = 16):
+    """The fp64 oracle as it stands (oracle/attn_oracle.py, untuned) on the
+    long_causal workload, in the same algorithmic flop units as the GPU:
+      * all cores: every query row of all 16 heads, split into interleaved
+        shares over a pool of worker processes (one BLAS thread each) -- the
+        host cores this process may use, at most max_workers (the CPU share
+        of one GPU on these hosts);
+      * one core: evenly spaced rows of every head, each with its full causal
+        prefix, sized from a short probe to take about target_1t_s.
+    Run before the GPU is initialised, so the pool forks a process with no
+    device context."""
+    import multiprocessing as mp
+    import oracle.attn_oracle as orc
+    from threadpoolctl import threadpool_limits
+    global _CPU_QKV
     c = workloads.make("long_causal")["calls"][0]
     Q, K, V = (c[k].float().double().numpy() for k in ("Q", "K", "V"))
     H, n = Q.shape[1], Q.shape[2]
-    ctx = threadpool_limits(limits=1) if threadpool_limits else None
-    try:
-        if ctx:
-            ctx.__enter__()
-        # probe: rows spread over the causal lengths; the mean row is half length
+    _CPU_QKV = (Q, K, V)
+    visible = len(os.sched_getaffinity(0))
+    workers = max(1, min(visible, max_workers))
+    model = _cpu_model()
+    flops_of = lambda rows: sum(4 * D * (i + 1) for (_, _, i) in rows)
+
+    # one core
+    with threadpool_limits(limits=1):
         probe = [(0, 0, i) for i in range(n - 1, 0, -(n // 8))]
         t0 = time.perf_counter()
         orc.attention(Q, K, V, mask_kind=orc.MASK_CAUSAL, scale=0.125, rows=probe)
         per_row = (time.perf_counter() - t0) / sum(i + 1 for (_, _, i) in probe) * (n / 2)
-        per_head = int(max(16, min(n, target_s / max(per_row, 1e-9) / H)))
+        per_head = int(max(16, min(n, target_1t_s / max(per_row, 1e-9) / H)))
         stride = max(1, n // per_head)
         rows = [(0, h, i) for h in range(H) for i in range((stride // 2 + h) % stride, n, stride)]
         t0 = time.perf_counter()
         orc.attention(Q, K, V, mask_kind=orc.MASK_CAUSAL, scale=0.125, rows=rows)
-        dt = time.perf_counter() - t0
-    finally:
-        if ctx:
-            ctx.__exit__(None, None, None)
-    flops = sum(4 * D * (i + 1) for (_, _, i) in rows)
-    what = ("all query rows" if stride == 1 else
-            f"every {stride}th query row (offset by head)")
-    return {
-        "value": flops / dt / 1e12,
-        "unit": "TFLOP/s",
-        "cores": 1,
-        "kind": "oracle",
-        "sample": f"long_causal (B1 h16 n=8192 causal): {what} of all {H} heads, "
-                  f"{len(rows)} rows, full causal prefix each; fp64 NumPy, 1 BLAS thread; "
-                  f"{dt:.1f} s",
+        dt1 = time.perf_counter() - t0
+    one = {
+        "value": flops_of(rows) / dt1 / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+        "sample": f"long_causal (B1 h16 n=8192 causal): every {stride}th query row of each head, "
+                  f"{len(rows)} rows, full causal prefix each; fp64 NumPy, 1 BLAS thread; {dt1:.1f} s",
+        "cpu_model": model, "host_cores_visible": visible,
     }
+
+    # all cores: interleaved shares of every row, so each worker gets the same
+    # mix of short and long causal prefixes
+    all_rows = [(0, h, i) for h in range(H) for i in range(n)]
+    shares = [all_rows[w::workers] for w in range(workers)]
+    ctx = mp.get_context("fork")
+    t0 = time.perf_counter()
+    with ctx.Pool(workers) as pool:
+        busy = pool.map(_cpu_rows, shares)
+    dtn = time.perf_counter() - t0
+    _CPU_QKV = None
+    allc = {
+        "value": flops_of(all_rows) / dtn / 1e12, "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
+        "sample": f"long_causal (B1 h16 n=8192 causal): all {len(all_rows)} query rows of all {H} heads, "
+                  f"full causal prefix each, split over {workers} worker processes (1 BLAS thread each); "
+                  f"fp64 NumPy; {dtn:.1f} s wall, {max(busy):.1f} s longest worker",
+        "cpu_model": model, "host_cores_visible": visible,
+    }
+    return allc, one
 
 
 # ------------------------------------------------------- rocprof summaries
@@ -431,6 +481,121 @@ def summarize_counters(fetch_csv: str, write_csv: str, copy_mib: int, out_json: 
     return "\n".join(lines)
 
 
+def summarize_pmc(csvs, trace_csv=None, n_simd: int = 1024, n_se: int = 32) -> str:
+    """Per-kernel MFMA and VALU figures from rocprofv3 --pmc runs of the bench
+    (one CSV per pass; counters averaged over a kernel's launches).  Kernel
+    durations come from a kernel-trace run of the same command when given
+    (counter runs serialise dispatches), else from the counter CSV.
+
+    mfma busy: SQ_VALU_MFMA_BUSY_CYCLES (summed over the SIMDs) over n_simd
+      SIMDs x duration x clock, at the 2.4 GHz peak clock and at the clock
+      the shader engines held (SQ_BUSY_CYCLES per engine over the duration, a
+      lower bound: an engine counts only while it holds waves).
+    mfma TFLOP/s: bf16 MFMA flops executed (SQ_INSTS_VALU_MFMA_MOPS_BF16 x
+      512, padding and row-sum products included) over the duration.
+    per wave: instructions issued per wave (SQ_INSTS_* over SQ_WAVES)."""
+    import csv
+    import collections
+    acc = collections.defaultdict(lambda: collections.defaultdict(list))
+    dur = collections.defaultdict(dict)
+    for path in csvs:
+        for r in csv.DictReader(open(path)):
+            k = (_short_kernel(r["Kernel_Name"]), int(r["Grid_Size"]))
+            acc[k][r["Counter_Name"]].append(float(r["Counter_Value"]))
+            dur[k][(path, r["Dispatch_Id"])] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+    tdur = {}
+    if trace_csv:
+        g = collections.defaultdict(list)
+        for r in csv.DictReader(open(trace_csv)):
+            grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+            g[(_short_kernel(r["Kernel_Name"]), grid)].append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        tdur = {k: sum(v) / len(v) for k, v in g.items()}
+    lines = ["| kernel | grid | leg | us | held clock GHz (>=) | mfma busy @2.4 GHz | mfma busy @held | "
+             "mfma TFLOP/s executed | VALU/wave | TRANS/wave | MFMA/wave | VALU co-issued with MFMA |",
+             "|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    for k in sorted(acc, key=lambda k: -sum(dur[k].values())):
+        c = {n: sum(v) / len(v) for n, v in acc[k].items()}
+        us = tdur.get(k, sum(dur[k].values()) / len(dur[k]))
+        if "SQ_VALU_MFMA_BUSY_CYCLES" not in c or us <= 0:
+            continue
+        busy = c["SQ_VALU_MFMA_BUSY_CYCLES"]
+        clk = c.get("SQ_BUSY_CYCLES", 0.0) / n_se / (us * 1e3) if "SQ_BUSY_CYCLES" in c else float("nan")
+        waves = c.get("SQ_WAVES", float("nan"))
+        per_wave = lambda n: c[n] / waves if n in c and waves == waves and waves > 0 else float("nan")
+        co = c.get("SQ_VALU_MFMA_COEXEC_CYCLES", float("nan")) / busy if busy > 0 else float("nan")
+        lines.append(
+            f"| {k[0]} | {k[1]} | {LEG_GRIDS.get(k, '')} | {us:.2f} | {clk:.2f} | "
+            f"{busy / (n_simd * us * 1e3 * 2.4):.3f} | {busy / (n_simd * us * 1e3 * clk):.3f} | "
+            f"{c.get('SQ_INSTS_VALU_MFMA_MOPS_BF16', 0) * 512 / (us * 1e-6) / 1e12:.1f} | "
+            f"{per_wave('SQ_INSTS_VALU'):.0f} | {per_wave('SQ_INSTS_VALU_TRANS_F32'):.0f} | "
+            f"{per_wave('SQ_INSTS_MFMA'):.0f} | {co:.2f} |")
+    return "\n".join(lines)
+
+
+# -------------------------------------------------- rooflines, device, floor
+RIDGE_FLOP_PER_BYTE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBPS * 1e9)  # 312.5
+
+
+def roof(kernel: str, flops: int, nbytes: int, ms: float) -> dict:
+    """Roofline entry of one leg: bound by whichever roof its arithmetic
+    intensity (algorithmic flops per algorithmic byte) meets first -- the
+    bf16 MFMA peak above the ridge, HBM below it."""
+    ai = flops / nbytes
+    if ai >= RIDGE_FLOP_PER_BYTE:
+        achieved, peak, unit, bound = flops / (ms * 1e-3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s", "mfma"
+    else:
+        achieved, peak, unit, bound = nbytes / (ms * 1e-3) / 1e9, PEAK_HBM_GBPS, "GB/s", "hbm"
+    return {"bound": bound, "kernel": kernel, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "flop_per_byte": round(ai, 1)}
+
+
+def device_info() -> dict:
+    """Compute units and peak clock as the HIP runtime reports them, and the
+    dense bf16 MFMA peak they imply (4096 flop per clock per CU)."""
+    import ctypes
+    props = torch.cuda.get_device_properties(0)
+    out = {"name": props.name, "arch": getattr(props, "gcnArchName", "")}
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        v = ctypes.c_int()
+        attrs = {"clock_khz": 5, "cu": 63}  # hipDeviceAttributeClockRate, ...MultiprocessorCount
+        for k, a in attrs.items():
+            if hip.hipDeviceGetAttribute(ctypes.byref(v), a, 0) == 0:
+                out[k] = v.value
+    except OSError:
+        pass
+    if "cu" in out and "clock_khz" in out:
+        out["max_clock_mhz"] = out.pop("clock_khz") / 1e3
+        out["bf16_peak_tflops_from_device"] = round(out["cu"] * out["max_clock_mhz"] * 1e6 * 4096 / 1e12, 1)
+    return out
+
+
+def launch_floor(stream, reps: int = 200) -> dict:
+    """Per-launch time of back-to-back launches on the bench's stream, timed
+    with HIP events: an empty kernel (torch's spin kernel with 0 cycles) and
+    the library's smallest forward call (one bf16 row of one head)."""
+    import head_attention_amd as ha
+    res = {}
+    q = torch.zeros((1, 1, 1, 64), dtype=torch.bfloat16, device="cuda")
+    o = torch.empty_like(q)
+    tests = [("forward_1row_us", lambda: ha.forward(q, q, q, out=o))]
+    if hasattr(torch.cuda, "_sleep"):
+        tests.insert(0, ("empty_kernel_us", lambda: torch.cuda._sleep(0)))
+    for name, fn in tests:
+        for _ in range(20):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res[name] = round(e0.elapsed_time(e1) * 1e3 / reps, 2)
+    return res
+
+
 # ------------------------------------------------------------------ main
 def main():
     ap = argparse.ArgumentParser()
@@ -448,7 +613,14 @@ def main():
                     help="print HBM traffic per launch from rocprofv3 --pmc runs (with "
                          "--copy-probe-mib naming the probe size) and exit")
     ap.add_argument("--traffic-json", help="with --summarize-counters: write the figures here")
+    ap.add_argument("--summarize-pmc", nargs="+", metavar="COUNTER_CSV",
+                    help="print per-kernel MFMA / VALU figures from rocprofv3 --pmc runs and exit")
+    ap.add_argument("--trace-csv", help="with --summarize-pmc: kernel-trace CSV for the durations")
     args = ap.parse_args()
+
+    if args.summarize_pmc:
+        print(summarize_pmc(args.summarize_pmc, args.trace_csv))
+        return
 
     if args.summarize_trace:
         print(summarize_trace(args.summarize_trace))
@@ -463,6 +635,10 @@ def main():
                                    "multi-GPU mode (each GPU would run the same kernels on its "
                                    "share of heads or sequences); run with --gpus 1"}))
         sys.exit(2)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline()  # before the GPU is initialised (its pool forks)
 
     import head_attention_amd as ha
     ha.lib()  # fail loudly if the library is missing
@@ -555,42 +731,22 @@ def main():
             "frac": round(lc_tflops / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
         },
-        "roofline_bwd": {
-            "bound": "mfma",
-            "kernel": "bwd_rowdot + bwd_dkdv + bwd_dq on long_causal_bwd (B1 h16 n8192)",
-            "achieved": round(legs[[l.name for l in legs].index("long_causal_bwd")].flops
-                              / (leg_ms[[l.name for l in legs].index("long_causal_bwd")] * 1e-3) / 1e12, 2),
-            "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s",
-        },
-        "roofline_proj": {
-            "bound": "mfma",
-            "kernel": "proj_gemm_kernel on mha_proj (decoder_big layer projections)",
-            "achieved": round(legs[[l.name for l in legs].index("mha_proj")].flops
-                              / (leg_ms[[l.name for l in legs].index("mha_proj")] * 1e-3) / 1e12, 2),
-            "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s",
-        },
-        "roofline_restricted": {
-            "bound": "mfma",
-            "kernel": "attn_fwd_bf16_pair_kernel<band> on long_restricted (B1 h16 n8192, radius 256)",
-            "achieved": round(legs[[l.name for l in legs].index("long_restricted")].flops
-                              / (leg_ms[[l.name for l in legs].index("long_restricted")] * 1e-3) / 1e12, 2),
-            "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s",
-        },
-        "roofline_decode": {
-            "bound": "hbm",
-            "kernel": "decode_partial_kernel + decode_merge_kernel on kv_decode",
-            "achieved": round(kd_gbps, 1),
-            "peak": PEAK_HBM_GBPS,
-            "unit": "GB/s",
-            "frac": round(kd_gbps / PEAK_HBM_GBPS, 4),
-        },
     }
-    out["roofline_proj"]["frac"] = round(out["roofline_proj"]["achieved"] / PEAK_BF16_TFLOPS, 4)
-    out["roofline_bwd"]["frac"] = round(out["roofline_bwd"]["achieved"] / PEAK_BF16_TFLOPS, 4)
-    out["roofline_restricted"]["frac"] = round(out["roofline_restricted"]["achieved"] / PEAK_BF16_TFLOPS, 4)
+    ix = {l.name: j for j, l in enumerate(legs)}
+
+    def leg_roof(name, kernel):
+        return roof(kernel, legs[ix[name]].flops, legs[ix[name]].bytes, leg_ms[ix[name]])
+
+    out["roofline_bwd"] = leg_roof("long_causal_bwd", "bwd_rowdot + bwd_dkdv + bwd_dq on long_causal_bwd (B1 h16 n8192)")
+    out["roofline_proj"] = leg_roof("mha_proj", "proj_gemm_kernel on mha_proj (decoder_big layer projections)")
+    out["roofline_restricted"] = leg_roof(
+        "long_restricted", "attn_fwd_bf16_pair_kernel<band> on long_restricted (B1 h16 n8192, radius 256)")
+    out["roofline_decode"] = leg_roof("kv_decode", "decode_partial_kernel + decode_merge_kernel on kv_decode")
+    out["roofline_n128"] = {n: leg_roof(n, k) for n, k in (
+        ("encoder_base", "attn_fwd_bf16_short_kernel<none> on encoder_base (B32 h8 n128, key padding)"),
+        ("decoder_big", "attn_fwd_bf16_short_kernel<causal> + <none> on decoder_big (B32 h16, 128 self, 128->160)"))}
+    out["device"] = device_info()
+    out["launch_floor"] = launch_floor(stream)
     if args.copy_probe_mib:
         src = torch.ones(args.copy_probe_mib * 2 ** 18, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
@@ -606,8 +762,8 @@ def main():
         out["sanity_append_rows_exact"] = bool(
             torch.equal(caches["Kcache"][bi, :, rows], ap["Knew"][:, :, 0])
             and torch.equal(caches["Vcache"][bi, :, rows], ap["Vnew"][:, :, 0]))
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline()
+    if cpu is not None:
+        out["cpu_baseline"], out["cpu_baseline_1core"] = cpu
     print(json.dumps(out), flush=True)
 
 
