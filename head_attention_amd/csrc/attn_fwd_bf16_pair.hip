@@ -2,11 +2,20 @@
 //
 // Computes O = softmax(Q K^T * scale + M) V per (b, h) ("[논문 리뷰]Attention
 // Is All You Need", §3.2.1 equation; masking by -inf logits before the
-// softmax, §3.2.3) with the same arithmetic as the 4-wave kernel in
-// attn_fwd_bf16.hip: exact bf16 Q (sign of scale folded in), S^T = K Q^T and
-// O^T += V^T P^T on v_mfma_f32_32x32x16_bf16, weights exp2(s c - m c) with a
-// lazy pivot, bf16 weights, fp32 accumulation.  What differs is how the work
-// is laid over the compute unit.
+// softmax, §3.2.3): exact bf16 Q (sign of scale folded in), S^T = K Q^T and
+// O^T += V^T P^T on v_mfma_f32_32x32x16_bf16, weights exp2(s c - m c), bf16
+// weights, fp32 accumulation.
+//
+// Two kernels per call.  The first forms every weight under a fixed pivot
+// m = 0 -- one multiply and one exponential per score, no row maxima -- and
+// checks at the end that every row's sum stayed in a range where that pivot
+// is exact up to rounding (softmax does not depend on the pivot).  A
+// workgroup with a row outside it (logits beyond about +64 or below about
+// -32 in log2 units: rare, adversarial inputs) writes a mark instead of its
+// results, and the second kernel, launched right after on the same grid,
+// recomputes exactly those workgroups with a pivot that moves to the row
+// maximum (the lazy pivot of the other bf16 kernels); every other workgroup
+// of the second kernel exits at once.
 //
 // Workgroup: 8 waves own 256 query rows of one (b, h).  The hardware puts
 // waves w and w + 4 on the same SIMD; both take the same 64 rows (row group
@@ -17,8 +26,8 @@
 //
 // Per tile a wave does two phases: an MFMA phase (O += P V of its previous
 // tile, then S = K Q^T of this tile: 32 matrix instructions) and a vector
-// phase (mask, row max and pivot check, exp2, bf16 pack of this tile: ~200
-// VALU instructions).  The pair runs one phase apart and a workgroup barrier
+// phase (mask, exp2 and bf16 pack of this tile: ~165 VALU instructions in
+// the first kernel; the moving pivot adds the row max and its checks).  The pair runs one phase apart and a workgroup barrier
 // closes every phase, so while one wave of a SIMD issues matrix instructions
 // the other issues the exponentials: the two kinds of work overlap across the
 // two waves instead of alternating inside one.  (Measured on MI355X: MFMA
@@ -100,7 +109,7 @@ constexpr int kSlots = 8;
 constexpr int kAhead = 5;
 // Row sums and pivots of the odd-tile waves for the final merge.
 __shared__ float2 g_lm[4][2][64];
-// Set when a row failed the fixed-pivot range check: the workgroup runs again.
+// Set when a row failed the fixed-pivot range check.
 __shared__ int g_redo;
 
 template <int S>
@@ -174,12 +183,29 @@ __device__ __forceinline__ void barrier_lds() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// One workgroup's whole computation, in one of two passes: FIXED = the
-// weights under the fixed pivot 0, followed by a range check (returns false,
-// writing nothing, when a row fails it); otherwise the moving pivot (always
-// succeeds).  The kernel inlines the first pass and calls the second, which is
-// rare, as a separate function: two copies of the pipeline in one function
-// spill the Q fragments inside the loop.
+// (b, h, query tile) of workgroup bid: the 8 XCDs take workgroup ids round
+// robin; when B*h divides by 8 each XCD gets whole heads.  Longest tiles
+// first under the causal mask.
+template <int MODE>
+__device__ __forceinline__ void wg_tile(const FwdArgs& a, int bid, int& bh, int& qt) {
+  const int n_qt = (a.n_q + kBM - 1) / kBM;
+  const int HB = a.H * a.B;
+  int rank;
+  if ((HB & 7) == 0) {
+    const int per = HB >> 3;
+    const int slot = bid >> 3;
+    rank = slot / per;
+    bh = (bid & 7) * per + slot % per;
+  } else {
+    bh = bid % HB;
+    rank = bid / HB;
+  }
+  qt = MODE == kModeCausal ? (n_qt - 1 - rank) : rank;
+}
+
+// One workgroup's computation.  FIXED: the weights under the fixed pivot 0,
+// then a range check of every row; returns false, having written nothing,
+// when a row fails it.  Otherwise: the moving pivot, which always succeeds.
 template <int MODE, bool FIXED>
 __device__ __forceinline__ bool pair_pass(const FwdArgs& a) {
   constexpr bool CAUSAL = MODE == kModeCausal;
@@ -192,23 +218,8 @@ __device__ __forceinline__ bool pair_pass(const FwdArgs& a) {
   const int rg = wave & 3;    // row group (waves rg and rg + 4 share a SIMD)
   const int par = wave >> 2;  // parity of the tiles this wave takes
 
-  // ---- (b, h, query tile): the 8 XCDs take workgroup ids round robin; when
-  // B*h divides by 8 each XCD gets whole heads.  Longest tiles first under
-  // the causal mask.
-  const int n_qt = (a.n_q + kBM - 1) / kBM;
-  const int HB = a.H * a.B;
-  const int bid = blockIdx.x;
-  int bh, rank;
-  if ((HB & 7) == 0) {
-    const int per = HB >> 3;
-    const int slot = bid >> 3;
-    rank = slot / per;
-    bh = (bid & 7) * per + slot % per;
-  } else {
-    bh = bid % HB;
-    rank = bid / HB;
-  }
-  const int qt = CAUSAL ? (n_qt - 1 - rank) : rank;
+  int bh, qt;
+  wg_tile<MODE>(a, blockIdx.x, bh, qt);
   const int b = bh / a.H;
 
   const __bf16* Q = static_cast<const __bf16*>(a.Q) + (size_t)bh * a.n_q * kHeadDim;
@@ -299,7 +310,7 @@ __device__ __forceinline__ bool pair_pass(const FwdArgs& a) {
   f32x16 o[2][2];    // O^T[d block][query block]
   f32x16 sc[2][2];   // S^T[key block][query block] of the current tile
   uint32_t pk[2][16];  // bf16 weights [query block][8 key block + pair]
-  float mc[2];  // pivot term m * c per query block
+  float mc[2] = {0.f, 0.f};  // pivot term m * c per query block
   // Row sums of the bf16 weights, accumulated on the matrix cores: one
   // v_mfma_f32_16x16x32_bf16 per key step and query block takes the weights
   // as they sit in the P registers (B operand: lane l supplies 8 values of
@@ -309,15 +320,25 @@ __device__ __forceinline__ bool pair_pass(const FwdArgs& a) {
   // 16 x 16 result then holds the sums of queries 0..15 and row 1 those of
   // queries 16..31: lanes 0..15, registers 0 and 1 (rows 2..15 stay 0).
   // Each product is an exact bf16 value times 1, summed in fp32.
-  f32x4 ls[2];
+  f32x4 ls[2] = {f32x4{}, f32x4{}};
   const bf16x8 sel = __builtin_bit_cast(
       bf16x8, (((lane & 15) == 0 && ((lane >> 4) & 1) == 0) || ((lane & 15) == 1 && ((lane >> 4) & 1) == 1))
                   ? make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u)
                   : make_uint4(0u, 0u, 0u, 0u));
   // Whether a row has summed a nonzero weight yet (the pivot may move down
-  // only before that); both half-waves of a row agree.  (All of this state is
-  // reset at the start of each pass.)
-  bool seen[2];
+  // only before that); both half-waves of a row agree.
+  bool seen[2] = {false, false};
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      o[i][j] = f32x16{};
+      sc[i][j] = f32x16{};
+    }
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) pk[qb][i] = 0u;
 
   // MFMA operand fragments, read from LDS in the MFMA phase in the order
   // of use with at most 12 reads in flight, so each group of products waits
@@ -527,7 +548,7 @@ __device__ __forceinline__ bool pair_pass(const FwdArgs& a) {
   // Weights of tile t under the fixed pivot 0 (the first pass): the same
   // masks, then x = s c and 2^x straight away -- no row maxima, no pivot
   // checks.  Whether the pivot was safe for every row is decided once, from
-  // the row sums at the end (see the range check after the loop).
+  // the row sums at the end (the range check after the loop).
   auto softmax_fixed = [&](int t) __attribute__((always_inline)) {
     const int k0 = k_base + t * kBN;
     bool need_mask = (k0 + kBN > kv_lim) || (CAUSAL && k0 + kBN - 1 > qw0);
@@ -580,116 +601,93 @@ __device__ __forceinline__ bool pair_pass(const FwdArgs& a) {
   using J6 = std::integral_constant<int, 6>;
   using J7 = std::integral_constant<int, 7>;
 
-  // The pass over the tiles, from a reset state.
-  auto run = [&]() __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        o[i][j] = f32x16{};
-        sc[i][j] = f32x16{};
+  if (n_tiles > 0) {
+    // Prologue: tiles 0 .. 4 (K and V) as if filled at phases -5 .. -1.
+    fill_k(J0(), 0);
+    fill_v(J0(), 0);
+    fill_k(J1(), 1);
+    fill_v(J1(), 1);
+    fill_k(J2(), 2);
+    fill_v(J2(), 2);
+    fill_k(J3(), 3);
+    fill_v(J3(), 3);
+    fill_k(J4(), 4);
+    fill_v(J4(), 4);
+    // The first MFMA phases of the two waves of a pair (p = 0, 1) read the
+    // V tiles of slots 6 and 7 with zero weights: zero them, since 0 * NaN
+    // of stale LDS contents would not be zero.
+    g_v6[tid] = make_uint4(0, 0, 0, 0);
+    g_v7[tid] = make_uint4(0, 0, 0, 0);
+    __builtin_amdgcn_s_waitcnt(0x0070 | 8);  // vmcnt(8), lgkmcnt(0): tile 0 has landed
+    barrier_lds();
+    // Even-tile waves run MFMA phases at even p, odd-tile waves at odd p;
+    // both run the same number of phases (and barriers).
+    const int n_phases = n_tiles + 2;
+    if (par == 0) {
+#pragma nounroll
+      for (int p = 0; p < n_phases; p += 8) {
+        fills(J0(), p);     mphase(J0()); sync();
+        fills(J1(), p + 1); vphase(p);              sync();
+        if (p + 2 >= n_phases) break;
+        fills(J2(), p + 2); mphase(J2()); sync();
+        fills(J3(), p + 3); vphase(p + 2);          sync();
+        if (p + 4 >= n_phases) break;
+        fills(J4(), p + 4); mphase(J4()); sync();
+        fills(J5(), p + 5); vphase(p + 4);          sync();
+        if (p + 6 >= n_phases) break;
+        fills(J6(), p + 6); mphase(J6()); sync();
+        fills(J7(), p + 7); vphase(p + 6);          sync();
       }
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) pk[qb][i] = 0u;
-      mc[qb] = 0.f;
-      ls[qb] = f32x4{};
-      seen[qb] = false;
-    }
-    if (n_tiles > 0) {
-      // Prologue: tiles 0 .. 4 (K and V) as if filled at phases -5 .. -1.
-      fill_k(J0(), 0);
-      fill_v(J0(), 0);
-      fill_k(J1(), 1);
-      fill_v(J1(), 1);
-      fill_k(J2(), 2);
-      fill_v(J2(), 2);
-      fill_k(J3(), 3);
-      fill_v(J3(), 3);
-      fill_k(J4(), 4);
-      fill_v(J4(), 4);
-      // The first MFMA phases of the two waves of a pair (p = 0, 1) read the
-      // V tiles of slots 6 and 7 with zero weights: zero them, since 0 * NaN
-      // of stale LDS contents would not be zero.
-      g_v6[tid] = make_uint4(0, 0, 0, 0);
-      g_v7[tid] = make_uint4(0, 0, 0, 0);
-      __builtin_amdgcn_s_waitcnt(0x0070 | 8);  // vmcnt(8), lgkmcnt(0): tile 0 has landed
-      barrier_lds();
-      // Even-tile waves run MFMA phases at even p, odd-tile waves at odd p;
-      // both run the same number of phases (and barriers).
-      const int n_phases = n_tiles + 2;
-      if (par == 0) {
-  #pragma nounroll
-        for (int p = 0; p < n_phases; p += 8) {
-          fills(J0(), p);     mphase(J0()); sync();
-          fills(J1(), p + 1); vphase(p);              sync();
-          if (p + 2 >= n_phases) break;
-          fills(J2(), p + 2); mphase(J2()); sync();
-          fills(J3(), p + 3); vphase(p + 2);          sync();
-          if (p + 4 >= n_phases) break;
-          fills(J4(), p + 4); mphase(J4()); sync();
-          fills(J5(), p + 5); vphase(p + 4);          sync();
-          if (p + 6 >= n_phases) break;
-          fills(J6(), p + 6); mphase(J6()); sync();
-          fills(J7(), p + 7); vphase(p + 6);          sync();
-        }
-      } else {
-  #pragma nounroll
-        for (int p = 0; p < n_phases; p += 8) {
-          fills(J0(), p);     vphase(p - 1);              sync();
-          fills(J1(), p + 1); mphase(J1()); sync();
-          if (p + 2 >= n_phases) break;
-          fills(J2(), p + 2); vphase(p + 1);              sync();
-          fills(J3(), p + 3); mphase(J3()); sync();
-          if (p + 4 >= n_phases) break;
-          fills(J4(), p + 4); vphase(p + 3);              sync();
-          fills(J5(), p + 5); mphase(J5()); sync();
-          if (p + 6 >= n_phases) break;
-          fills(J6(), p + 6); vphase(p + 5);              sync();
-          fills(J7(), p + 7); mphase(J7()); sync();
-        }
+    } else {
+#pragma nounroll
+      for (int p = 0; p < n_phases; p += 8) {
+        fills(J0(), p);     vphase(p - 1);              sync();
+        fills(J1(), p + 1); mphase(J1()); sync();
+        if (p + 2 >= n_phases) break;
+        fills(J2(), p + 2); vphase(p + 1);              sync();
+        fills(J3(), p + 3); mphase(J3()); sync();
+        if (p + 4 >= n_phases) break;
+        fills(J4(), p + 4); vphase(p + 3);              sync();
+        fills(J5(), p + 5); mphase(J5()); sync();
+        if (p + 6 >= n_phases) break;
+        fills(J6(), p + 6); vphase(p + 5);              sync();
+        fills(J7(), p + 7); mphase(J7()); sync();
       }
-      __builtin_amdgcn_s_waitcnt(0x0F70 | 0);  // no fill may land in the merge area
-      barrier_lds();
     }
-  };
+    __builtin_amdgcn_s_waitcnt(0x0F70 | 0);  // no fill may land in the merge area
+    barrier_lds();
+  }
 
-  // ---- hand the odd-tile waves' (O, l, m) to their partners through LDS.
-  // Eight 8 KB tiles (64 KB) hold O as 16 vec4 groups ([d block][query
-  // block][register / 4]) x 4 row groups x 64 lanes; group vg sits in tile
-  // vg / 2, so every index is a compile-time tile.
+  // ---- merge the pair: the odd-tile wave hands (O, l, m) to its partner
+  // through LDS.  Eight 8 KB tiles (64 KB) hold O as 16 vec4 groups
+  // ([d block][query block][register / 4]) x 4 row groups x 64 lanes; group
+  // vg sits in tile vg / 2, so every index is a compile-time tile.
   auto mptr = [&](auto vg_tag) __attribute__((always_inline)) -> float4* {
     constexpr int VG = decltype(vg_tag)::value;
     return reinterpret_cast<float4*>(mslot<VG / 2>()) + ((VG & 1) * 4 + rg) * 64 + lane;
   };
+  // Full row sums in the row layout: lane (ln, hh) takes query ln's sum from
+  // lane ln % 16, register ln / 16.
   float l[2];
-  auto handoff = [&]() __attribute__((always_inline)) {
-    // Full row sums in the row layout: lane (ln, hh) takes query ln's sum
-    // from lane ln % 16, register ln / 16.
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const float v0 = __int_as_float(__builtin_amdgcn_ds_bpermute((lane & 15) * 4, __float_as_int(ls[qb][0])));
-      const float v1 = __int_as_float(__builtin_amdgcn_ds_bpermute((lane & 15) * 4, __float_as_int(ls[qb][1])));
-      l[qb] = (ln < 16) ? v0 : v1;
-    }
-    if (par == 1) {
-      static_for<16>([&](auto vg_tag) {
-        constexpr int VG = decltype(vg_tag)::value;
-        constexpr int DB = VG / 8, QB = (VG / 4) % 2, R = 4 * (VG % 4);
-        *mptr(vg_tag) = make_float4(o[DB][QB][R], o[DB][QB][R + 1], o[DB][QB][R + 2], o[DB][QB][R + 3]);
-      });
+  for (int qb = 0; qb < 2; ++qb) {
+    const float v0 = __int_as_float(__builtin_amdgcn_ds_bpermute((lane & 15) * 4, __float_as_int(ls[qb][0])));
+    const float v1 = __int_as_float(__builtin_amdgcn_ds_bpermute((lane & 15) * 4, __float_as_int(ls[qb][1])));
+    l[qb] = (ln < 16) ? v0 : v1;
+  }
+  if (par == 1) {
+    static_for<16>([&](auto vg_tag) {
+      constexpr int VG = decltype(vg_tag)::value;
+      constexpr int DB = VG / 8, QB = (VG / 4) % 2, R = 4 * (VG % 4);
+      *mptr(vg_tag) = make_float4(o[DB][QB][R], o[DB][QB][R + 1], o[DB][QB][R + 2], o[DB][QB][R + 3]);
+    });
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) g_lm[rg][qb][lane] = make_float2(l[qb], mc[qb]);
-    }
-    __syncthreads();
-  };
-
+    for (int qb = 0; qb < 2; ++qb) g_lm[rg][qb][lane] = make_float2(l[qb], mc[qb]);
+  }
   if constexpr (FIXED) {
     if (tid == 0) g_redo = 0;
   }
-  run();
-  handoff();
+  __syncthreads();
   if constexpr (FIXED) {
     // Range check of the fixed pivot.  Under pivot 0 every weight of a row
     // is at most its sum l, so l_A, l_B < 2^64 bounds every weight, partial
@@ -699,7 +697,7 @@ __device__ __forceinline__ bool pair_pass(const FwdArgs& a) {
     // weight that fell into the subnormal range is below 2^-70 of it and
     // changes no result.  A row with an allowed key that fails either bound
     // -- logits far above 64 or far below -32 in log2 units -- sends the
-    // whole workgroup through the second pass.  Rows without an allowed key
+    // whole workgroup to the moving-pivot pass.  Rows without an allowed key
     // (padded, kv_len = 0, an empty window) are zeros either way.
     if (par == 0) {
       bool bad = false;
@@ -721,11 +719,7 @@ __device__ __forceinline__ bool pair_pass(const FwdArgs& a) {
   if (par == 1) return true;
 
   // O = (2^(mA - M) O_A + 2^(mB - M) O_B) / (2^(mA - M) l_A + 2^(mB - M) l_B)
-  // with M the larger pivot of the waves that summed a weight (l > 0); 2^0 =
-  // 1 exactly.  A wave that saw no key of the row keeps its starting pivot 0,
-  // which says nothing about the row's scale: it takes factor 0 and no part
-  // in M (otherwise a partner pivot far below 0, moved down at its first
-  // key, would give 2^(mA - 0) = 0 and lose the row).
+  // with M = max(mA, mB); 2^0 = 1 exactly, and both pivots are finite.
   float fa[2], fb[2], inv[2];
   bool live[2];
 #pragma unroll
@@ -765,44 +759,38 @@ __device__ __forceinline__ bool pair_pass(const FwdArgs& a) {
   return true;
 }
 
-// Every lane holds the same value: take lane 0's, so that the compiler
-// treats it (and everything derived from it) as uniform.
-__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
-__device__ __forceinline__ float uni(float v) { return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v))); }
-template <typename T>
-__device__ __forceinline__ T* uni(T* p) {
-  const uint64_t v = (uint64_t)(uintptr_t)p;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  return (T*)(uintptr_t)(((uint64_t)hi << 32) | lo);
-}
+// Marks a workgroup whose rows failed the fixed-pivot range check: the
+// first pass writes it into the first element of the workgroup's first
+// output row, in place of its results, and the second kernel finds it there.
+// (A result that happens to carry the same bits -- a NaN -- only makes the
+// second kernel recompute that workgroup, to the same result.)
+constexpr uint16_t kRedoMark = 0xFFFFu;
 
-// The second pass.  The call's arguments come in by value, in per-lane
-// registers or memory, so each field is made uniform again first (the
-// buffer descriptors and every address derived from them must be scalar).
-template <int MODE>
-__device__ __attribute__((noinline)) void pair_pass_moving(FwdArgs v) {
-  FwdArgs a;
-  a.Q = uni(v.Q);
-  a.K = uni(v.K);
-  a.V = uni(v.V);
-  a.O = uni(v.O);
-  a.q_lens = uni(v.q_lens);
-  a.kv_lens = uni(v.kv_lens);
-  a.B = uni(v.B);
-  a.H = uni(v.H);
-  a.n_q = uni(v.n_q);
-  a.n_k = uni(v.n_k);
-  a.scale = uni(v.scale);
-  a.causal = uni((int)v.causal) != 0;
-  a.lse = uni(v.lse);
-  a.radius = uni(v.radius);
-  pair_pass<MODE, false>(a);
-}
-
+// First pass: the fixed pivot.  No fallback code lives in this kernel (a
+// second copy of the pipeline, inlined or called, costs registers or
+// per-lane scratch memory, and a kernel that needs scratch is dispatched
+// more slowly).
 template <int MODE>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_pair_kernel(FwdArgs a) {
-  if (!pair_pass<MODE, true>(a)) pair_pass_moving<MODE>(a);
+  if (!pair_pass<MODE, true>(a) && threadIdx.x == 0) {
+    int bh, qt;
+    wg_tile<MODE>(a, blockIdx.x, bh, qt);
+    uint16_t* O = static_cast<uint16_t*>(a.O) + ((size_t)bh * a.n_q + (size_t)qt * kBM) * kHeadDim;
+    *O = kRedoMark;
+  }
+}
+
+// Second kernel, launched right after the first on the same stream with the
+// same grid: a workgroup whose mark is set runs the moving-pivot pass; all
+// others exit at once.
+template <int MODE>
+__global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_pair_redo_kernel(FwdArgs a) {
+  int bh, qt;
+  wg_tile<MODE>(a, blockIdx.x, bh, qt);
+  const uint16_t* O = static_cast<const uint16_t*>(a.O) + ((size_t)bh * a.n_q + (size_t)qt * kBM) * kHeadDim;
+  if (__builtin_amdgcn_readfirstlane(*O) != kRedoMark) return;
+  __syncthreads();  // every wave has read the mark before any output is rewritten
+  pair_pass<MODE, false>(a);
 }
 
 }  // namespace
@@ -816,7 +804,13 @@ hipError_t launch_fwd_bf16_pair(const FwdArgs& a, hipStream_t s) {
   const void* fn = mode == kModeBand     ? reinterpret_cast<const void*>(&attn_fwd_bf16_pair_kernel<kModeBand>)
                    : mode == kModeCausal ? reinterpret_cast<const void*>(&attn_fwd_bf16_pair_kernel<kModeCausal>)
                                          : reinterpret_cast<const void*>(&attn_fwd_bf16_pair_kernel<kModeNone>);
-  return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(kThreads), kargs, 0, s);
+  const void* redo = mode == kModeBand ? reinterpret_cast<const void*>(&attn_fwd_bf16_pair_redo_kernel<kModeBand>)
+                     : mode == kModeCausal
+                         ? reinterpret_cast<const void*>(&attn_fwd_bf16_pair_redo_kernel<kModeCausal>)
+                         : reinterpret_cast<const void*>(&attn_fwd_bf16_pair_redo_kernel<kModeNone>);
+  hipError_t e = hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(kThreads), kargs, 0, s);
+  if (e != hipSuccess) return e;
+  return hipLaunchKernel(redo, dim3((unsigned)blocks), dim3(kThreads), kargs, 0, s);
 }
 
 }  // namespace headattn
