@@ -48,30 +48,14 @@
 // zero rows with L = +inf, so they contribute nothing.
 #include <type_traits>
 
-#include "common.h"
+#include "kernel_util.h"
 
 namespace headattn {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
-
 constexpr int kThreads = 256;
 constexpr int kTile = 64;   // rows per streamed tile
 constexpr int kSlots = 3;   // LDS ring: the tile in use and two in flight
-constexpr uint32_t kRowBytes = kHeadDim * 2;
-constexpr uint32_t kBufferWord3 = 0x00020000u;  // raw buffer, 32-bit elements (gfx9 family)
-constexpr uint32_t kOutOfRange = 0x80000000u;   // an offset the range check always rejects
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  f32x2 v = {lo, hi};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-}
 
 // A streamed 64-row tile in LDS: row-major, 16-byte chunk c of row r at
 // position c ^ swz(r), swz(r) = 2 (r % 4) ^ (r / 4) % 4.  Row reads (16

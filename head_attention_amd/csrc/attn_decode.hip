@@ -24,14 +24,10 @@
 // sums under different pivots combine after rescaling to a common pivot.
 #include <mutex>
 
-#include "common.h"
+#include "kernel_util.h"
 
 namespace headattn {
 namespace {
-
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 template <typename T>
 struct Elem;

@@ -44,25 +44,15 @@
 // one barrier per tile separates reuse.
 #include <type_traits>
 
-#include "common.h"
+#include "kernel_util.h"
 
 namespace headattn {
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
 constexpr int kBM = 32 * kWaves;  // query rows per workgroup
 constexpr int kBN = 64;           // keys per tile
 constexpr int kThreads = 64 * kWaves;
-constexpr uint32_t kRowBytes = kHeadDim * 2;  // one bf16 row of K or V
-constexpr uint32_t kBufferWord3 = 0x00020000u;  // raw buffer, 32-bit elements (gfx9 family)
-constexpr float kPivotHigh = 0x1p64f;  // a tile sum above this moves the pivot up
-constexpr float kPivotLow = 0x1p-64f;  // a first-tile row sum below this moves it down
 
 // One LDS tile: 64 rows x 128 B as 8 chunks of 16 B.  K tiles are stored
 // [key][chunk] (positions k_swz of the shared header), V^T tiles [d][chunk
@@ -84,26 +74,6 @@ __device__ __forceinline__ int vt_swz(int d) { return (d ^ (d >> 3)) & 7; }
 // 4 blk + 2 j + hh of the row: first half keys 16j+4hh.., second 16j+8+4hh..
 __device__ __forceinline__ int vt_chunk_of_group(int g) { return 2 * (g >> 2) + (g & 1); }
 __device__ __forceinline__ int vt_half_of_group(int g) { return (g >> 1) & 1; }
-
-// Lanes l and l ^ 32 hold the same query row: combine the two half-waves.
-__device__ __forceinline__ float half_swap_max(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float half_swap_sum(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-__device__ __forceinline__ bool half_swap_or(bool x) {
-  auto r = __builtin_amdgcn_permlane32_swap((uint32_t)x, (uint32_t)x, false, false);
-  return (r[0] | r[1]) != 0;
-}
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  f32x2 v = {lo, hi};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-}
 
 __device__ __forceinline__ uint4 as_uint4(u32x4 v) { return make_uint4(v[0], v[1], v[2], v[3]); }
 

@@ -56,45 +56,16 @@
 // XOR-swizzled by row; V stays row-major (chunks swizzled by row % 4) and is
 // read transposed with ds_read_b64_tr_b16, which hands each lane four
 // consecutive keys of one d -- the A-operand order of O^T += V^T P^T.
-#include <utility>
-
-#include "common.h"
+#include "kernel_util.h"
 
 namespace headattn {
 namespace {
-
-template <typename F, int... I>
-__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
-  (f(std::integral_constant<int, I>()), ...);
-}
-// f(integral_constant<int, 0>), ..., f(integral_constant<int, N - 1>)
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  static_for_impl(f, std::make_integer_sequence<int, N>());
-}
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef short s16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 
 constexpr int kThreads = 512;
 constexpr int kWaveRows = 64;
 constexpr int kBM = 4 * kWaveRows;  // query rows per workgroup
 constexpr int kBN = 64;             // keys per tile
-constexpr uint32_t kRowBytes = kHeadDim * 2;
 constexpr uint32_t kTileBytes = kBN * kRowBytes;
-constexpr uint32_t kBufferWord3 = 0x00020000u;  // raw buffer, 32-bit elements (gfx9 family)
-// Pivot moves, in exponent (log2) units of a tile's largest weight under the
-// pivot in force: up when it would pass 2^64, down (only while a row has
-// summed nothing) when it would fall below 2^-64.
-constexpr float kPivotUp = 64.f;
-constexpr float kPivotDown = -64.f;
 
 // Ring of 8 slots, each the K and the V tile of one 64-key tile (8 KB each:
 // 64 rows x 8 chunks of 16 B).  Every tile is its own object, so the
@@ -127,18 +98,6 @@ template <int S>
 __device__ __forceinline__ uint4* mslot() {
   return S < 4 ? (S == 0 ? g_k0 : S == 1 ? g_k1 : S == 2 ? g_k2 : g_k3)
                : (S == 4 ? g_v0 : S == 5 ? g_v1 : S == 6 ? g_v2 : g_v3);
-}
-
-// Lanes l and l ^ 32 hold the same query row: combine the two half-waves.
-__device__ __forceinline__ float half_swap_max(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  const uint32_t a = r[0], b = r[1];
-  return fmaxf(__uint_as_float(a), __uint_as_float(b));
-}
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  f32x2 v = {lo, hi};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 // Weights 2^x of one query block of a tile from its exponents x (key blocks

@@ -27,51 +27,20 @@
 // keys of one d -- the A-operand order of O^T += V^T P^T, with the keys in
 // the order the S accumulator registers hold them, so the weights feed the
 // B operand straight from registers.
-#include "common.h"
+#include "kernel_util.h"
 
 namespace headattn {
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBM = 32 * kWaves;  // query rows per workgroup
 constexpr int kBN = 64;           // keys per tile
 constexpr int kMaxTiles = kShortMaxKeys / kBN;
-constexpr uint32_t kRowBytes = kHeadDim * 2;
 constexpr uint32_t kTileChunks = kBN * 8;  // 16-byte chunks per tile
-constexpr uint32_t kBufferWord3 = 0x00020000u;  // raw buffer, 32-bit elements (gfx9 family)
-constexpr float kPivotHigh = 0x1p64f;  // a tile sum above this moves the pivot up
-constexpr float kPivotLow = 0x1p-64f;  // a first-tile row sum below this moves it down
 
 __shared__ uint4 s_k[kMaxTiles * kTileChunks];
 __shared__ uint4 s_v[kMaxTiles * kTileChunks];
-
-// Lanes l and l ^ 32 hold the same query row: combine the two half-waves.
-__device__ __forceinline__ float half_swap_max(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float half_swap_sum(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-__device__ __forceinline__ bool half_swap_or(bool x) {
-  auto r = __builtin_amdgcn_permlane32_swap((uint32_t)x, (uint32_t)x, false, false);
-  return (r[0] | r[1]) != 0;
-}
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  f32x2 v = {lo, hi};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-}
 
 // Weights of one tile under pivot term mc = m c: exp2(s c - mc), packed to
 // bf16 pairs in the order P.V consumes them (keys 0..31 from s0, 32..63 from

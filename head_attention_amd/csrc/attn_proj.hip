@@ -28,24 +28,16 @@
 // [n, 64] slab: a per-row offset, no gather of single elements.
 #include <type_traits>
 
-#include "common.h"
+#include "kernel_util.h"
 
 namespace headattn {
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr int kThreads = 256;
 constexpr int kBN = 128;  // output features per workgroup
 constexpr int kBK = 32;   // k per step
 constexpr int kSlots = 3;
 constexpr uint32_t kStepBytes = kBK * 2;        // bytes of one row in one step
-constexpr uint32_t kBufferWord3 = 0x00020000u;  // raw buffer, 32-bit elements (gfx9 family)
-constexpr uint32_t kOutOfRange = 0x80000000u;   // an offset the range check always rejects
 
 // Ring slots: the W tile (128 rows) and the A tile (up to 256 rows) of one
 // step, rows of 64 B (4 chunks of 16 B; chunk c of row r at position
@@ -64,11 +56,6 @@ __device__ __forceinline__ uint4* wslot() {
 template <int S>
 __device__ __forceinline__ uint4* aslot() {
   return S == 0 ? g_a0 : S == 1 ? g_a1 : g_a2;
-}
-
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  f32x2 v = {lo, hi};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 // Wait until at most N of this wave's buffer loads are outstanding and its
