@@ -545,10 +545,12 @@ __device__ __forceinline__ bool pair_pass(const FwdArgs& a) {
       if constexpr (FIXED) softmax_fixed(t);
       else softmax(t);
     } else {
+      // Zeros written from inline assembly: a plain 0 here is a constant
+      // the compiler materialises before the branch, in every phase.
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) pk[qb][i] = 0u;
+        for (int i = 0; i < 16; ++i) asm volatile("v_mov_b32 %0, 0" : "=v"(pk[qb][i]));
     }
   };
   using J0 = std::integral_constant<int, 0>;
