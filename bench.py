@@ -419,7 +419,10 @@ LEG_GRIDS = {("attn_fwd_bf16_short_kernel<none>", 65536): "encoder_base",
              ("attn_fwd_bf16_pair_redo_kernel<causal>", 262144): "long_causal (redo pass, exits)",
              ("attn_fwd_bf16_pair_redo_kernel<band>", 262144): "long_restricted (redo pass, exits)",
              ("decode_partial_kernel", 4194304): "kv_decode",
-             ("decode_merge_kernel", 65536): "kv_decode"}
+             ("decode_merge_kernel", 65536): "kv_decode",
+             ("attn_fwd_bf16_short_kernel<none>", 256): "launch floor (1-row forward)",
+             ("at::cuda::(anonymous namespace)::spin_kernel(long)", 1): "launch floor (empty kernel)",
+             ("copyBuffer", 512): "bench set-up copies"}
 
 
 def summarize_trace(path: str) -> str:
@@ -440,9 +443,11 @@ def summarize_trace(path: str) -> str:
 
 
 def summarize_counters(fetch_csv: str, write_csv: str, copy_mib: int, out_json: str | None):
-    """HBM traffic per launch from FETCH_SIZE / WRITE_SIZE runs (KiB per
-    dispatch), each scaled by what the same counter reads for the plain copy
-    of copy_mib MiB that bench.py --copy-probe-mib runs."""
+    """Bytes per launch that miss L2 (FETCH_SIZE: reads served by the MALL or
+    HBM; WRITE_SIZE: writes leaving L2), from counter runs in KiB per
+    dispatch, each scaled by what the same counter reads for the plain copy
+    of copy_mib MiB that bench.py --copy-probe-mib runs.  The MALL can serve
+    some of these reads, so they bound HBM traffic from above."""
     import csv
     import collections
 
@@ -461,7 +466,7 @@ def summarize_counters(fetch_csv: str, write_csv: str, copy_mib: int, out_json: 
     lines = [f"copy probe ({copy_mib} MiB each way, {copy_key[0]} grid {copy_key[1]}): "
              f"FETCH_SIZE {fetch[copy_key]:.1f} KiB -> scale {f_fetch:.4f}; "
              f"WRITE_SIZE {write[copy_key]:.1f} KiB -> scale {f_write:.4f}", "",
-             "| kernel | grid | leg | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM read MB | HBM write MB |",
+             "| kernel | grid | leg | FETCH_SIZE KiB | WRITE_SIZE KiB | read past L2 MB | written past L2 MB |",
              "|---|---|---|---|---|---|---|"]
     res = {}
     for k in sorted(fetch):
@@ -483,18 +488,26 @@ def summarize_counters(fetch_csv: str, write_csv: str, copy_mib: int, out_json: 
     return "\n".join(lines)
 
 
-def summarize_pmc(csvs, trace_csv=None, n_simd: int = 1024, n_se: int = 32) -> str:
+def summarize_pmc(csvs, trace_csv=None, n_simd: int = 1024, n_xcd: int = 8) -> str:
     """Per-kernel MFMA and VALU figures from rocprofv3 --pmc runs of the bench
-    (one CSV per pass; counters averaged over a kernel's launches).  Kernel
-    durations come from a kernel-trace run of the same command when given
-    (counter runs serialise dispatches), else from the counter CSV.
+    (one CSV per pass; counters averaged over a kernel's launches).
 
-    mfma busy: SQ_VALU_MFMA_BUSY_CYCLES (summed over the SIMDs) over n_simd
-      SIMDs x duration x clock, at the 2.4 GHz peak clock and at the clock
-      the shader engines held (SQ_BUSY_CYCLES per engine over the duration, a
-      lower bound: an engine counts only while it holds waves).
-    mfma TFLOP/s: bf16 MFMA flops executed (SQ_INSTS_VALU_MFMA_MOPS_BF16 x
-      512, padding and row-sum products included) over the duration.
+    us: average duration from a kernel-trace run of the same command when
+      given (counter runs serialise dispatches), else from the counter runs.
+    clock: GRBM_GUI_ACTIVE (busy GPU clocks, summed over the n_xcd XCDs) per
+      XCD, less what it reads for the empty kernel the bench launches
+      (torch's spin kernel: the counter window's own overhead, about 20k
+      clocks), over the duration of the same counter-run dispatches.  Cycle
+      fractions below are per SIMD over those cycles (n_simd SIMDs).
+    mfma busy: SQ_VALU_MFMA_BUSY_CYCLES; also at the 2.4 GHz peak clock over
+      the trace duration, i.e. the fraction of the bf16 MFMA peak the matrix
+      cores were busy for.
+    mfma TFLOP/s executed: SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 (padding and
+      row-sum products included) over the trace duration.
+    valu busy: SQ_ACTIVE_INST_VALU (quad-cycles a wave works on VALU
+      instructions, summed over waves) x 4.
+    co-issue: SQ_VALU_MFMA_COEXEC_CYCLES (MFMA busy while a VALU
+      instruction issued).  neither ~ 1 - mfma - valu + co-issue.
     per wave: instructions issued per wave (SQ_INSTS_* over SQ_WAVES)."""
     import csv
     import collections
@@ -513,25 +526,38 @@ def summarize_pmc(csvs, trace_csv=None, n_simd: int = 1024, n_se: int = 32) -> s
             g[(_short_kernel(r["Kernel_Name"]), grid)].append(
                 (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
         tdur = {k: sum(v) / len(v) for k, v in g.items()}
-    lines = ["| kernel | grid | leg | us | held clock GHz (>=) | mfma busy @2.4 GHz | mfma busy @held | "
-             "mfma TFLOP/s executed | VALU/wave | TRANS/wave | MFMA/wave | VALU co-issued with MFMA |",
-             "|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    nan = float("nan")
+    empty = [k for k in acc if k[0].startswith("at::cuda::") and "GRBM_GUI_ACTIVE" in acc[k]]
+    offset = (sum(acc[empty[0]]["GRBM_GUI_ACTIVE"]) / len(acc[empty[0]]["GRBM_GUI_ACTIVE"]) / n_xcd
+              if empty else 0.0)
+    lines = [f"clock offset (empty kernel, per XCD): {offset:.0f} GRBM clocks", "",
+             "| kernel | grid | leg | us | clock GHz | mfma busy | mfma busy @2.4 GHz | mfma TFLOP/s executed | "
+             "valu busy | co-issue | neither | VALU/wave | TRANS/wave | MFMA/wave |",
+             "|---|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
     for k in sorted(acc, key=lambda k: -sum(dur[k].values())):
         c = {n: sum(v) / len(v) for n, v in acc[k].items()}
-        us = tdur.get(k, sum(dur[k].values()) / len(dur[k]))
-        if "SQ_VALU_MFMA_BUSY_CYCLES" not in c or us <= 0:
+        pmc_us = sum(dur[k].values()) / len(dur[k])
+        us = tdur.get(k, pmc_us)
+        if "SQ_VALU_MFMA_BUSY_CYCLES" not in c or us <= 0 or pmc_us <= 0:
             continue
-        busy = c["SQ_VALU_MFMA_BUSY_CYCLES"]
-        clk = c.get("SQ_BUSY_CYCLES", 0.0) / n_se / (us * 1e3) if "SQ_BUSY_CYCLES" in c else float("nan")
-        waves = c.get("SQ_WAVES", float("nan"))
-        per_wave = lambda n: c[n] / waves if n in c and waves == waves and waves > 0 else float("nan")
-        co = c.get("SQ_VALU_MFMA_COEXEC_CYCLES", float("nan")) / busy if busy > 0 else float("nan")
+        if k[0].startswith("at::cuda::") or k[0] in ("copyBuffer", "elementwise"):
+            continue
+        if pmc_us < 5.0:  # the window overhead swamps the clock count of a launch this short
+            continue
+        cyc = c.get("GRBM_GUI_ACTIVE", nan) / n_xcd - offset  # clocks per XCD in the dispatch
+        clk = cyc / (pmc_us * 1e3)
+        per_simd = lambda n: c.get(n, nan) / n_simd / cyc
+        mfma, co = per_simd("SQ_VALU_MFMA_BUSY_CYCLES"), per_simd("SQ_VALU_MFMA_COEXEC_CYCLES")
+        valu = 4 * per_simd("SQ_ACTIVE_INST_VALU")
+        waves = c.get("SQ_WAVES", nan)
+        per_wave = lambda n: c[n] / waves if n in c and waves == waves and waves > 0 else nan
         lines.append(
-            f"| {k[0]} | {k[1]} | {LEG_GRIDS.get(k, '')} | {us:.2f} | {clk:.2f} | "
-            f"{busy / (n_simd * us * 1e3 * 2.4):.3f} | {busy / (n_simd * us * 1e3 * clk):.3f} | "
+            f"| {k[0]} | {k[1]} | {LEG_GRIDS.get(k, '')} | {us:.2f} | {clk:.2f} | {mfma:.3f} | "
+            f"{c['SQ_VALU_MFMA_BUSY_CYCLES'] / (n_simd * us * 1e3 * 2.4):.3f} | "
             f"{c.get('SQ_INSTS_VALU_MFMA_MOPS_BF16', 0) * 512 / (us * 1e-6) / 1e12:.1f} | "
+            f"{valu:.3f} | {co:.3f} | {1 - mfma - valu + co:.3f} | "
             f"{per_wave('SQ_INSTS_VALU'):.0f} | {per_wave('SQ_INSTS_VALU_TRANS_F32'):.0f} | "
-            f"{per_wave('SQ_INSTS_MFMA'):.0f} | {co:.2f} |")
+            f"{per_wave('SQ_INSTS_MFMA'):.0f} |")
     return "\n".join(lines)
 
 
