@@ -27,8 +27,9 @@
 // Per tile a wave does two phases: an MFMA phase (O += P V of its previous
 // tile, then S = K Q^T of this tile: 32 matrix instructions) and a vector
 // phase (mask, exp2 and bf16 pack of this tile: ~165 VALU instructions in
-// the first kernel; the moving pivot adds the row max and its checks).  The pair runs one phase apart and a workgroup barrier
-// closes every phase, so while one wave of a SIMD issues matrix instructions
+// the first kernel; the moving pivot adds the row max and its checks).  The
+// pair runs one phase apart and a workgroup barrier closes every phase, so
+// while one wave of a SIMD issues matrix instructions
 // the other issues the exponentials: the two kinds of work overlap across the
 // two waves instead of alternating inside one.  (Measured on MI355X: MFMA
 // and fma/exp/cvt work from two waves of one SIMD overlap, while v_dot2
@@ -52,7 +53,19 @@
 // the descriptor's range check, so padded K/V memory (even NaN) is never
 // read.  Tiles sit in an 8-slot ring, K five phases and V seven phases ahead
 // of use; a phase ends with a wait for this wave's fills of four phases ago
-// and a barrier.  K rows keep their 16-byte chunks
+// and a barrier.
+//
+// Restricted self-attention (a band of keys around each row) runs its own
+// schedule: the four row groups of a workgroup need windows that start one
+// tile apart, so row group g walks only its own window, d <= g tiles into
+// the workgroup's range: at phase p the row groups work on tiles p .. p + 3
+// of the ring at once.  A workgroup then runs as many phases as one window
+// has tiles (9 or 10 for 64 rows and a 256-key radius) instead of as many as
+// its whole range (12 or 13), and no row group idles through tiles outside
+// its window.  Reading 3 tiles ahead of the ring position, a phase ends with
+// a wait for all but this phase's fills.
+//
+// K rows keep their 16-byte chunks
 // XOR-swizzled by row; V stays row-major (chunks swizzled by row % 4) and is
 // read transposed with ds_read_b64_tr_b16, which hands each lane four
 // consecutive keys of one d -- the A-operand order of O^T += V^T P^T.
@@ -68,13 +81,14 @@ constexpr int kBN = 64;             // keys per tile
 constexpr uint32_t kTileBytes = kBN * kRowBytes;
 
 // Ring of 8 slots, each the K and the V tile of one 64-key tile (8 KB each:
-// 64 rows x 8 chunks of 16 B).  Every tile is its own object, so the
-// compiler tracks the asynchronous LDS writes of the fills per tile (a slot
-// as one object holding K and V made it wait for every fill in flight
-// before each V read).
-__shared__ uint4 g_k0[512], g_k1[512], g_k2[512], g_k3[512], g_k4[512], g_k5[512], g_k6[512], g_k7[512];
-__shared__ uint4 g_v0[512], g_v1[512], g_v2[512], g_v3[512], g_v4[512], g_v5[512], g_v6[512], g_v7[512];
+// 64 rows x 8 chunks of 16 B): K of slot s at g_ring[s], its V at
+// g_ring[8 + s].  Under the band schedule each row group reads its own
+// slot, chosen at run time.  The fills are issued from inline assembly
+// (lds_fill16_at), which the compiler does not track (with the builtin it
+// would wait for every fill in flight before any read of the array): the
+// phase loop's explicit vmcnt waits and barriers order them.
 constexpr int kSlots = 8;
+__shared__ uint4 g_ring[2 * kSlots][512];
 // Fills run this many phases ahead: the fill at phase p is tile p + 5,
 // into the slot of tile p - 3, whose V was last read at phase p - 1.
 constexpr int kAhead = 5;
@@ -83,21 +97,17 @@ __shared__ float2 g_lm[4][2][64];
 // Set when a row failed the fixed-pivot range check.
 __shared__ int g_redo;
 
-template <int S>
-__device__ __forceinline__ uint4* kslot() {
-  return S == 0 ? g_k0 : S == 1 ? g_k1 : S == 2 ? g_k2 : S == 3 ? g_k3
-       : S == 4 ? g_k4 : S == 5 ? g_k5 : S == 6 ? g_k6 : g_k7;
-}
-template <int S>
-__device__ __forceinline__ uint4* vslot() {
-  return S == 0 ? g_v0 : S == 1 ? g_v1 : S == 2 ? g_v2 : S == 3 ? g_v3
-       : S == 4 ? g_v4 : S == 5 ? g_v5 : S == 6 ? g_v6 : g_v7;
+typedef __attribute__((address_space(3))) uint4 lds_uint4;
+typedef __attribute__((address_space(3))) char lds_char;
+// LDS byte address of ring row r (K of slot r, or V of slot r - 8), kept
+// as an integer so that a slot chosen at run time costs one add.
+__device__ __forceinline__ uint32_t ring_addr(int r) {
+  return (uint32_t)(uintptr_t)(lds_void_t*)&g_ring[0][0] + (uint32_t)r * (512u * 16u);
 }
 // Tiles K0 .. K3 and V0 .. V3 as the 8 KB parts of the 64 KB merge area.
 template <int S>
 __device__ __forceinline__ uint4* mslot() {
-  return S < 4 ? (S == 0 ? g_k0 : S == 1 ? g_k1 : S == 2 ? g_k2 : g_k3)
-               : (S == 4 ? g_v0 : S == 5 ? g_v1 : S == 6 ? g_v2 : g_v3);
+  return S < 4 ? g_ring[S] : g_ring[kSlots + S - 4];
 }
 
 // Weights 2^x of one query block of a tile from its exponents x (key blocks
@@ -208,6 +218,23 @@ __device__ __forceinline__ bool pair_pass(const FwdArgs& a) {
   if (qw0 >= q_len) wave_end = 0;
   const int wave_tiles = max(0, (wave_end + kBN - 1) / kBN - t0);
   const int wave_first = BAND ? max(0, qw0 - wl) / kBN - t0 : 0;
+  // Band schedule: row group rg walks only its own window, which starts
+  // d = wave_first tiles into the workgroup's range (0 <= d <= rg), so at
+  // phase p the four row groups work on ring tiles p .. p + 3 at once and
+  // the workgroup runs as many phases as its longest window (9 or 10 tiles
+  // for 64 rows and a 256-key radius) rather than its whole range (12 or
+  // 13).  Otherwise d = 0 and every row group walks the whole range.
+  const int d = BAND ? wave_first : 0;
+  int n_run = n_tiles;
+  if (BAND) {
+    n_run = 0;
+    for (int g = 0; g < 4; ++g) {
+      const int qg = q0 + kWaveRows * g;
+      const int eg = qg >= q_len ? 0 : min(end, qg + kWaveRows + wr);
+      const int first = max(0, qg - wl) / kBN - t0;
+      n_run = max(n_run, (eg + kBN - 1) / kBN - t0 - first);
+    }
+  }
 
   const int k_base = t0 * kBN;  // first key of relative tile 0
   K += (size_t)k_base * kHeadDim;
@@ -229,13 +256,11 @@ __device__ __forceinline__ bool pair_pass(const FwdArgs& a) {
   const uint32_t voff = (uint32_t)frow * kRowBytes + 16u * (uint32_t)(fpos ^ (2 * (frow & 3)));
   auto fill_k = [&](auto slot_tag, int t) __attribute__((always_inline)) {
     constexpr int S = decltype(slot_tag)::value;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(kslot<S>() + 64 * wave), 16,
-                                             (uint32_t)t * kTileBytes + koff, 0, 0, 0);
+    lds_fill16_at(rk, ring_addr(S) + 1024u * wave, (uint32_t)t * kTileBytes + koff);
   };
   auto fill_v = [&](auto slot_tag, int t) __attribute__((always_inline)) {
     constexpr int S = decltype(slot_tag)::value;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(vslot<S>() + 64 * wave), 16,
-                                             (uint32_t)t * kTileBytes + voff, 0, 0, 0);
+    lds_fill16_at(rv, ring_addr(kSlots + S) + 1024u * wave, (uint32_t)t * kTileBytes + voff);
   };
 
   // ---- Q fragments: B operand of S^T = K Q^T for query block qb and d-step
@@ -314,7 +339,8 @@ __device__ __forceinline__ bool pair_pass(const FwdArgs& a) {
   auto load_v_step = [&](auto slot_tag, auto j_tag, bf16x8 (&va)[2][4]) __attribute__((always_inline)) {
     constexpr int S = decltype(slot_tag)::value;
     constexpr int j = decltype(j_tag)::value;
-    const char* vt = reinterpret_cast<const char*>(vslot<S>());
+    // The slot of tile p + d (d = 0 outside the band schedule).
+    const lds_char* vt = (const lds_char*)(uintptr_t)ring_addr(kSlots + ((S + d) & (kSlots - 1)));
     const int g = lane >> 4;
     const int i = lane & 15;
 #pragma unroll
@@ -325,7 +351,7 @@ __device__ __forceinline__ bool pair_pass(const FwdArgs& a) {
         const int kr = 16 * j + 8 * x + 4 * (g >> 1) + (i >> 2);
         const int h = 8 * db + 4 * (g & 1) + (i & 3);
         const int byte = kr * (int)kRowBytes + 16 * ((h >> 1) ^ (2 * (kr & 3))) + 8 * (h & 1);
-        part[x] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(vt + byte));
+        part[x] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(lds_char*)(vt + byte));
       }
       va[db][j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7));
     }
@@ -335,7 +361,7 @@ __device__ __forceinline__ bool pair_pass(const FwdArgs& a) {
   auto load_k_step = [&](auto slot_tag, auto s_tag, bf16x8 (&ka)[2][4]) __attribute__((always_inline)) {
     constexpr int S = decltype(slot_tag)::value;
     constexpr int s = decltype(s_tag)::value;
-    const uint4* kt = kslot<S>();
+    const lds_uint4* kt = (const lds_uint4*)(uintptr_t)ring_addr((S + d) & (kSlots - 1));
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int row = 32 * kb + ln;
@@ -458,7 +484,10 @@ __device__ __forceinline__ bool pair_pass(const FwdArgs& a) {
   };
   auto sync = [&]() __attribute__((always_inline)) {
     // vmcnt(8): the fills of this and the three previous phases may fly.
-    __builtin_amdgcn_s_waitcnt(0x0F70 | 8);
+    // Under the band schedule a row group reads up to 3 tiles ahead of the
+    // ring position, so only this phase's fills may: vmcnt(2).
+    if constexpr (BAND) __builtin_amdgcn_s_waitcnt(0x0F70 | 2);
+    else __builtin_amdgcn_s_waitcnt(0x0F70 | 8);
     barrier_lds();
   };
   // MFMA phase at phase p (slot J = p % 8): P.V of tile p - 2, then S of
@@ -577,41 +606,44 @@ __device__ __forceinline__ bool pair_pass(const FwdArgs& a) {
     // The first MFMA phases of the two waves of a pair (p = 0, 1) read the
     // V tiles of slots 6 and 7 with zero weights: zero them, since 0 * NaN
     // of stale LDS contents would not be zero.
-    g_v6[tid] = make_uint4(0, 0, 0, 0);
-    g_v7[tid] = make_uint4(0, 0, 0, 0);
-    __builtin_amdgcn_s_waitcnt(0x0070 | 8);  // vmcnt(8), lgkmcnt(0): tile 0 has landed
+    g_ring[kSlots + 6][tid] = make_uint4(0, 0, 0, 0);
+    g_ring[kSlots + 7][tid] = make_uint4(0, 0, 0, 0);
+    // vmcnt(8) (tile 0 has landed), or vmcnt(2) under the band schedule
+    // (tiles 0 .. 3: a row group may start up to 3 tiles in); lgkmcnt(0).
+    if constexpr (BAND) __builtin_amdgcn_s_waitcnt(0x0070 | 2);
+    else __builtin_amdgcn_s_waitcnt(0x0070 | 8);
     barrier_lds();
     // Even-tile waves run MFMA phases at even p, odd-tile waves at odd p;
     // both run the same number of phases (and barriers).
-    const int n_phases = n_tiles + 2;
+    const int n_phases = n_run + 2;
     if (par == 0) {
 #pragma nounroll
       for (int p = 0; p < n_phases; p += 8) {
         fills(J0(), p);     mphase(J0()); sync();
-        fills(J1(), p + 1); vphase(p);              sync();
+        fills(J1(), p + 1); vphase(p + d);              sync();
         if (p + 2 >= n_phases) break;
         fills(J2(), p + 2); mphase(J2()); sync();
-        fills(J3(), p + 3); vphase(p + 2);          sync();
+        fills(J3(), p + 3); vphase(p + 2 + d);          sync();
         if (p + 4 >= n_phases) break;
         fills(J4(), p + 4); mphase(J4()); sync();
-        fills(J5(), p + 5); vphase(p + 4);          sync();
+        fills(J5(), p + 5); vphase(p + 4 + d);          sync();
         if (p + 6 >= n_phases) break;
         fills(J6(), p + 6); mphase(J6()); sync();
-        fills(J7(), p + 7); vphase(p + 6);          sync();
+        fills(J7(), p + 7); vphase(p + 6 + d);          sync();
       }
     } else {
 #pragma nounroll
       for (int p = 0; p < n_phases; p += 8) {
-        fills(J0(), p);     vphase(p - 1);              sync();
+        fills(J0(), p);     vphase(p - 1 + d);              sync();
         fills(J1(), p + 1); mphase(J1()); sync();
         if (p + 2 >= n_phases) break;
-        fills(J2(), p + 2); vphase(p + 1);              sync();
+        fills(J2(), p + 2); vphase(p + 1 + d);              sync();
         fills(J3(), p + 3); mphase(J3()); sync();
         if (p + 4 >= n_phases) break;
-        fills(J4(), p + 4); vphase(p + 3);              sync();
+        fills(J4(), p + 4); vphase(p + 3 + d);              sync();
         fills(J5(), p + 5); mphase(J5()); sync();
         if (p + 6 >= n_phases) break;
-        fills(J6(), p + 6); vphase(p + 5);              sync();
+        fills(J6(), p + 6); vphase(p + 5 + d);              sync();
         fills(J7(), p + 7); mphase(J7()); sync();
       }
     }
@@ -683,6 +715,10 @@ __device__ __forceinline__ bool pair_pass(const FwdArgs& a) {
   // with M = max(mA, mB); 2^0 = 1 exactly, and both pivots are finite.
   float fa[2], fb[2], inv[2];
   bool live[2];
+  // A fresh copy of the lane's row index: the output addresses are rebuilt
+  // from it here instead of being held in registers through the tile loop.
+  int ln_e = ln;
+  asm volatile("" : "+v"(ln_e));
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const float2 lm = g_lm[rg][qb][lane];
@@ -691,7 +727,7 @@ __device__ __forceinline__ bool pair_pass(const FwdArgs& a) {
     fa[qb] = ea ? __builtin_amdgcn_exp2f(mc[qb] - M) : 0.f;
     fb[qb] = eb ? __builtin_amdgcn_exp2f(lm.y - M) : 0.f;
     const float l_row = fa[qb] * l[qb] + fb[qb] * lm.x;
-    const int qi = qw0 + 32 * qb + ln;
+    const int qi = qw0 + 32 * qb + ln_e;
     live[qb] = qi < q_len && l_row > 0.f;
     inv[qb] = live[qb] ? 1.f / l_row : 0.f;
     // Row log-sum-exp (M + log2 l) ln 2; -inf for padded or keyless rows.
@@ -704,7 +740,7 @@ __device__ __forceinline__ bool pair_pass(const FwdArgs& a) {
   static_for<16>([&](auto vg_tag) {
     constexpr int VG = decltype(vg_tag)::value;
     constexpr int DB = VG / 8, QB = (VG / 4) % 2, G = VG % 4, R = 4 * G;
-    const int qi = qw0 + 32 * QB + ln;
+    const int qi = qw0 + 32 * QB + ln_e;
     const float4 ob = *mptr(vg_tag);
     const float x0 = (fa[QB] * o[DB][QB][R] + fb[QB] * ob.x) * inv[QB];
     const float x1 = (fa[QB] * o[DB][QB][R + 1] + fb[QB] * ob.y) * inv[QB];

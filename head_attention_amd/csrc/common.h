@@ -53,6 +53,14 @@ __device__ __forceinline__ void lds_fill16(__amdgpu_buffer_rsrc_t rsrc, const vo
                : "memory");
 }
 
+// The same with the LDS destination given as its byte address.
+__device__ __forceinline__ void lds_fill16_at(__amdgpu_buffer_rsrc_t rsrc, uint32_t lds_addr, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "v"(voff), "s"(rsrc)
+               : "memory");
+}
+
 // Position of the 16-byte chunks of row r of a K tile that is only read by
 // rows (16 bytes per lane, lanes on consecutive rows): chunk c sits at
 // c ^ k_swz(r), distinct over any 8 consecutive rows and, for 16
