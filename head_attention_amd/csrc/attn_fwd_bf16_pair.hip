@@ -476,18 +476,44 @@ __device__ __forceinline__ bool pair_pass(const FwdArgs& a) {
   // (and V(p - 1), filled two phases earlier still).  The slot of tile t
   // holds its K and its V; it is refilled only after the phase that last
   // read it (the P.V of tile t, at phase t + 2) has ended.
-  auto fills = [&](auto j_tag, int p) __attribute__((always_inline)) {
+  // In the loop only the vector-role wave of each SIMD fills: 16 rows of
+  // the K and V tiles each (rows 16 rg .. 16 rg + 15), issued with its
+  // exponentials, while the matrix-role wave's LDS reads run undisturbed by
+  // its own fill instructions.  Called in every phase, it fills only in the
+  // wave's vector phases (VROLE).
+  const int lrow = 16 * rg + (lane >> 3);
+  const uint32_t koff_a = (uint32_t)lrow * kRowBytes + 16u * (uint32_t)(fpos ^ k_swz(lrow));
+  const uint32_t koff_b = (uint32_t)(lrow + 8) * kRowBytes + 16u * (uint32_t)(fpos ^ k_swz(lrow + 8));
+  const uint32_t voff_a = (uint32_t)lrow * kRowBytes + 16u * (uint32_t)(fpos ^ (2 * (lrow & 3)));
+  auto fills = [&](auto j_tag, int p, auto vrole_tag) __attribute__((always_inline)) {
     constexpr int J = decltype(j_tag)::value;
-    using SF = std::integral_constant<int, (J + kAhead) % kSlots>;
-    fill_k(SF(), p + kAhead);
-    fill_v(SF(), p + kAhead);
+    if constexpr (decltype(vrole_tag)::value) {
+      constexpr int SF = (J + kAhead) % kSlots;
+      const uint32_t toff = (uint32_t)(p + kAhead) * kTileBytes;
+      const uint32_t kdst = ring_addr(SF) + 2048u * rg, vdst = ring_addr(kSlots + SF) + 2048u * rg;
+      lds_fill16_at(rk, kdst, toff + koff_a);
+      lds_fill16_at(rk, kdst + 1024u, toff + koff_b);
+      lds_fill16_at(rv, vdst, toff + voff_a);
+      lds_fill16_at(rv, vdst + 1024u, toff + voff_a + 1024u);
+    }
   };
-  auto sync = [&]() __attribute__((always_inline)) {
-    // vmcnt(8): the fills of this and the three previous phases may fly.
-    // Under the band schedule a row group reads up to 3 tiles ahead of the
-    // ring position, so only this phase's fills may: vmcnt(2).
-    if constexpr (BAND) __builtin_amdgcn_s_waitcnt(0x0F70 | 2);
-    else __builtin_amdgcn_s_waitcnt(0x0F70 | 8);
+  auto sync = [&](auto vrole_tag) __attribute__((always_inline)) {
+    // A wave fills in every second phase.  After its vector phase p, the
+    // fills of phases p and p - 2 may fly (vmcnt(8)): the tile read at
+    // phase p + 1 was filled at phase p - 4.  After a matrix phase,
+    // vmcnt(6), which also covers the prologue: its ten fills per wave
+    // (tiles 0 .. 4, filled by all waves) must land tile by tile over the
+    // first phases.  Under the band schedule a row group reads up to 3
+    // tiles ahead of the ring position, so only this phase's fills may fly:
+    // vmcnt(4) after a vector phase, vmcnt(0) after a matrix phase (whose
+    // wave filled, in the phase before, the tile read next).
+    if constexpr (BAND) {
+      if constexpr (decltype(vrole_tag)::value) __builtin_amdgcn_s_waitcnt(0x0F70 | 4);
+      else __builtin_amdgcn_s_waitcnt(0x0F70 | 0);
+    } else {
+      if constexpr (decltype(vrole_tag)::value) __builtin_amdgcn_s_waitcnt(0x0F70 | 8);
+      else __builtin_amdgcn_s_waitcnt(0x0F70 | 6);
+    }
     barrier_lds();
   };
   // MFMA phase at phase p (slot J = p % 8): P.V of tile p - 2, then S of
@@ -616,35 +642,37 @@ __device__ __forceinline__ bool pair_pass(const FwdArgs& a) {
     // Even-tile waves run MFMA phases at even p, odd-tile waves at odd p;
     // both run the same number of phases (and barriers).
     const int n_phases = n_run + 2;
+    using M = std::false_type;  // matrix phase: no fills
+    using F = std::true_type;   // vector phase: this wave fills
     if (par == 0) {
 #pragma nounroll
       for (int p = 0; p < n_phases; p += 8) {
-        fills(J0(), p);     mphase(J0()); sync();
-        fills(J1(), p + 1); vphase(p + d);              sync();
+        mphase(J0());                            sync(M());
+        fills(J1(), p + 1, F()); vphase(p + d);       sync(F());
         if (p + 2 >= n_phases) break;
-        fills(J2(), p + 2); mphase(J2()); sync();
-        fills(J3(), p + 3); vphase(p + 2 + d);          sync();
+        mphase(J2());                            sync(M());
+        fills(J3(), p + 3, F()); vphase(p + 2 + d);   sync(F());
         if (p + 4 >= n_phases) break;
-        fills(J4(), p + 4); mphase(J4()); sync();
-        fills(J5(), p + 5); vphase(p + 4 + d);          sync();
+        mphase(J4());                            sync(M());
+        fills(J5(), p + 5, F()); vphase(p + 4 + d);   sync(F());
         if (p + 6 >= n_phases) break;
-        fills(J6(), p + 6); mphase(J6()); sync();
-        fills(J7(), p + 7); vphase(p + 6 + d);          sync();
+        mphase(J6());                            sync(M());
+        fills(J7(), p + 7, F()); vphase(p + 6 + d);   sync(F());
       }
     } else {
 #pragma nounroll
       for (int p = 0; p < n_phases; p += 8) {
-        fills(J0(), p);     vphase(p - 1 + d);              sync();
-        fills(J1(), p + 1); mphase(J1()); sync();
+        fills(J0(), p, F());     vphase(p - 1 + d);   sync(F());
+        mphase(J1());                            sync(M());
         if (p + 2 >= n_phases) break;
-        fills(J2(), p + 2); vphase(p + 1 + d);              sync();
-        fills(J3(), p + 3); mphase(J3()); sync();
+        fills(J2(), p + 2, F()); vphase(p + 1 + d);   sync(F());
+        mphase(J3());                            sync(M());
         if (p + 4 >= n_phases) break;
-        fills(J4(), p + 4); vphase(p + 3 + d);              sync();
-        fills(J5(), p + 5); mphase(J5()); sync();
+        fills(J4(), p + 4, F()); vphase(p + 3 + d);   sync(F());
+        mphase(J5());                            sync(M());
         if (p + 6 >= n_phases) break;
-        fills(J6(), p + 6); vphase(p + 5 + d);              sync();
-        fills(J7(), p + 7); mphase(J7()); sync();
+        fills(J6(), p + 6, F()); vphase(p + 5 + d);   sync(F());
+        mphase(J7());                            sync(M());
       }
     }
     __builtin_amdgcn_s_waitcnt(0x0F70 | 0);  // no fill may land in the merge area
