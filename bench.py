@@ -422,7 +422,10 @@ LEG_GRIDS = {("attn_fwd_bf16_short_kernel<none>", 65536): "encoder_base",
              ("decode_merge_kernel", 65536): "kv_decode",
              ("attn_fwd_bf16_short_kernel<none>", 256): "launch floor (1-row forward)",
              ("at::cuda::(anonymous namespace)::spin_kernel(long)", 1): "launch floor (empty kernel)",
-             ("copyBuffer", 512): "bench set-up copies"}
+             ("copyBuffer", 512): "bench set-up copies",
+             ("attn_fwd_bf16_kernel<true>", 393216): "mid_causal_300 (B32 h16 n300)",
+             ("attn_fwd_bf16_kernel<false>", 65536): "mid_cross_128_300 (B32 h8 128->300)",
+             ("attn_fwd_bf16_kernel<true>", 131072): "mid_causal_500 (B8 h16 n500)"}
 
 
 def summarize_trace(path: str) -> str:
@@ -624,6 +627,52 @@ def launch_floor(stream, reps: int = 200) -> dict:
     return res
 
 
+# Shapes between the short-key and the paired kernels (256 < n_k, n_q < 512),
+# which run on the 4-wave kernel: the decoder of the big model at n = 300
+# (causal self) and cross attention from 128 decoder rows to 300 encoder rows
+# with key padding, and B8 h16 n500 causal.  Timed apart from the step.
+MID_SHAPES = (("mid_causal_300", 32, 16, 300, 300, True, False),
+              ("mid_cross_128_300", 32, 8, 128, 300, False, True),
+              ("mid_causal_500", 8, 16, 500, 500, True, False))
+
+
+def mid_shapes(stream, reps: int = 20) -> dict:
+    """Back-to-back forward calls at MID_SHAPES, timed with HIP events."""
+    import head_attention_amd as ha
+    g = torch.Generator().manual_seed(1300)
+    res = {}
+    for name, B, H, nq, nk, causal, kpad in MID_SHAPES:
+        Q = torch.randn((B, H, nq, 64), generator=g).to(torch.bfloat16).cuda()
+        K = torch.randn((B, H, nk, 64), generator=g).to(torch.bfloat16).cuda()
+        V = torch.randn((B, H, nk, 64), generator=g).to(torch.bfloat16).cuda()
+        kl = torch.randint(16, nk + 1, (B,), generator=g, dtype=torch.int32) if kpad else None
+        mk = ha.ATTN_MASK_CAUSAL if causal else (ha.ATTN_MASK_KEY_PADDING if kpad else ha.ATTN_MASK_NONE)
+        kld = kl.cuda() if kpad else None
+        out = torch.empty_like(Q)
+
+        def call():
+            ha.forward(Q, K, V, mask_kind=mk, kv_lens=kld, scale=0.125, out=out)
+        for _ in range(5):
+            call()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        if causal:
+            pairs = B * H * nq * (nq + 1) // 2
+        elif kpad:
+            pairs = H * nq * int(kl.sum())
+        else:
+            pairs = B * H * nq * nk
+        res[name] = {"shape": f"B{B} h{H} {nq}x{nk}{' causal' if causal else ''}{' key padding' if kpad else ''}",
+                     "us": round(us, 2), "TFLOP/s": round(4 * 64 * pairs / (us * 1e-6) / 1e12, 2)}
+    return res
+
+
 # ------------------------------------------------------------------ main
 def main():
     ap = argparse.ArgumentParser()
@@ -775,6 +824,7 @@ def main():
         ("decoder_big", "attn_fwd_bf16_short_kernel<causal> + <none> on decoder_big (B32 h16, 128 self, 128->160)"))}
     out["device"] = device_info()
     out["launch_floor"] = launch_floor(stream)
+    out["mid_shapes"] = mid_shapes(stream)
     if args.copy_probe_mib:
         src = torch.ones(args.copy_probe_mib * 2 ** 18, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
