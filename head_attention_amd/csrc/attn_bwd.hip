@@ -79,12 +79,15 @@ __device__ __forceinline__ int swz(int r) { return (2 * (r & 3)) ^ ((r >> 2) & 3
 // beyond the descriptor's range read as zero.  256 threads, 2 instructions
 // per wave.
 __device__ __forceinline__ void fill_tile(Tile& t, __amdgpu_buffer_rsrc_t r, int r0, int wave, int lane) {
+  // The tile's LDS byte address as an integer (a generic pointer here would
+  // be kept in registers and converted back, with a null check, per fill).
+  const uint32_t base = (uint32_t)(uintptr_t)(lds_void_t*)&t.c[0];
   const int fpos = lane & 7;
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
     const int row = 32 * half + 8 * wave + (lane >> 3);
     const uint32_t off = (uint32_t)(r0 + row) * kRowBytes + 16u * (uint32_t)(fpos ^ swz(row));
-    lds_fill16(r, &t.c[256 * half + 64 * wave], off);
+    lds_fill16_at(r, base + 16u * (uint32_t)(256 * half + 64 * wave), off);
   }
 }
 
@@ -309,7 +312,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
     fill_tile(bslot<S>(), rdo, q0, wave, lane);
     if (wave == 0) {
       const uint32_t off = ld_base == kOutOfRange ? kOutOfRange : ld_base + (uint32_t)q0 * 4u;
-      lds_fill16(rld, ldslot<S>(), off);
+      lds_fill16_at(rld, (uint32_t)(uintptr_t)(lds_void_t*)ldslot<S>(), off);
     }
   };
 
@@ -351,6 +354,23 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
     // bf16 in the register order the k slots of the next products use.
     bool need_mask = (kw0 + 32 > kv_lim) || (CAUSAL && q0 < kw0 + 32);
     if (BAND) need_mask = need_mask || !(q0 + kTile - 1 - wl <= kw0 && kw0 + 31 <= q0 + wr);
+    // Masked scores become -inf (so P = 0) in a block of their own, taken
+    // only by tiles that cross an edge.  The compiler turned the test into
+    // selects on every tile (inside the exponential loop, and as a separate
+    // block too); the empty volatile statement keeps the block a branch.
+    if (need_mask) {
+      asm volatile("");
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int qi = q0 + 32 * qb + 8 * (r >> 2) + 4 * hh + (r & 3);
+          bool ok = key < kv_lim;
+          if (CAUSAL) ok = ok && key <= qi;
+          if (BAND) ok = ok && key >= qi - wl && key <= qi + wr;
+          s_[qb][r] = ok ? s_[qb][r] : -INFINITY;
+        }
+    }
     uint32_t pp[16], ps[16];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
@@ -365,14 +385,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * gq + e;
-          float x = fmaf(s_[qb][r], c, -lv[e]);
-          if (need_mask) {
-            const int qi = q0 + ql + e;
-            bool ok = key < kv_lim;
-            if (CAUSAL) ok = ok && key <= qi;
-            if (BAND) ok = ok && key >= qi - wl && key <= qi + wr;
-            x = ok ? x : -INFINITY;
-          }
+          // -inf for a masked key (c > 0); L = +inf gives 0 for padded rows
+          const float x = fmaf(s_[qb][r], c, -lv[e]);
           p[e] = __builtin_amdgcn_exp2f(x);
           g[e] = p[e] * (dp[qb][r] - dvv[e]);
         }
