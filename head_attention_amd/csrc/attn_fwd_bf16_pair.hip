@@ -97,8 +97,6 @@ __shared__ float2 g_lm[4][2][64];
 // Set when a row failed the fixed-pivot range check.
 __shared__ int g_redo;
 
-typedef __attribute__((address_space(3))) uint4 lds_uint4;
-typedef __attribute__((address_space(3))) char lds_char;
 // LDS byte address of ring row r (K of slot r, or V of slot r - 8), kept
 // as an integer so that a slot chosen at run time costs one add.
 __device__ __forceinline__ uint32_t ring_addr(int r) {
@@ -108,48 +106,6 @@ __device__ __forceinline__ uint32_t ring_addr(int r) {
 template <int S>
 __device__ __forceinline__ uint4* mslot() {
   return S < 4 ? g_ring[S] : g_ring[kSlots + S - 4];
-}
-
-// Weights 2^x of one query block of a tile from its exponents x (key blocks
-// x0: keys 0..31, x1: keys 32..63), packed to bf16 pairs in the order P.V
-// consumes them.
-__device__ __forceinline__ void exp_pack(const f32x16& x0, const f32x16& x1, uint32_t (&pk)[16]) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    pk[i] = pack_bf16x2(__builtin_amdgcn_exp2f(x0[2 * i]), __builtin_amdgcn_exp2f(x0[2 * i + 1]));
-    pk[8 + i] = pack_bf16x2(__builtin_amdgcn_exp2f(x1[2 * i]), __builtin_amdgcn_exp2f(x1[2 * i + 1]));
-  }
-}
-
-// Max of the 32 values of two accumulator blocks as a shallow tree of
-// 3-input maxima.  The inputs are results of fp32 arithmetic (canonical), so
-// each fmaxf pair folds into one v_max3_f32.
-__device__ __forceinline__ float max32(const f32x16& a, const f32x16& b) {
-  float v[32];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    v[i] = a[i];
-    v[16 + i] = b[i];
-  }
-  float m[11];
-#pragma unroll
-  for (int i = 0; i < 10; ++i) m[i] = fmaxf(fmaxf(v[3 * i], v[3 * i + 1]), v[3 * i + 2]);
-  m[10] = fmaxf(v[30], v[31]);
-  const float n0 = fmaxf(fmaxf(m[0], m[1]), m[2]);
-  const float n1 = fmaxf(fmaxf(m[3], m[4]), m[5]);
-  const float n2 = fmaxf(fmaxf(m[6], m[7]), m[8]);
-  const float n3 = fmaxf(m[9], m[10]);
-  return fmaxf(fmaxf(fmaxf(n0, n1), n2), n3);
-}
-
-__device__ __forceinline__ void barrier_lds() {
-  // Block the compiler from moving memory accesses across, without the
-  // vmcnt(0) a workgroup fence would add for the in-flight LDS fills; the
-  // scheduling barriers keep register-only work (MFMAs on prefetched
-  // fragments) in its phase as well.
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_barrier" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
 }
 
 // (b, h, query tile) of workgroup bid: the 8 XCDs take workgroup ids round

@@ -22,6 +22,8 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
+typedef __attribute__((address_space(3))) uint4 lds_uint4;
+typedef __attribute__((address_space(3))) char lds_char;
 
 // One bf16 row of K, V, Q or O (d = 64).
 constexpr uint32_t kRowBytes = kHeadDim * 2;
@@ -65,6 +67,48 @@ __device__ __forceinline__ bool half_swap_or(bool x) {
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   f32x2 v = {lo, hi};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// Weights 2^x of one query block of a tile from its exponents x (key blocks
+// x0: keys 0..31, x1: keys 32..63), packed to bf16 pairs in the order P.V
+// consumes them.
+__device__ __forceinline__ void exp_pack(const f32x16& x0, const f32x16& x1, uint32_t (&pk)[16]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    pk[i] = pack_bf16x2(__builtin_amdgcn_exp2f(x0[2 * i]), __builtin_amdgcn_exp2f(x0[2 * i + 1]));
+    pk[8 + i] = pack_bf16x2(__builtin_amdgcn_exp2f(x1[2 * i]), __builtin_amdgcn_exp2f(x1[2 * i + 1]));
+  }
+}
+
+// Max of the 32 values of two accumulator blocks as a shallow tree of
+// 3-input maxima.  The inputs are results of fp32 arithmetic (canonical), so
+// each fmaxf pair folds into one v_max3_f32.
+__device__ __forceinline__ float max32(const f32x16& a, const f32x16& b) {
+  float v[32];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    v[i] = a[i];
+    v[16 + i] = b[i];
+  }
+  float m[11];
+#pragma unroll
+  for (int i = 0; i < 10; ++i) m[i] = fmaxf(fmaxf(v[3 * i], v[3 * i + 1]), v[3 * i + 2]);
+  m[10] = fmaxf(v[30], v[31]);
+  const float n0 = fmaxf(fmaxf(m[0], m[1]), m[2]);
+  const float n1 = fmaxf(fmaxf(m[3], m[4]), m[5]);
+  const float n2 = fmaxf(fmaxf(m[6], m[7]), m[8]);
+  const float n3 = fmaxf(m[9], m[10]);
+  return fmaxf(fmaxf(fmaxf(n0, n1), n2), n3);
+}
+
+__device__ __forceinline__ void barrier_lds() {
+  // Block the compiler from moving memory accesses across, without the
+  // vmcnt(0) a workgroup fence would add for the in-flight LDS fills; the
+  // scheduling barriers keep register-only work (MFMAs on prefetched
+  // fragments) in its phase as well.
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 template <typename F, int... I>
