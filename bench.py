@@ -59,8 +59,8 @@ D = 64
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
 # Sources of every kernel the bench launches: the traffic figures are reported
 # only while these are unchanged since the counters were taken.
-KERNEL_SOURCES = ["attn_fwd_bf16_pair.hip", "attn_fwd_bf16_short.hip", "attn_fwd_bf16.hip",
-                  "attn_decode.hip", "attn_cache.hip", "attn_proj.hip", "attn_bwd.hip", "common.h"]
+KERNEL_SOURCES = ["attn_fwd_bf16_pair.hip", "attn_fwd_bf16_band.hip", "attn_fwd_bf16_short.hip", "attn_fwd_bf16.hip",
+                  "attn_decode.hip", "attn_cache.hip", "attn_proj.hip", "attn_bwd.hip", "common.h", "kernel_util.h"]
 
 
 def kernel_source_hash() -> str:
@@ -386,7 +386,7 @@ def _short_kernel(name: str) -> str:
     if m:
         causal = m.group(2) in ("true", "1")
         return f"{m.group(1)}<{'true' if causal else 'false'}>"
-    for key in ("attn_fwd_f32_kernel", "decode_partial_kernel", "decode_merge_kernel",
+    for key in ("attn_fwd_bf16_band_kernel", "attn_fwd_f32_kernel", "decode_partial_kernel", "decode_merge_kernel",
                 "cache_append_kernel", "bwd_rowdot_kernel", "copyBuffer", "elementwise"):
         if key in name:
             return key
@@ -398,7 +398,7 @@ def _short_kernel(name: str) -> str:
 LEG_GRIDS = {("attn_fwd_bf16_short_kernel<none>", 65536): "encoder_base",
              ("attn_fwd_bf16_short_kernel<causal>", 131072): "decoder_big (causal self)",
              ("attn_fwd_bf16_short_kernel<none>", 131072): "decoder_big (cross)",
-             ("attn_fwd_bf16_pair_kernel<band>", 262144): "long_restricted",
+             ("attn_fwd_bf16_band_kernel", 131072): "long_restricted",
              ("cache_append_kernel", 8192): "kv_append",
              ("bwd_dkdv_kernel<causal>", 262144): "long_causal_bwd",
              ("bwd_dq_kernel<causal>", 262144): "long_causal_bwd",
@@ -417,7 +417,6 @@ LEG_GRIDS = {("attn_fwd_bf16_short_kernel<none>", 65536): "encoder_base",
              ("proj_gemm_kernel<false>", 65536): "mha_proj (self and cross output)",
              ("attn_fwd_bf16_pair_kernel<causal>", 262144): "long_causal",
              ("attn_fwd_bf16_pair_redo_kernel<causal>", 262144): "long_causal (redo pass, exits)",
-             ("attn_fwd_bf16_pair_redo_kernel<band>", 262144): "long_restricted (redo pass, exits)",
              ("decode_partial_kernel", 4194304): "kv_decode",
              ("decode_merge_kernel", 65536): "kv_decode",
              ("attn_fwd_bf16_short_kernel<none>", 256): "launch floor (1-row forward)",
@@ -817,7 +816,7 @@ def main():
     out["roofline_bwd"] = leg_roof("long_causal_bwd", "bwd_rowdot + bwd_dkdv + bwd_dq on long_causal_bwd (B1 h16 n8192)")
     out["roofline_proj"] = leg_roof("mha_proj", "proj_gemm_kernel on mha_proj (decoder_big layer projections)")
     out["roofline_restricted"] = leg_roof(
-        "long_restricted", "attn_fwd_bf16_pair_kernel<band> on long_restricted (B1 h16 n8192, radius 256)")
+        "long_restricted", "attn_fwd_bf16_band_kernel on long_restricted (B1 h16 n8192, radius 256)")
     out["roofline_decode"] = leg_roof("kv_decode", "decode_partial_kernel + decode_merge_kernel on kv_decode")
     out["roofline_n128"] = {n: leg_roof(n, k) for n, k in (
         ("encoder_base", "attn_fwd_bf16_short_kernel<none> on encoder_base (B32 h8 n128, key padding)"),

@@ -16,6 +16,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "libheadattn.so")
 SOURCES = ["attn_api.cpp", "attn_fwd_f32.hip", "attn_fwd_bf16.hip", "attn_fwd_bf16_pair.hip", "attn_fwd_bf16_short.hip",
+           "attn_fwd_bf16_band.hip",
            "attn_decode.hip", "attn_cache.hip", "attn_proj.hip",
            "attn_bwd.hip"]
 

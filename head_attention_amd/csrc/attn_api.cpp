@@ -154,7 +154,8 @@ attn_status forward_impl(const void* Q, const void* K, const void* V, attn_layou
   hipError_t e;
   if (layout.dtype == ATTN_F32) e = launch_fwd_f32(a, s);
   else if (layout.n_k <= kShortMaxKeys) e = launch_fwd_bf16_short(a, s);
-  else if (layout.n_q >= kPairMinRows || restricted) e = launch_fwd_bf16_pair(a, s);
+  else if (restricted) e = launch_fwd_bf16_band(a, s);
+  else if (layout.n_q >= kPairMinRows) e = launch_fwd_bf16_pair(a, s);
   else e = launch_fwd_bf16(a, s);
   if (e != hipSuccess) {
     g_last_hip = e;

@@ -166,6 +166,9 @@ hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s);
 hipError_t launch_fwd_bf16_pair(const FwdArgs& a, hipStream_t s);
 hipError_t launch_fwd_bf16_short(const FwdArgs& a, hipStream_t s);
+// Restricted self-attention with n_k > kShortMaxKeys: 512-row workgroups of
+// eight row groups, each walking its own window of keys.
+hipError_t launch_fwd_bf16_band(const FwdArgs& a, hipStream_t s);
 
 // bf16 forward: calls whose key range fits LDS whole (n_k <= 256) run on the
 // short-sequence kernel, which loads all of a (b, h)'s K and V at once.

@@ -58,7 +58,8 @@ def _run(Q, K, V, mask, kv_lens=None, radius=None):
 
 CASES = {
     # id: (B, H, n_q, n_k, mask, kv_lens, radius) -- kernels: short (n_k <= 256),
-    # 4-wave (256 < n_k, n_q < 512), paired (n_q >= 512, or any restricted call)
+    # 4-wave (256 < n_k, n_q < 512), paired (n_q >= 512), band (any
+    # restricted call with n_k > 256)
     "short_none_150": (1, 2, 150, 150, 0, None, None),
     "short_causal_150": (1, 2, 150, 150, 2, None, None),
     "fourwave_none_300": (1, 2, 300, 300, 0, None, None),
@@ -76,6 +77,7 @@ CASES = {
     "band_causal_r0_700": (1, 2, 700, 700, 6, None, 0),
     "band_r20_700": (1, 2, 700, 700, 4, None, 20),
     "band_causal_r40_600": (1, 2, 600, 600, 6, None, 40),
+    "band_r300_1100": (1, 2, 1100, 1100, 4, None, 300),
     "short_band_r0_150": (1, 2, 150, 150, 4, None, 0),
 }
 
@@ -122,3 +124,21 @@ def test_far_negative_decode():
     torch.cuda.synchronize()
     ref = orc.decode(np64(q), np64(Kc), np64(Vc), lens.numpy(), scale=0.125)
     check(np64(out), ref, BF16, "far-negative decode")
+
+
+@pytest.mark.parametrize("radius", [None, 300], ids=["paired", "band"])
+def test_mixed_workgroups(radius):
+    """Only some workgroups fall back to the moving pivot: query rows 512 ..
+    1023 have far-negative logits, the others N(0,1) rows.  The second kernel
+    must recompute exactly the workgroups that failed the fixed-pivot range
+    check and leave the results of the others as they are."""
+    B, H, n = 1, 3, 1500
+    Q, K, V = _far_negative(5200, B, H, n, n, BF16)
+    g = workloads.generator(5201)
+    Qn = workloads.randn(g, (B, H, n, 64), BF16)
+    Q[:, :, :512] = Qn[:, :, :512]
+    Q[:, :, 1024:] = Qn[:, :, 1024:]
+    mask = 0 if radius is None else ha.ATTN_MASK_RESTRICTED
+    say(f"[mixed workgroups radius={radius}] B{B} H{H} n{n}")
+    out, ref = _run(Q, K, V, mask, None, radius)
+    check(out, ref, BF16, f"mixed workgroups radius={radius}")

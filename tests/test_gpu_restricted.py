@@ -3,12 +3,13 @@ query attends only to the keys within `radius` of its position (the past
 half under the causal mask), against the fp64 oracle on the same inputs.
 
 Cases reach every kernel that serves the restricted mask -- the short-key
-bf16 kernel (n <= 256), the paired bf16 kernel (any longer n, also below its
-usual 512-row threshold) and the fp32 path -- with radii from 0 (a row sees
-only itself) through windows narrower than, equal to and wider than a 64-key
-tile, to radii beyond the sequence; key padding and padded query rows,
-including rows whose whole window lies beyond kv_len; ragged n; B*h
-divisible by 8 or not.  Bars are those of the plain forward (2e-2 max abs and
+bf16 kernel (n <= 256), the bf16 band kernel (any longer n: 512-row
+workgroups whose first key tile may lie before key 0) and the fp32 path --
+with radii from 0 (a row sees only itself) through windows narrower than,
+equal to and wider than a 64-key tile, to radii beyond the sequence (windows
+wider than a workgroup's rows); key padding and padded query rows, including
+rows whose whole window lies beyond kv_len; ragged n; several workgroups per
+head; B*h divisible by 8 or not.  Bars are those of the plain forward (2e-2 max abs and
 1e-2 relative L2 on bf16, 1e-5 relative on fp32) and of the log-sum-exp
 (1e-2 bf16, 1e-5 fp32).  The bench's long_restricted workload (B1 h16
 n=8192, radius 256) is checked on sampled rows at full size.
@@ -36,13 +37,16 @@ CASES = {
     "short_r40_causal_pad": (BF16, 2, 4, 256, 40, True, True, False),
     "short_r63_causal": (BF16, 1, 8, 190, 63, True, False, True),
     "short_r300": (BF16, 1, 2, 130, 300, False, False, False),
-    "pair_300_r17_pad": (BF16, 2, 2, 300, 17, False, True, True),
-    "pair_1000_r100_causal_pad": (BF16, 1, 3, 1000, 100, True, True, True),
-    "pair_1000_r64": (BF16, 2, 2, 1000, 64, False, False, False),
-    "pair_777_r1_pad": (BF16, 1, 8, 777, 1, False, True, False),
-    "pair_600_r600_causal": (BF16, 1, 2, 600, 600, True, False, False),
-    "pair_700_r255_causal": (BF16, 1, 2, 700, 255, True, False, True),
-    "pair_520_r0_pad": (BF16, 2, 2, 520, 0, False, True, False),
+    "band_300_r17_pad": (BF16, 2, 2, 300, 17, False, True, True),
+    "band_1000_r100_causal_pad": (BF16, 1, 3, 1000, 100, True, True, True),
+    "band_1000_r64": (BF16, 2, 2, 1000, 64, False, False, False),
+    "band_777_r1_pad": (BF16, 1, 8, 777, 1, False, True, False),
+    "band_600_r600_causal": (BF16, 1, 2, 600, 600, True, False, False),
+    "band_700_r255_causal": (BF16, 1, 2, 700, 255, True, False, True),
+    "band_520_r0_pad": (BF16, 2, 2, 520, 0, False, True, False),
+    "band_2100_r700_pad": (BF16, 2, 4, 2100, 700, False, True, True),
+    "band_1300_r257_causal": (BF16, 1, 5, 1300, 257, True, False, False),
+    "band_1600_r1000": (BF16, 1, 2, 1600, 1000, False, False, False),
     "f32_200_r7_pad": (F32, 2, 2, 200, 7, False, True, True),
     "f32_700_r70_causal_pad": (F32, 1, 2, 700, 70, True, True, False),
     "f32_130_r200": (F32, 1, 3, 130, 200, False, False, False),
@@ -94,7 +98,7 @@ def test_restricted_parity(name):
     assert torch.equal(out, _run(Q, K, V, radius, mask, ql, kl, 0.125))
 
 
-@pytest.mark.parametrize("dtype,n", [(BF16, 200), (BF16, 900), (F32, 300)], ids=["short", "pair", "fp32"])
+@pytest.mark.parametrize("dtype,n", [(BF16, 200), (BF16, 900), (F32, 300)], ids=["short", "band", "fp32"])
 def test_radius_zero_returns_v(dtype, n):
     """radius 0: a row's only key is itself, so O_i = V_i exactly (its weight
     is exactly 1); rows at or past kv_len have no key and are 0."""
