@@ -55,16 +55,6 @@
 // of use; a phase ends with a wait for this wave's fills of four phases ago
 // and a barrier.
 //
-// Restricted self-attention (a band of keys around each row) runs its own
-// schedule: the four row groups of a workgroup need windows that start one
-// tile apart, so row group g walks only its own window, d <= g tiles into
-// the workgroup's range: at phase p the row groups work on tiles p .. p + 3
-// of the ring at once.  A workgroup then runs as many phases as one window
-// has tiles (9 or 10 for 64 rows and a 256-key radius) instead of as many as
-// its whole range (12 or 13), and no row group idles through tiles outside
-// its window.  Reading 3 tiles ahead of the ring position, a phase ends with
-// a wait for all but this phase's fills.
-//
 // K rows keep their 16-byte chunks
 // XOR-swizzled by row; V stays row-major (chunks swizzled by row % 4) and is
 // read transposed with ds_read_b64_tr_b16, which hands each lane four
@@ -82,8 +72,7 @@ constexpr uint32_t kTileBytes = kBN * kRowBytes;
 
 // Ring of 8 slots, each the K and the V tile of one 64-key tile (8 KB each:
 // 64 rows x 8 chunks of 16 B): K of slot s at g_ring[s], its V at
-// g_ring[8 + s].  Under the band schedule each row group reads its own
-// slot, chosen at run time.  The fills are issued from inline assembly
+// g_ring[8 + s].  The fills are issued from inline assembly
 // (lds_fill16_at), which the compiler does not track (with the builtin it
 // would wait for every fill in flight before any read of the array): the
 // phase loop's explicit vmcnt waits and barriers order them.
@@ -134,7 +123,6 @@ __device__ __forceinline__ void wg_tile(const FwdArgs& a, int bid, int& bh, int&
 template <int MODE, bool FIXED>
 __device__ __forceinline__ bool pair_pass(const FwdArgs& a) {
   constexpr bool CAUSAL = MODE == kModeCausal;
-  constexpr bool BAND = MODE == kModeBand;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
@@ -157,47 +145,17 @@ __device__ __forceinline__ bool pair_pass(const FwdArgs& a) {
   const int q0 = qt * kBM;
   const int qw0 = q0 + kWaveRows * rg;  // first query row of this wave
 
-  // Restricted self-attention: row i sees keys i - wl .. i + wr.  The
-  // workgroup then starts at key tile t0 (tile indices below are relative
-  // to it) and a row group skips the tiles wholly before its rows' windows.
-  const int wl = BAND ? a.radius : 0;
-  const int wr = BAND ? (a.causal ? 0 : a.radius) : 0;
-  const int t0 = BAND ? max(0, q0 - wl) / kBN : 0;
   int end = kv_lim;  // keys the workgroup needs
   if (CAUSAL) end = min(end, q0 + kBM);
-  if (BAND) end = min(end, q0 + kBM + wr);
   if (q0 >= q_len) end = 0;
-  const int n_tiles = max(0, (end + kBN - 1) / kBN - t0);
+  const int n_tiles = max(0, (end + kBN - 1) / kBN);
   int wave_end = end;  // keys this row group needs
   if (CAUSAL) wave_end = min(wave_end, qw0 + kWaveRows);
-  if (BAND) wave_end = min(wave_end, qw0 + kWaveRows + wr);
   if (qw0 >= q_len) wave_end = 0;
-  const int wave_tiles = max(0, (wave_end + kBN - 1) / kBN - t0);
-  const int wave_first = BAND ? max(0, qw0 - wl) / kBN - t0 : 0;
-  // Band schedule: row group rg walks only its own window, which starts
-  // d = wave_first tiles into the workgroup's range (0 <= d <= rg), so at
-  // phase p the four row groups work on ring tiles p .. p + 3 at once and
-  // the workgroup runs as many phases as its longest window (9 or 10 tiles
-  // for 64 rows and a 256-key radius) rather than its whole range (12 or
-  // 13).  Otherwise d = 0 and every row group walks the whole range.
-  const int d = BAND ? wave_first : 0;
-  int n_run = n_tiles;
-  if (BAND) {
-    n_run = 0;
-    for (int g = 0; g < 4; ++g) {
-      const int qg = q0 + kWaveRows * g;
-      const int eg = qg >= q_len ? 0 : min(end, qg + kWaveRows + wr);
-      const int first = max(0, qg - wl) / kBN - t0;
-      n_run = max(n_run, (eg + kBN - 1) / kBN - t0 - first);
-    }
-  }
-
-  const int k_base = t0 * kBN;  // first key of relative tile 0
-  K += (size_t)k_base * kHeadDim;
-  V += (size_t)k_base * kHeadDim;
+  const int wave_tiles = max(0, (wave_end + kBN - 1) / kBN);
   // The descriptors end at the last key the workgroup may use: the ring's
   // fills past its last tile read zeros without touching memory.
-  const uint32_t n_bytes = (uint32_t)max(0, end - k_base) * kRowBytes;
+  const uint32_t n_bytes = (uint32_t)max(0, end) * kRowBytes;
   const __amdgpu_buffer_rsrc_t rk =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(K), (short)0, (int)n_bytes, kBufferWord3);
   const __amdgpu_buffer_rsrc_t rv =
@@ -295,8 +253,7 @@ __device__ __forceinline__ bool pair_pass(const FwdArgs& a) {
   auto load_v_step = [&](auto slot_tag, auto j_tag, bf16x8 (&va)[2][4]) __attribute__((always_inline)) {
     constexpr int S = decltype(slot_tag)::value;
     constexpr int j = decltype(j_tag)::value;
-    // The slot of tile p + d (d = 0 outside the band schedule).
-    const lds_char* vt = (const lds_char*)(uintptr_t)ring_addr(kSlots + ((S + d) & (kSlots - 1)));
+    const lds_char* vt = (const lds_char*)(uintptr_t)ring_addr(kSlots + S);
     const int g = lane >> 4;
     const int i = lane & 15;
 #pragma unroll
@@ -317,7 +274,7 @@ __device__ __forceinline__ bool pair_pass(const FwdArgs& a) {
   auto load_k_step = [&](auto slot_tag, auto s_tag, bf16x8 (&ka)[2][4]) __attribute__((always_inline)) {
     constexpr int S = decltype(slot_tag)::value;
     constexpr int s = decltype(s_tag)::value;
-    const lds_uint4* kt = (const lds_uint4*)(uintptr_t)ring_addr((S + d) & (kSlots - 1));
+    const lds_uint4* kt = (const lds_uint4*)(uintptr_t)ring_addr(S);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int row = 32 * kb + ln;
@@ -358,23 +315,20 @@ __device__ __forceinline__ bool pair_pass(const FwdArgs& a) {
   // A fully masked row (max -inf) and NaN (garbage in padded query rows)
   // never move.
   auto softmax = [&](int t) __attribute__((always_inline)) {
-    const int k0 = k_base + t * kBN;
-    bool need_mask = (k0 + kBN > kv_lim) || (CAUSAL && k0 + kBN - 1 > qw0);
-    if (BAND) need_mask = need_mask || (k0 + kBN - 1 > qw0 + wr) || (k0 < qw0 + kWaveRows - 1 - wl);
+    const int k0 = t * kBN;
+    const bool need_mask = (k0 + kBN > kv_lim) || (CAUSAL && k0 + kBN - 1 > qw0);
     if (need_mask) {
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         const int qi = qw0 + 32 * qb + ln;
-        int hi = kv_lim;  // keys below hi and at or above lo are allowed
+        int hi = kv_lim;  // keys below hi are allowed
         if (CAUSAL) hi = min(hi, qi + 1);
-        if (BAND) hi = min(hi, qi + wr + 1);
         const int lim = hi - k0 - 4 * hh;
-        const int lo = BAND ? qi - wl - k0 - 4 * hh : INT_MIN;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int off = 8 * (r >> 2) + (r & 3);
-          sc[0][qb][r] = (off < lim && off >= lo) ? sc[0][qb][r] : -INFINITY;
-          sc[1][qb][r] = (off + 32 < lim && off + 32 >= lo) ? sc[1][qb][r] : -INFINITY;
+          sc[0][qb][r] = off < lim ? sc[0][qb][r] : -INFINITY;
+          sc[1][qb][r] = off + 32 < lim ? sc[1][qb][r] : -INFINITY;
         }
       }
     }
@@ -459,17 +413,9 @@ __device__ __forceinline__ bool pair_pass(const FwdArgs& a) {
     // phase p + 1 was filled at phase p - 4.  After a matrix phase,
     // vmcnt(6), which also covers the prologue: its ten fills per wave
     // (tiles 0 .. 4, filled by all waves) must land tile by tile over the
-    // first phases.  Under the band schedule a row group reads up to 3
-    // tiles ahead of the ring position, so only this phase's fills may fly:
-    // vmcnt(4) after a vector phase, vmcnt(0) after a matrix phase (whose
-    // wave filled, in the phase before, the tile read next).
-    if constexpr (BAND) {
-      if constexpr (decltype(vrole_tag)::value) __builtin_amdgcn_s_waitcnt(0x0F70 | 4);
-      else __builtin_amdgcn_s_waitcnt(0x0F70 | 0);
-    } else {
-      if constexpr (decltype(vrole_tag)::value) __builtin_amdgcn_s_waitcnt(0x0F70 | 8);
-      else __builtin_amdgcn_s_waitcnt(0x0F70 | 6);
-    }
+    // first phases.
+    if constexpr (decltype(vrole_tag)::value) __builtin_amdgcn_s_waitcnt(0x0F70 | 8);
+    else __builtin_amdgcn_s_waitcnt(0x0F70 | 6);
     barrier_lds();
   };
   // MFMA phase at phase p (slot J = p % 8): P.V of tile p - 2, then S of
@@ -520,23 +466,20 @@ __device__ __forceinline__ bool pair_pass(const FwdArgs& a) {
   // checks.  Whether the pivot was safe for every row is decided once, from
   // the row sums at the end (the range check after the loop).
   auto softmax_fixed = [&](int t) __attribute__((always_inline)) {
-    const int k0 = k_base + t * kBN;
-    bool need_mask = (k0 + kBN > kv_lim) || (CAUSAL && k0 + kBN - 1 > qw0);
-    if (BAND) need_mask = need_mask || (k0 + kBN - 1 > qw0 + wr) || (k0 < qw0 + kWaveRows - 1 - wl);
+    const int k0 = t * kBN;
+    const bool need_mask = (k0 + kBN > kv_lim) || (CAUSAL && k0 + kBN - 1 > qw0);
     if (need_mask) {
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         const int qi = qw0 + 32 * qb + ln;
         int hi = kv_lim;
         if (CAUSAL) hi = min(hi, qi + 1);
-        if (BAND) hi = min(hi, qi + wr + 1);
         const int lim = hi - k0 - 4 * hh;
-        const int lo = BAND ? qi - wl - k0 - 4 * hh : INT_MIN;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int off = 8 * (r >> 2) + (r & 3);
-          sc[0][qb][r] = (off < lim && off >= lo) ? sc[0][qb][r] : -INFINITY;
-          sc[1][qb][r] = (off + 32 < lim && off + 32 >= lo) ? sc[1][qb][r] : -INFINITY;
+          sc[0][qb][r] = off < lim ? sc[0][qb][r] : -INFINITY;
+          sc[1][qb][r] = off + 32 < lim ? sc[1][qb][r] : -INFINITY;
         }
       }
     }
@@ -552,7 +495,7 @@ __device__ __forceinline__ bool pair_pass(const FwdArgs& a) {
   // Vector phase of tile t: the weights of tile t, or zero weights for a
   // phase before this wave's first tile or past its last.
   auto vphase = [&](int t) __attribute__((always_inline)) {
-    if (t >= wave_first && t < wave_tiles) {
+    if (t >= 0 && t < wave_tiles) {
       if constexpr (FIXED) softmax_fixed(t);
       else softmax(t);
     } else {
@@ -590,44 +533,42 @@ __device__ __forceinline__ bool pair_pass(const FwdArgs& a) {
     // of stale LDS contents would not be zero.
     g_ring[kSlots + 6][tid] = make_uint4(0, 0, 0, 0);
     g_ring[kSlots + 7][tid] = make_uint4(0, 0, 0, 0);
-    // vmcnt(8) (tile 0 has landed), or vmcnt(2) under the band schedule
-    // (tiles 0 .. 3: a row group may start up to 3 tiles in); lgkmcnt(0).
-    if constexpr (BAND) __builtin_amdgcn_s_waitcnt(0x0070 | 2);
-    else __builtin_amdgcn_s_waitcnt(0x0070 | 8);
+    // vmcnt(8) (tile 0 has landed), lgkmcnt(0).
+    __builtin_amdgcn_s_waitcnt(0x0070 | 8);
     barrier_lds();
     // Even-tile waves run MFMA phases at even p, odd-tile waves at odd p;
     // both run the same number of phases (and barriers).
-    const int n_phases = n_run + 2;
+    const int n_phases = n_tiles + 2;
     using M = std::false_type;  // matrix phase: no fills
     using F = std::true_type;   // vector phase: this wave fills
     if (par == 0) {
 #pragma nounroll
       for (int p = 0; p < n_phases; p += 8) {
         mphase(J0());                            sync(M());
-        fills(J1(), p + 1, F()); vphase(p + d);       sync(F());
+        fills(J1(), p + 1, F()); vphase(p);       sync(F());
         if (p + 2 >= n_phases) break;
         mphase(J2());                            sync(M());
-        fills(J3(), p + 3, F()); vphase(p + 2 + d);   sync(F());
+        fills(J3(), p + 3, F()); vphase(p + 2);   sync(F());
         if (p + 4 >= n_phases) break;
         mphase(J4());                            sync(M());
-        fills(J5(), p + 5, F()); vphase(p + 4 + d);   sync(F());
+        fills(J5(), p + 5, F()); vphase(p + 4);   sync(F());
         if (p + 6 >= n_phases) break;
         mphase(J6());                            sync(M());
-        fills(J7(), p + 7, F()); vphase(p + 6 + d);   sync(F());
+        fills(J7(), p + 7, F()); vphase(p + 6);   sync(F());
       }
     } else {
 #pragma nounroll
       for (int p = 0; p < n_phases; p += 8) {
-        fills(J0(), p, F());     vphase(p - 1 + d);   sync(F());
+        fills(J0(), p, F());     vphase(p - 1);   sync(F());
         mphase(J1());                            sync(M());
         if (p + 2 >= n_phases) break;
-        fills(J2(), p + 2, F()); vphase(p + 1 + d);   sync(F());
+        fills(J2(), p + 2, F()); vphase(p + 1);   sync(F());
         mphase(J3());                            sync(M());
         if (p + 4 >= n_phases) break;
-        fills(J4(), p + 4, F()); vphase(p + 3 + d);   sync(F());
+        fills(J4(), p + 4, F()); vphase(p + 3);   sync(F());
         mphase(J5());                            sync(M());
         if (p + 6 >= n_phases) break;
-        fills(J6(), p + 6, F()); vphase(p + 5 + d);   sync(F());
+        fills(J6(), p + 6, F()); vphase(p + 5);   sync(F());
         mphase(J7());                            sync(M());
       }
     }
@@ -682,9 +623,7 @@ __device__ __forceinline__ bool pair_pass(const FwdArgs& a) {
       for (int qb = 0; qb < 2; ++qb) {
         const float2 lm = g_lm[rg][qb][lane];
         const int qi = qw0 + 32 * qb + ln;
-        const int lo = BAND ? max(0, qi - wl) : 0;
-        const int hi = BAND ? min(kv_lim, qi + wr + 1) : kv_lim;
-        const bool keys = qi < q_len && lo < hi;
+        const bool keys = qi < q_len && kv_lim > 0;
         const bool ok = l[qb] + lm.x >= 0x1p-32f && l[qb] < 0x1p64f && lm.x < 0x1p64f;
         bad = bad || (keys && !ok);
       }
@@ -781,14 +720,13 @@ hipError_t launch_fwd_bf16_pair(const FwdArgs& a, hipStream_t s) {
   const long long blocks = (long long)n_qt * a.H * a.B;
   FwdArgs args = a;
   void* kargs[] = {&args};
+  // Restricted attention runs on the band kernel.
   const int mode = fwd_mode(a);
-  const void* fn = mode == kModeBand     ? reinterpret_cast<const void*>(&attn_fwd_bf16_pair_kernel<kModeBand>)
-                   : mode == kModeCausal ? reinterpret_cast<const void*>(&attn_fwd_bf16_pair_kernel<kModeCausal>)
-                                         : reinterpret_cast<const void*>(&attn_fwd_bf16_pair_kernel<kModeNone>);
-  const void* redo = mode == kModeBand ? reinterpret_cast<const void*>(&attn_fwd_bf16_pair_redo_kernel<kModeBand>)
-                     : mode == kModeCausal
-                         ? reinterpret_cast<const void*>(&attn_fwd_bf16_pair_redo_kernel<kModeCausal>)
-                         : reinterpret_cast<const void*>(&attn_fwd_bf16_pair_redo_kernel<kModeNone>);
+  if (mode == kModeBand) return hipErrorInvalidValue;
+  const void* fn = mode == kModeCausal ? reinterpret_cast<const void*>(&attn_fwd_bf16_pair_kernel<kModeCausal>)
+                                       : reinterpret_cast<const void*>(&attn_fwd_bf16_pair_kernel<kModeNone>);
+  const void* redo = mode == kModeCausal ? reinterpret_cast<const void*>(&attn_fwd_bf16_pair_redo_kernel<kModeCausal>)
+                                         : reinterpret_cast<const void*>(&attn_fwd_bf16_pair_redo_kernel<kModeNone>);
   hipError_t e = hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(kThreads), kargs, 0, s);
   if (e != hipSuccess) return e;
   return hipLaunchKernel(redo, dim3((unsigned)blocks), dim3(kThreads), kargs, 0, s);
