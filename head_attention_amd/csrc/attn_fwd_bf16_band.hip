@@ -301,16 +301,70 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_band_kernel(FwdArgs
       }
     }
   };
-  // Weights of tile T under the fixed pivot 0: x = s c, 2^x.
-  auto softmax_fixed = [&](int T) __attribute__((always_inline)) {
-    mask_tile(T);
+  // Weights of tile T under the fixed pivot 0: x = s c, 2^x.  The mask is
+  // plain VALU arithmetic folded into the scaling: a key at offset o of the
+  // tile (o = 4 hh + the register's compile-time offset) is allowed iff
+  // o < hi and o >= lo, i.e. iff t_hi = (hi - 1/2 - o) 2^120 and
+  // t_lo = (o - lo + 1/2) 2^120 are both positive, and x = s c + min(t_hi,
+  // t_lo, 0) in one FMA: exactly s c where allowed, at most -2^119 where
+  // not, whose 2^x is 0.  A lane's bound times 2^120 may round or overflow
+  // to +-inf only when it lies 2^23 or more from the tile, far from every
+  // offset, so the sign of t is always right.  Each bound applies only to
+  // tiles that cross it: a subtract and a min per score and bound.  (A
+  // compare-and-select costs two compares, a scalar AND and a select per
+  // score, chained through the scalar unit: about 0.5 us per masked phase.)
+  auto scale_mask = [&](int k0, auto hi_tag, auto lo_tag) __attribute__((always_inline)) {
+    constexpr bool HI = decltype(hi_tag)::value, LO = decltype(lo_tag)::value;
+    constexpr float kS = 0x1p120f;
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
+      if constexpr (HI || LO) {
+        // The row index from an opaque copy of the lane's: the bounds are
+        // rebuilt here rather than hoisted and held through the loop.
+        int lnm = ln;
+        asm volatile("" : "+v"(lnm));
+        const int qi = qw0 + 32 * qb + lnm;
+        float hi = HI ? ((float)(min(kv_lim, qi + wr + 1) - k0 - 4 * hh) - 0.5f) * kS : 0.f;
+        float lo = LO ? ((float)(max(0, qi - wl) - k0 - 4 * hh) - 0.5f) * kS : 0.f;
+        // Opaque, so that hi - o stays a subtract of a literal instead of
+        // being fused into the product above with o held in a register.
+        asm volatile("" : "+v"(hi), "+v"(lo));
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sc[kb][qb][r] *= c;
+          for (int r = 0; r < 16; ++r) {
+            const float o = (float)(32 * kb + 8 * (r >> 2) + (r & 3)) * kS;
+            float pen = 0.f;
+            if constexpr (HI) pen = fminf(pen, hi - o);
+            if constexpr (LO) pen = fminf(pen, o - lo);
+            sc[kb][qb][r] = fmaf(sc[kb][qb][r], c, pen);
+          }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sc[kb][qb][r] *= c;
+      }
       exp_pack(sc[0][qb], sc[1][qb], pk[qb]);
+    }
+  };
+  auto softmax_fixed = [&](int T) __attribute__((always_inline)) {
+    const int k0 = (t0 + T) * kBN;
+    const bool need_hi = k0 + kBN > kv_lim || k0 + kBN - 1 > qw0 + wr;
+    const bool need_lo = k0 < 0 || k0 < qw0 + kWaveRows - 1 - wl;
+    using Y = std::true_type;
+    using N = std::false_type;
+    if (need_hi && need_lo) {
+      asm volatile("");
+      scale_mask(k0, Y(), Y());
+    } else if (need_hi) {
+      asm volatile("");
+      scale_mask(k0, Y(), N());
+    } else if (need_lo) {
+      asm volatile("");
+      scale_mask(k0, N(), Y());
+    } else {
+      scale_mask(k0, N(), N());
     }
   };
   // Weights of tile T under the moving pivot (the paired kernel's): the
