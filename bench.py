@@ -378,7 +378,7 @@ def _short_kernel(name: str) -> str:
     the bool-templated kernels -> <true|false>; other kernels of the library by
     their plain name."""
     import re
-    m = re.search(r"(attn_fwd_bf16(?:_pair(?:_redo)?|_short)?_kernel|bwd_dkdv_kernel|bwd_dq_kernel)(?:<|ILi)(\d)", name)
+    m = re.search(r"(attn_fwd_bf16(?:_pair|_short)?_kernel|bwd_dkdv_kernel|bwd_dq_kernel)(?:<|ILi)(\d)", name)
     if m:
         return f"{m.group(1)}<{FWD_MODES[m.group(2)]}>"
     m = re.search(r"(attn_fwd_bf16(?:_pair|_short)?_kernel|proj_gemm_kernel|bwd_dkdv_kernel|bwd_dq_kernel)<(true|false)", name) or \
@@ -416,7 +416,6 @@ LEG_GRIDS = {("attn_fwd_bf16_short_kernel<none>", 65536): "encoder_base",
              ("proj_gemm_kernel<true>", 81920): "mha_proj (cross K, V)",
              ("proj_gemm_kernel<false>", 65536): "mha_proj (self and cross output)",
              ("attn_fwd_bf16_pair_kernel<causal>", 262144): "long_causal",
-             ("attn_fwd_bf16_pair_redo_kernel<causal>", 262144): "long_causal (redo pass, exits)",
              ("decode_partial_kernel", 4194304): "kv_decode",
              ("decode_merge_kernel", 65536): "kv_decode",
              ("attn_fwd_bf16_short_kernel<none>", 256): "launch floor (1-row forward)",

@@ -6,16 +6,14 @@
 // O^T += V^T P^T on v_mfma_f32_32x32x16_bf16, weights exp2(s c - m c), bf16
 // weights, fp32 accumulation.
 //
-// Two kernels per call.  The first forms every weight under a fixed pivot
-// m = 0 -- one multiply and one exponential per score, no row maxima -- and
-// checks at the end that every row's sum stayed in a range where that pivot
-// is exact up to rounding (softmax does not depend on the pivot).  A
-// workgroup with a row outside it (logits beyond about +64 or below about
-// -32 in log2 units: rare, adversarial inputs) writes a mark instead of its
-// results, and the second kernel, launched right after on the same grid,
-// recomputes exactly those workgroups with a pivot that moves to the row
-// maximum (the lazy pivot of the other bf16 kernels); every other workgroup
-// of the second kernel exits at once.
+// The pipeline forms every weight under a fixed pivot m = 0 -- one multiply
+// and one exponential per score, no row maxima -- and checks at the end that
+// every row's sum stayed in a range where that pivot is exact up to rounding
+// (softmax does not depend on the pivot).  A row group with a row outside it
+// (logits beyond about +64 or below about -32 in log2 units: rare,
+// adversarial inputs) is recomputed in the same launch, one tile at a time,
+// with a pivot that moves to the row maximum (the lazy pivot of the other
+// bf16 kernels).
 //
 // Workgroup: 8 waves own 256 query rows of one (b, h).  The hardware puts
 // waves w and w + 4 on the same SIMD; both take the same 64 rows (row group
@@ -83,8 +81,8 @@ __shared__ uint4 g_ring[2 * kSlots][512];
 constexpr int kAhead = 5;
 // Row sums and pivots of the odd-tile waves for the final merge.
 __shared__ float2 g_lm[4][2][64];
-// Set when a row failed the fixed-pivot range check.
-__shared__ int g_redo;
+// Per row group: a row failed the fixed-pivot range check.
+__shared__ int g_bad[4];
 
 // LDS byte address of ring row r (K of slot r, or V of slot r - 8), kept
 // as an integer so that a slot chosen at run time costs one add.
@@ -117,11 +115,11 @@ __device__ __forceinline__ void wg_tile(const FwdArgs& a, int bid, int& bh, int&
   qt = MODE == kModeCausal ? (n_qt - 1 - rank) : rank;
 }
 
-// One workgroup's computation.  FIXED: the weights under the fixed pivot 0,
-// then a range check of every row; returns false, having written nothing,
-// when a row fails it.  Otherwise: the moving pivot, which always succeeds.
-template <int MODE, bool FIXED>
-__device__ __forceinline__ bool pair_pass(const FwdArgs& a) {
+// One workgroup's computation: the weights under the fixed pivot 0, then a
+// range check of every row; a row group with a row that fails it is
+// recomputed under the moving pivot.
+template <int MODE>
+__global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_pair_kernel(FwdArgs a) {
   constexpr bool CAUSAL = MODE == kModeCausal;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -250,10 +248,9 @@ __device__ __forceinline__ bool pair_pass(const FwdArgs& a) {
   // of 4 keys: lane i of 16-lane group g names row (key) kr and 8-byte chunk
   // h, and the read returns to lane i the 4 keys kr - i/4 .. +3 of d = dbase
   // + i.
-  auto load_v_step = [&](auto slot_tag, auto j_tag, bf16x8 (&va)[2][4]) __attribute__((always_inline)) {
-    constexpr int S = decltype(slot_tag)::value;
+  auto load_v_at = [&](uint32_t vbase, auto j_tag, bf16x8 (&va)[2][4]) __attribute__((always_inline)) {
     constexpr int j = decltype(j_tag)::value;
-    const lds_char* vt = (const lds_char*)(uintptr_t)ring_addr(kSlots + S);
+    const lds_char* vt = (const lds_char*)(uintptr_t)vbase;
     const int g = lane >> 4;
     const int i = lane & 15;
 #pragma unroll
@@ -271,15 +268,21 @@ __device__ __forceinline__ bool pair_pass(const FwdArgs& a) {
   };
   // K: [key block][d-step]; lane (ln, hh) holds K[32 kb + ln][16 s + 8 hh +
   // 0..7].
-  auto load_k_step = [&](auto slot_tag, auto s_tag, bf16x8 (&ka)[2][4]) __attribute__((always_inline)) {
-    constexpr int S = decltype(slot_tag)::value;
+  auto load_k_at = [&](uint32_t kbase, auto s_tag, bf16x8 (&ka)[2][4]) __attribute__((always_inline)) {
     constexpr int s = decltype(s_tag)::value;
-    const lds_uint4* kt = (const lds_uint4*)(uintptr_t)ring_addr(S);
+    const lds_uint4* kt = (const lds_uint4*)(uintptr_t)kbase;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int row = 32 * kb + ln;
       ka[kb][s] = __builtin_bit_cast(bf16x8, kt[row * 8 + ((2 * s + hh) ^ k_swz(row))]);
     }
+  };
+  // The same from ring slot S (K) or kSlots + S (V).
+  auto load_v_step = [&](auto slot_tag, auto j_tag, bf16x8 (&va)[2][4]) __attribute__((always_inline)) {
+    load_v_at(ring_addr(kSlots + decltype(slot_tag)::value), j_tag, va);
+  };
+  auto load_k_step = [&](auto slot_tag, auto s_tag, bf16x8 (&ka)[2][4]) __attribute__((always_inline)) {
+    load_k_at(ring_addr(decltype(slot_tag)::value), s_tag, ka);
   };
   // O^T += V^T P^T for key step j, and the row sums of that step's weights.
   auto pv_step = [&](auto j_tag, const bf16x8 (&va)[2][4]) __attribute__((always_inline)) {
@@ -496,8 +499,7 @@ __device__ __forceinline__ bool pair_pass(const FwdArgs& a) {
   // phase before this wave's first tile or past its last.
   auto vphase = [&](int t) __attribute__((always_inline)) {
     if (t >= 0 && t < wave_tiles) {
-      if constexpr (FIXED) softmax_fixed(t);
-      else softmax(t);
+      softmax_fixed(t);
     } else {
       // Zeros written from inline assembly: a plain 0 here is a constant
       // the compiler materialises before the branch, in every phase.
@@ -587,13 +589,16 @@ __device__ __forceinline__ bool pair_pass(const FwdArgs& a) {
   // Full row sums in the row layout: lane (ln, hh) takes query ln's sum from
   // lane ln % 16, register ln / 16.
   float l[2];
+  auto row_sums = [&]() __attribute__((always_inline)) {
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const float v0 = __int_as_float(__builtin_amdgcn_ds_bpermute((lane & 15) * 4, __float_as_int(ls[qb][0])));
-    const float v1 = __int_as_float(__builtin_amdgcn_ds_bpermute((lane & 15) * 4, __float_as_int(ls[qb][1])));
-    l[qb] = (ln < 16) ? v0 : v1;
-  }
-  if (par == 1) {
+    for (int qb = 0; qb < 2; ++qb) {
+      const float v0 = __int_as_float(__builtin_amdgcn_ds_bpermute((lane & 15) * 4, __float_as_int(ls[qb][0])));
+      const float v1 = __int_as_float(__builtin_amdgcn_ds_bpermute((lane & 15) * 4, __float_as_int(ls[qb][1])));
+      l[qb] = (ln < 16) ? v0 : v1;
+    }
+  };
+  // The odd-tile wave's (O, l, m) into the merge area.
+  auto hand_over = [&]() __attribute__((always_inline)) {
     static_for<16>([&](auto vg_tag) {
       constexpr int VG = decltype(vg_tag)::value;
       constexpr int DB = VG / 8, QB = (VG / 4) % 2, R = 4 * (VG % 4);
@@ -601,116 +606,157 @@ __device__ __forceinline__ bool pair_pass(const FwdArgs& a) {
     });
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) g_lm[rg][qb][lane] = make_float2(l[qb], mc[qb]);
-  }
-  if constexpr (FIXED) {
-    if (tid == 0) g_redo = 0;
-  }
+  };
+  // The even-tile wave merges and stores:
+  // O = (2^(mA - M) O_A + 2^(mB - M) O_B) / (2^(mA - M) l_A + 2^(mB - M) l_B)
+  // with M = max(mA, mB); 2^0 = 1 exactly, and both pivots are finite.  Row
+  // log-sum-exp (M + log2 l) ln 2; -inf for padded or keyless rows.
+  // Register r of block (db, qb) holds d = 32 db + 8 (r / 4) + 4 hh + r % 4
+  // of query row qw0 + 32 qb + ln: four consecutive d per 8-byte store;
+  // padded rows and rows with no allowed key are written as exact zeros.
+  // The output addresses are rebuilt from a fresh copy of the lane's row
+  // index instead of being held in registers through the tile loop.
+  auto merge_store = [&]() __attribute__((always_inline)) {
+    float fa[2], fb[2], inv[2];
+    bool live[2];
+    int ln_e = ln;
+    asm volatile("" : "+v"(ln_e));
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const float2 lm = g_lm[rg][qb][lane];
+      const bool ea = l[qb] > 0.f, eb = lm.x > 0.f;
+      const float M = ea ? (eb ? fmaxf(mc[qb], lm.y) : mc[qb]) : lm.y;
+      fa[qb] = ea ? __builtin_amdgcn_exp2f(mc[qb] - M) : 0.f;
+      fb[qb] = eb ? __builtin_amdgcn_exp2f(lm.y - M) : 0.f;
+      const float l_row = fa[qb] * l[qb] + fb[qb] * lm.x;
+      const int qi = qw0 + 32 * qb + ln_e;
+      live[qb] = qi < q_len && l_row > 0.f;
+      inv[qb] = live[qb] ? 1.f / l_row : 0.f;
+      if (a.lse && hh == 0 && qi < a.n_q)
+        a.lse[(size_t)bh * a.n_q + qi] = live[qb] ? (M + __builtin_amdgcn_logf(l_row)) * kLn2 : -INFINITY;
+    }
+    static_for<16>([&](auto vg_tag) {
+      constexpr int VG = decltype(vg_tag)::value;
+      constexpr int DB = VG / 8, QB = (VG / 4) % 2, G = VG % 4, R = 4 * G;
+      const int qi = qw0 + 32 * QB + ln_e;
+      const float4 ob = *mptr(vg_tag);
+      const float x0 = (fa[QB] * o[DB][QB][R] + fb[QB] * ob.x) * inv[QB];
+      const float x1 = (fa[QB] * o[DB][QB][R + 1] + fb[QB] * ob.y) * inv[QB];
+      const float x2 = (fa[QB] * o[DB][QB][R + 2] + fb[QB] * ob.z) * inv[QB];
+      const float x3 = (fa[QB] * o[DB][QB][R + 3] + fb[QB] * ob.w) * inv[QB];
+      if (qi < a.n_q) {
+        uint2 w;
+        w.x = live[QB] ? pack_bf16x2(x0, x1) : 0u;
+        w.y = live[QB] ? pack_bf16x2(x2, x3) : 0u;
+        *reinterpret_cast<uint2*>(O + (size_t)qi * kHeadDim + 32 * DB + 8 * G + 4 * hh) = w;
+      }
+    });
+  };
+
+  row_sums();
+  if (par == 1) hand_over();
   __syncthreads();
-  if constexpr (FIXED) {
+  if (par == 0) {
     // Range check of the fixed pivot.  Under pivot 0 every weight of a row
     // is at most its sum l, so l_A, l_B < 2^64 bounds every weight, partial
     // sum and product below fp32 overflow (a weight of 2^128 or more shows
     // as l = inf, NaN as a NaN sum).  l_A + l_B >= 2^-32 puts the row's
-    // largest weight at 2^-56 or more (a row has fewer than 2^24 keys), so a
-    // weight that fell into the subnormal range is below 2^-70 of it and
+    // largest weight at 2^-56 or more (a row has fewer than 2^24 keys), so
+    // a weight that fell into the subnormal range is below 2^-70 of it and
     // changes no result.  A row with an allowed key that fails either bound
-    // -- logits far above 64 or far below -32 in log2 units -- sends the
-    // whole workgroup to the moving-pivot pass.  Rows without an allowed key
-    // (padded, kv_len = 0, an empty window) are zeros either way.
-    if (par == 0) {
-      bool bad = false;
+    // -- logits far above 64 or far below -32 in log2 units -- sends its row
+    // group to the moving-pivot recomputation below.  Rows without an
+    // allowed key (padded, kv_len = 0) are zeros either way.  The bounds
+    // come from a fresh copy of the lane's row index.
+    int ln_c = ln;
+    asm volatile("" : "+v"(ln_c));
+    bool bad = false;
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const float2 lm = g_lm[rg][qb][lane];
-        const int qi = qw0 + 32 * qb + ln;
-        const bool keys = qi < q_len && kv_lim > 0;
-        const bool ok = l[qb] + lm.x >= 0x1p-32f && l[qb] < 0x1p64f && lm.x < 0x1p64f;
-        bad = bad || (keys && !ok);
+    for (int qb = 0; qb < 2; ++qb) {
+      const float2 lm = g_lm[rg][qb][lane];
+      const int qi = qw0 + 32 * qb + ln_c;
+      const bool keys = qi < q_len && kv_lim > 0;
+      const bool in_range = l[qb] + lm.x >= 0x1p-32f && l[qb] < 0x1p64f && lm.x < 0x1p64f;
+      bad = bad || (keys && !in_range);
+    }
+    // The ballot with every lane active (inside the lane-0 branch it would
+    // see lane 0 alone).
+    const bool group_bad = __builtin_amdgcn_ballot_w64(bad) != 0;
+    if (lane == 0) g_bad[rg] = group_bad;
+    // Stored whatever the check found: a row group that failed it stores
+    // again below, over these rows (same wave, program order).  Storing
+    // first lets the loop's accumulators die before the recomputation,
+    // which would not fit the registers beside them.
+    merge_store();
+  }
+  // Every verdict is in g_bad, and every merge-area read is done.
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  barrier_lds();
+  if (__builtin_amdgcn_readfirstlane(g_bad[0] | g_bad[1] | g_bad[2] | g_bad[3]) == 0) return;
+
+  // ---- some row group failed the range check: its two waves take their
+  // tiles again (even, odd), under the moving pivot, one tile at a time
+  // through ring slots `wave` (K) and 8 + `wave` (V), then merge as above.
+  // The split, the order of the tiles and of the products, and the merge
+  // are those of the pipeline, so a row whose pivot never moves gets the
+  // same bits as there.  Each wave fills whole tiles itself; the
+  // workgroup's barriers stay uniform (every wave passes them).
+  const bool mine = __builtin_amdgcn_readfirstlane(g_bad[rg]) != 0;
+  if (mine) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      mc[i] = 0.f;
+      ls[i] = f32x4{};
+      seen[i] = false;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) o[i][j] = f32x16{};
+    }
+    const uint32_t kdst = ring_addr(wave), vdst = ring_addr(kSlots + wave);
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using I3 = std::integral_constant<int, 3>;
+#pragma nounroll
+    for (int t = par; t < wave_tiles; t += 2) {
+      // Fill offsets from a fresh copy of the lane index each tile: held
+      // through the loop they would not fit the registers.
+      int lf = lane;
+      asm volatile("" : "+v"(lf));
+      const int qrow = lf >> 3, fp = lf & 7;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int r = 8 * j + qrow;
+        const uint32_t roff = (uint32_t)t * kTileBytes + (uint32_t)r * kRowBytes;
+        lds_fill16_at(rk, kdst + 1024u * j, roff + 16u * (uint32_t)(fp ^ k_swz(r)));
+        lds_fill16_at(rv, vdst + 1024u * j, roff + 16u * (uint32_t)(fp ^ (2 * (r & 3))));
       }
-      if (__builtin_amdgcn_ballot_w64(bad) != 0 && lane == 0) g_redo = 1;
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): both tiles have landed
+      bf16x8 ka[2][4];
+      load_k_at(kdst, I0(), ka);
+      load_k_at(kdst, I1(), ka);
+      load_k_at(kdst, I2(), ka);
+      load_k_at(kdst, I3(), ka);
+      qk_smajor(ka);
+      softmax(t);
+      bf16x8 va[2][4];
+      load_v_at(vdst, I0(), va);
+      load_v_at(vdst, I1(), va);
+      load_v_at(vdst, I2(), va);
+      load_v_at(vdst, I3(), va);
+      pv_step(I0(), va);
+      pv_step(I1(), va);
+      pv_step(I2(), va);
+      pv_step(I3(), va);
     }
-    __syncthreads();
-    if (__builtin_amdgcn_readfirstlane(g_redo) != 0) return false;
+    row_sums();
   }
-  if (par == 1) return true;
-
-  // O = (2^(mA - M) O_A + 2^(mB - M) O_B) / (2^(mA - M) l_A + 2^(mB - M) l_B)
-  // with M = max(mA, mB); 2^0 = 1 exactly, and both pivots are finite.
-  float fa[2], fb[2], inv[2];
-  bool live[2];
-  // A fresh copy of the lane's row index: the output addresses are rebuilt
-  // from it here instead of being held in registers through the tile loop.
-  int ln_e = ln;
-  asm volatile("" : "+v"(ln_e));
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const float2 lm = g_lm[rg][qb][lane];
-    const bool ea = l[qb] > 0.f, eb = lm.x > 0.f;
-    const float M = ea ? (eb ? fmaxf(mc[qb], lm.y) : mc[qb]) : lm.y;
-    fa[qb] = ea ? __builtin_amdgcn_exp2f(mc[qb] - M) : 0.f;
-    fb[qb] = eb ? __builtin_amdgcn_exp2f(lm.y - M) : 0.f;
-    const float l_row = fa[qb] * l[qb] + fb[qb] * lm.x;
-    const int qi = qw0 + 32 * qb + ln_e;
-    live[qb] = qi < q_len && l_row > 0.f;
-    inv[qb] = live[qb] ? 1.f / l_row : 0.f;
-    // Row log-sum-exp (M + log2 l) ln 2; -inf for padded or keyless rows.
-    if (a.lse && hh == 0 && qi < a.n_q)
-      a.lse[(size_t)bh * a.n_q + qi] = live[qb] ? (M + __builtin_amdgcn_logf(l_row)) * kLn2 : -INFINITY;
-  }
-  // Register r of block (db, qb) holds d = 32 db + 8 (r / 4) + 4 hh + r % 4
-  // of query row qw0 + 32 qb + ln: four consecutive d per 8-byte store.
-  // Padded rows and rows with no allowed key are written as exact zeros.
-  static_for<16>([&](auto vg_tag) {
-    constexpr int VG = decltype(vg_tag)::value;
-    constexpr int DB = VG / 8, QB = (VG / 4) % 2, G = VG % 4, R = 4 * G;
-    const int qi = qw0 + 32 * QB + ln_e;
-    const float4 ob = *mptr(vg_tag);
-    const float x0 = (fa[QB] * o[DB][QB][R] + fb[QB] * ob.x) * inv[QB];
-    const float x1 = (fa[QB] * o[DB][QB][R + 1] + fb[QB] * ob.y) * inv[QB];
-    const float x2 = (fa[QB] * o[DB][QB][R + 2] + fb[QB] * ob.z) * inv[QB];
-    const float x3 = (fa[QB] * o[DB][QB][R + 3] + fb[QB] * ob.w) * inv[QB];
-    if (qi < a.n_q) {
-      uint2 w;
-      w.x = live[QB] ? pack_bf16x2(x0, x1) : 0u;
-      w.y = live[QB] ? pack_bf16x2(x2, x3) : 0u;
-      *reinterpret_cast<uint2*>(O + (size_t)qi * kHeadDim + 32 * DB + 8 * G + 4 * hh) = w;
-    }
-  });
-  return true;
-}
-
-// Marks a workgroup whose rows failed the fixed-pivot range check: the
-// first pass writes it into the first element of the workgroup's first
-// output row, in place of its results, and the second kernel finds it there.
-// (A result that happens to carry the same bits -- a NaN -- only makes the
-// second kernel recompute that workgroup, to the same result.)
-constexpr uint16_t kRedoMark = 0xFFFFu;
-
-// First pass: the fixed pivot.  No fallback code lives in this kernel (a
-// second copy of the pipeline, inlined or called, costs registers or
-// per-lane scratch memory, and a kernel that needs scratch is dispatched
-// more slowly).
-template <int MODE>
-__global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_pair_kernel(FwdArgs a) {
-  if (!pair_pass<MODE, true>(a) && threadIdx.x == 0) {
-    int bh, qt;
-    wg_tile<MODE>(a, blockIdx.x, bh, qt);
-    uint16_t* O = static_cast<uint16_t*>(a.O) + ((size_t)bh * a.n_q + (size_t)qt * kBM) * kHeadDim;
-    *O = kRedoMark;
-  }
-}
-
-// Second kernel, launched right after the first on the same stream with the
-// same grid: a workgroup whose mark is set runs the moving-pivot pass; all
-// others exit at once.
-template <int MODE>
-__global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_pair_redo_kernel(FwdArgs a) {
-  int bh, qt;
-  wg_tile<MODE>(a, blockIdx.x, bh, qt);
-  const uint16_t* O = static_cast<const uint16_t*>(a.O) + ((size_t)bh * a.n_q + (size_t)qt * kBM) * kHeadDim;
-  if (__builtin_amdgcn_readfirstlane(*O) != kRedoMark) return;
-  __syncthreads();  // every wave has read the mark before any output is rewritten
-  pair_pass<MODE, false>(a);
+  // The merge area overlaps the slots just used.
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  barrier_lds();
+  if (mine && par == 1) hand_over();
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  barrier_lds();
+  if (mine && par == 0) merge_store();
 }
 
 }  // namespace
@@ -725,11 +771,7 @@ hipError_t launch_fwd_bf16_pair(const FwdArgs& a, hipStream_t s) {
   if (mode == kModeBand) return hipErrorInvalidValue;
   const void* fn = mode == kModeCausal ? reinterpret_cast<const void*>(&attn_fwd_bf16_pair_kernel<kModeCausal>)
                                        : reinterpret_cast<const void*>(&attn_fwd_bf16_pair_kernel<kModeNone>);
-  const void* redo = mode == kModeCausal ? reinterpret_cast<const void*>(&attn_fwd_bf16_pair_redo_kernel<kModeCausal>)
-                                         : reinterpret_cast<const void*>(&attn_fwd_bf16_pair_redo_kernel<kModeNone>);
-  hipError_t e = hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(kThreads), kargs, 0, s);
-  if (e != hipSuccess) return e;
-  return hipLaunchKernel(redo, dim3((unsigned)blocks), dim3(kThreads), kargs, 0, s);
+  return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(kThreads), kargs, 0, s);
 }
 
 }  // namespace headattn

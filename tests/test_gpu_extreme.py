@@ -142,3 +142,21 @@ def test_mixed_workgroups(radius):
     say(f"[mixed workgroups radius={radius}] B{B} H{H} n{n}")
     out, ref = _run(Q, K, V, mask, None, radius)
     check(out, ref, BF16, f"mixed workgroups radius={radius}")
+
+
+@pytest.mark.parametrize("radius", [None, 300], ids=["paired", "band"])
+def test_few_extreme_rows(radius):
+    """A handful of rows with logits far above 64 (log2 units) inside row
+    groups whose other rows are ordinary -- none of them the first row of
+    its 32-row block: the fixed-pivot range check must flag the whole group
+    whichever lanes hold the failing rows, and the recomputation must give
+    every row of the group, extreme or ordinary, its softmax."""
+    B, H, n = 1, 2, 700
+    g = workloads.generator(5300)
+    Q, K, V = (workloads.randn(g, (B, H, n, 64), BF16) for _ in range(3))
+    for r in (37, 251, 252, 253, 254, 255, 600):
+        Q[:, :, r] = 1000.0
+    mask = 2 if radius is None else ha.ATTN_MASK_RESTRICTED | ha.ATTN_MASK_CAUSAL
+    say(f"[few extreme rows radius={radius}] B{B} H{H} n{n}")
+    out, ref = _run(Q, K, V, mask, None, radius)
+    check(out, ref, BF16, f"few extreme rows radius={radius}")
