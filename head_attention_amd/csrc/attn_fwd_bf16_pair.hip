@@ -178,27 +178,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_pair_kernel(FwdArgs
   // ---- Q fragments: B operand of S^T = K Q^T for query block qb and d-step
   // s: lane (ln, hh) holds Q[qw0 + 32 qb + ln][16 s + 8 hh + 0..7], sign of
   // scale folded in; c = |scale| log2(e), floored at 2^-100 (below that
-  // every weight is exactly 1.0f either way).
+  // every weight is exactly 1.0f either way).  Q goes through LDS, filled
+  // with the first tiles (see the prologue); its descriptor ends at q_len,
+  // so padded query rows (i >= q_len, written as zeros) enter as zeros: the
+  // row-sum products multiply other rows' weights by 0, which must not meet
+  // NaN from padded memory.
   const float c = fmaxf(fabsf(a.scale) * kLog2e, 0x1p-100f);
   const uint32_t sign = a.scale < 0.f ? 0x80008000u : 0u;
+  const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<__bf16*>(Q), (short)0, (int)((uint32_t)max(0, q_len) * kRowBytes), kBufferWord3);
   bf16x8 qf[2][4];
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int qi = qw0 + 32 * qb + ln;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      uint4 v = make_uint4(0, 0, 0, 0);
-      // Padded query rows (i >= q_len, written as zeros) enter as zeros: the
-      // row-sum products multiply other rows' weights by 0, which must not
-      // meet NaN from padded memory.
-      if (qi < q_len) v = *reinterpret_cast<const uint4*>(Q + (size_t)qi * kHeadDim + 16 * s + 8 * hh);
-      v.x ^= sign;
-      v.y ^= sign;
-      v.z ^= sign;
-      v.w ^= sign;
-      qf[qb][s] = __builtin_bit_cast(bf16x8, v);
-    }
-  }
 
   // ---- per-wave softmax state.  Accumulator register r of a 32x32 block
   // holds row/column 8 (r / 4) + 4 hh + r % 4 of the block's M side and
@@ -519,7 +508,18 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_pair_kernel(FwdArgs
   using J7 = std::integral_constant<int, 7>;
 
   if (n_tiles > 0) {
-    // Prologue: tiles 0 .. 4 (K and V) as if filled at phases -5 .. -1.
+    // Prologue: this row group's 64 Q rows (the wave of parity p fills rows
+    // 32 p .. 32 p + 31, in a K tile's layout) into a slot the ring first
+    // fills at phase 0 or later -- K 5, 6, 7 or V 5 -- then tiles 0 .. 4 (K
+    // and V) as if filled at phases -5 .. -1.  Q lands first, so the first
+    // products wait for Q and tile 0 together, not one after the other.
+    const uint32_t qdst = ring_addr(rg < 3 ? 5 + rg : kSlots + 5);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 32 * par + 8 * i + (lane >> 3);
+      lds_fill16_at(rq, qdst + 4096u * par + 1024u * i,
+                    (uint32_t)(qw0 + r) * kRowBytes + 16u * (uint32_t)(fpos ^ k_swz(r)));
+    }
     fill_k(J0(), 0);
     fill_v(J0(), 0);
     fill_k(J1(), 1);
@@ -535,7 +535,28 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_pair_kernel(FwdArgs
     // of stale LDS contents would not be zero.
     g_ring[kSlots + 6][tid] = make_uint4(0, 0, 0, 0);
     g_ring[kSlots + 7][tid] = make_uint4(0, 0, 0, 0);
-    // vmcnt(8) (tile 0 has landed), lgkmcnt(0).
+    // vmcnt(10): this wave's Q fills have landed; after the barrier, the
+    // pair's.
+    __builtin_amdgcn_s_waitcnt(0x0F70 | 10);
+    barrier_lds();
+    {
+      const lds_uint4* qs = (const lds_uint4*)(uintptr_t)qdst;
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const int row = 32 * qb + ln;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          uint4 v = __builtin_bit_cast(uint4, qs[row * 8 + ((2 * s + hh) ^ k_swz(row))]);
+          v.x ^= sign;
+          v.y ^= sign;
+          v.z ^= sign;
+          v.w ^= sign;
+          qf[qb][s] = __builtin_bit_cast(bf16x8, v);
+        }
+      }
+    }
+    // vmcnt(8) (tile 0 has landed), lgkmcnt(0): Q is in registers, and its
+    // slots may be refilled after this barrier.
     __builtin_amdgcn_s_waitcnt(0x0070 | 8);
     barrier_lds();
     // Even-tile waves run MFMA phases at even p, odd-tile waves at odd p;
