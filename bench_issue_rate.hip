@@ -219,7 +219,9 @@ __global__ __launch_bounds__(512, 1) void two_waves_lds(const float* in, float* 
 // issues two 16-byte-per-lane buffer loads into LDS per tile (8 KB of K and
 // 8 KB of V per workgroup), into one of four 16 KB slots at 32 KB..96 KB
 // that the products never read, and waits for those of four tiles ago
-// (vmcnt(8)) before the barrier
+// (vmcnt(8)) before the barrier.  Source offsets wrap with a mask (src_bytes
+// is a power of two): a modulo by the run-time size would add an integer
+// division's worth of vector instructions per tile to both waves.
 template <int TWO>
 __global__ __launch_bounds__(512, 1) void two_waves_fill(const float* in, float* out, uint64_t* cyc, int iters,
                                                         const void* src, int src_bytes) {
@@ -237,7 +239,7 @@ __global__ __launch_bounds__(512, 1) void two_waves_fill(const float* in, float*
     for (int h = 0; h < 2; ++h) {
       const int t = it + h;
       const uint32_t slot = lds0 + (uint32_t)(t & 3) * 16384u + 1024u * wave;
-      const uint32_t goff = ((uint32_t)t * 16384u + 1024u * wave + 16u * lane) % (uint32_t)src_bytes;
+      const uint32_t goff = ((uint32_t)t * 16384u + 1024u * wave + 16u * lane) & ((uint32_t)src_bytes - 1u);
       asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" :: "s"(__builtin_amdgcn_readfirstlane(slot)), "v"(goff), "s"(rs) : "memory");
       asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" :: "s"(__builtin_amdgcn_readfirstlane(slot + 8192u)), "v"(goff + 8192u), "s"(rs) : "memory");
       if (par == h) mfma_tile_lds(s, lane); else valu_tile<0>(s);

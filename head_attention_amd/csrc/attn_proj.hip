@@ -9,8 +9,10 @@
 //                           the [B, h, n, 64] attention output in place (no
 //                           concatenation copy).
 //
-// Both are one GEMM kernel, C^T = W A^T with W [N, K] (one row per output
-// feature, k contiguous) and A [M, K] (one row per token): on
+// Both run on one GEMM, C^T = W A^T with W [N, K] (one row per output
+// feature, k contiguous) and A [M, K] (one row per token), in two kernels
+// (the 4-wave kernel below, and an 8-wave kernel with larger tiles for
+// shapes whose 4-wave tiles would load the compute units unevenly): on
 // v_mfma_f32_32x32x16_bf16 the A operand is a W fragment and the B operand
 // an A fragment, both 16 contiguous bytes of a k-contiguous row, and each
 // lane ends up holding four consecutive output features of one token -- one
@@ -26,6 +28,7 @@
 // the descriptor's range check.  For the output projection two K steps make
 // one head, so the A tile of a step is a 32-wide column band of one head's
 // [n, 64] slab: a per-row offset, no gather of single elements.
+#include <algorithm>
 #include <type_traits>
 
 #include "kernel_util.h"
@@ -250,6 +253,231 @@ __global__ __launch_bounds__(kThreads, 2) void proj_gemm_kernel(ProjArgs a) {
   }
 }
 
+// ---- large shapes: one 8-wave workgroup per compute unit.  The tile is TM
+// tokens x TN features with TM + TN = 448 rows per k step, the waves on a
+// WM x WN grid (WM WN = 8), each owning 32 TBW tokens x 32 FBW features:
+// 256 x 192 (WM 4, TBW 2, FBW 3) or 320 x 128 (WM 2, TBW 5, FBW 1).  A
+// shape whose tiles of that size number about the compute units (the
+// decoder's self Q, K, V at 4096 x 3072 makes exactly 256 of 256 x 192)
+// then gives every compute unit the same work, where the 4-wave kernel's
+// tiles leave some compute units two and others one.  Two waves per SIMD,
+// as in the 4-wave kernel at two workgroups per compute unit.  K runs in
+// steps of 32 through a ring of five slots (28 KB each), filled four steps
+// ahead by LDS-direct buffer loads, one bare barrier per step.
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
+constexpr int kRows8 = 448;
+constexpr int kSlots8 = 5;
+constexpr uint32_t kSlotBytes8 = kRows8 * kStepBytes;
+__shared__ uint4 g_ring8[kSlots8 * kRows8 * 4];
+
+__device__ __forceinline__ uint32_t ring8_addr(int slot) {
+  return (uint32_t)(uintptr_t)(lds_void_t*)&g_ring8[0] + (uint32_t)slot * kSlotBytes8;
+}
+
+template <bool HEAD_OUT, int WM, int TBW, int FBW>
+__global__ __launch_bounds__(512, 1) void proj_gemm8_kernel(ProjArgs a) {
+  constexpr int WN = 8 / WM;
+  constexpr int TM = 32 * TBW * WM;  // tokens per workgroup
+  constexpr int TN = 32 * FBW * WN;  // output features per workgroup
+  static_assert(WM * WN == 8 && TM + TN == kRows8, "tile shape");
+  constexpr int kFillW = TN / 16;          // fill instructions of the W rows
+  constexpr int kFill = kRows8 / 16;       // fill instructions per step (28)
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int ln = lane & 31;
+  const int hh = lane >> 5;
+  const int wn = wave % WN;  // feature group of the tile
+  const int wm = wave / WN;  // token group of the tile
+
+  // Tile of this workgroup, XCD-aware as in the 4-wave kernel.
+  const int n_blocks = (a.N + TN - 1) / TN;
+  int nb = blockIdx.x % n_blocks;
+  int mb = blockIdx.x / n_blocks;
+  if (a.xcd_fp > 0) {
+    const int fp = a.xcd_fp;
+    const int x = blockIdx.x & 7;
+    const int l = blockIdx.x >> 3;
+    const int nbr = n_blocks / fp;
+    const int mbr = ((a.M + TM - 1) / TM) / (8 / fp);
+    const int g0 = l / (8 * nbr) * 8;
+    const int gs = min(8, mbr - g0);
+    const int r = l - g0 * nbr;
+    nb = (x % fp) * nbr + r / gs;
+    mb = (x / fp) * mbr + g0 + r % gs;
+  }
+  const int n0 = nb * TN;
+  const int m0 = mb * TM;
+  const int K = a.K;
+  const int nk = K / kBK;
+
+  // ---- fills.  A step's slot holds the tile's W rows (0 .. TN - 1) then
+  // its A rows (TN .. TN + TM - 1), 64 B each, chunk c of row r at position
+  // c ^ ((r / 4) % 4).  Fill instruction q writes rows 16 q .. 16 q + 15
+  // (1 KB); wave w issues q = w, w + 8, w + 16, w + 24 (< 28): four fills a
+  // step for waves 0-3, three for waves 4-7.
+  const __amdgpu_buffer_rsrc_t rw =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.W), (short)0, (int)a.w_bytes, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t ra =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.A), (short)0, (int)a.a_bytes, kBufferWord3);
+  const int fpos = lane & 3;
+  uint32_t f_off[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int q = wave + 8 * i;
+    const int row = 16 * q + (lane >> 2);
+    const uint32_t chunk = 16u * (uint32_t)(fpos ^ ((row >> 2) & 3));
+    if (q < kFillW) {
+      const int n = n0 + row;
+      f_off[i] = n < a.N ? (uint32_t)n * (uint32_t)K * 2u + chunk : kOutOfRange;
+    } else {
+      const int m = m0 + row - TN;
+      if (HEAD_OUT) {
+        f_off[i] = m < a.M ? (uint32_t)m * (uint32_t)K * 2u + chunk : kOutOfRange;
+      } else {
+        const int b = m / a.n_seq;
+        const int t = m - b * a.n_seq;
+        f_off[i] = m < a.M ? ((uint32_t)b * (uint32_t)a.H * (uint32_t)a.n_seq + (uint32_t)t) * (kHeadDim * 2u) + chunk
+                           : kOutOfRange;
+      }
+    }
+  }
+  auto a_step = [&](int kt) __attribute__((always_inline)) -> uint32_t {
+    return HEAD_OUT ? (uint32_t)kt * kStepBytes
+                    : (uint32_t)(kt >> 1) * (uint32_t)a.n_seq * (kHeadDim * 2u) + (uint32_t)(kt & 1) * kStepBytes;
+  };
+  auto fill = [&](auto slot_tag, int kt) __attribute__((always_inline)) {
+    constexpr int S = decltype(slot_tag)::value;
+    const uint32_t base = ring8_addr(S);
+    const uint32_t ws = (uint32_t)kt * kStepBytes, as = a_step(kt);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = wave + 8 * i;
+      if (q < kFill) {
+        const bool isw = q < kFillW;
+        const uint32_t o = f_off[i] == kOutOfRange ? kOutOfRange : f_off[i] + (isw ? ws : as);
+        lds_fill16_at(isw ? rw : ra, base + 1024u * (uint32_t)q, o);
+      }
+    }
+  };
+
+  f32x16 acc[FBW][TBW];  // [feature block][token block]
+#pragma unroll
+  for (int i = 0; i < FBW; ++i)
+#pragma unroll
+    for (int j = 0; j < TBW; ++j) acc[i][j] = f32x16{};
+
+  // One step: S = kt % 5 is its slot.  Step kt has landed (only the fills of
+  // steps kt + 1 .. kt + 3 may be in flight) and every wave is done with
+  // step kt - 1, whose slot step kt + 4 takes.  Fragments of k sub-step s:
+  // lane (ln, hh) reads W row 32 (FBW wn + i) + ln and A row TN + 32 (TBW wm
+  // + j) + ln, chunk 2 s + hh (k 16 s + 8 hh .. + 7).
+  auto step = [&](auto slot_tag, int kt) __attribute__((always_inline)) {
+    constexpr int S = decltype(slot_tag)::value;
+    using SF = std::integral_constant<int, (S + kSlots8 - 1) % kSlots8>;
+    if (kt >= nk) return;
+    if (wave < 4) wait_barrier<3 * 4>();
+    else wait_barrier<3 * 3>();
+    fill(SF(), kt + kSlots8 - 1);
+    const lds_uint4* t = (const lds_uint4*)(uintptr_t)ring8_addr(S);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int ch = 2 * s + hh;
+      bf16x8 wf[FBW], af[TBW];
+#pragma unroll
+      for (int i = 0; i < FBW; ++i) {
+        const int r = 32 * (FBW * wn + i) + ln;
+        wf[i] = __builtin_bit_cast(bf16x8, t[r * 4 + (ch ^ ((r >> 2) & 3))]);
+      }
+#pragma unroll
+      for (int j = 0; j < TBW; ++j) {
+        const int r = TN + 32 * (TBW * wm + j) + ln;
+        af[j] = __builtin_bit_cast(bf16x8, t[r * 4 + (ch ^ ((r >> 2) & 3))]);
+      }
+#pragma unroll
+      for (int i = 0; i < FBW; ++i)
+#pragma unroll
+        for (int j = 0; j < TBW; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[i], af[j], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  using S3 = std::integral_constant<int, 3>;
+  using S4 = std::integral_constant<int, 4>;
+  fill(S0(), 0);
+  fill(S1(), 1);
+  fill(S2(), 2);
+  fill(S3(), 3);
+  for (int kt = 0; kt < nk; kt += kSlots8) {
+    step(S0(), kt);
+    step(S1(), kt + 1);
+    step(S2(), kt + 2);
+    step(S3(), kt + 3);
+    step(S4(), kt + 4);
+  }
+  // The fills past the end of K (out of range or never read) land before
+  // the workgroup's LDS is released.
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0)
+
+  // ---- epilogue through LDS, so that every global store writes whole
+  // 128-byte rows (8 lanes a row; 16-byte pieces at a 128-byte stride, as
+  // the registers hold them, left the L2 merging partial lines).  The tile
+  // is TN / 64 chunks of 64 features -- each one head of one projection
+  // (heads are 64-aligned) -- by TM tokens; chunk c, token u sits at
+  // c TM 128 + u 128 bytes, its 16-byte piece q (d 8 q .. 8 q + 7) at
+  // position q ^ (u % 8).  Register r of block (i, j) holds feature
+  // 32 (FBW wn + i) + 8 (r / 4) + 4 hh + r % 4 of token 32 (TBW wm + j) + ln
+  // of the tile.
+  constexpr int kChunks = TN / 64;
+  barrier_lds();  // every wave is done with the ring
+  {
+    lds_char* st = (lds_char*)(uintptr_t)ring8_addr(0);
+#pragma unroll
+    for (int i = 0; i < FBW; ++i)
+#pragma unroll
+      for (int j = 0; j < TBW; ++j) {
+        const int u = 32 * (TBW * wm + j) + ln;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int f = 32 * (FBW * wn + i) + 8 * g + 4 * hh;  // first of the lane's 4 features
+          const int c = f >> 6, q = (f & 63) >> 3;
+          u32x2 v;
+          v.x = pack_bf16x2(acc[i][j][4 * g], acc[i][j][4 * g + 1]);
+          v.y = pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+          *(lds_u32x2*)(st + (c * TM + u) * 128 + ((q ^ (u & 7)) << 4) + (f & 4) * 2) = v;
+        }
+      }
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  barrier_lds();
+  const int d_model = a.H * kHeadDim;
+  const lds_char* st = (const lds_char*)(uintptr_t)ring8_addr(0);
+  const int q = lane & 7;
+#pragma unroll 2
+  for (int it = 0; it < kChunks * TM / 64; ++it) {
+    const int row = 64 * it + 8 * wave + (lane >> 3);
+    const int c = row / TM, u = row - c * TM;
+    const int nf = n0 + 64 * c;  // first feature of the chunk
+    const int m = m0 + u;
+    const uint4 v = __builtin_bit_cast(uint4, *(const lds_uint4*)(st + row * 128 + ((q ^ (u & 7)) << 4)));
+    if (nf >= a.N || m >= a.M) continue;
+    __bf16* dst;
+    if (HEAD_OUT) {
+      const int p = nf / d_model;
+      const int hd = (nf - p * d_model) / kHeadDim;
+      const int b = m / a.n_seq;
+      const int t = m - b * a.n_seq;
+      dst = static_cast<__bf16*>(a.out[p]) + (((size_t)b * a.H + hd) * a.n_seq + t) * kHeadDim;
+    } else {
+      dst = static_cast<__bf16*>(a.out[0]) + (size_t)m * a.N + nf;
+    }
+    *reinterpret_cast<uint4*>(dst + 8 * q) = v;
+  }
+}
+
 // The XCD split with the fewest L2 fills, W rows read by 8/f XCDs and X rows
 // by f: f minimising w_bytes * 8/f + a_bytes * f among those that divide the
 // tile grid evenly; 0 (plain order) when none does.
@@ -269,20 +497,45 @@ int xcd_split(const ProjArgs& a, long long n_blocks, long long m_blocks) {
 
 template <bool HEAD_OUT>
 hipError_t launch_tb(const ProjArgs& a, hipStream_t s) {
-  // 256-token tiles while they still give every compute unit a workgroup.
-  const long long n_blocks = (a.N + kBN - 1) / kBN;
-  const long long big = n_blocks * ((a.M + 255) / 256);
+  // The candidate with the least work on its busiest compute unit (ties go
+  // to the earlier one in this order): the 4-wave kernel's 128 x 256 or
+  // 128 x 128 tiles (two workgroups per compute unit; the smaller tile reads
+  // 4/3 the LDS bytes per product, so its work counts 4/3) or the 8-wave
+  // kernel's 256 x 192 or 320 x 128 tiles (one workgroup per compute unit).
+  // Workgroups are spread evenly over the 256 compute units.
+  const long long M = a.M, N = a.N;
+  auto per_cu = [](long long tiles, long long outputs) { return (tiles + 255) / 256 * outputs; };
+  const long long nb4 = (N + kBN - 1) / kBN;
+  const long long big = nb4 * ((M + 255) / 256), small = nb4 * ((M + 127) / 128);
+  const long long nb8a = (N + 191) / 192, mb8a = (M + 255) / 256;
+  const long long nb8b = (N + 127) / 128, mb8b = (M + 319) / 320;
+  const long long c_big = per_cu(big, 128 * 256);
+  const long long c_small = per_cu(small, 128 * 128) * 4 / 3;
+  const long long c_8a = per_cu(nb8a * mb8a, 256 * 192);
+  const long long c_8b = per_cu(nb8b * mb8b, 320 * 128);
+  const long long best = std::min(std::min(c_big, c_small), std::min(c_8a, c_8b));
   ProjArgs args = a;
   void* kargs[] = {&args};
-  if (big >= 256) {
-    args.xcd_fp = xcd_split(a, n_blocks, (a.M + 255) / 256);
+  if (c_big == best) {
+    args.xcd_fp = xcd_split(a, nb4, (M + 255) / 256);
     return hipLaunchKernel(reinterpret_cast<const void*>(&proj_gemm_kernel<HEAD_OUT, 4>), dim3((unsigned)big),
                            dim3(kThreads), kargs, 0, s);
   }
-  const long long small = n_blocks * ((a.M + 127) / 128);
-  args.xcd_fp = xcd_split(a, n_blocks, (a.M + 127) / 128);
-  return hipLaunchKernel(reinterpret_cast<const void*>(&proj_gemm_kernel<HEAD_OUT, 2>), dim3((unsigned)small),
-                         dim3(kThreads), kargs, 0, s);
+  if (c_small == best) {
+    args.xcd_fp = xcd_split(a, nb4, (M + 127) / 128);
+    return hipLaunchKernel(reinterpret_cast<const void*>(&proj_gemm_kernel<HEAD_OUT, 2>), dim3((unsigned)small),
+                           dim3(kThreads), kargs, 0, s);
+  }
+  if (c_8a == best) {
+    args.xcd_fp = xcd_split(a, nb8a, mb8a);
+    return hipLaunchKernel(reinterpret_cast<const void*>(&proj_gemm8_kernel<HEAD_OUT, 4, 2, 3>),
+                           dim3((unsigned)(nb8a * mb8a)), dim3(512), kargs, 0, s);
+  }
+  {
+    args.xcd_fp = xcd_split(a, nb8b, mb8b);
+    return hipLaunchKernel(reinterpret_cast<const void*>(&proj_gemm8_kernel<HEAD_OUT, 2, 5, 1>),
+                           dim3((unsigned)(nb8b * mb8b)), dim3(512), kargs, 0, s);
+  }
 }
 
 }  // namespace

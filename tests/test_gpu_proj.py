@@ -2,8 +2,9 @@
 fp64 oracle on the same bf16 inputs, and of the whole multi-head sub-layer
 (projections + attention + output projection) built from the library's
 entry points.  Weights are seeded N(0, 1/d_model) draws (no trained weights
-are needed: the projections are plain linear maps).  The shapes reach both
-tile sizes and every tile order the launcher picks: XCD rectangles of all,
+are needed: the projections are plain linear maps).  The shapes reach every
+tile the launcher picks (128 x 256 and 128 x 128 on four waves, 256 x 192 and
+320 x 128 on eight) and every tile order: XCD rectangles of all,
 1/2, 1/4 or 1/8 of the feature blocks, a last partial group of token blocks,
 and the plain order for grids the split does not divide.
 
@@ -49,6 +50,7 @@ def _weights(g, rows, d_model):
     (2, 128, 16, 3),    # few tokens: each XCD takes 1/8 of the feature blocks
     (8, 128, 16, 2),    # XCD rectangles of 1/4 of the feature blocks by 1/2 of the tokens
     (144, 128, 16, 1),  # 9 token blocks per XCD: a full group of 8 and a group of 1
+    (32, 128, 40, 1),   # 256 x 192 tiles with a partial last feature block (N = 2560)
 ])
 def test_head_projection(B, n, h, n_out):
     g = workloads.generator(800 + n + h)
@@ -66,7 +68,8 @@ def test_head_projection(B, n, h, n_out):
 
 @pytest.mark.parametrize("B,n,h", [(32, 128, 8), (32, 128, 16), (3, 77, 3), (1, 1, 1),
                                    (16, 257, 38),   # ragged M = 4112, N = 2432 (not a multiple of 128)
-                                   (64, 128, 32)])  # M = 8192, N = 2048
+                                   (64, 128, 32),   # M = 8192, N = 2048
+                                   (16, 256, 48)])  # 256 x 192 tiles, M = 4096, N = 3072
 def test_output_projection(B, n, h):
     g = workloads.generator(900 + n + h)
     d = 64 * h
