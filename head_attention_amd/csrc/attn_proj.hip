@@ -36,6 +36,9 @@
 namespace headattn {
 namespace {
 
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
+
 constexpr int kThreads = 256;
 constexpr int kBN = 128;  // output features per workgroup
 constexpr int kBK = 32;   // k per step
@@ -49,16 +52,17 @@ constexpr uint32_t kStepBytes = kBK * 2;        // bytes of one row in one step
 // r + 12 fall on the same banks and take 4 different positions, so the read
 // is free of bank conflicts.  ((r / 2) % 4 gave those rows 2 positions:
 // half of the kernel's active LDS cycles were conflict stalls.)
-__shared__ uint4 g_w0[kBN * 4], g_w1[kBN * 4], g_w2[kBN * 4];
-__shared__ uint4 g_a0[256 * 4], g_a1[256 * 4], g_a2[256 * 4];
+// Slot S: its W tile at row 384 S, its A tile at row 384 S + 128.  The
+// epilogue reuses the whole ring.
+__shared__ uint4 g_ring4[kSlots * (kBN + 256) * 4];
 
 template <int S>
 __device__ __forceinline__ uint4* wslot() {
-  return S == 0 ? g_w0 : S == 1 ? g_w1 : g_w2;
+  return g_ring4 + S * (kBN + 256) * 4;
 }
 template <int S>
 __device__ __forceinline__ uint4* aslot() {
-  return S == 0 ? g_a0 : S == 1 ? g_a1 : g_a2;
+  return g_ring4 + S * (kBN + 256) * 4 + kBN * 4;
 }
 
 // Wait until at most N of this wave's buffer loads are outstanding and its
@@ -221,35 +225,55 @@ __global__ __launch_bounds__(kThreads, 2) void proj_gemm_kernel(ProjArgs a) {
   // land before the workgroup's LDS is released.
   __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0)
 
-  // ---- epilogue.  Register r of block (i, j) holds feature n0 + 64 wn +
-  // 32 i + 8 (r / 4) + 4 hh + r % 4 of token m0 + 32 TB wm + 32 j + ln:
-  // four consecutive features per 8-byte store.  A wave's 64 features are
-  // one head of one projection (64-aligned), so the output tensor and head
-  // are wave-uniform.
-  const int nw = n0 + 64 * wn;  // first feature of this wave
-  if (nw >= a.N) return;
-  const int d_model = a.H * kHeadDim;
-  const int p = nw / d_model;
-  const int hd = (nw - p * d_model) / kHeadDim;
-  __bf16* const out = static_cast<__bf16*>(a.out[HEAD_OUT ? p : 0]);
+  // ---- epilogue through LDS, as in the 8-wave kernel below: whole
+  // 128-byte rows per store.  The tile is 2 chunks of 64 features (each one
+  // head of one projection) by kBM tokens; chunk c, token u at (c kBM + u)
+  // 128 bytes, its 16-byte piece q at position q ^ (u % 8).  Register r of
+  // block (i, j) holds feature 64 wn + 32 i + 8 (r / 4) + 4 hh + r % 4 (chunk
+  // wn) of token 32 TB wm + 32 j + ln of the tile.
+  barrier_lds();  // every wave is done with the ring
+  {
+    lds_char* st = (lds_char*)(uintptr_t)(lds_void_t*)g_ring4;
 #pragma unroll
-  for (int j = 0; j < TB; ++j) {
-    const int m = m0 + 32 * TB * wm + 32 * j + ln;
-    if (m >= a.M) continue;
-    const int b = m / a.n_seq;
-    const int t = m - b * a.n_seq;
-    __bf16* const row = HEAD_OUT ? out + (((size_t)b * a.H + hd) * a.n_seq + t) * kHeadDim
-                                 : out + (size_t)m * a.N + nw;
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+      for (int j = 0; j < TB; ++j) {
+        const int u = 32 * TB * wm + 32 * j + ln;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        uint2 v;
-        v.x = pack_bf16x2(acc[i][j][4 * g], acc[i][j][4 * g + 1]);
-        v.y = pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
-        *reinterpret_cast<uint2*>(row + 32 * i + 8 * g + 4 * hh) = v;
+        for (int g = 0; g < 4; ++g) {
+          const int f = 32 * i + 8 * g + 4 * hh;  // lane's first feature within the chunk
+          const int q = f >> 3;
+          u32x2 v;
+          v.x = pack_bf16x2(acc[i][j][4 * g], acc[i][j][4 * g + 1]);
+          v.y = pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+          *(lds_u32x2*)(st + (wn * kBM + u) * 128 + ((q ^ (u & 7)) << 4) + (f & 4) * 2) = v;
+        }
       }
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  barrier_lds();
+  const int d_model = a.H * kHeadDim;
+  const lds_char* st = (const lds_char*)(uintptr_t)(lds_void_t*)g_ring4;
+  const int q = lane & 7;
+#pragma unroll 2
+  for (int it = 0; it < 2 * kBM / 32; ++it) {
+    const int row = 32 * it + 8 * wave + (lane >> 3);
+    const int c = row / kBM, u = row - c * kBM;
+    const int nf = n0 + 64 * c;  // first feature of the chunk
+    const int m = m0 + u;
+    const uint4 v = __builtin_bit_cast(uint4, *(const lds_uint4*)(st + row * 128 + ((q ^ (u & 7)) << 4)));
+    if (nf >= a.N || m >= a.M) continue;
+    __bf16* dst;
+    if (HEAD_OUT) {
+      const int p = nf / d_model;
+      const int hd = (nf - p * d_model) / kHeadDim;
+      const int b = m / a.n_seq;
+      const int t = m - b * a.n_seq;
+      dst = static_cast<__bf16*>(a.out[p]) + (((size_t)b * a.H + hd) * a.n_seq + t) * kHeadDim;
+    } else {
+      dst = static_cast<__bf16*>(a.out[0]) + (size_t)m * a.N + nf;
     }
+    *reinterpret_cast<uint4*>(dst + 8 * q) = v;
   }
 }
 
@@ -264,8 +288,6 @@ __global__ __launch_bounds__(kThreads, 2) void proj_gemm_kernel(ProjArgs a) {
 // as in the 4-wave kernel at two workgroups per compute unit.  K runs in
 // steps of 32 through a ring of five slots (28 KB each), filled four steps
 // ahead by LDS-direct buffer loads, one bare barrier per step.
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
 constexpr int kRows8 = 448;
 constexpr int kSlots8 = 5;
 constexpr uint32_t kSlotBytes8 = kRows8 * kStepBytes;
