@@ -278,20 +278,24 @@ __global__ __launch_bounds__(kThreads, 2) void proj_gemm_kernel(ProjArgs a) {
 }
 
 // ---- large shapes: one 8-wave workgroup per compute unit.  The tile is TM
-// tokens x TN features with TM + TN = 448 rows per k step, the waves on a
-// WM x WN grid (WM WN = 8), each owning 32 TBW tokens x 32 FBW features:
-// 256 x 192 (WM 4, TBW 2, FBW 3) or 320 x 128 (WM 2, TBW 5, FBW 1).  A
-// shape whose tiles of that size number about the compute units (the
-// decoder's self Q, K, V at 4096 x 3072 makes exactly 256 of 256 x 192)
-// then gives every compute unit the same work, where the 4-wave kernel's
-// tiles leave some compute units two and others one.  Two waves per SIMD,
-// as in the 4-wave kernel at two workgroups per compute unit.  K runs in
-// steps of 32 through a ring of five slots (28 KB each), filled four steps
-// ahead by LDS-direct buffer loads, one bare barrier per step.
+// tokens x TN features with TM + TN = 448 rows, the waves on a WM x WN grid
+// (WM WN = 8), each owning 32 TBW tokens x 32 FBW features: 256 x 192 (WM 4,
+// TBW 2, FBW 3) or 320 x 128 (WM 2, TBW 5, FBW 1).  A shape whose tiles of
+// that size number about the compute units (the decoder's self Q, K, V at
+// 4096 x 3072 makes exactly 256 of 256 x 192) then gives every compute unit
+// the same work, where the 4-wave kernel's tiles leave some compute units
+// two and others one.  Two waves per SIMD, as in the 4-wave kernel at two
+// workgroups per compute unit.  K runs in steps of 64 through two slots of
+// 56 KB: a row's step is 128 bytes, so every fill reads whole cache lines
+// (the 4-wave kernel's 64-byte steps read half lines, and fetched about
+// 26 bytes per clock per compute unit here against the products' need).
+// The next step's fills go out as soon as its slot frees, one bare barrier
+// per step.
 constexpr int kRows8 = 448;
-constexpr int kSlots8 = 5;
-constexpr uint32_t kSlotBytes8 = kRows8 * kStepBytes;
-__shared__ uint4 g_ring8[kSlots8 * kRows8 * 4];
+constexpr int kSlots8 = 2;
+constexpr uint32_t kRowBytes8 = 128;  // k 64 per step: 8 chunks of 16 bytes
+constexpr uint32_t kSlotBytes8 = kRows8 * kRowBytes8;
+__shared__ uint4 g_ring8[kSlots8 * kRows8 * 8];
 
 __device__ __forceinline__ uint32_t ring8_addr(int slot) {
   return (uint32_t)(uintptr_t)(lds_void_t*)&g_ring8[0] + (uint32_t)slot * kSlotBytes8;
@@ -303,8 +307,8 @@ __global__ __launch_bounds__(512, 1) void proj_gemm8_kernel(ProjArgs a) {
   constexpr int TM = 32 * TBW * WM;  // tokens per workgroup
   constexpr int TN = 32 * FBW * WN;  // output features per workgroup
   static_assert(WM * WN == 8 && TM + TN == kRows8, "tile shape");
-  constexpr int kFillW = TN / 16;          // fill instructions of the W rows
-  constexpr int kFill = kRows8 / 16;       // fill instructions per step (28)
+  constexpr int kFillW = TN / 8;  // fill instructions of the W rows
+  static_assert(kRows8 / 8 == 7 * 8, "56 fill instructions per step, 7 per wave");
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
@@ -332,24 +336,25 @@ __global__ __launch_bounds__(512, 1) void proj_gemm8_kernel(ProjArgs a) {
   const int n0 = nb * TN;
   const int m0 = mb * TM;
   const int K = a.K;
-  const int nk = K / kBK;
+  const int nk = K / 64;
 
   // ---- fills.  A step's slot holds the tile's W rows (0 .. TN - 1) then
-  // its A rows (TN .. TN + TM - 1), 64 B each, chunk c of row r at position
-  // c ^ ((r / 4) % 4).  Fill instruction q writes rows 16 q .. 16 q + 15
-  // (1 KB); wave w issues q = w, w + 8, w + 16, w + 24 (< 28): four fills a
-  // step for waves 0-3, three for waves 4-7.
+  // its A rows (TN .. TN + TM - 1), 128 B each, chunk c of row r at position
+  // c ^ k_swz(r) (16-lane row reads conflict-free).  Fill instruction q
+  // writes rows 8 q .. 8 q + 7 (1 KB, 8 lanes a row); wave w issues q = w,
+  // w + 8, .., w + 48.  For the output projection a step is one whole head:
+  // A row m's step kt is O[b, kt, t, :].
   const __amdgpu_buffer_rsrc_t rw =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.W), (short)0, (int)a.w_bytes, kBufferWord3);
   const __amdgpu_buffer_rsrc_t ra =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.A), (short)0, (int)a.a_bytes, kBufferWord3);
-  const int fpos = lane & 3;
-  uint32_t f_off[4];
+  const int fpos = lane & 7;
+  uint32_t f_off[7];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < 7; ++i) {
     const int q = wave + 8 * i;
-    const int row = 16 * q + (lane >> 2);
-    const uint32_t chunk = 16u * (uint32_t)(fpos ^ ((row >> 2) & 3));
+    const int row = 8 * q + (lane >> 3);
+    const uint32_t chunk = 16u * (uint32_t)(fpos ^ k_swz(row));
     if (q < kFillW) {
       const int n = n0 + row;
       f_off[i] = n < a.N ? (uint32_t)n * (uint32_t)K * 2u + chunk : kOutOfRange;
@@ -365,57 +370,51 @@ __global__ __launch_bounds__(512, 1) void proj_gemm8_kernel(ProjArgs a) {
       }
     }
   }
-  auto a_step = [&](int kt) __attribute__((always_inline)) -> uint32_t {
-    return HEAD_OUT ? (uint32_t)kt * kStepBytes
-                    : (uint32_t)(kt >> 1) * (uint32_t)a.n_seq * (kHeadDim * 2u) + (uint32_t)(kt & 1) * kStepBytes;
-  };
   auto fill = [&](auto slot_tag, int kt) __attribute__((always_inline)) {
     constexpr int S = decltype(slot_tag)::value;
     const uint32_t base = ring8_addr(S);
-    const uint32_t ws = (uint32_t)kt * kStepBytes, as = a_step(kt);
+    const uint32_t ws = (uint32_t)kt * 128u;
+    const uint32_t as = HEAD_OUT ? (uint32_t)kt * 128u : (uint32_t)kt * (uint32_t)a.n_seq * (kHeadDim * 2u);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 7; ++i) {
       const int q = wave + 8 * i;
-      if (q < kFill) {
-        const bool isw = q < kFillW;
-        const uint32_t o = f_off[i] == kOutOfRange ? kOutOfRange : f_off[i] + (isw ? ws : as);
-        lds_fill16_at(isw ? rw : ra, base + 1024u * (uint32_t)q, o);
-      }
+      const bool isw = q < kFillW;
+      const uint32_t o = f_off[i] == kOutOfRange ? kOutOfRange : f_off[i] + (isw ? ws : as);
+      lds_fill16_at(isw ? rw : ra, base + 1024u * (uint32_t)q, o);
     }
   };
-
   f32x16 acc[FBW][TBW];  // [feature block][token block]
 #pragma unroll
   for (int i = 0; i < FBW; ++i)
 #pragma unroll
     for (int j = 0; j < TBW; ++j) acc[i][j] = f32x16{};
 
-  // One step: S = kt % 5 is its slot.  Step kt has landed (only the fills of
-  // steps kt + 1 .. kt + 3 may be in flight) and every wave is done with
-  // step kt - 1, whose slot step kt + 4 takes.  Fragments of k sub-step s:
-  // lane (ln, hh) reads W row 32 (FBW wn + i) + ln and A row TN + 32 (TBW wm
-  // + j) + ln, chunk 2 s + hh (k 16 s + 8 hh .. + 7).
+  // One step: S = kt % 2 is its slot.  The wait lands step kt (the only
+  // fills in flight), and the barrier publishes it and frees the other slot
+  // (every wave is done with step kt - 1), which step kt + 1 then takes.
+  // Fragments of k sub-step s: lane (ln, hh) reads W row 32 (FBW wn + i) +
+  // ln and A row TN + 32 (TBW wm + j) + ln, chunk 2 s + hh (k 16 s + 8 hh
+  // .. + 7).
   auto step = [&](auto slot_tag, int kt) __attribute__((always_inline)) {
     constexpr int S = decltype(slot_tag)::value;
-    using SF = std::integral_constant<int, (S + kSlots8 - 1) % kSlots8>;
+    using SO = std::integral_constant<int, 1 - S>;
     if (kt >= nk) return;
-    if (wave < 4) wait_barrier<3 * 4>();
-    else wait_barrier<3 * 3>();
-    fill(SF(), kt + kSlots8 - 1);
+    wait_barrier<0>();
+    fill(SO(), kt + 1);
     const lds_uint4* t = (const lds_uint4*)(uintptr_t)ring8_addr(S);
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
+    for (int s = 0; s < 4; ++s) {
       const int ch = 2 * s + hh;
       bf16x8 wf[FBW], af[TBW];
 #pragma unroll
       for (int i = 0; i < FBW; ++i) {
         const int r = 32 * (FBW * wn + i) + ln;
-        wf[i] = __builtin_bit_cast(bf16x8, t[r * 4 + (ch ^ ((r >> 2) & 3))]);
+        wf[i] = __builtin_bit_cast(bf16x8, t[r * 8 + (ch ^ k_swz(r))]);
       }
 #pragma unroll
       for (int j = 0; j < TBW; ++j) {
         const int r = TN + 32 * (TBW * wm + j) + ln;
-        af[j] = __builtin_bit_cast(bf16x8, t[r * 4 + (ch ^ ((r >> 2) & 3))]);
+        af[j] = __builtin_bit_cast(bf16x8, t[r * 8 + (ch ^ k_swz(r))]);
       }
 #pragma unroll
       for (int i = 0; i < FBW; ++i)
@@ -423,24 +422,14 @@ __global__ __launch_bounds__(512, 1) void proj_gemm8_kernel(ProjArgs a) {
         for (int j = 0; j < TBW; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[i], af[j], acc[i][j], 0, 0, 0);
     }
   };
-
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
-  using S2 = std::integral_constant<int, 2>;
-  using S3 = std::integral_constant<int, 3>;
-  using S4 = std::integral_constant<int, 4>;
   fill(S0(), 0);
-  fill(S1(), 1);
-  fill(S2(), 2);
-  fill(S3(), 3);
-  for (int kt = 0; kt < nk; kt += kSlots8) {
+  for (int kt = 0; kt < nk; kt += 2) {
     step(S0(), kt);
     step(S1(), kt + 1);
-    step(S2(), kt + 2);
-    step(S3(), kt + 3);
-    step(S4(), kt + 4);
   }
-  // The fills past the end of K (out of range or never read) land before
+  // The fill past the end of K (out of range or never read) lands before
   // the workgroup's LDS is released.
   __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0)
 
