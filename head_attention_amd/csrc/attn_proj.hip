@@ -18,10 +18,10 @@
 // lane ends up holding four consecutive output features of one token -- one
 // 8-byte store, along a head's 64 dimensions or along Y's row.
 //
-// Workgroup: 4 waves, 2 (features) x 2 (tokens); a wave owns 64 features x
+// 4-wave kernel: 2 (features) x 2 (tokens) waves; a wave owns 64 features x
 // 32 TB tokens (2 x TB blocks of 32 x 32), so per 16-wide k step it reads
-// 2 + TB fragments from LDS for 2 TB products.  TB = 4 (a 128 x 256 tile)
-// when the grid still fills the chip, else TB = 2 (128 x 128).  K runs in
+// 2 + TB fragments from LDS for 2 TB products; the launcher uses TB = 4, a
+// 128 x 256 tile, two workgroups per compute unit.  K runs in
 // steps of 32: the W and A tiles of a step reach LDS by buffer loads that
 // write LDS directly, into a ring of three slots two steps ahead of use, one
 // bare barrier per step.  Rows past the end of W or A read as zero through
@@ -280,25 +280,25 @@ __global__ __launch_bounds__(kThreads, 2) void proj_gemm_kernel(ProjArgs a) {
 // ---- large shapes: one 8-wave workgroup per compute unit.  The tile is TM
 // tokens x TN features with TM + TN = 448 rows, the waves on a WM x WN grid
 // (WM WN = 8), each owning 32 TBW tokens x 32 FBW features: 256 x 192 (WM 4,
-// TBW 2, FBW 3) or 320 x 128 (WM 2, TBW 5, FBW 1).  A shape whose tiles of
-// that size number about the compute units (the decoder's self Q, K, V at
-// 4096 x 3072 makes exactly 256 of 256 x 192) then gives every compute unit
-// the same work, where the 4-wave kernel's tiles leave some compute units
-// two and others one.  Two waves per SIMD, as in the 4-wave kernel at two
-// workgroups per compute unit.  K runs in steps of 64 through two slots of
-// 56 KB: a row's step is 128 bytes, so every fill reads whole cache lines
-// (the 4-wave kernel's 64-byte steps read half lines, and fetched about
-// 26 bytes per clock per compute unit here against the products' need).
-// The next step's fills go out as soon as its slot frees, one bare barrier
-// per step.
-constexpr int kRows8 = 448;
-constexpr int kSlots8 = 2;
+// TBW 2, FBW 3), 320 x 128 (WM 2, TBW 5, FBW 1) or 128 x 128 (WM 2, TBW 2,
+// FBW 1).  A shape whose tiles of one of these sizes number about the
+// compute units (the decoder's self Q, K, V at 4096 x 3072 makes exactly 256
+// of 256 x 192, its cross K, V at 5120 x 2048 256 of 320 x 128) then gives
+// every compute unit the same work, where the 4-wave kernel's tiles leave
+// some compute units two and others one; and 128 x 128 tiles keep two waves
+// per SIMD where the 4-wave kernel would have one.  K runs in steps of 64
+// through two slots (448 rows, 56 KB each) or three (256 rows): a row's
+// step is 128 bytes, so every fill reads whole cache lines (64-byte steps
+// read half lines and fetched about 26 bytes per clock per compute unit
+// here, against what the products need).  A step's fills go out as soon as
+// its slot frees, one bare barrier per step.
 constexpr uint32_t kRowBytes8 = 128;  // k 64 per step: 8 chunks of 16 bytes
-constexpr uint32_t kSlotBytes8 = kRows8 * kRowBytes8;
-__shared__ uint4 g_ring8[kSlots8 * kRows8 * 8];
+// The ring: two slots of 448 rows, or three of 256 (112 KB either way at most).
+__shared__ uint4 g_ring8[2 * 448 * 8];
 
+template <int ROWS>
 __device__ __forceinline__ uint32_t ring8_addr(int slot) {
-  return (uint32_t)(uintptr_t)(lds_void_t*)&g_ring8[0] + (uint32_t)slot * kSlotBytes8;
+  return (uint32_t)(uintptr_t)(lds_void_t*)&g_ring8[0] + (uint32_t)slot * (ROWS * kRowBytes8);
 }
 
 template <bool HEAD_OUT, int WM, int TBW, int FBW>
@@ -306,9 +306,12 @@ __global__ __launch_bounds__(512, 1) void proj_gemm8_kernel(ProjArgs a) {
   constexpr int WN = 8 / WM;
   constexpr int TM = 32 * TBW * WM;  // tokens per workgroup
   constexpr int TN = 32 * FBW * WN;  // output features per workgroup
-  static_assert(WM * WN == 8 && TM + TN == kRows8, "tile shape");
-  constexpr int kFillW = TN / 8;  // fill instructions of the W rows
-  static_assert(kRows8 / 8 == 7 * 8, "56 fill instructions per step, 7 per wave");
+  constexpr int kRows = TM + TN;              // rows of a step
+  constexpr int kSlots = kRows > 256 ? 2 : 3;  // ring slots
+  constexpr int kFillW = TN / 8;               // fill instructions of the W rows
+  constexpr int kFillPerWave = kRows / 64;     // fill instructions per wave and step
+  static_assert(WM * WN == 8 && kRows % 64 == 0 && kSlots * kRows <= 2 * 448, "tile shape");
+  static_assert(TN % 64 == 0, "a tile's features are whole 64-wide heads");
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
@@ -349,9 +352,9 @@ __global__ __launch_bounds__(512, 1) void proj_gemm8_kernel(ProjArgs a) {
   const __amdgpu_buffer_rsrc_t ra =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.A), (short)0, (int)a.a_bytes, kBufferWord3);
   const int fpos = lane & 7;
-  uint32_t f_off[7];
+  uint32_t f_off[kFillPerWave];
 #pragma unroll
-  for (int i = 0; i < 7; ++i) {
+  for (int i = 0; i < kFillPerWave; ++i) {
     const int q = wave + 8 * i;
     const int row = 8 * q + (lane >> 3);
     const uint32_t chunk = 16u * (uint32_t)(fpos ^ k_swz(row));
@@ -372,11 +375,11 @@ __global__ __launch_bounds__(512, 1) void proj_gemm8_kernel(ProjArgs a) {
   }
   auto fill = [&](auto slot_tag, int kt) __attribute__((always_inline)) {
     constexpr int S = decltype(slot_tag)::value;
-    const uint32_t base = ring8_addr(S);
+    const uint32_t base = ring8_addr<kRows>(S);
     const uint32_t ws = (uint32_t)kt * 128u;
     const uint32_t as = HEAD_OUT ? (uint32_t)kt * 128u : (uint32_t)kt * (uint32_t)a.n_seq * (kHeadDim * 2u);
 #pragma unroll
-    for (int i = 0; i < 7; ++i) {
+    for (int i = 0; i < kFillPerWave; ++i) {
       const int q = wave + 8 * i;
       const bool isw = q < kFillW;
       const uint32_t o = f_off[i] == kOutOfRange ? kOutOfRange : f_off[i] + (isw ? ws : as);
@@ -389,19 +392,20 @@ __global__ __launch_bounds__(512, 1) void proj_gemm8_kernel(ProjArgs a) {
 #pragma unroll
     for (int j = 0; j < TBW; ++j) acc[i][j] = f32x16{};
 
-  // One step: S = kt % 2 is its slot.  The wait lands step kt (the only
-  // fills in flight), and the barrier publishes it and frees the other slot
-  // (every wave is done with step kt - 1), which step kt + 1 then takes.
+  // One step: S = kt % kSlots is its slot.  The wait lands step kt (with
+  // three slots step kt + 1's fills may still fly), and the barrier
+  // publishes it and frees the slot of step kt - 1 (every wave is done with
+  // it), which step kt + kSlots - 1 then takes.
   // Fragments of k sub-step s: lane (ln, hh) reads W row 32 (FBW wn + i) +
   // ln and A row TN + 32 (TBW wm + j) + ln, chunk 2 s + hh (k 16 s + 8 hh
   // .. + 7).
   auto step = [&](auto slot_tag, int kt) __attribute__((always_inline)) {
     constexpr int S = decltype(slot_tag)::value;
-    using SO = std::integral_constant<int, 1 - S>;
+    using SF = std::integral_constant<int, (S + kSlots - 1) % kSlots>;
     if (kt >= nk) return;
-    wait_barrier<0>();
-    fill(SO(), kt + 1);
-    const lds_uint4* t = (const lds_uint4*)(uintptr_t)ring8_addr(S);
+    wait_barrier<(kSlots - 2) * kFillPerWave>();
+    fill(SF(), kt + kSlots - 1);
+    const lds_uint4* t = (const lds_uint4*)(uintptr_t)ring8_addr<kRows>(S);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int ch = 2 * s + hh;
@@ -424,10 +428,20 @@ __global__ __launch_bounds__(512, 1) void proj_gemm8_kernel(ProjArgs a) {
   };
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
   fill(S0(), 0);
-  for (int kt = 0; kt < nk; kt += 2) {
-    step(S0(), kt);
-    step(S1(), kt + 1);
+  if constexpr (kSlots == 2) {
+    for (int kt = 0; kt < nk; kt += 2) {
+      step(S0(), kt);
+      step(S1(), kt + 1);
+    }
+  } else {
+    fill(S1(), 1);
+    for (int kt = 0; kt < nk; kt += 3) {
+      step(S0(), kt);
+      step(S1(), kt + 1);
+      step(S2(), kt + 2);
+    }
   }
   // The fill past the end of K (out of range or never read) lands before
   // the workgroup's LDS is released.
@@ -445,7 +459,7 @@ __global__ __launch_bounds__(512, 1) void proj_gemm8_kernel(ProjArgs a) {
   constexpr int kChunks = TN / 64;
   barrier_lds();  // every wave is done with the ring
   {
-    lds_char* st = (lds_char*)(uintptr_t)ring8_addr(0);
+    lds_char* st = (lds_char*)(uintptr_t)ring8_addr<kRows>(0);
 #pragma unroll
     for (int i = 0; i < FBW; ++i)
 #pragma unroll
@@ -465,7 +479,7 @@ __global__ __launch_bounds__(512, 1) void proj_gemm8_kernel(ProjArgs a) {
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
   barrier_lds();
   const int d_model = a.H * kHeadDim;
-  const lds_char* st = (const lds_char*)(uintptr_t)ring8_addr(0);
+  const lds_char* st = (const lds_char*)(uintptr_t)ring8_addr<kRows>(0);
   const int q = lane & 7;
 #pragma unroll 2
   for (int it = 0; it < kChunks * TM / 64; ++it) {
@@ -509,22 +523,22 @@ int xcd_split(const ProjArgs& a, long long n_blocks, long long m_blocks) {
 template <bool HEAD_OUT>
 hipError_t launch_tb(const ProjArgs& a, hipStream_t s) {
   // The candidate with the least work on its busiest compute unit (ties go
-  // to the earlier one in this order): the 4-wave kernel's 128 x 256 or
-  // 128 x 128 tiles (two workgroups per compute unit; the smaller tile reads
-  // 4/3 the LDS bytes per product, so its work counts 4/3) or the 8-wave
-  // kernel's 256 x 192 or 320 x 128 tiles (one workgroup per compute unit).
+  // to the earlier one in this order): the 4-wave kernel's 128 x 256 tiles
+  // (two workgroups per compute unit) or the 8-wave kernel's 256 x 192,
+  // 320 x 128 or 128 x 128 tiles (one workgroup per compute unit).
   // Workgroups are spread evenly over the 256 compute units.
   const long long M = a.M, N = a.N;
   auto per_cu = [](long long tiles, long long outputs) { return (tiles + 255) / 256 * outputs; };
   const long long nb4 = (N + kBN - 1) / kBN;
-  const long long big = nb4 * ((M + 255) / 256), small = nb4 * ((M + 127) / 128);
+  const long long big = nb4 * ((M + 255) / 256);
   const long long nb8a = (N + 191) / 192, mb8a = (M + 255) / 256;
   const long long nb8b = (N + 127) / 128, mb8b = (M + 319) / 320;
+  const long long nb8c = (N + 127) / 128, mb8c = (M + 127) / 128;
   const long long c_big = per_cu(big, 128 * 256);
-  const long long c_small = per_cu(small, 128 * 128) * 4 / 3;
   const long long c_8a = per_cu(nb8a * mb8a, 256 * 192);
   const long long c_8b = per_cu(nb8b * mb8b, 320 * 128);
-  const long long best = std::min(std::min(c_big, c_small), std::min(c_8a, c_8b));
+  const long long c_8c = per_cu(nb8c * mb8c, 128 * 128);
+  const long long best = std::min(std::min(c_big, c_8a), std::min(c_8b, c_8c));
   ProjArgs args = a;
   void* kargs[] = {&args};
   if (c_big == best) {
@@ -532,21 +546,19 @@ hipError_t launch_tb(const ProjArgs& a, hipStream_t s) {
     return hipLaunchKernel(reinterpret_cast<const void*>(&proj_gemm_kernel<HEAD_OUT, 4>), dim3((unsigned)big),
                            dim3(kThreads), kargs, 0, s);
   }
-  if (c_small == best) {
-    args.xcd_fp = xcd_split(a, nb4, (M + 127) / 128);
-    return hipLaunchKernel(reinterpret_cast<const void*>(&proj_gemm_kernel<HEAD_OUT, 2>), dim3((unsigned)small),
-                           dim3(kThreads), kargs, 0, s);
-  }
   if (c_8a == best) {
     args.xcd_fp = xcd_split(a, nb8a, mb8a);
     return hipLaunchKernel(reinterpret_cast<const void*>(&proj_gemm8_kernel<HEAD_OUT, 4, 2, 3>),
                            dim3((unsigned)(nb8a * mb8a)), dim3(512), kargs, 0, s);
   }
-  {
+  if (c_8b == best) {
     args.xcd_fp = xcd_split(a, nb8b, mb8b);
     return hipLaunchKernel(reinterpret_cast<const void*>(&proj_gemm8_kernel<HEAD_OUT, 2, 5, 1>),
                            dim3((unsigned)(nb8b * mb8b)), dim3(512), kargs, 0, s);
   }
+  args.xcd_fp = xcd_split(a, nb8c, mb8c);
+  return hipLaunchKernel(reinterpret_cast<const void*>(&proj_gemm8_kernel<HEAD_OUT, 2, 2, 1>),
+                         dim3((unsigned)(nb8c * mb8c)), dim3(512), kargs, 0, s);
 }
 
 }  // namespace

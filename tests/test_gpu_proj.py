@@ -3,8 +3,8 @@ fp64 oracle on the same bf16 inputs, and of the whole multi-head sub-layer
 (projections + attention + output projection) built from the library's
 entry points.  Weights are seeded N(0, 1/d_model) draws (no trained weights
 are needed: the projections are plain linear maps).  The shapes reach every
-tile the launcher picks (128 x 256 and 128 x 128 on four waves, 256 x 192 and
-320 x 128 on eight) and every tile order: XCD rectangles of all,
+tile the launcher picks (128 x 256 on four waves; 256 x 192, 320 x 128 and
+128 x 128 on eight) and every tile order: XCD rectangles of all,
 1/2, 1/4 or 1/8 of the feature blocks, a last partial group of token blocks,
 and the plain order for grids the split does not divide.
 
@@ -45,8 +45,8 @@ def _weights(g, rows, d_model):
     (32, 160, 16, 2),   # Transformer-big encoder output -> K, V of cross attention
     (3, 77, 3, 1),      # ragged tokens (M = 231) and features (N = 192)
     (1, 1, 1, 3),       # one token, one head
-    (32, 128, 16, 3),   # Transformer-big self-attention Q, K, V (256-token tiles)
-    (41, 97, 13, 3),    # 256-token tiles, ragged M = 3977 and N = 2496 (not a multiple of 128)
+    (32, 128, 16, 3),   # Transformer-big self-attention Q, K, V (256 x 192 tiles)
+    (41, 97, 13, 3),    # 256 x 192 tiles, ragged M = 3977, N = 2496
     (2, 128, 16, 3),    # few tokens: each XCD takes 1/8 of the feature blocks
     (8, 128, 16, 2),    # XCD rectangles of 1/4 of the feature blocks by 1/2 of the tokens
     (144, 128, 16, 1),  # 9 token blocks per XCD: a full group of 8 and a group of 1
