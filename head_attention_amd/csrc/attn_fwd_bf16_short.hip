@@ -41,6 +41,8 @@ constexpr uint32_t kTileChunks = kBN * 8;  // 16-byte chunks per tile
 
 __shared__ uint4 s_k[kMaxTiles * kTileChunks];
 __shared__ uint4 s_v[kMaxTiles * kTileChunks];
+// Each wave's output rows on their way to memory (32 rows x 128 bytes).
+__shared__ uint4 s_o[kWaves * 32 * 8];
 
 // Weights of one tile under pivot term mc = m c: exp2(s c - mc), packed to
 // bf16 pairs in the order P.V consumes them (keys 0..31 from s0, 32..63 from
@@ -283,19 +285,29 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_short_kernel(FwdArg
   // padded row or a row with no allowed key (one lane per row writes).
   if (a.lse && hh == 0 && qi < a.n_q)
     a.lse[(size_t)bh * a.n_q + qi] = live ? (mc + __builtin_amdgcn_logf(l_row)) * kLn2 : -INFINITY;
-  if (qi < a.n_q) {
-    __bf16* orow = O + (size_t)qi * kHeadDim;
+  // The rows go through this wave's own LDS area, so that each store
+  // writes whole 128-byte rows (8 lanes a row) rather than 16-byte pieces
+  // of 32 rows: row ln's 16-byte piece c (d 8 c .. 8 c + 7) sits at
+  // position c ^ (ln % 8).  A wave's LDS operations complete in order, so
+  // its reads see its writes.
+  lds_char* so = (lds_char*)(uintptr_t)(lds_void_t*)(s_o + 256 * wave);
 #pragma unroll
-    for (int ob = 0; ob < 2; ++ob) {
-      const f32x16& o = ob ? o1 : o0;
+  for (int ob = 0; ob < 2; ++ob) {
+    const f32x16& o = ob ? o1 : o0;
 #pragma unroll
-      for (int gg = 0; gg < 4; ++gg) {
-        uint2 w;
-        w.x = live ? pack_bf16x2(o[4 * gg + 0] * inv, o[4 * gg + 1] * inv) : 0u;
-        w.y = live ? pack_bf16x2(o[4 * gg + 2] * inv, o[4 * gg + 3] * inv) : 0u;
-        *reinterpret_cast<uint2*>(orow + 32 * ob + 8 * gg + 4 * hh) = w;
-      }
+    for (int gg = 0; gg < 4; ++gg) {
+      u32x2 w;
+      w.x = live ? pack_bf16x2(o[4 * gg + 0] * inv, o[4 * gg + 1] * inv) : 0u;
+      w.y = live ? pack_bf16x2(o[4 * gg + 2] * inv, o[4 * gg + 3] * inv) : 0u;
+      *(lds_u32x2*)(so + ln * 128 + (((4 * ob + gg) ^ (ln & 7)) << 4) + 8 * hh) = w;
     }
+  }
+  const int q = lane & 7;
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int row = 8 * it + (lane >> 3);
+    const uint4 v = __builtin_bit_cast(uint4, *(const lds_uint4*)(so + row * 128 + ((q ^ (row & 7)) << 4)));
+    if (qw0 + row < a.n_q) *reinterpret_cast<uint4*>(O + (size_t)(qw0 + row) * kHeadDim + 8 * q) = v;
   }
 }
 

@@ -36,9 +36,6 @@
 namespace headattn {
 namespace {
 
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
-
 constexpr int kThreads = 256;
 constexpr int kBN = 128;  // output features per workgroup
 constexpr int kBK = 32;   // k per step

@@ -24,6 +24,8 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 typedef __attribute__((address_space(3))) uint4 lds_uint4;
 typedef __attribute__((address_space(3))) char lds_char;
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
 
 // One bf16 row of K, V, Q or O (d = 64).
 constexpr uint32_t kRowBytes = kHeadDim * 2;
