@@ -34,8 +34,8 @@
 // Against the paired kernel on this workload (512-row workgroups instead of
 // 256): half the workgroups, so one dispatch round where it took two; no
 // pair merge through LDS; one prologue per 512 rows; no second launch for
-// the moving-pivot fallback; a row group stores its rows as soon as its
-// last product is done, while the other half of the workgroup finishes.
+// the moving-pivot fallback.  Each row group's rows leave through LDS
+// once the workgroup has passed its last barrier, as whole 128-byte rows.
 //
 // Layouts as in the paired kernel: K rows (and the staged Q rows) keep
 // their 16-byte chunks XOR-swizzled by row; V stays row-major (chunks
@@ -498,12 +498,22 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_band_kernel(FwdArgs
     }
   };
   // O = acc / l, bf16; log-sum-exp (m + log2 l) ln 2.  Padded rows and rows
-  // with no allowed key are written as exact zeros (lse -inf).  A fresh copy
-  // of the lane's row index: the output addresses are rebuilt from it here
-  // instead of being held in registers through the tile loop.
-  auto store_rows = [&](const float (&l)[2]) __attribute__((always_inline)) {
-    int ln_e = ln;
-    asm volatile("" : "+v"(ln_e));
+  // with no allowed key are written as exact zeros (lse -inf).  pack_rows
+  // forms the bf16 rows in registers (and writes the lse); store_rows sends
+  // them through K slot `wave` (free once every wave has passed the last
+  // barrier, and used by no other wave after it), so that each store writes
+  // whole 128-byte rows, 8 lanes a row, rather than 16-byte pieces of 32
+  // rows: row r's 16-byte piece c (d 8 c .. 8 c + 7) sits at position
+  // c ^ (r % 8).  A wave's LDS operations complete in order, so its reads
+  // see its writes.  Both rebuild their addresses from a fresh copy of the
+  // lane index instead of holding them in registers through the tile loop.
+  // Register r of block (db, qb) holds d = 32 db + 8 (r / 4) + 4 hh + r % 4
+  // of query row qw0 + 32 qb + ln: four consecutive d, packed into w[vg]
+  // with vg = 8 db + 4 qb + r / 4.
+  auto pack_rows = [&](const float (&l)[2], u32x2 (&w)[16]) __attribute__((always_inline)) {
+    int lane_e = lane;
+    asm volatile("" : "+v"(lane_e));
+    const int ln_e = lane_e & 31;
     float inv[2];
     bool live[2];
 #pragma unroll
@@ -511,22 +521,34 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_band_kernel(FwdArgs
       const int qi = qw0 + 32 * qb + ln_e;
       live[qb] = qi < q_len && l[qb] > 0.f;
       inv[qb] = live[qb] ? 1.f / l[qb] : 0.f;
-      if (a.lse && hh == 0 && qi < a.n_q)
+      if (a.lse && lane_e < 32 && qi < a.n_q)
         a.lse[(size_t)bh * a.n_q + qi] = live[qb] ? (mc[qb] + __builtin_amdgcn_logf(l[qb])) * kLn2 : -INFINITY;
     }
-    // Register r of block (db, qb) holds d = 32 db + 8 (r / 4) + 4 hh + r % 4
-    // of query row qw0 + 32 qb + ln: four consecutive d per 8-byte store.
     static_for<16>([&](auto vg_tag) {
       constexpr int VG = decltype(vg_tag)::value;
       constexpr int DB = VG / 8, QB = (VG / 4) % 2, G = VG % 4, R = 4 * G;
-      const int qi = qw0 + 32 * QB + ln_e;
-      if (qi < a.n_q) {
-        uint2 w;
-        w.x = live[QB] ? pack_bf16x2(o[DB][QB][R] * inv[QB], o[DB][QB][R + 1] * inv[QB]) : 0u;
-        w.y = live[QB] ? pack_bf16x2(o[DB][QB][R + 2] * inv[QB], o[DB][QB][R + 3] * inv[QB]) : 0u;
-        *reinterpret_cast<uint2*>(O + (size_t)qi * kHeadDim + 32 * DB + 8 * G + 4 * hh) = w;
-      }
+      w[VG].x = live[QB] ? pack_bf16x2(o[DB][QB][R] * inv[QB], o[DB][QB][R + 1] * inv[QB]) : 0u;
+      w[VG].y = live[QB] ? pack_bf16x2(o[DB][QB][R + 2] * inv[QB], o[DB][QB][R + 3] * inv[QB]) : 0u;
     });
+  };
+  auto store_rows = [&](const u32x2 (&w)[16]) __attribute__((always_inline)) {
+    int lane_e = lane;
+    asm volatile("" : "+v"(lane_e));
+    const int ln_e = lane_e & 31, hh_e = lane_e >> 5;
+    lds_char* so = (lds_char*)(uintptr_t)kslot_addr(wave);
+    static_for<16>([&](auto vg_tag) {
+      constexpr int VG = decltype(vg_tag)::value;
+      constexpr int DB = VG / 8, QB = (VG / 4) % 2, G = VG % 4;
+      const int r = 32 * QB + ln_e;
+      *(lds_u32x2*)(so + r * 128 + (((4 * DB + G) ^ (r & 7)) << 4) + 8 * hh_e) = w[VG];
+    });
+    const int q = lane_e & 7;
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int r = 8 * it + (lane_e >> 3);
+      const uint4 v = __builtin_bit_cast(uint4, *(const lds_uint4*)(so + r * 128 + ((q ^ (r & 7)) << 4)));
+      if (qw0 + r < a.n_q) *reinterpret_cast<uint4*>(O + (size_t)(qw0 + r) * kHeadDim + 8 * q) = v;
+    }
   };
 
   // ---- the fixed-pivot pass over the rings.
@@ -627,6 +649,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_band_kernel(FwdArgs
   // above 64 or far below -32 in log2 units -- is recomputed below; rows
   // without one (padded, kv_len = 0, an empty window) are zeros either way.
   bool ok;
+  u32x2 w[16];
   {
     float l[2];
     row_sums(l);
@@ -645,12 +668,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_band_kernel(FwdArgs
       bad = bad || (keys && !in_range);
     }
     ok = __builtin_amdgcn_ballot_w64(bad) == 0;
-    if (ok) store_rows(l);
+    if (ok) pack_rows(l, w);
   }
-  if (n_run == 0) return;
   // No wave reads a ring or has a fill in flight past this barrier.
-  barrier_lds();
-  if (ok) return;
+  if (n_run > 0) barrier_lds();
+  if (ok) {
+    store_rows(w);
+    return;
+  }
 
   // ---- a row group that failed the range check: its window again, under
   // the moving pivot, one tile at a time through its own K and V slots
@@ -664,12 +689,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_band_kernel(FwdArgs
     for (int u = 0; u < cnt; ++u) {
       const int T = g + u;
       const uint32_t toff = tile_off(T);
+      // Fill offsets from a fresh copy of the lane index each tile: held
+      // through the pipeline they would not fit the registers.
+      int lf = lane;
+      asm volatile("" : "+v"(lf));
+      const int frow = lf >> 3, fp = lf & 7;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const int r = 8 * j + qrow;
+        const int r = 8 * j + frow;
         const uint32_t roff = toff + (uint32_t)r * kRowBytes;
-        lds_fill16_at(rk, kdst + 1024u * j, roff + 16u * (uint32_t)(fpos ^ k_swz(r)));
-        lds_fill16_at(rv, vdst + 1024u * j, roff + 16u * (uint32_t)(fpos ^ (2 * (r & 3))));
+        lds_fill16_at(rk, kdst + 1024u * j, roff + 16u * (uint32_t)(fp ^ k_swz(r)));
+        lds_fill16_at(rv, vdst + 1024u * j, roff + 16u * (uint32_t)(fp ^ (2 * (r & 3))));
       }
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): both tiles have landed
       bf16x8 ka[2][4];
@@ -691,7 +721,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_band_kernel(FwdArgs
     }
     float l[2];
     row_sums(l);
-    store_rows(l);
+    pack_rows(l, w);
+    store_rows(w);
   }
 }
 
