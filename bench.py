@@ -375,12 +375,19 @@ FWD_MODES = {"0": "none", "1": "causal", "2": "band"}
 def _short_kernel(name: str) -> str:
     """attn_fwd_bf16[_pair|_short]_kernel<mode> and the backward's dK/dV and dQ
     kernels -> ..._kernel<none|causal|band>;
-    the bool-templated kernels -> <true|false>; other kernels of the library by
-    their plain name."""
+    the projection kernel -> proj_gemm_kernel<head_out, tokens x features of
+    its tile>; the bool-templated kernels -> <true|false>; other kernels of
+    the library by their plain name."""
     import re
     m = re.search(r"(attn_fwd_bf16(?:_pair|_short)?_kernel|bwd_dkdv_kernel|bwd_dq_kernel)(?:<|ILi)(\d)", name)
     if m:
         return f"{m.group(1)}<{FWD_MODES[m.group(2)]}>"
+    m = re.search(r"proj_gemm_kernel<(true|false), (\d), (\d), (\d)>", name) or \
+        re.search(r"proj_gemm_kernelILb(\d)ELi(\d)ELi(\d)ELi(\d)E", name)
+    if m:
+        wm, tbw, fbw = int(m.group(2)), int(m.group(3)), int(m.group(4))
+        head_out = m.group(1) in ("true", "1")
+        return f"proj_gemm_kernel<{'true' if head_out else 'false'}, {32 * tbw * wm}x{32 * fbw * (8 // wm)}>"
     m = re.search(r"(attn_fwd_bf16(?:_pair|_short)?_kernel|proj_gemm_kernel|bwd_dkdv_kernel|bwd_dq_kernel)<(true|false)", name) or \
         re.search(r"(attn_fwd_bf16(?:_pair|_short)?_kernel|proj_gemm_kernel|bwd_dkdv_kernel|bwd_dq_kernel)ILb(\d)", name)
     if m:
@@ -411,10 +418,10 @@ LEG_GRIDS = {("attn_fwd_bf16_short_kernel<none>", 65536): "encoder_base",
              ("bwd_dkdv_kernel<none>", 262144): "decoder_big_bwd (cross)",
              ("bwd_dq_kernel<none>", 131072): "decoder_big_bwd (cross)",
              ("bwd_rowdot_kernel", 524288): "decoder_big_bwd (self and cross)",
-             ("proj_gemm_kernel<true>", 98304): "mha_proj (self Q, K, V)",
-             ("proj_gemm_kernel<true>", 65536): "mha_proj (cross Q)",
-             ("proj_gemm_kernel<true>", 81920): "mha_proj (cross K, V)",
-             ("proj_gemm_kernel<false>", 65536): "mha_proj (self and cross output)",
+             ("proj_gemm_kernel<true, 256x192>", 131072): "mha_proj (self Q, K, V)",
+             ("proj_gemm_kernel<true, 128x128>", 131072): "mha_proj (cross Q)",
+             ("proj_gemm_kernel<true, 320x128>", 131072): "mha_proj (cross K, V)",
+             ("proj_gemm_kernel<false, 128x128>", 131072): "mha_proj (self and cross output)",
              ("attn_fwd_bf16_pair_kernel<causal>", 262144): "long_causal",
              ("decode_partial_kernel", 4194304): "kv_decode",
              ("decode_merge_kernel", 65536): "kv_decode",

@@ -9,25 +9,30 @@
 //                           the [B, h, n, 64] attention output in place (no
 //                           concatenation copy).
 //
-// Both run on one GEMM, C^T = W A^T with W [N, K] (one row per output
-// feature, k contiguous) and A [M, K] (one row per token), in two kernels
-// (the 4-wave kernel below, and an 8-wave kernel with larger tiles for
-// shapes whose 4-wave tiles would load the compute units unevenly): on
+// Both run on one GEMM kernel, C^T = W A^T with W [N, K] (one row per output
+// feature, k contiguous) and A [M, K] (one row per token): on
 // v_mfma_f32_32x32x16_bf16 the A operand is a W fragment and the B operand
 // an A fragment, both 16 contiguous bytes of a k-contiguous row, and each
-// lane ends up holding four consecutive output features of one token -- one
-// 8-byte store, along a head's 64 dimensions or along Y's row.
+// lane ends up holding four consecutive output features of one token.
 //
-// 4-wave kernel: 2 (features) x 2 (tokens) waves; a wave owns 64 features x
-// 32 TB tokens (2 x TB blocks of 32 x 32), so per 16-wide k step it reads
-// 2 + TB fragments from LDS for 2 TB products; the launcher uses TB = 4, a
-// 128 x 256 tile, two workgroups per compute unit.  K runs in
-// steps of 32: the W and A tiles of a step reach LDS by buffer loads that
-// write LDS directly, into a ring of three slots two steps ahead of use, one
-// bare barrier per step.  Rows past the end of W or A read as zero through
-// the descriptor's range check.  For the output projection two K steps make
-// one head, so the A tile of a step is a 32-wide column band of one head's
-// [n, 64] slab: a per-row offset, no gather of single elements.
+// One 8-wave workgroup per compute unit.  The tile is TM tokens x TN
+// features, the waves on a WM x WN grid (WM WN = 8), each owning 32 TBW
+// tokens x 32 FBW features: 256 x 192 (WM 4, TBW 2, FBW 3), 320 x 128 (WM 2,
+// TBW 5, FBW 1) or 128 x 128 (WM 2, TBW 2, FBW 1), whichever leaves the least
+// work on the busiest compute unit.  The decoder's self Q, K, V at
+// 4096 x 3072 makes exactly 256 tiles of 256 x 192 and its cross K, V at
+// 5120 x 2048 exactly 256 of 320 x 128, so every compute unit gets the same
+// work.  Two waves per SIMD.  K runs in steps of 64 through two slots (448
+// rows, 56 KB each) or three (256 rows): the W and A rows of a step reach
+// LDS by buffer loads that write LDS directly, and a row's step is 128
+// bytes, so every fill reads whole cache lines (64-byte steps read half
+// lines, and fetched about 26 bytes per clock per compute unit here, against
+// what the products need).  A step's fills go out as soon as its slot
+// frees, one bare barrier per step.  Rows past the end of W or A read as
+// zero through the descriptor's range check.  For the output projection a
+// step is one whole head: A row m's step kt is O[b, kt, t, :], a per-row
+// offset, no gather of single elements.  The output leaves through LDS in
+// whole 128-byte rows.
 #include <algorithm>
 #include <type_traits>
 
@@ -35,32 +40,6 @@
 
 namespace headattn {
 namespace {
-
-constexpr int kThreads = 256;
-constexpr int kBN = 128;  // output features per workgroup
-constexpr int kBK = 32;   // k per step
-constexpr int kSlots = 3;
-constexpr uint32_t kStepBytes = kBK * 2;        // bytes of one row in one step
-
-// Ring slots: the W tile (128 rows) and the A tile (up to 256 rows) of one
-// step, rows of 64 B (4 chunks of 16 B; chunk c of row r at position
-// c ^ ((r / 4) % 4)).  A fragment read has its lanes on consecutive rows and
-// the LDS serves 16 lanes (256 bytes) per cycle: rows r, r + 4, r + 8,
-// r + 12 fall on the same banks and take 4 different positions, so the read
-// is free of bank conflicts.  ((r / 2) % 4 gave those rows 2 positions:
-// half of the kernel's active LDS cycles were conflict stalls.)
-// Slot S: its W tile at row 384 S, its A tile at row 384 S + 128.  The
-// epilogue reuses the whole ring.
-__shared__ uint4 g_ring4[kSlots * (kBN + 256) * 4];
-
-template <int S>
-__device__ __forceinline__ uint4* wslot() {
-  return g_ring4 + S * (kBN + 256) * 4;
-}
-template <int S>
-__device__ __forceinline__ uint4* aslot() {
-  return g_ring4 + S * (kBN + 256) * 4 + kBN * 4;
-}
 
 // Wait until at most N of this wave's buffer loads are outstanding and its
 // LDS operations are done, then a bare workgroup barrier (a workgroup fence
@@ -74,232 +53,17 @@ __device__ __forceinline__ void wait_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <bool HEAD_OUT, int TB>
-__global__ __launch_bounds__(kThreads, 2) void proj_gemm_kernel(ProjArgs a) {
-  constexpr int kBM = 64 * TB;  // tokens per workgroup
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63;
-  const int ln = lane & 31;
-  const int hh = lane >> 5;
-  const int wn = wave & 1;   // feature half of the tile
-  const int wm = wave >> 1;  // token half of the tile
-
-  // Tile of this workgroup.  Workgroup ids go round robin over the 8 XCDs;
-  // with xcd_fp = f each XCD owns a rectangle of f/8 of the token blocks by
-  // 1/f of the feature blocks, so a tile's X rows and W rows are mostly
-  // already in that XCD's L2 (the plain order sends the 8 feature blocks of
-  // one token block to 8 different XCDs, each fetching the same X rows).
-  const int n_blocks = (a.N + kBN - 1) / kBN;
-  int nb = blockIdx.x % n_blocks;
-  int mb = blockIdx.x / n_blocks;
-  if (a.xcd_fp > 0) {
-    const int fp = a.xcd_fp;
-    const int x = blockIdx.x & 7;
-    const int l = blockIdx.x >> 3;
-    const int nbr = n_blocks / fp;                               // feature blocks per rectangle
-    const int mbr = ((a.M + kBM - 1) / kBM) / (8 / fp);         // token blocks per rectangle
-    // Inside the rectangle, groups of up to 8 token blocks walk all its
-    // feature blocks, so the workgroups an XCD runs at once share X rows
-    // and W rows (a long rectangle walked row by row would stream all its W
-    // rows through L2 once per token block).
-    const int g0 = l / (8 * nbr) * 8;  // first token block of l's group
-    const int gs = min(8, mbr - g0);   // token blocks in the group
-    const int r = l - g0 * nbr;
-    nb = (x % fp) * nbr + r / gs;
-    mb = (x / fp) * mbr + g0 + r % gs;
-  }
-  const int n0 = nb * kBN;
-  const int m0 = mb * kBM;
-  const int K = a.K;
-  const int nk = K / kBK;
-
-  // ---- fills: one instruction of a wave covers 16 rows of a tile; lane l
-  // writes position l % 4 of row l / 4, which receives the row's chunk
-  // (l % 4) ^ ((row / 4) % 4).  Per step a wave fills 32 rows of W
-  // (2 loads) and 16 TB rows of A (TB loads).
-  const __amdgpu_buffer_rsrc_t rw =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.W), (short)0, (int)a.w_bytes, kBufferWord3);
-  const __amdgpu_buffer_rsrc_t ra =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.A), (short)0, (int)a.a_bytes, kBufferWord3);
-  const int fpos = lane & 3;
-  uint32_t w_off[2], a_off[TB];
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int row = 32 * wave + 16 * q + (lane >> 2);
-    const uint32_t chunk = 16u * (uint32_t)(fpos ^ ((row >> 2) & 3));
-    const int n = n0 + row;
-    w_off[q] = n < a.N ? (uint32_t)n * (uint32_t)K * 2u + chunk : kOutOfRange;
-  }
-#pragma unroll
-  for (int q = 0; q < TB; ++q) {
-    const int row = 16 * TB * wave + 16 * q + (lane >> 2);
-    const uint32_t chunk = 16u * (uint32_t)(fpos ^ ((row >> 2) & 3));
-    const int m = m0 + row;
-    if (HEAD_OUT) {
-      // A = X [M, K] row-major
-      a_off[q] = m < a.M ? (uint32_t)m * (uint32_t)K * 2u + chunk : kOutOfRange;
-    } else {
-      // A = Concat(heads of O): row m = (b, t), head s of O[b, s, t, :]
-      const int b = m / a.n_seq;
-      const int t = m - b * a.n_seq;
-      a_off[q] = m < a.M ? ((uint32_t)b * (uint32_t)a.H * (uint32_t)a.n_seq + (uint32_t)t) * (kHeadDim * 2u) + chunk
-                         : kOutOfRange;
-    }
-  }
-  // Byte offset of step kt along an A row: 64 B per step for X; for O, head
-  // kt / 2 (n_seq rows of 128 B further each) and half kt % 2 of its 64 d.
-  auto a_step = [&](int kt) __attribute__((always_inline)) -> uint32_t {
-    return HEAD_OUT ? (uint32_t)kt * kStepBytes
-                    : (uint32_t)(kt >> 1) * (uint32_t)a.n_seq * (kHeadDim * 2u) + (uint32_t)(kt & 1) * kStepBytes;
-  };
-  auto fill = [&](auto slot_tag, int kt) __attribute__((always_inline)) {
-    constexpr int S = decltype(slot_tag)::value;
-    const uint32_t ws = (uint32_t)kt * kStepBytes, as = a_step(kt);
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const uint32_t wo = w_off[q] == kOutOfRange ? kOutOfRange : w_off[q] + ws;
-      lds_fill16(rw, wslot<S>() + 128 * wave + 64 * q, wo);
-    }
-#pragma unroll
-    for (int q = 0; q < TB; ++q) {
-      const uint32_t ao = a_off[q] == kOutOfRange ? kOutOfRange : a_off[q] + as;
-      lds_fill16(ra, aslot<S>() + 64 * TB * wave + 64 * q, ao);
-    }
-  };
-
-  f32x16 acc[2][TB];  // [feature block][token block]
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < TB; ++j) acc[i][j] = f32x16{};
-
-  // One step: S = kt % 3 is its slot.  Step kt has landed (only step kt + 1's
-  // loads may be in flight) and every wave is done with step kt - 1, whose
-  // slot step kt + 2 takes.  Fragments of k sub-step s: lane (ln, hh) reads
-  // row 64 wn + 32 blk + ln of W (32 TB wm + 32 blk + ln of A), chunk
-  // 2 s + hh (k 16 s + 8 hh .. + 7).
-  auto step = [&](auto slot_tag, int kt) __attribute__((always_inline)) {
-    constexpr int S = decltype(slot_tag)::value;
-    using S2 = std::integral_constant<int, (S + 2) % kSlots>;
-    if (kt >= nk) return;
-    wait_barrier<2 + TB>();
-    fill(S2(), kt + 2);
-    const uint4* wt = wslot<S>();
-    const uint4* at = aslot<S>();
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int ch = 2 * s + hh;
-      bf16x8 wf[2], af[TB];
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
-        const int r = 64 * wn + 32 * blk + ln;
-        wf[blk] = __builtin_bit_cast(bf16x8, wt[r * 4 + (ch ^ ((r >> 2) & 3))]);
-      }
-#pragma unroll
-      for (int blk = 0; blk < TB; ++blk) {
-        const int r = 32 * TB * wm + 32 * blk + ln;
-        af[blk] = __builtin_bit_cast(bf16x8, at[r * 4 + (ch ^ ((r >> 2) & 3))]);
-      }
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < TB; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[i], af[j], acc[i][j], 0, 0, 0);
-    }
-  };
-
-  using Slot0 = std::integral_constant<int, 0>;
-  using Slot1 = std::integral_constant<int, 1>;
-  using Slot2 = std::integral_constant<int, 2>;
-  fill(Slot0(), 0);
-  fill(Slot1(), 1);
-  for (int kt = 0; kt < nk; kt += kSlots) {
-    step(Slot0(), kt);
-    step(Slot1(), kt + 1);
-    step(Slot2(), kt + 2);
-  }
-  // The last two fills (past the end of K: out of range, zeros, never read)
-  // land before the workgroup's LDS is released.
-  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0)
-
-  // ---- epilogue through LDS, as in the 8-wave kernel below: whole
-  // 128-byte rows per store.  The tile is 2 chunks of 64 features (each one
-  // head of one projection) by kBM tokens; chunk c, token u at (c kBM + u)
-  // 128 bytes, its 16-byte piece q at position q ^ (u % 8).  Register r of
-  // block (i, j) holds feature 64 wn + 32 i + 8 (r / 4) + 4 hh + r % 4 (chunk
-  // wn) of token 32 TB wm + 32 j + ln of the tile.
-  barrier_lds();  // every wave is done with the ring
-  {
-    lds_char* st = (lds_char*)(uintptr_t)(lds_void_t*)g_ring4;
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < TB; ++j) {
-        const int u = 32 * TB * wm + 32 * j + ln;
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int f = 32 * i + 8 * g + 4 * hh;  // lane's first feature within the chunk
-          const int q = f >> 3;
-          u32x2 v;
-          v.x = pack_bf16x2(acc[i][j][4 * g], acc[i][j][4 * g + 1]);
-          v.y = pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
-          *(lds_u32x2*)(st + (wn * kBM + u) * 128 + ((q ^ (u & 7)) << 4) + (f & 4) * 2) = v;
-        }
-      }
-  }
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-  barrier_lds();
-  const int d_model = a.H * kHeadDim;
-  const lds_char* st = (const lds_char*)(uintptr_t)(lds_void_t*)g_ring4;
-  const int q = lane & 7;
-#pragma unroll 2
-  for (int it = 0; it < 2 * kBM / 32; ++it) {
-    const int row = 32 * it + 8 * wave + (lane >> 3);
-    const int c = row / kBM, u = row - c * kBM;
-    const int nf = n0 + 64 * c;  // first feature of the chunk
-    const int m = m0 + u;
-    const uint4 v = __builtin_bit_cast(uint4, *(const lds_uint4*)(st + row * 128 + ((q ^ (u & 7)) << 4)));
-    if (nf >= a.N || m >= a.M) continue;
-    __bf16* dst;
-    if (HEAD_OUT) {
-      const int p = nf / d_model;
-      const int hd = (nf - p * d_model) / kHeadDim;
-      const int b = m / a.n_seq;
-      const int t = m - b * a.n_seq;
-      dst = static_cast<__bf16*>(a.out[p]) + (((size_t)b * a.H + hd) * a.n_seq + t) * kHeadDim;
-    } else {
-      dst = static_cast<__bf16*>(a.out[0]) + (size_t)m * a.N + nf;
-    }
-    *reinterpret_cast<uint4*>(dst + 8 * q) = v;
-  }
-}
-
-// ---- large shapes: one 8-wave workgroup per compute unit.  The tile is TM
-// tokens x TN features with TM + TN = 448 rows, the waves on a WM x WN grid
-// (WM WN = 8), each owning 32 TBW tokens x 32 FBW features: 256 x 192 (WM 4,
-// TBW 2, FBW 3), 320 x 128 (WM 2, TBW 5, FBW 1) or 128 x 128 (WM 2, TBW 2,
-// FBW 1).  A shape whose tiles of one of these sizes number about the
-// compute units (the decoder's self Q, K, V at 4096 x 3072 makes exactly 256
-// of 256 x 192, its cross K, V at 5120 x 2048 256 of 320 x 128) then gives
-// every compute unit the same work, where the 4-wave kernel's tiles leave
-// some compute units two and others one; and 128 x 128 tiles keep two waves
-// per SIMD where the 4-wave kernel would have one.  K runs in steps of 64
-// through two slots (448 rows, 56 KB each) or three (256 rows): a row's
-// step is 128 bytes, so every fill reads whole cache lines (64-byte steps
-// read half lines and fetched about 26 bytes per clock per compute unit
-// here, against what the products need).  A step's fills go out as soon as
-// its slot frees, one bare barrier per step.
-constexpr uint32_t kRowBytes8 = 128;  // k 64 per step: 8 chunks of 16 bytes
+constexpr uint32_t kStepRowBytes = 128;  // a row's k step of 64: 8 chunks of 16 bytes
 // The ring: two slots of 448 rows, or three of 256 (112 KB either way at most).
-__shared__ uint4 g_ring8[2 * 448 * 8];
+__shared__ uint4 g_ring[2 * 448 * 8];
 
 template <int ROWS>
-__device__ __forceinline__ uint32_t ring8_addr(int slot) {
-  return (uint32_t)(uintptr_t)(lds_void_t*)&g_ring8[0] + (uint32_t)slot * (ROWS * kRowBytes8);
+__device__ __forceinline__ uint32_t ring_addr(int slot) {
+  return (uint32_t)(uintptr_t)(lds_void_t*)&g_ring[0] + (uint32_t)slot * (ROWS * kStepRowBytes);
 }
 
 template <bool HEAD_OUT, int WM, int TBW, int FBW>
-__global__ __launch_bounds__(512, 1) void proj_gemm8_kernel(ProjArgs a) {
+__global__ __launch_bounds__(512, 1) void proj_gemm_kernel(ProjArgs a) {
   constexpr int WN = 8 / WM;
   constexpr int TM = 32 * TBW * WM;  // tokens per workgroup
   constexpr int TN = 32 * FBW * WN;  // output features per workgroup
@@ -317,7 +81,14 @@ __global__ __launch_bounds__(512, 1) void proj_gemm8_kernel(ProjArgs a) {
   const int wn = wave % WN;  // feature group of the tile
   const int wm = wave / WN;  // token group of the tile
 
-  // Tile of this workgroup, XCD-aware as in the 4-wave kernel.
+  // Tile of this workgroup.  Workgroup ids go round robin over the 8 XCDs;
+  // with xcd_fp = f each XCD owns a rectangle of f/8 of the token blocks by
+  // 1/f of the feature blocks, so a tile's X rows and W rows are mostly
+  // already in that XCD's L2 (the plain order sends the feature blocks of
+  // one token block to different XCDs, each fetching the same X rows).
+  // Inside the rectangle, groups of up to 8 token blocks walk all its
+  // feature blocks, so the workgroups an XCD runs at once share X rows and
+  // W rows.
   const int n_blocks = (a.N + TN - 1) / TN;
   int nb = blockIdx.x % n_blocks;
   int mb = blockIdx.x / n_blocks;
@@ -372,7 +143,7 @@ __global__ __launch_bounds__(512, 1) void proj_gemm8_kernel(ProjArgs a) {
   }
   auto fill = [&](auto slot_tag, int kt) __attribute__((always_inline)) {
     constexpr int S = decltype(slot_tag)::value;
-    const uint32_t base = ring8_addr<kRows>(S);
+    const uint32_t base = ring_addr<kRows>(S);
     const uint32_t ws = (uint32_t)kt * 128u;
     const uint32_t as = HEAD_OUT ? (uint32_t)kt * 128u : (uint32_t)kt * (uint32_t)a.n_seq * (kHeadDim * 2u);
 #pragma unroll
@@ -402,7 +173,7 @@ __global__ __launch_bounds__(512, 1) void proj_gemm8_kernel(ProjArgs a) {
     if (kt >= nk) return;
     wait_barrier<(kSlots - 2) * kFillPerWave>();
     fill(SF(), kt + kSlots - 1);
-    const lds_uint4* t = (const lds_uint4*)(uintptr_t)ring8_addr<kRows>(S);
+    const lds_uint4* t = (const lds_uint4*)(uintptr_t)ring_addr<kRows>(S);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int ch = 2 * s + hh;
@@ -456,7 +227,7 @@ __global__ __launch_bounds__(512, 1) void proj_gemm8_kernel(ProjArgs a) {
   constexpr int kChunks = TN / 64;
   barrier_lds();  // every wave is done with the ring
   {
-    lds_char* st = (lds_char*)(uintptr_t)ring8_addr<kRows>(0);
+    lds_char* st = (lds_char*)(uintptr_t)ring_addr<kRows>(0);
 #pragma unroll
     for (int i = 0; i < FBW; ++i)
 #pragma unroll
@@ -476,7 +247,7 @@ __global__ __launch_bounds__(512, 1) void proj_gemm8_kernel(ProjArgs a) {
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
   barrier_lds();
   const int d_model = a.H * kHeadDim;
-  const lds_char* st = (const lds_char*)(uintptr_t)ring8_addr<kRows>(0);
+  const lds_char* st = (const lds_char*)(uintptr_t)ring_addr<kRows>(0);
   const int q = lane & 7;
 #pragma unroll 2
   for (int it = 0; it < kChunks * TM / 64; ++it) {
@@ -519,43 +290,32 @@ int xcd_split(const ProjArgs& a, long long n_blocks, long long m_blocks) {
 
 template <bool HEAD_OUT>
 hipError_t launch_tb(const ProjArgs& a, hipStream_t s) {
-  // The candidate with the least work on its busiest compute unit (ties go
-  // to the earlier one in this order): the 4-wave kernel's 128 x 256 tiles
-  // (two workgroups per compute unit) or the 8-wave kernel's 256 x 192,
-  // 320 x 128 or 128 x 128 tiles (one workgroup per compute unit).
-  // Workgroups are spread evenly over the 256 compute units.
+  // The tile with the least work on its busiest compute unit (ties go to the
+  // earlier one in this order); workgroups are spread evenly over the 256
+  // compute units.
   const long long M = a.M, N = a.N;
   auto per_cu = [](long long tiles, long long outputs) { return (tiles + 255) / 256 * outputs; };
-  const long long nb4 = (N + kBN - 1) / kBN;
-  const long long big = nb4 * ((M + 255) / 256);
-  const long long nb8a = (N + 191) / 192, mb8a = (M + 255) / 256;
-  const long long nb8b = (N + 127) / 128, mb8b = (M + 319) / 320;
-  const long long nb8c = (N + 127) / 128, mb8c = (M + 127) / 128;
-  const long long c_big = per_cu(big, 128 * 256);
-  const long long c_8a = per_cu(nb8a * mb8a, 256 * 192);
-  const long long c_8b = per_cu(nb8b * mb8b, 320 * 128);
-  const long long c_8c = per_cu(nb8c * mb8c, 128 * 128);
-  const long long best = std::min(std::min(c_big, c_8a), std::min(c_8b, c_8c));
+  const long long nba = (N + 191) / 192, mba = (M + 255) / 256;
+  const long long nbb = (N + 127) / 128, mbb = (M + 319) / 320;
+  const long long nbc = (N + 127) / 128, mbc = (M + 127) / 128;
+  const long long ca = per_cu(nba * mba, 256 * 192);
+  const long long cb = per_cu(nbb * mbb, 320 * 128);
+  const long long cc = per_cu(nbc * mbc, 128 * 128);
   ProjArgs args = a;
   void* kargs[] = {&args};
-  if (c_big == best) {
-    args.xcd_fp = xcd_split(a, nb4, (M + 255) / 256);
-    return hipLaunchKernel(reinterpret_cast<const void*>(&proj_gemm_kernel<HEAD_OUT, 4>), dim3((unsigned)big),
-                           dim3(kThreads), kargs, 0, s);
+  if (ca <= cb && ca <= cc) {
+    args.xcd_fp = xcd_split(a, nba, mba);
+    return hipLaunchKernel(reinterpret_cast<const void*>(&proj_gemm_kernel<HEAD_OUT, 4, 2, 3>),
+                           dim3((unsigned)(nba * mba)), dim3(512), kargs, 0, s);
   }
-  if (c_8a == best) {
-    args.xcd_fp = xcd_split(a, nb8a, mb8a);
-    return hipLaunchKernel(reinterpret_cast<const void*>(&proj_gemm8_kernel<HEAD_OUT, 4, 2, 3>),
-                           dim3((unsigned)(nb8a * mb8a)), dim3(512), kargs, 0, s);
+  if (cb <= cc) {
+    args.xcd_fp = xcd_split(a, nbb, mbb);
+    return hipLaunchKernel(reinterpret_cast<const void*>(&proj_gemm_kernel<HEAD_OUT, 2, 5, 1>),
+                           dim3((unsigned)(nbb * mbb)), dim3(512), kargs, 0, s);
   }
-  if (c_8b == best) {
-    args.xcd_fp = xcd_split(a, nb8b, mb8b);
-    return hipLaunchKernel(reinterpret_cast<const void*>(&proj_gemm8_kernel<HEAD_OUT, 2, 5, 1>),
-                           dim3((unsigned)(nb8b * mb8b)), dim3(512), kargs, 0, s);
-  }
-  args.xcd_fp = xcd_split(a, nb8c, mb8c);
-  return hipLaunchKernel(reinterpret_cast<const void*>(&proj_gemm8_kernel<HEAD_OUT, 2, 2, 1>),
-                         dim3((unsigned)(nb8c * mb8c)), dim3(512), kargs, 0, s);
+  args.xcd_fp = xcd_split(a, nbc, mbc);
+  return hipLaunchKernel(reinterpret_cast<const void*>(&proj_gemm_kernel<HEAD_OUT, 2, 2, 1>),
+                         dim3((unsigned)(nbc * mbc)), dim3(512), kargs, 0, s);
 }
 
 }  // namespace

@@ -3,8 +3,8 @@ fp64 oracle on the same bf16 inputs, and of the whole multi-head sub-layer
 (projections + attention + output projection) built from the library's
 entry points.  Weights are seeded N(0, 1/d_model) draws (no trained weights
 are needed: the projections are plain linear maps).  The shapes reach every
-tile the launcher picks (128 x 256 on four waves; 256 x 192, 320 x 128 and
-128 x 128 on eight) and every tile order: XCD rectangles of all,
+tile the launcher picks (256 x 192, 320 x 128 and 128 x 128) and every tile
+order: XCD rectangles of all,
 1/2, 1/4 or 1/8 of the feature blocks, a last partial group of token blocks,
 and the plain order for grids the split does not divide.
 
