@@ -119,17 +119,22 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_short_kernel(FwdArg
   const int wave_tiles = (wave_end + kBN - 1) / kBN;
   const int wave_first = BAND ? max(0, qw0 - wl) / kBN : 0;
 
-  // ---- all loads at once.  Q: B operand of S^T = K Q^T, lane (ln, hh)
-  // holds Q[qi][16 s + 8 hh + 0..7], sign of scale folded in; c = |scale|
-  // log2(e), floored at 2^-100 (below that every weight is exactly 1.0f).
+  // ---- loads.  Every load is issued at once, in the order of use: each
+  // wave's 32 Q rows into its own 4 KB of s_o, then the K and V tiles,
+  // tile by tile.  The loop below waits for one tile at a time, so a
+  // wave's products on tile t overlap the landing of the later tiles (the
+  // whole chip loads at once here, and HBM is the limit of that burst).
+  // The fills are issued from inline assembly (lds_fill16_at), which the
+  // compiler does not track: the loop's vmcnt waits and barriers order them.
+  // Q: B operand of S^T = K Q^T, lane (ln, hh) holds Q[qi][16 s + 8 hh +
+  // 0..7], sign of scale folded in; c = |scale| log2(e), floored at 2^-100
+  // (below that every weight is exactly 1.0f).  Rows at or beyond n_q read
+  // as zeros through the descriptor's range check.
   const float c = fmaxf(fabsf(a.scale) * kLog2e, 0x1p-100f);
   const uint32_t sign = a.scale < 0.f ? 0x80008000u : 0u;
-  uint4 qraw[4];
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    qraw[s] = make_uint4(0, 0, 0, 0);
-    if (qi < a.n_q && wave_tiles > 0) qraw[s] = *reinterpret_cast<const uint4*>(Q + (size_t)qi * kHeadDim + 16 * s + 8 * hh);
-  }
+  const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<__bf16*>(Q), (short)0, (int)((uint32_t)a.n_q * kRowBytes), kBufferWord3);
+  const uint32_t qdst = (uint32_t)(uintptr_t)(lds_void_t*)(s_o + 256 * wave);
   // K and V tiles: one instruction of the workgroup covers 32 rows of a
   // tile.  Lane l of wave w writes chunk 64 w + l of that half, i.e. row
   // 32 half + 8 w + l / 8, position l % 8, which receives the row's chunk
@@ -141,6 +146,13 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_short_kernel(FwdArg
   const __amdgpu_buffer_rsrc_t rv =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(V), (short)0, (int)n_bytes, kBufferWord3);
   const int fpos = lane & 7;
+  if (n_tiles > 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 8 * i + (lane >> 3);
+      lds_fill16_at(rq, qdst + 1024u * i, (uint32_t)(qw0 + row) * kRowBytes + 16u * (uint32_t)(fpos ^ k_swz(row)));
+    }
+  }
   for (int t = 0; t < n_tiles; ++t) {
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
@@ -149,21 +161,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_short_kernel(FwdArg
       const uint32_t koff = base + 16u * (uint32_t)(fpos ^ k_swz(row));
       const uint32_t voff = base + 16u * (uint32_t)(fpos ^ (2 * (row & 3)));
       const uint32_t chunk0 = (uint32_t)t * kTileChunks + 256u * half + 64u * wave;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(s_k + chunk0), 16, koff, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(s_v + chunk0), 16, voff, 0, 0, 0);
+      lds_fill16_at(rk, (uint32_t)(uintptr_t)(lds_void_t*)(s_k + chunk0), koff);
+      lds_fill16_at(rv, (uint32_t)(uintptr_t)(lds_void_t*)(s_v + chunk0), voff);
     }
   }
   bf16x8 qf[4];
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    uint4 v = qraw[s];
-    v.x ^= sign;
-    v.y ^= sign;
-    v.z ^= sign;
-    v.w ^= sign;
-    qf[s] = __builtin_bit_cast(bf16x8, v);
-  }
-  __syncthreads();  // waits for every load, then publishes the LDS tiles
 
   f32x16 o0 = {}, o1 = {};  // O^T blocks: d 0..31 and d 32..63, column = query ln
   float mc = 0.f;           // pivot term of the exponent, m * c
@@ -177,7 +179,30 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_short_kernel(FwdArg
 
   const int g = lane >> 4;
   const int i16 = lane & 15;
-  for (int t = wave_first; t < wave_tiles; ++t) {
+  for (int t = 0; t < n_tiles; ++t) {
+    // Tile t has landed when at most the 4 fills of each later tile are in
+    // flight; the barrier publishes every wave's share of it.  Every wave
+    // passes every barrier, whether or not it needs the tile.
+    const int later = n_tiles - 1 - t;
+    if (later >= 3) __builtin_amdgcn_s_waitcnt(0x0070 | 12);  // vmcnt(12), lgkmcnt(0)
+    else if (later == 2) __builtin_amdgcn_s_waitcnt(0x0070 | 8);
+    else if (later == 1) __builtin_amdgcn_s_waitcnt(0x0070 | 4);
+    else __builtin_amdgcn_s_waitcnt(0x0070);
+    barrier_lds();
+    if (t == 0) {
+      // This wave's own Q rows, filled ahead of tile 0.
+      const lds_uint4* qs = (const lds_uint4*)(uintptr_t)qdst;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        uint4 v = __builtin_bit_cast(uint4, qs[ln * 8 + ((2 * s + hh) ^ k_swz(ln))]);
+        v.x ^= sign;
+        v.y ^= sign;
+        v.z ^= sign;
+        v.w ^= sign;
+        qf[s] = __builtin_bit_cast(bf16x8, v);
+      }
+    }
+    if (t < wave_first || t >= wave_tiles) continue;
     // S^T = K Q^T: lane (ln, hh) of key block kb reads K[64 t + 32 kb + ln]
     // [16 s + 8 hh + 0..7].
     const uint4* kt = s_k + t * kTileChunks;
