@@ -647,6 +647,333 @@ __global__ __launch_bounds__(kThreads, 3) void bwd_dq_kernel(BwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- dQ, paired
+// For long unmasked or causal rows: 8 waves, 128 queries (32 per wave, query
+// block qb = wave % 4), the two waves of a SIMD (qb and qb + 4) taking the
+// even and the odd key tiles of the same rows.  The waves of a pair
+// alternate roles each phase (the paired forward's structure): at phase p
+// the wave of parity p % 2 runs its matrix work -- dQ^T += K^T dS^T of tile
+// p - 2, then S^T and dP^T of tile p -- while its partner forms P and dS of
+// tile p - 1 on the vector unit; a workgroup barrier closes each phase.
+// K and V go through an 8-slot ring exactly as K and V do in the paired
+// forward (the fills of phase p are tile p + 5, into the slot of tile p - 3;
+// only vector-role waves fill in the loop).  Q, dO, L and D are staged in
+// slots the ring first fills at phase 0 or later.  At the end the odd-tile
+// wave hands its dQ to its partner through LDS, which adds and stores.
+constexpr int kPairThreads = 512;
+constexpr int kPairRing = 8;
+__shared__ Tile g_prk[kPairRing], g_prv[kPairRing];
+__shared__ float g_pld[256];  // L of the 128 queries, then D
+
+__device__ __forceinline__ uint32_t tile_addr(const Tile& t) {
+  return (uint32_t)(uintptr_t)(lds_void_t*)&t.c[0];
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kPairThreads, 1) void bwd_dq_pair_kernel(BwdArgs a) {
+  constexpr bool CAUSAL = MODE == kModeCausal;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int ln = lane & 31;
+  const int hh = lane >> 5;
+  const int qb = wave & 3;    // query block (waves qb and qb + 4 share a SIMD)
+  const int par = wave >> 2;  // parity of the key tiles this wave takes
+
+  const int n_qb = (a.n_q + 127) / 128;
+  int bh, qblk;
+  bh_block(blockIdx.x, n_qb, a.B * a.H, CAUSAL, bh, qblk);
+  const int b = bh / a.H;
+  const int q_len = __builtin_amdgcn_readfirstlane(a.q_lens ? clamp_len(a.q_lens[b], a.n_q) : a.n_q);
+  const int kv_lim = __builtin_amdgcn_readfirstlane(a.kv_lens ? clamp_len(a.kv_lens[b], a.n_k) : a.n_k);
+  const int q0 = qblk * 128;
+  const int qw0 = q0 + 32 * qb;
+
+  const __bf16* Q = static_cast<const __bf16*>(a.Q) + (size_t)bh * a.n_q * kHeadDim;
+  const __bf16* K = static_cast<const __bf16*>(a.K) + (size_t)bh * a.n_k * kHeadDim;
+  const __bf16* V = static_cast<const __bf16*>(a.V) + (size_t)bh * a.n_k * kHeadDim;
+  const __bf16* dO = static_cast<const __bf16*>(a.dO) + (size_t)bh * a.n_q * kHeadDim;
+
+  int end = kv_lim;  // keys the workgroup needs
+  if (CAUSAL) end = min(end, q0 + 128);
+  if (q0 >= q_len) end = 0;
+  const int n_tiles = max(0, (end + kTile - 1) / kTile);
+  int wave_end = end;  // keys this wave's rows need
+  if (CAUSAL) wave_end = min(wave_end, qw0 + 32);
+  if (qw0 >= q_len) wave_end = 0;
+  const int wave_tiles = max(0, (wave_end + kTile - 1) / kTile);
+
+  // Descriptors: K and V end at the workgroup's last key (fills past its
+  // last tile read zeros); Q and dO at q_len (padded rows read as zeros).
+  const uint32_t k_bytes = (uint32_t)max(0, end) * kRowBytes;
+  const __amdgpu_buffer_rsrc_t rk =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(K), (short)0, (int)k_bytes, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rv =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(V), (short)0, (int)k_bytes, kBufferWord3);
+  const uint32_t q_bytes = (uint32_t)max(0, q_len) * kRowBytes;
+  const __amdgpu_buffer_rsrc_t rq =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(Q), (short)0, (int)q_bytes, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rdo =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(dO), (short)0, (int)q_bytes, kBufferWord3);
+
+  const uint32_t sign = a.scale < 0.f ? 0x80008000u : 0u;
+  const float c = fmaxf(fabsf(a.scale) * kLog2e, 0x1p-100f);
+
+  // ---- fills.  Prologue: wave w fills rows 8 w .. 8 w + 7 of a tile (one
+  // instruction); loop: the vector-role wave of query block qb fills rows
+  // 16 qb .. 16 qb + 15 of K and of V (two instructions each).  Lane l
+  // writes position l % 8 of its row, which receives chunk (l % 8) ^ swz(row).
+  const int fpos = lane & 7;
+  auto fill_rows = [&](__amdgpu_buffer_rsrc_t r, const Tile& t, int r0, int row) __attribute__((always_inline)) {
+    lds_fill16_at(r, tile_addr(t) + 128u * (uint32_t)(row - (lane >> 3)),
+                  (uint32_t)(r0 + row) * kRowBytes + 16u * (uint32_t)(fpos ^ swz(row)));
+  };
+  auto fills = [&](auto j_tag, int p, auto vrole_tag) __attribute__((always_inline)) {
+    constexpr int J = decltype(j_tag)::value;
+    if constexpr (decltype(vrole_tag)::value) {
+      constexpr int SF = (J + 5) % kPairRing;
+      const int k0 = (p + 5) * kTile;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int row = 16 * qb + 8 * i + (lane >> 3);
+        fill_rows(rk, g_prk[SF], k0, row);
+        fill_rows(rv, g_prv[SF], k0, row);
+      }
+    }
+  };
+  auto sync = [&](auto vrole_tag) __attribute__((always_inline)) {
+    // As in the paired forward: after a vector phase the fills of that phase
+    // and of two phases earlier may fly; after a matrix phase vmcnt(6),
+    // which also lets the prologue's tile fills land tile by tile.
+    if constexpr (decltype(vrole_tag)::value) __builtin_amdgcn_s_waitcnt(0x0F70 | 8);
+    else __builtin_amdgcn_s_waitcnt(0x0F70 | 6);
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  bf16x8 qf[4], gf[4];
+  float lrow = INFINITY;
+  f32x16 dq[2] = {f32x16{}, f32x16{}};  // dQ^T [d block], column = query ln
+  f32x16 st[2], dpt[2];                 // S^T, dP^T of the current tile [key block]
+  uint32_t ps[16];                      // dS^T of the last tile, bf16 pairs
+  float dval = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) ps[i] = 0u;
+
+  // Matrix phase J (phase p = 8 k + J): dQ from tile p - 2's K (slot
+  // (J + 6) % 8) and the dS formed at phase p - 1, then S^T and dP^T of
+  // tile p (slot J).  It runs unconditionally: before a wave's first tile
+  // and past its last one dS is zero, so dQ gains exact zeros.
+  auto mphase = [&](auto j_tag) __attribute__((always_inline)) {
+    constexpr int J = decltype(j_tag)::value;
+    constexpr int SD = (J + kPairRing - 2) % kPairRing;
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bf16x8 sb = __builtin_bit_cast(bf16x8, make_uint4(ps[4 * j], ps[4 * j + 1], ps[4 * j + 2], ps[4 * j + 3]));
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+        dq[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(g_prk[SD], db, j, lane), sb, dq[db], 0, 0, 0);
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x16 sa = f32x16{}, pa = f32x16{};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(g_prk[J], 32 * kb + ln, s, hh), qf[s], sa, 0, 0, 0);
+        pa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(g_prv[J], 32 * kb + ln, s, hh), gf[s], pa, 0, 0, 0);
+      }
+      st[kb] = sa;
+      dpt[kb] = pa;
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
+  // Vector phase of tile t: P = exp2(s c - L) under the mask and dS = P (dP
+  // - D), packed to bf16 in the k order of the dQ product; zeros for a
+  // phase before this wave's first tile or past its last.
+  auto vphase = [&](int t) __attribute__((always_inline)) {
+    if (t >= 0 && t < wave_tiles) {
+      const int k0 = t * kTile;
+      const bool need_mask = (k0 + kTile > kv_lim) || (CAUSAL && k0 + kTile - 1 > qw0);
+      if (need_mask) {
+        int lnm = ln;
+        asm volatile("" : "+v"(lnm));
+        const int qi = qw0 + lnm;
+        int hi = kv_lim;
+        if (CAUSAL) hi = min(hi, qi + 1);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const int lim = hi - (k0 + 32 * kb + 4 * hh);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int off = 8 * (r >> 2) + (r & 3);
+            st[kb][r] = off < lim ? st[kb][r] : -INFINITY;
+          }
+        }
+      }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r2 = 0; r2 < 8; ++r2) {
+          float g[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int r = 2 * r2 + e;
+            const float x = fmaf(st[kb][r], c, -lrow);  // -inf for a masked key (c > 0)
+            const float p = __builtin_amdgcn_exp2f(x);
+            g[e] = p * (dpt[kb][r] - dval);
+          }
+          ps[8 * kb + r2] = pack_bf16x2(g[0], g[1]);
+        }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) asm volatile("v_mov_b32 %0, 0" : "=v"(ps[i]));
+    }
+  };
+  using J0 = std::integral_constant<int, 0>;
+  using J1 = std::integral_constant<int, 1>;
+  using J2 = std::integral_constant<int, 2>;
+  using J3 = std::integral_constant<int, 3>;
+  using J4 = std::integral_constant<int, 4>;
+  using J5 = std::integral_constant<int, 5>;
+  using J6 = std::integral_constant<int, 6>;
+  using J7 = std::integral_constant<int, 7>;
+
+  if (n_tiles > 0) {
+    // Prologue: Q rows 0-63 into K slot 5, 64-127 into K slot 6, dO rows
+    // 0-63 into K slot 7, 64-127 into V slot 5; L and D of the 128 rows
+    // (wave 0: lanes 0-31 L, lanes 32-63 D, 16 bytes each); then tiles 0-4
+    // as if filled at phases -5 .. -1.
+    {
+      const int row = 8 * wave + (lane >> 3);  // 0..63
+      fill_rows(rq, g_prk[5], q0, row);
+      fill_rows(rq, g_prk[6], q0 + 64, row);
+      fill_rows(rdo, g_prk[7], q0, row);
+      fill_rows(rdo, g_prv[5], q0 + 64, row);
+      if (wave == 0) {
+        const uint32_t bhp = (uint32_t)a.B * a.H * a.n_pad;
+        const __amdgpu_buffer_rsrc_t rld =
+            __builtin_amdgcn_make_buffer_rsrc(a.D, (short)0, (int)(bhp * 8u), kBufferWord3);
+        const uint32_t first = (uint32_t)bh * a.n_pad + (uint32_t)q0 + 4u * (uint32_t)(lane & 31);
+        const uint32_t off = (lane < 32 ? bhp + first : first) * 4u;
+        lds_fill16_at(rld, (uint32_t)(uintptr_t)(lds_void_t*)&g_pld[0], off);
+      }
+#pragma unroll
+      for (int t = 0; t < 5; ++t) {
+        fill_rows(rk, g_prk[t], t * kTile, row);
+        fill_rows(rv, g_prv[t], t * kTile, row);
+      }
+    }
+    // vmcnt(8): the staging fills and tile 0 have landed; after the
+    // barrier, every wave's share of them.
+    __builtin_amdgcn_s_waitcnt(0x0F70 | 8);
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    {
+      const Tile& tq = qb < 2 ? g_prk[5] : g_prk[6];
+      const Tile& tg = qb < 2 ? g_prk[7] : g_prv[5];
+      const int row = 32 * (qb & 1) + ln;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        uint4 v = __builtin_bit_cast(uint4, tq.c[row * 8 + ((2 * s + hh) ^ swz(row))]);
+        v.x ^= sign;
+        v.y ^= sign;
+        v.z ^= sign;
+        v.w ^= sign;
+        qf[s] = __builtin_bit_cast(bf16x8, v);
+        gf[s] = row_frag(tg, row, s, hh);
+      }
+      // Rows at or beyond q_len have L = +inf (P = 0) from the row kernel.
+      lrow = g_pld[32 * qb + ln];
+      dval = g_pld[128 + 32 * qb + ln];
+      if (qw0 + ln >= a.n_q) lrow = INFINITY;
+    }
+    // The first matrix phases of the two waves of a pair (p = 0, 1) read K
+    // slots 6 and 7 for dQ with dS = 0: their contents are finite (Q, dO
+    // staged there) or zero-filled tiles, so the products add exact zeros.
+    // vmcnt(8) keeps tile 0 landed; lgkmcnt(0): every staged value is in
+    // registers before the slots are refilled.
+    __builtin_amdgcn_s_waitcnt(0x0070 | 8);
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    const int n_phases = n_tiles + 2;
+    using M = std::false_type;
+    using F = std::true_type;
+    if (par == 0) {
+#pragma nounroll
+      for (int p = 0; p < n_phases; p += 8) {
+        mphase(J0());                            sync(M());
+        fills(J1(), p + 1, F()); vphase(p);       sync(F());
+        if (p + 2 >= n_phases) break;
+        mphase(J2());                            sync(M());
+        fills(J3(), p + 3, F()); vphase(p + 2);   sync(F());
+        if (p + 4 >= n_phases) break;
+        mphase(J4());                            sync(M());
+        fills(J5(), p + 5, F()); vphase(p + 4);   sync(F());
+        if (p + 6 >= n_phases) break;
+        mphase(J6());                            sync(M());
+        fills(J7(), p + 7, F()); vphase(p + 6);   sync(F());
+      }
+    } else {
+#pragma nounroll
+      for (int p = 0; p < n_phases; p += 8) {
+        fills(J0(), p, F());     vphase(p - 1);   sync(F());
+        mphase(J1());                            sync(M());
+        if (p + 2 >= n_phases) break;
+        fills(J2(), p + 2, F()); vphase(p + 1);   sync(F());
+        mphase(J3());                            sync(M());
+        if (p + 4 >= n_phases) break;
+        fills(J4(), p + 4, F()); vphase(p + 3);   sync(F());
+        mphase(J5());                            sync(M());
+        if (p + 6 >= n_phases) break;
+        fills(J6(), p + 6, F()); vphase(p + 5);   sync(F());
+        mphase(J7());                            sync(M());
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0), lgkmcnt(0): no fill lands in the hand-over area
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // ---- the odd-tile wave hands its dQ to its partner through the ring
+  // (32 floats per lane: 8 KB per wave, K slot qb), which adds and stores
+  // dQ = scale sum ds K (the sign of scale sits in Q').
+  float4* hand = reinterpret_cast<float4*>(&g_prk[qb].c[0]);
+  if (par == 1) {
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4)
+        hand[(4 * db + g4) * 64 + lane] = make_float4(dq[db][4 * g4], dq[db][4 * g4 + 1], dq[db][4 * g4 + 2], dq[db][4 * g4 + 3]);
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __syncthreads();
+  if (par == 0) {
+    int lnm = ln;
+    asm volatile("" : "+v"(lnm));
+    const int qi = qw0 + lnm;
+    if (qi < a.n_q) {
+      const bool row_live = qi < q_len;
+      __bf16* dQr = static_cast<__bf16*>(a.dQ) + ((size_t)bh * a.n_q + qi) * kHeadDim;
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const float4 o = hand[(4 * db + g4) * 64 + lane];
+          const int d = 32 * db + 8 * g4 + 4 * hh;
+          uint2 w;
+          w.x = row_live ? pack_bf16x2((dq[db][4 * g4] + o.x) * a.scale, (dq[db][4 * g4 + 1] + o.y) * a.scale) : 0u;
+          w.y = row_live ? pack_bf16x2((dq[db][4 * g4 + 2] + o.z) * a.scale, (dq[db][4 * g4 + 3] + o.w) * a.scale) : 0u;
+          *reinterpret_cast<uint2*>(dQr + d) = w;
+        }
+    }
+  }
+}
+
 const void* dkdv_fn(int mode) {
   return mode == kModeBand     ? reinterpret_cast<const void*>(&bwd_dkdv_kernel<kModeBand>)
          : mode == kModeCausal ? reinterpret_cast<const void*>(&bwd_dkdv_kernel<kModeCausal>)
@@ -679,6 +1006,14 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t s) {
   }
   if (a.n_q == 0) return hipSuccess;
   const int64_t blocks = (int64_t)((a.n_q + 127) / 128) * a.H * a.B;
+  // Long unmasked or causal rows: the paired dQ kernel (8 waves, one
+  // workgroup per CU); shorter ones and restricted attention keep the
+  // 4-wave kernel, three workgroups per CU.
+  if (mode != kModeBand && a.n_q >= 512) {
+    const void* fn = mode == kModeCausal ? reinterpret_cast<const void*>(&bwd_dq_pair_kernel<kModeCausal>)
+                                         : reinterpret_cast<const void*>(&bwd_dq_pair_kernel<kModeNone>);
+    return hipLaunchKernel(fn, dim3((unsigned)blocks), dim3(kPairThreads), kargs, 0, s);
+  }
   return hipLaunchKernel(dq_fn(mode), dim3((unsigned)blocks), dim3(kThreads), kargs, 0, s);
 }
 
