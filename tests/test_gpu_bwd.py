@@ -78,6 +78,10 @@ BWD = {
     "causal_2000_h8": (1, 8, 2000, 2000, 2, None, None, 0.125),
     "causal_kpad_1100": (2, 4, 1100, 1100, 3, [1100, 517], [1100, 517], 0.125),
     "none_700x1300": (1, 3, 700, 1300, 0, None, None, 0.125),
+    # the paired dQ kernel (n_q >= 512): sign of scale folded into Q, and
+    # key padding down to one key and to one 64-key tile
+    "negative_scale_causal_600": (1, 2, 600, 600, 2, None, None, -0.3),
+    "kpad_600": (3, 2, 600, 600, 1, [600, 333, 515], [600, 1, 64], 0.125),
 }
 
 
