@@ -374,12 +374,12 @@ FWD_MODES = {"0": "none", "1": "causal", "2": "band"}
 
 def _short_kernel(name: str) -> str:
     """attn_fwd_bf16[_pair|_short]_kernel<mode> and the backward's dK/dV and dQ
-    kernels (both dQ kernels) -> ..._kernel<none|causal|band>;
+    kernels (both kinds of each) -> ..._kernel<none|causal|band>;
     the projection kernel -> proj_gemm_kernel<head_out, tokens x features of
     its tile>; the bool-templated kernels -> <true|false>; other kernels of
     the library by their plain name."""
     import re
-    m = re.search(r"(attn_fwd_bf16(?:_pair|_short)?_kernel|bwd_dkdv_kernel|bwd_dq(?:_pair)?_kernel)(?:<|ILi)(\d)", name)
+    m = re.search(r"(attn_fwd_bf16(?:_pair|_short)?_kernel|bwd_dkdv(?:_pair)?_kernel|bwd_dq(?:_pair)?_kernel)(?:<|ILi)(\d)", name)
     if m:
         return f"{m.group(1)}<{FWD_MODES[m.group(2)]}>"
     m = re.search(r"proj_gemm_kernel<(true|false), (\d), (\d), (\d)>", name) or \
@@ -407,7 +407,7 @@ LEG_GRIDS = {("attn_fwd_bf16_short_kernel<none>", 65536): "encoder_base",
              ("attn_fwd_bf16_short_kernel<none>", 131072): "decoder_big (cross)",
              ("attn_fwd_bf16_band_kernel", 131072): "long_restricted",
              ("cache_append_kernel", 8192): "kv_append",
-             ("bwd_dkdv_kernel<causal>", 262144): "long_causal_bwd",
+             ("bwd_dkdv_pair_kernel<causal>", 262144): "long_causal_bwd",
              ("bwd_dq_pair_kernel<causal>", 524288): "long_causal_bwd",
              ("bwd_rowdot_kernel", 1048576): "long_causal_bwd",
              ("bwd_dkdv_kernel<none>", 65536): "encoder_base_bwd",

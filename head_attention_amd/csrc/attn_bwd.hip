@@ -33,6 +33,10 @@
 //                chain of products and exponentials.  No atomics: every
 //                output element has one owner, so the gradients are bitwise
 //                reproducible.
+// Long ranges (n_k >= 512 for dK/dV, n_q >= 512 for dQ; no mask or causal)
+// take the paired variants instead: 8-wave workgroups, one per CU, whose
+// two waves on each SIMD alternate matrix and vector phases, as in the
+// paired forward (each is described at its kernel).
 //
 // Streaming: tiles reach LDS by buffer loads that write LDS directly, into a
 // ring of three slots, two tiles ahead of use; one barrier per tile both
@@ -974,6 +978,315 @@ __global__ __launch_bounds__(kPairThreads, 1) void bwd_dq_pair_kernel(BwdArgs a)
   }
 }
 
+// ---------------------------------------------------------------- dK, dV, paired
+// For long unmasked or causal key ranges: 8 waves, 256 keys (32 per wave,
+// wave w owns keys kb0 + 32 w ..), the two waves of a SIMD (w and w + 4)
+// on different keys and the same query tiles, one phase apart.  Per tile a
+// wave runs a matrix phase -- dV^T += dO^T P and dK^T += Q^T dS of the
+// previous tile, then S and dP of this tile -- and a vector phase (P and dS
+// of this tile); while one wave of a SIMD issues its products the other
+// forms its weights, and a workgroup barrier closes each phase.  There is
+// no key split, so nothing is merged at the end.
+//
+// Query tiles (Q, dO, L, D) stream through a 4-slot ring: tile t sits in
+// slot t % 4.  Waves 0-3 run tile u's matrix phase at phase 2u and its
+// vector phase at 2u + 1; waves 4-7 one phase later.  Tile u is last read
+// at phase 2u + 3 (the products of waves 4-7), so at phase 2v the slot of
+// tile v - 2 takes tile v + 2, filled by waves 4-7 (their vector phase) and
+// first read at phase 2v + 4.  Only waves 4-7 fill in the loop.  The Q and
+// dO tiles of all four slots lie within 64 KB, so every fragment read is
+// one per-lane offset plus an immediate, whatever the slot.
+constexpr int kDkvRing = 4;
+constexpr int kDkvThreads = 512;
+struct QdoSlot {
+  Tile a, b;
+};
+__shared__ QdoSlot g_dr[kDkvRing];
+__shared__ float4 g_dld[kDkvRing][64];
+
+template <int MODE>
+__global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
+  constexpr bool CAUSAL = MODE == kModeCausal;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int ln = lane & 31;
+  const int hh = lane >> 5;
+  const int par = wave >> 2;   // 0: matrix phase first; 1: one phase later, fills
+  const int fw = wave & 3;     // this wave's quarter of a fill
+
+  const int n_kb = (a.n_k + 255) / 256;
+  int bh, kb;
+  bh_block(blockIdx.x, n_kb, a.B * a.H, false, bh, kb);
+  const int b = bh / a.H;
+  const int q_len = __builtin_amdgcn_readfirstlane(a.q_lens ? clamp_len(a.q_lens[b], a.n_q) : a.n_q);
+  const int kv_lim = __builtin_amdgcn_readfirstlane(a.kv_lens ? clamp_len(a.kv_lens[b], a.n_k) : a.n_k);
+  const int kb0 = kb * 256;
+  const int kw0 = kb0 + 32 * wave;  // this wave's first key
+  const int key = kw0 + ln;          // this lane's key
+
+  const __bf16* Q = static_cast<const __bf16*>(a.Q) + (size_t)bh * a.n_q * kHeadDim;
+  const __bf16* K = static_cast<const __bf16*>(a.K) + (size_t)bh * a.n_k * kHeadDim;
+  const __bf16* V = static_cast<const __bf16*>(a.V) + (size_t)bh * a.n_k * kHeadDim;
+  const __bf16* dO = static_cast<const __bf16*>(a.dO) + (size_t)bh * a.n_q * kHeadDim;
+  const __amdgpu_buffer_rsrc_t rq =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(Q), (short)0, (int)((uint32_t)q_len * kRowBytes), kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rdo =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(dO), (short)0, (int)((uint32_t)q_len * kRowBytes), kBufferWord3);
+  // L and D as in the 4-wave kernel: lanes 0..15 of the filling wave load 4
+  // rows of L each, lanes 16..31 4 rows of D.
+  const uint32_t bhp = (uint32_t)a.B * a.H * a.n_pad;
+  const __amdgpu_buffer_rsrc_t rld = __builtin_amdgcn_make_buffer_rsrc(a.D, (short)0, (int)(bhp * 8u), kBufferWord3);
+  const uint32_t ld_base = lane < 16   ? (bhp + (uint32_t)bh * a.n_pad + 4u * lane) * 4u
+                           : lane < 32 ? ((uint32_t)bh * a.n_pad + 4u * (lane - 16)) * 4u
+                                       : kOutOfRange;
+
+  const uint32_t sign = a.scale < 0.f ? 0x80008000u : 0u;
+  const float c = fmaxf(fabsf(a.scale) * kLog2e, 0x1p-100f);
+  bf16x8 kf[4], vf[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    uint4 kv = make_uint4(0, 0, 0, 0), vv = kv;
+    if (key < kv_lim) {
+      kv = *reinterpret_cast<const uint4*>(K + (size_t)key * kHeadDim + 16 * s + 8 * hh);
+      vv = *reinterpret_cast<const uint4*>(V + (size_t)key * kHeadDim + 16 * s + 8 * hh);
+    }
+    kv.x ^= sign;
+    kv.y ^= sign;
+    kv.z ^= sign;
+    kv.w ^= sign;
+    kf[s] = __builtin_bit_cast(bf16x8, kv);
+    vf[s] = __builtin_bit_cast(bf16x8, vv);
+  }
+
+  f32x16 dk[2] = {f32x16{}, f32x16{}};  // dK^T [d block], column = key ln
+  f32x16 dv[2] = {f32x16{}, f32x16{}};  // dV^T [d block]
+  const int q_start = CAUSAL ? kb0 : 0;
+  const int q_end = kb0 >= kv_lim ? 0 : q_len;
+  const int n_tiles = q_end > q_start ? (q_end - q_start + kTile - 1) / kTile : 0;
+
+  auto fill = [&](auto slot_tag, int u) __attribute__((always_inline)) {
+    constexpr int S = decltype(slot_tag)::value;
+    const int q0 = q_start + u * kTile;
+    fill_tile(g_dr[S].a, rq, q0, fw, lane);
+    fill_tile(g_dr[S].b, rdo, q0, fw, lane);
+    if (fw == 0) {
+      const uint32_t off = ld_base == kOutOfRange ? kOutOfRange : ld_base + (uint32_t)q0 * 4u;
+      lds_fill16_at(rld, (uint32_t)(uintptr_t)(lds_void_t*)&g_dld[S][0], off);
+    }
+  };
+  // Phase ends.  Waves 0-3 have nothing in flight in the loop; waves 4-7
+  // wait at the end of their matrix phases (phase 2t - 1) until tile t has
+  // landed: the tile filled after it (t + 1) may still fly, 4 loads (5 for
+  // the wave that also loads L and D).
+  auto sync = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto sync_fills = [&]() __attribute__((always_inline)) {
+    if (fw == 0) wait_barrier<5>();
+    else wait_barrier<4>();
+  };
+
+  f32x16 s_[2], dp[2];  // S and dP of the current tile [query block]
+  uint32_t pp[16], ps[16];  // P and dS of the previous tile, bf16 pairs
+
+  // Matrix phase of tile u in slot J: products of tile u - 1 (slot J - 1),
+  // then S and dP of tile u.  Every phase runs in full, also for a wave
+  // none of whose keys a tile's queries see (the mask zeroes its weights):
+  // the pair's partner and the barrier set the phase's length anyway, and
+  // values assigned on every path keep the compiler from holding the
+  // previous tile's S, dP, P and dS through the loop.  S and dP of tile
+  // n_tiles (the last phase) are computed and never used.
+  // The fragment reads go out one step ahead of the products that use them
+  // (sched_barrier fences), so at most two steps' fragments are in flight.
+  auto mphase = [&](auto j_tag, int u) __attribute__((always_inline)) {
+    constexpr int J = decltype(j_tag)::value;
+    constexpr int SP = (J + kDkvRing - 1) % kDkvRing;
+    __builtin_amdgcn_s_setprio(1);
+    if (u > 0) {
+      const Tile& tq = g_dr[SP].a;
+      const Tile& tdo = g_dr[SP].b;
+      bf16x8 fo[2][2], fq[2][2];  // [step parity][d block]: dO^T and Q^T
+      auto read = [&](int j) __attribute__((always_inline)) {
+#pragma unroll
+        for (int db = 0; db < 2; ++db) {
+          fo[j & 1][db] = tr_frag(tdo, db, j, lane);
+          fq[j & 1][db] = tr_frag(tq, db, j, lane);
+        }
+      };
+      read(0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (j < 3) read(j + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        const bf16x8 pb = __builtin_bit_cast(bf16x8, make_uint4(pp[4 * j], pp[4 * j + 1], pp[4 * j + 2], pp[4 * j + 3]));
+        const bf16x8 sb = __builtin_bit_cast(bf16x8, make_uint4(ps[4 * j], ps[4 * j + 1], ps[4 * j + 2], ps[4 * j + 3]));
+#pragma unroll
+        for (int db = 0; db < 2; ++db) {
+          dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fo[j & 1][db], pb, dv[db], 0, 0, 0);
+          dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fq[j & 1][db], sb, dk[db], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    {
+      const Tile& tq = g_dr[J].a;
+      const Tile& tdo = g_dr[J].b;
+      bf16x8 rq_[2][2], rd_[2][2];  // [step parity][d half of the step pair]
+      f32x16 sa[2] = {f32x16{}, f32x16{}}, pa[2] = {f32x16{}, f32x16{}};
+      // Step i = 2 qb + h covers query block qb, d steps 2h and 2h + 1.
+      auto read = [&](int i) __attribute__((always_inline)) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          rq_[i & 1][e] = row_frag(tq, 32 * (i >> 1) + ln, 2 * (i & 1) + e, hh);
+          rd_[i & 1][e] = row_frag(tdo, 32 * (i >> 1) + ln, 2 * (i & 1) + e, hh);
+        }
+      };
+      read(0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (i < 3) read(i + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        const int qb = i >> 1;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int st = 2 * (i & 1) + e;
+          sa[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rq_[i & 1][e], kf[st], sa[qb], 0, 0, 0);
+          pa[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rd_[i & 1][e], vf[st], pa[qb], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      s_[0] = sa[0];
+      s_[1] = sa[1];
+      dp[0] = pa[0];
+      dp[1] = pa[1];
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
+  // Vector phase of tile u: P = exp2(s c - L) under the mask, dS = P (dP -
+  // D), both packed to bf16 in the k order of the next phase's products.
+  auto vphase = [&](auto j_tag, int u) __attribute__((always_inline)) {
+    constexpr int J = decltype(j_tag)::value;
+    const int q0 = q_start + u * kTile;
+    if ((kw0 + 32 > kv_lim) || (CAUSAL && q0 < kw0 + 32)) {
+      asm volatile("");
+      int ln_m = ln;
+      asm volatile("" : "+v"(ln_m));
+      const int key_m = kw0 + ln_m;
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int qi = q0 + 32 * qb + 8 * (r >> 2) + 4 * hh + (r & 3);
+          bool ok = key_m < kv_lim;
+          if (CAUSAL) ok = ok && key_m <= qi;
+          s_[qb][r] = ok ? s_[qb][r] : -INFINITY;
+        }
+    }
+    const float* tld = reinterpret_cast<const float*>(&g_dld[J][0]);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int ql = 32 * qb + 8 * gq + 4 * hh;
+        const float4 l4 = *reinterpret_cast<const float4*>(&tld[ql]);
+        const float4 d4 = *reinterpret_cast<const float4*>(&tld[kTile + ql]);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+        const float dvv[4] = {d4.x, d4.y, d4.z, d4.w};
+        float p[4], g[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * gq + e;
+          const float x = fmaf(s_[qb][r], c, -lv[e]);
+          p[e] = __builtin_amdgcn_exp2f(x);
+          g[e] = p[e] * (dp[qb][r] - dvv[e]);
+        }
+        pp[8 * qb + 2 * gq] = pack_bf16x2(p[0], p[1]);
+        pp[8 * qb + 2 * gq + 1] = pack_bf16x2(p[2], p[3]);
+        ps[8 * qb + 2 * gq] = pack_bf16x2(g[0], g[1]);
+        ps[8 * qb + 2 * gq + 1] = pack_bf16x2(g[2], g[3]);
+      }
+    }
+  };
+  using R0 = std::integral_constant<int, 0>;
+  using R1 = std::integral_constant<int, 1>;
+  using R2 = std::integral_constant<int, 2>;
+  using R3 = std::integral_constant<int, 3>;
+
+  if (n_tiles > 0) {
+    // Prologue: tiles 0 and 1 from waves 0-3; they and the K and V
+    // fragments land before the first phase.
+    if (par == 0) {
+      fill(R0(), 0);
+      fill(R1(), 1);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0), lgkmcnt(0)
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    // Phases 0 .. 2 n_tiles + 1.  Waves 0-3: matrix phase of tile u at 2u
+    // (u = 0 .. n_tiles, the last one only the products of tile n_tiles -
+    // 1), vector phase at 2u + 1, and one closing barrier.  Waves 4-7: at
+    // 2u the fill of tile u + 2 and the vector phase of tile u - 1, at
+    // 2u + 1 the matrix phase of tile u.
+    if (par == 0) {
+#pragma nounroll
+      for (int u = 0;; u += kDkvRing) {
+        mphase(R0(), u);     sync(); if (u >= n_tiles) break;
+        vphase(R0(), u);     sync();
+        mphase(R1(), u + 1); sync(); if (u + 1 >= n_tiles) break;
+        vphase(R1(), u + 1); sync();
+        mphase(R2(), u + 2); sync(); if (u + 2 >= n_tiles) break;
+        vphase(R2(), u + 2); sync();
+        mphase(R3(), u + 3); sync(); if (u + 3 >= n_tiles) break;
+        vphase(R3(), u + 3); sync();
+      }
+      sync();
+    } else {
+      auto fill_ahead = [&](auto slot_tag, int u) __attribute__((always_inline)) {
+        if (u + 2 < n_tiles) fill(slot_tag, u + 2);
+      };
+#pragma nounroll
+      for (int u = 0;; u += kDkvRing) {
+        fill_ahead(R2(), u);     if (u > 0) vphase(R3(), u - 1); sync();
+        mphase(R0(), u);         sync_fills(); if (u >= n_tiles) break;
+        fill_ahead(R3(), u + 1); vphase(R0(), u);     sync();
+        mphase(R1(), u + 1);     sync_fills(); if (u + 1 >= n_tiles) break;
+        fill_ahead(R0(), u + 2); vphase(R1(), u + 1); sync();
+        mphase(R2(), u + 2);     sync_fills(); if (u + 2 >= n_tiles) break;
+        fill_ahead(R1(), u + 3); vphase(R2(), u + 2); sync();
+        mphase(R3(), u + 3);     sync_fills(); if (u + 3 >= n_tiles) break;
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0): no fill in flight at exit
+  }
+
+  // Store, as in the 4-wave kernel: dK = scale sum ds Q (sign in K').
+  int ln_s = ln;
+  asm volatile("" : "+v"(ln_s));
+  const int key_s = kw0 + ln_s;
+  if (key_s < a.n_k) {
+    __bf16* dKr = static_cast<__bf16*>(a.dK) + ((size_t)bh * a.n_k + key_s) * kHeadDim;
+    __bf16* dVr = static_cast<__bf16*>(a.dV) + ((size_t)bh * a.n_k + key_s) * kHeadDim;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) {
+        const int d = 32 * db + 8 * gg + 4 * hh;
+        uint2 wk, wv;
+        wk.x = pack_bf16x2(dk[db][4 * gg] * a.scale, dk[db][4 * gg + 1] * a.scale);
+        wk.y = pack_bf16x2(dk[db][4 * gg + 2] * a.scale, dk[db][4 * gg + 3] * a.scale);
+        wv.x = pack_bf16x2(dv[db][4 * gg], dv[db][4 * gg + 1]);
+        wv.y = pack_bf16x2(dv[db][4 * gg + 2], dv[db][4 * gg + 3]);
+        *reinterpret_cast<uint2*>(dKr + d) = wk;
+        *reinterpret_cast<uint2*>(dVr + d) = wv;
+      }
+  }
+}
+
 const void* dkdv_fn(int mode) {
   return mode == kModeBand     ? reinterpret_cast<const void*>(&bwd_dkdv_kernel<kModeBand>)
          : mode == kModeCausal ? reinterpret_cast<const void*>(&bwd_dkdv_kernel<kModeCausal>)
@@ -1001,7 +1314,16 @@ hipError_t launch_backward(const BwdArgs& a, hipStream_t s) {
   }
   if (a.n_k > 0) {
     const int64_t blocks = (int64_t)((a.n_k + 127) / 128) * a.H * a.B;
-    e = hipLaunchKernel(dkdv_fn(mode), dim3((unsigned)blocks), dim3(kThreads), kargs, 0, s);
+    // Long unmasked or causal key ranges: the paired dK/dV kernel (8 waves,
+    // 256 keys, one workgroup per CU).
+    if (mode != kModeBand && a.n_k >= 512) {
+      const void* fn = mode == kModeCausal ? reinterpret_cast<const void*>(&bwd_dkdv_pair_kernel<kModeCausal>)
+                                           : reinterpret_cast<const void*>(&bwd_dkdv_pair_kernel<kModeNone>);
+      e = hipLaunchKernel(fn, dim3((unsigned)((int64_t)((a.n_k + 255) / 256) * a.H * a.B)), dim3(kDkvThreads), kargs,
+                          0, s);
+    } else {
+      e = hipLaunchKernel(dkdv_fn(mode), dim3((unsigned)blocks), dim3(kThreads), kargs, 0, s);
+    }
     if (e != hipSuccess) return e;
   }
   if (a.n_q == 0) return hipSuccess;
