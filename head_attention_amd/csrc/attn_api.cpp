@@ -309,9 +309,10 @@ attn_status attn_output_projection(const void* O, const void* Wo, attn_layout L,
 
 size_t attn_backward_workspace_bytes(attn_layout L) {
   if (check_layout(L) != ATTN_OK) return 0;
-  // Two fp32 values per query row, rows rounded up to a multiple of 64.
+  // Per query row, rows rounded up to a multiple of 64: two fp32 values
+  // and 16 bytes of bf16 parts.
   const size_t n_pad = ((size_t)L.n_q + 63) / 64 * 64;
-  return (size_t)L.B * L.h * n_pad * 2 * sizeof(float);
+  return (size_t)L.B * L.h * n_pad * (2 * sizeof(float) + 16);
 }
 
 namespace {
@@ -367,6 +368,7 @@ attn_status backward_impl(const void* Q, const void* K, const void* V, const voi
   a.lse = LSE;
   a.D = static_cast<float*>(workspace);
   a.L = a.D + (size_t)L.B * L.h * n_pad;
+  a.LD16 = reinterpret_cast<uint4*>(a.L + (size_t)L.B * L.h * n_pad);  // 16-byte aligned: n_pad % 64 == 0
   a.dQ = dQ;
   a.dK = dK;
   a.dV = dV;

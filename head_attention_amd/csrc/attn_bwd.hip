@@ -186,6 +186,16 @@ using Slot0 = std::integral_constant<int, 0>;
 using Slot1 = std::integral_constant<int, 1>;
 using Slot2 = std::integral_constant<int, 2>;
 
+// x as hi + mid + lo, each rounded to the nearest bf16 (the sum is x to
+// within 2^-24 |x|, about fp32's precision), packed as (hi, mid), (lo, 0).
+__device__ __forceinline__ void split3_bf16(float x, uint32_t& w01, uint32_t& w23) {
+  const uint32_t ph = pack_bf16x2(x, 0.f);
+  const float r = x - __uint_as_float(ph << 16);
+  const uint32_t pm = pack_bf16x2(r, 0.f);
+  w01 = (ph & 0xFFFFu) | (pm << 16);
+  w23 = pack_bf16x2(r - __uint_as_float(pm << 16), 0.f);
+}
+
 // ---------------------------------------------------------------- D, L = rowdot
 __global__ __launch_bounds__(kThreads) void bwd_rowdot_kernel(BwdArgs a) {
   // 8 lanes per row, 16 bytes each: 32 rows per workgroup, over the padded
@@ -222,6 +232,15 @@ __global__ __launch_bounds__(kThreads) void bwd_rowdot_kernel(BwdArgs a) {
     }
     a.D[row] = valid ? acc : 0.f;
     a.L[row] = l;
+    // -L/c and -D as sums of three bf16 parts (for the paired dK/dV
+    // kernel, which adds them inside its S and dP products); a row with L =
+    // +inf gets -2^100, finite, so that its products with zero stay zero.
+    const float c = fmaxf(fabsf(a.scale) * kLog2e, 0x1p-100f);
+    const float lc = l == INFINITY ? -0x1p100f : -(l / c);
+    uint32_t w[4];
+    split3_bf16(lc, w[0], w[1]);
+    split3_bf16(valid ? -acc : 0.f, w[2], w[3]);
+    a.LD16[row] = make_uint4(w[0], w[1], w[2], w[3]);
   }
 }
 
@@ -1002,7 +1021,7 @@ struct QdoSlot {
   Tile a, b;
 };
 __shared__ QdoSlot g_dr[kDkvRing];
-__shared__ float4 g_dld[kDkvRing][64];
+__shared__ uint4 g_aug[kDkvRing][64];  // per tile row: -L/c and -D parts
 
 template <int MODE>
 __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_pair_kernel(BwdArgs a) {
@@ -1033,13 +1052,11 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_pair_kernel(BwdArgs a
       __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(Q), (short)0, (int)((uint32_t)q_len * kRowBytes), kBufferWord3);
   const __amdgpu_buffer_rsrc_t rdo =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(dO), (short)0, (int)((uint32_t)q_len * kRowBytes), kBufferWord3);
-  // L and D as in the 4-wave kernel: lanes 0..15 of the filling wave load 4
-  // rows of L each, lanes 16..31 4 rows of D.
+  // The rows' -L/c and -D parts (16 bytes a row, from the row kernel):
+  // lane l of the filling wave loads row q0 + l of a tile.
   const uint32_t bhp = (uint32_t)a.B * a.H * a.n_pad;
-  const __amdgpu_buffer_rsrc_t rld = __builtin_amdgcn_make_buffer_rsrc(a.D, (short)0, (int)(bhp * 8u), kBufferWord3);
-  const uint32_t ld_base = lane < 16   ? (bhp + (uint32_t)bh * a.n_pad + 4u * lane) * 4u
-                           : lane < 32 ? ((uint32_t)bh * a.n_pad + 4u * (lane - 16)) * 4u
-                                       : kOutOfRange;
+  const __amdgpu_buffer_rsrc_t raug = __builtin_amdgcn_make_buffer_rsrc(a.LD16, (short)0, (int)(bhp * 16u), kBufferWord3);
+  const uint32_t aug_base = ((uint32_t)bh * a.n_pad + (uint32_t)lane) * 16u;
 
   const uint32_t sign = a.scale < 0.f ? 0x80008000u : 0u;
   const float c = fmaxf(fabsf(a.scale) * kLog2e, 0x1p-100f);
@@ -1070,10 +1087,7 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_pair_kernel(BwdArgs a
     const int q0 = q_start + u * kTile;
     fill_tile(g_dr[S].a, rq, q0, fw, lane);
     fill_tile(g_dr[S].b, rdo, q0, fw, lane);
-    if (fw == 0) {
-      const uint32_t off = ld_base == kOutOfRange ? kOutOfRange : ld_base + (uint32_t)q0 * 4u;
-      lds_fill16_at(rld, (uint32_t)(uintptr_t)(lds_void_t*)&g_dld[S][0], off);
-    }
+    if (fw == 0) lds_fill16_at(raug, (uint32_t)(uintptr_t)(lds_void_t*)&g_aug[S][0], aug_base + (uint32_t)q0 * 16u);
   };
   // Phase ends.  Waves 0-3 have nothing in flight in the loop; waves 4-7
   // wait at the end of their matrix phases (phase 2t - 1) until tile t has
@@ -1106,6 +1120,11 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_pair_kernel(BwdArgs a
     constexpr int J = decltype(j_tag)::value;
     constexpr int SP = (J + kDkvRing - 1) % kDkvRing;
     __builtin_amdgcn_s_setprio(1);
+    // The rows' -L/c and -D parts of tile u, read first: a row's 8 parts
+    // (both lane halves read them).
+    bf16x8 ag[2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) ag[qb] = __builtin_bit_cast(bf16x8, g_aug[J][32 * qb + ln]);
     if (u > 0) {
       const Tile& tq = g_dr[SP].a;
       const Tile& tdo = g_dr[SP].b;
@@ -1136,7 +1155,24 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_pair_kernel(BwdArgs a
       const Tile& tq = g_dr[J].a;
       const Tile& tdo = g_dr[J].b;
       bf16x8 rq_[2][2], rd_[2][2];  // [step parity][d half of the step pair]
-      f32x16 sa[2] = {f32x16{}, f32x16{}}, pa[2] = {f32x16{}, f32x16{}};
+      // A first k step of 16 puts the rows' -L/c into S and -D into dP:
+      // A operand the rows' parts, B operand ones against the L parts (or
+      // the D parts) in the first lane half and zeros in the second (ones
+      // from an opaque copy of the lane half, so that the compiler builds
+      // them here rather than holding them through the loop).
+      f32x16 sa[2], pa[2];
+      {
+        int hh_c = hh;
+        asm volatile("" : "+v"(hh_c));
+        const uint32_t e3 = hh_c ? 0u : 0x3F803F80u, e1 = hh_c ? 0u : 0x3F80u;  // bf16 1.0 pairs
+        const bf16x8 one_l = __builtin_bit_cast(bf16x8, make_uint4(e3, e1, 0u, 0u));
+        const bf16x8 one_d = __builtin_bit_cast(bf16x8, make_uint4(0u, 0u, e3, e1));
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          sa[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ag[qb], one_l, f32x16{}, 0, 0, 0);
+          pa[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ag[qb], one_d, f32x16{}, 0, 0, 0);
+        }
+      }
       // Step i = 2 qb + h covers query block qb, d steps 2h and 2h + 1.
       auto read = [&](int i) __attribute__((always_inline)) {
 #pragma unroll
@@ -1167,7 +1203,8 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_pair_kernel(BwdArgs a
     __builtin_amdgcn_s_setprio(0);
   };
   // Vector phase of tile u: P = exp2(s c - L) under the mask, dS = P (dP -
-  // D), both packed to bf16 in the k order of the next phase's products.
+  // D), both packed to bf16 in the k order of the next phase's products
+  // (s and dP arrive with -L/c and -D added by the matrix phase).
   auto vphase = [&](auto j_tag, int u) __attribute__((always_inline)) {
     constexpr int J = decltype(j_tag)::value;
     const int q0 = q_start + u * kTile;
@@ -1186,23 +1223,16 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_pair_kernel(BwdArgs a
           s_[qb][r] = ok ? s_[qb][r] : -INFINITY;
         }
     }
-    const float* tld = reinterpret_cast<const float*>(&g_dld[J][0]);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
-        const int ql = 32 * qb + 8 * gq + 4 * hh;
-        const float4 l4 = *reinterpret_cast<const float4*>(&tld[ql]);
-        const float4 d4 = *reinterpret_cast<const float4*>(&tld[kTile + ql]);
-        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-        const float dvv[4] = {d4.x, d4.y, d4.z, d4.w};
         float p[4], g[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * gq + e;
-          const float x = fmaf(s_[qb][r], c, -lv[e]);
-          p[e] = __builtin_amdgcn_exp2f(x);
-          g[e] = p[e] * (dp[qb][r] - dvv[e]);
+          p[e] = __builtin_amdgcn_exp2f(s_[qb][r] * c);  // -inf for a masked key (c > 0)
+          g[e] = p[e] * dp[qb][r];
         }
         pp[8 * qb + 2 * gq] = pack_bf16x2(p[0], p[1]);
         pp[8 * qb + 2 * gq + 1] = pack_bf16x2(p[2], p[3]);

@@ -134,6 +134,8 @@ struct BwdArgs {
   const float* lse;        // [B*H*n_q] natural-log row normalisers from the forward
   float* D;                // workspace [B*H*n_pad]: dO . O per row (0 for padded rows)
   float* L;                // workspace [B*H*n_pad]: lse log2(e) per row (+inf for padded rows)
+  uint4* LD16;             // workspace [B*H*n_pad]: per row 8 bf16, -L/c as the sum of three parts, 0,
+                           // -D as the sum of three parts, 0 (c = |scale| log2 e; -2^100 for +inf L)
   void* dQ;
   void* dK;
   void* dV;

@@ -291,8 +291,10 @@ attn_status attn_output_projection(const void* O, const void* Wo, attn_layout la
  *   dK, dV          [B, h, n_k, 64] bf16, written (excluded keys as 0)
  *   workspace       device buffer of at least attn_backward_workspace_bytes
  *                   (per query row, padded to a multiple of 64 rows: fp32
- *                   dO . O, then fp32 LSE log2(e)); contents on entry do not
- *                   matter; calls that share it must be ordered (same stream)
+ *                   dO . O, then fp32 LSE log2(e), then 8 bf16 holding
+ *                   -LSE / |scale| and -dO . O, each as a sum of three bf16
+ *                   parts); contents on entry do not matter; calls that share
+ *                   it must be ordered (same stream)
  *   stream          hipStream_t or NULL.
  * Three kernels on `stream` (row dots, key-major dK/dV, query-major dQ); no
  * atomics, so the results are bitwise reproducible.  bf16 products, fp32
@@ -322,9 +324,10 @@ attn_status attn_backward_restricted(const void* Q, const void* K, const void* V
                                      void* dV, void* workspace, size_t workspace_bytes,
                                      void* stream);
 
-/* Bytes of workspace attn_backward and attn_backward_restricted need: two
- * fp32 values per query row, rows of each (b, h) rounded up to a multiple
- * of 64; 0 if the layout is invalid.  Pure host arithmetic. */
+/* Bytes of workspace attn_backward and attn_backward_restricted need: 24
+ * bytes per query row (two fp32 values and 16 bytes of bf16 parts), rows of
+ * each (b, h) rounded up to a multiple of 64; 0 if the layout is invalid.
+ * Pure host arithmetic. */
 size_t attn_backward_workspace_bytes(attn_layout layout);
 
 /* Bytes of fp32 split partials attn_decode needs for this cache layout; 0 if

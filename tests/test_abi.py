@@ -207,8 +207,8 @@ def test_forward_lse_and_backward_validation():
     assert L.attn_forward_lse(None, None, None, attn_layout(0, 3, 16, 16, 64, BF16), 0, None, None, 0.125,
                               None, None, None) == OK
     # per (b, h): n_q rounded up to 64 rows, two fp32 values per row
-    assert L.attn_backward_workspace_bytes(lay_) == 2 * 3 * 64 * 8
-    assert L.attn_backward_workspace_bytes(attn_layout(1, 2, 130, 16, 64, BF16)) == 2 * 192 * 8
+    assert L.attn_backward_workspace_bytes(lay_) == 2 * 3 * 64 * 24
+    assert L.attn_backward_workspace_bytes(attn_layout(1, 2, 130, 16, 64, BF16)) == 2 * 192 * 24
     assert L.attn_backward_workspace_bytes(attn_layout(1, 2, 0, 16, 64, BF16)) == 0
     assert L.attn_backward_workspace_bytes(attn_layout(2, 3, 16, 16, 32, BF16)) == 0
 
