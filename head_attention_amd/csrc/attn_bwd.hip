@@ -1007,9 +1007,10 @@ __global__ __launch_bounds__(kPairThreads, 1) void bwd_dq_pair_kernel(BwdArgs a)
 // forms its weights, and a workgroup barrier closes each phase.  There is
 // no key split, so nothing is merged at the end.
 //
-// Query tiles (Q, dO, L, D) stream through a 4-slot ring: tile t sits in
-// slot t % 4.  Waves 0-3 run tile u's matrix phase at phase 2u and its
-// vector phase at 2u + 1; waves 4-7 one phase later.  Tile u is last read
+// Query tiles (Q, dO, and the rows' -L/c and -D parts) stream through a
+// 4-slot ring: tile t sits in slot t % 4.  Waves 0-3 run tile u's matrix
+// phase at phase 2u and its vector phase at 2u + 1; waves 4-7 one phase
+// later.  Tile u is last read
 // at phase 2u + 3 (the products of waves 4-7), so at phase 2v the slot of
 // tile v - 2 takes tile v + 2, filled by waves 4-7 (their vector phase) and
 // first read at phase 2v + 4.  Only waves 4-7 fill in the loop.  The Q and
@@ -1092,7 +1093,7 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkdv_pair_kernel(BwdArgs a
   // Phase ends.  Waves 0-3 have nothing in flight in the loop; waves 4-7
   // wait at the end of their matrix phases (phase 2t - 1) until tile t has
   // landed: the tile filled after it (t + 1) may still fly, 4 loads (5 for
-  // the wave that also loads L and D).
+  // the wave that also loads the rows' parts).
   auto sync = [&]() __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
     __builtin_amdgcn_sched_barrier(0);
