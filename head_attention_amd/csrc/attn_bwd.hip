@@ -687,6 +687,7 @@ constexpr int kPairThreads = 512;
 constexpr int kPairRing = 8;
 __shared__ Tile g_prk[kPairRing], g_prv[kPairRing];
 __shared__ float g_pld[256];  // L of the 128 queries, then D
+__shared__ uint4 g_pag[128];  // the 128 queries' -L/c and -D bf16 parts
 
 __device__ __forceinline__ uint32_t tile_addr(const Tile& t) {
   return (uint32_t)(uintptr_t)(lds_void_t*)&t.c[0];
@@ -780,7 +781,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void bwd_dq_pair_kernel(BwdArgs a)
   f32x16 dq[2] = {f32x16{}, f32x16{}};  // dQ^T [d block], column = query ln
   f32x16 st[2], dpt[2];                 // S^T, dP^T of the current tile [key block]
   uint32_t ps[16];                      // dS^T of the last tile, bf16 pairs
-  float dval = 0.f;
+  bf16x8 dparts;  // this lane's query row: -L/c and -D as bf16 parts (k slots 0-7)
 #pragma unroll
   for (int i = 0; i < 16; ++i) ps[i] = 0u;
 
@@ -810,11 +811,24 @@ __global__ __launch_bounds__(kPairThreads, 1) void bwd_dq_pair_kernel(BwdArgs a)
       st[kb] = sa;
       dpt[kb] = pa;
     }
+    // -D of each query into dP^T: one more k step, A ones against the three
+    // D parts in the first lane half (zeros in the second), B the queries'
+    // parts (ones from an opaque copy of the lane half, built here rather
+    // than held through the loop).
+    {
+      int hh_c = hh;
+      asm volatile("" : "+v"(hh_c));
+      const uint32_t e3 = hh_c ? 0u : 0x3F803F80u, e1 = hh_c ? 0u : 0x3F80u;  // bf16 1.0 pairs
+      const bf16x8 one_d = __builtin_bit_cast(bf16x8, make_uint4(0u, 0u, e3, e1));
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) dpt[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(one_d, dparts, dpt[kb], 0, 0, 0);
+    }
     __builtin_amdgcn_s_setprio(0);
   };
   // Vector phase of tile t: P = exp2(s c - L) under the mask and dS = P (dP
-  // - D), packed to bf16 in the k order of the dQ product; zeros for a
-  // phase before this wave's first tile or past its last.
+  // - D) (dP arrives with -D added), packed to bf16 in the k order of the dQ
+  // product; zeros for a phase before this wave's first tile or past its
+  // last.
   auto vphase = [&](int t) __attribute__((always_inline)) {
     if (t >= 0 && t < wave_tiles) {
       const int k0 = t * kTile;
@@ -845,7 +859,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void bwd_dq_pair_kernel(BwdArgs a)
             const int r = 2 * r2 + e;
             const float x = fmaf(st[kb][r], c, -lrow);  // -inf for a masked key (c > 0)
             const float p = __builtin_amdgcn_exp2f(x);
-            g[e] = p * (dpt[kb][r] - dval);
+            g[e] = p * dpt[kb][r];
           }
           ps[8 * kb + r2] = pack_bf16x2(g[0], g[1]);
         }
@@ -866,8 +880,9 @@ __global__ __launch_bounds__(kPairThreads, 1) void bwd_dq_pair_kernel(BwdArgs a)
   if (n_tiles > 0) {
     // Prologue: Q rows 0-63 into K slot 5, 64-127 into K slot 6, dO rows
     // 0-63 into K slot 7, 64-127 into V slot 5; L and D of the 128 rows
-    // (wave 0: lanes 0-31 L, lanes 32-63 D, 16 bytes each); then tiles 0-4
-    // as if filled at phases -5 .. -1.
+    // (wave 0: lanes 0-31 L, lanes 32-63 D, 16 bytes each) and their bf16
+    // parts (wave 0, two loads); then tiles 0-4 as if filled at phases -5
+    // .. -1.
     {
       const int row = 8 * wave + (lane >> 3);  // 0..63
       fill_rows(rq, g_prk[5], q0, row);
@@ -881,6 +896,12 @@ __global__ __launch_bounds__(kPairThreads, 1) void bwd_dq_pair_kernel(BwdArgs a)
         const uint32_t first = (uint32_t)bh * a.n_pad + (uint32_t)q0 + 4u * (uint32_t)(lane & 31);
         const uint32_t off = (lane < 32 ? bhp + first : first) * 4u;
         lds_fill16_at(rld, (uint32_t)(uintptr_t)(lds_void_t*)&g_pld[0], off);
+        // The 128 rows' bf16 parts (16 bytes a row), two loads.
+        const __amdgpu_buffer_rsrc_t rag =
+            __builtin_amdgcn_make_buffer_rsrc(a.LD16, (short)0, (int)(bhp * 16u), kBufferWord3);
+        const uint32_t ag0 = ((uint32_t)bh * a.n_pad + (uint32_t)q0 + (uint32_t)lane) * 16u;
+        lds_fill16_at(rag, (uint32_t)(uintptr_t)(lds_void_t*)&g_pag[0], ag0);
+        lds_fill16_at(rag, (uint32_t)(uintptr_t)(lds_void_t*)&g_pag[64], ag0 + 1024u);
       }
 #pragma unroll
       for (int t = 0; t < 5; ++t) {
@@ -910,7 +931,7 @@ __global__ __launch_bounds__(kPairThreads, 1) void bwd_dq_pair_kernel(BwdArgs a)
       }
       // Rows at or beyond q_len have L = +inf (P = 0) from the row kernel.
       lrow = g_pld[32 * qb + ln];
-      dval = g_pld[128 + 32 * qb + ln];
+      dparts = __builtin_bit_cast(bf16x8, g_pag[32 * qb + ln]);
       if (qw0 + ln >= a.n_q) lrow = INFINITY;
     }
     // The first matrix phases of the two waves of a pair (p = 0, 1) read K
